@@ -1,0 +1,208 @@
+"""Seeded synthetic decode workloads (inputs only; no attention arithmetic).
+
+This module is the one piece shared by the GPU tests, the benchmark and the
+fp64 oracle's tests: it draws the inputs both sides receive.  It computes
+nothing of the method itself.
+
+The workloads mirror the long-context decode settings that "Flash-Decoding
+for long-context inference" (Stanford CRFM) motivates in its "Motivation"
+section (batch 1 at tens of thousands of tokens, small batches at long
+context, large batches at short context) plus a variable-length batch as in
+serving.  The pages name no dataset; everything is synthetic.
+
+Recipe (every stream is an independent PCG64 seeded from
+``SeedSequence(seed, spawn_key=...)`` so any one slab can be rebuilt alone):
+
+* q           spawn_key (0,)        standard normal float32 -> dtype
+* seqlens     spawn_key (4,)        u ~ U[0,1): floor(lo * (hi/lo)**u), <= hi
+* K[b, g]     spawn_key (1, b, g)   standard normal float32 rows [0, L_b)
+* V[b, g]     spawn_key (2, b, g)   standard normal float32 rows [0, L_b)
+* peaks[b, g] spawn_key (3, b, g)   ceil(frac * L_b) distinct rows of K
+                                     multiplied by ``peak_mult`` (exact)
+* rows >= L_b of a padded slab hold NaN (bf16 0xFFFF, fp32 0xFFFFFFFF) so
+  that a kernel reading past the valid prefix is caught.
+
+bf16 values are produced by rounding float32 to nearest-even on the bit
+pattern and are handled as ``numpy.uint16`` arrays throughout.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN = np.uint16(0xFFFF)
+F32_NAN_BITS = np.uint32(0xFFFFFFFF)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    Lmax: int
+    dtype: str            # "bf16" or "f32"
+    seed: int
+    peak_frac: float = 0.0
+    peak_mult: float = 8.0
+    varlen: tuple | None = None   # (lo, hi) for log-uniform seqlens
+    note: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def np_dtype(self):
+        return np.uint16 if self.dtype == "bf16" else np.float32
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+# The five decode settings, by what they are.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_mha_f32_b1_h8_d64_l1024", B=1, Hq=8, Hkv=8, D=64,
+                 Lmax=1024, dtype="f32", seed=1,
+                 note="tiny multi-head decode in fp32"),
+        Workload("b1_gqa8_h64_d128_l65536", B=1, Hq=64, Hkv=8, D=128,
+                 Lmax=65536, dtype="bf16", seed=2,
+                 note="batch-1 long context, grouped-query (8 per KV head)"),
+        Workload("b4_mha_h32_d128_l32768_peaked", B=4, Hq=32, Hkv=32, D=128,
+                 Lmax=32768, dtype="bf16", seed=3, peak_frac=0.01,
+                 peak_mult=8.0,
+                 note="small batch, longer context, 1% of keys x8"),
+        Workload("b64_gqa4_h32_d128_l4096", B=64, Hq=32, Hkv=8, D=128,
+                 Lmax=4096, dtype="bf16", seed=4,
+                 note="batch-dominated short context"),
+        Workload("varlen_b16_gqa8_h64_d128_lmax131072", B=16, Hq=64, Hkv=8,
+                 D=128, Lmax=131072, dtype="bf16", seed=5,
+                 varlen=(1024, 131072),
+                 note="variable-length batch, log-uniform seqlens"),
+    ]
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+BENCH_WORKLOAD = "b1_gqa8_h64_d128_l65536"
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence(seed, spawn_key=tuple(key))))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (NaN stays NaN)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u + np.uint32(0x7FFF) + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = ((u[nan] >> 16) | 0x0040).astype(np.uint16)
+    return r
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(
+        np.float32)
+
+
+def _encode(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(x32) if dtype == "bf16" else x32.astype(np.float32)
+
+
+def gen_seqlens(w: Workload) -> np.ndarray | None:
+    """Per-sequence valid lengths (None: every sequence is Lmax long)."""
+    if w.varlen is None:
+        return None
+    lo, hi = w.varlen
+    u = _rng(w.seed, 4).random(w.B)
+    s = np.floor(lo * np.power(hi / lo, u)).astype(np.int64)
+    return np.minimum(s, hi).astype(np.int32)
+
+
+def seqlen_of(w: Workload, seqlens, b: int) -> int:
+    return w.Lmax if seqlens is None else int(seqlens[b])
+
+
+def gen_q(w: Workload) -> np.ndarray:
+    x = _rng(w.seed, 0).standard_normal((w.B, w.Hq, w.D), dtype=np.float32)
+    return _encode(x, w.dtype)
+
+
+def peak_rows(w: Workload, b: int, g: int, L: int) -> np.ndarray:
+    """Rows of K[b, g] that are multiplied by peak_mult (sorted)."""
+    if w.peak_frac <= 0.0 or L <= 0:
+        return np.zeros(0, dtype=np.int64)
+    n = min(L, int(math.ceil(w.peak_frac * L)))
+    return np.sort(_rng(w.seed, 3, b, g).choice(L, size=n, replace=False))
+
+
+def fill_slab(w: Workload, b: int, g: int, L: int, k_out: np.ndarray,
+              v_out: np.ndarray) -> None:
+    """Write K[b, g] and V[b, g] ([Lmax, D], storage dtype) in place."""
+    D = w.D
+    assert k_out.shape == (w.Lmax, D) and v_out.shape == (w.Lmax, D)
+    kx = _rng(w.seed, 1, b, g).standard_normal((L, D), dtype=np.float32)
+    pr = peak_rows(w, b, g, L)
+    if pr.size:
+        kx[pr] *= np.float32(w.peak_mult)
+    vx = _rng(w.seed, 2, b, g).standard_normal((L, D), dtype=np.float32)
+    k_out[:L] = _encode(kx, w.dtype)
+    v_out[:L] = _encode(vx, w.dtype)
+    if L < w.Lmax:
+        if w.dtype == "bf16":
+            k_out[L:] = BF16_NAN
+            v_out[L:] = BF16_NAN
+        else:
+            k_out[L:].view(np.uint32)[:] = F32_NAN_BITS
+            v_out[L:].view(np.uint32)[:] = F32_NAN_BITS
+
+
+def gen_slab(w: Workload, b: int, g: int, seqlens=None):
+    """K[b, g], V[b, g] as fresh [Lmax, D] arrays."""
+    L = seqlen_of(w, seqlens, b)
+    k = np.empty((w.Lmax, w.D), dtype=w.np_dtype)
+    v = np.empty((w.Lmax, w.D), dtype=w.np_dtype)
+    fill_slab(w, b, g, L, k, v)
+    return k, v
+
+
+def gen_all(w: Workload):
+    """q, k, v, seqlens as host arrays (only for workloads that fit easily)."""
+    seqlens = gen_seqlens(w)
+    q = gen_q(w)
+    k = np.empty((w.B, w.Hkv, w.Lmax, w.D), dtype=w.np_dtype)
+    v = np.empty_like(k)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            fill_slab(w, b, g, seqlen_of(w, seqlens, b), k[b, g], v[b, g])
+    return q, k, v, seqlens
+
+
+def algorithmic_bytes(w: Workload, seqlens=None) -> int:
+    """Bytes one decode step must move at minimum: every valid K and V row
+    once, q, out, and the fp32 lse."""
+    eb = w.elem_bytes
+    rows = (w.Lmax * w.B if seqlens is None
+            else int(np.sum(np.clip(seqlens, 0, w.Lmax))))
+    kv = 2 * rows * w.Hkv * w.D * eb
+    return kv + 2 * w.B * w.Hq * w.D * eb + 4 * w.B * w.Hq
+
+
+def flops(w: Workload, seqlens=None) -> int:
+    rows = (w.Lmax * w.B if seqlens is None
+            else int(np.sum(np.clip(seqlens, 0, w.Lmax))))
+    return 4 * rows * w.Hq * w.D

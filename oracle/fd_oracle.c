@@ -1,0 +1,308 @@
+/*
+ * fd_oracle.c -- exact fp64 CPU oracle for single-query decode attention.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
+ * smoke check and the benchmark's CPU-baseline leg may load this library.
+ * It shares no source, header, table or helper with the GPU library; it
+ * decodes bf16 itself and needs nothing but libc, libm and OpenMP.
+ *
+ * What it computes.  "Flash-Decoding for long-context inference" (Dao,
+ * Haziza, Massa, Sizov; Stanford CRFM blog), section "Multi-head attention
+ * for decoding": while decoding, the one new query of a head attends to
+ * every earlier token held in the KV cache.  The page's formula did not
+ * survive extraction; the plain reading taken here is softmax attention
+ * with a caller-given scale and no mask:
+ *
+ *     s_j  = scale * sum_d q[d] * K[j][d]          j = 0 .. L-1
+ *     m    = max_j s_j
+ *     l    = sum_j exp(s_j - m)
+ *     out  = (sum_j exp(s_j - m) * V[j]) / l
+ *     lse  = m + ln(l)                              (natural log)
+ *     L = 0  ->  out = 0, lse = -inf
+ *
+ * Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ * Cache layout K, V: [B][Hkv][Lmax][D], contiguous; q, out: [B][Hq][D].
+ * seqlens (optional) gives the valid prefix of each sequence; rows at or
+ * beyond it are never read.  A seqlen outside [0, Lmax] is clamped.
+ *
+ * The split/combine twin follows the section "A faster attention for
+ * decoding: Flash-Decoding" of the same page: the keys/values are cut into
+ * contiguous chunks, each chunk's attention is computed on its own together
+ * with one log-sum-exp per row and chunk, and the chunks are then merged by
+ * weighting each chunk's output with exp(its lse - max lse).  It exists so
+ * that tests can check that splitting and merging reproduce the exact
+ * result; it is written in fp64 with nothing reordered beyond that.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (never
+ * -ffast-math: exp/log/max must keep IEEE semantics, NaN included).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define FDO_BF16 0
+#define FDO_F32 1
+
+#define FDO_OK 0
+#define FDO_EINVAL -1
+#define FDO_ENOMEM -2
+
+/* bf16 is the top half of an IEEE binary32; widening is exact. */
+static double load_elem(const void *base, size_t idx, int dtype)
+{
+    if (dtype == FDO_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[idx];
+}
+
+/*
+ * One query row against L rows of one KV slab.  q_off / kv_off are element
+ * offsets into q and into k/v; rows of the slab are D elements apart.
+ * scratch must hold L doubles.  Two exact passes: scores and their max,
+ * then the exp-weighted sums.
+ */
+static void attend_row(const void *q, size_t q_off, const void *k,
+                       const void *v, size_t kv_off, int L, int D,
+                       double scale, int dtype, double *out, double *lse,
+                       double *scratch)
+{
+    if (L <= 0) {
+        for (int d = 0; d < D; ++d)
+            out[d] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    int saw_nan = 0;
+    for (int j = 0; j < L; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += load_elem(q, q_off + d, dtype) *
+                   load_elem(k, kv_off + (size_t)j * D + d, dtype);
+        double s = scale * dot;
+        scratch[j] = s;
+        if (isnan(s))
+            saw_nan = 1;
+        else if (s > m)
+            m = s;
+    }
+    if (saw_nan)
+        m = NAN; /* a NaN score makes the whole row NaN */
+    double l = 0.0;
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    for (int j = 0; j < L; ++j) {
+        double p = exp(scratch[j] - m);
+        l += p;
+        for (int d = 0; d < D; ++d)
+            out[d] += p * load_elem(v, kv_off + (size_t)j * D + d, dtype);
+    }
+    for (int d = 0; d < D; ++d)
+        out[d] /= l;
+    *lse = m + log(l);
+}
+
+static int clamp_len(const int32_t *seqlens, int b, int Lmax)
+{
+    if (!seqlens)
+        return Lmax;
+    int L = seqlens[b];
+    if (L < 0)
+        L = 0;
+    if (L > Lmax)
+        L = Lmax;
+    return L;
+}
+
+static int check_dims(int B, int Hq, int Hkv, int D, int Lmax, int dtype)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Lmax <= 0)
+        return FDO_EINVAL;
+    if (Hq % Hkv != 0)
+        return FDO_EINVAL;
+    if (dtype != FDO_BF16 && dtype != FDO_F32)
+        return FDO_EINVAL;
+    return FDO_OK;
+}
+
+/*
+ * Whole batch, exact definition.  out: [B][Hq][D] doubles, lse: [B][Hq].
+ * nthreads <= 0 lets OpenMP choose.
+ */
+int fdo_decode(const void *q, const void *k, const void *v,
+               const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+               int Lmax, double scale, int dtype, int nthreads, double *out,
+               double *lse)
+{
+    int rc = check_dims(B, Hq, Hkv, D, Lmax, dtype);
+    if (rc)
+        return rc;
+    const int G = Hq / Hkv;
+    const long rows = (long)B * Hq;
+    int failed = 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)Lmax);
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < rows; ++r) {
+            if (!scratch)
+                continue;
+            int b = (int)(r / Hq), h = (int)(r % Hq);
+            int g = h / G;
+            size_t q_off = ((size_t)b * Hq + h) * D;
+            size_t kv_off = ((size_t)b * Hkv + g) * (size_t)Lmax * D;
+            attend_row(q, q_off, k, v, kv_off, clamp_len(seqlens, b, Lmax), D,
+                       scale, dtype, out + (size_t)r * D, lse + r, scratch);
+        }
+        free(scratch);
+    }
+    return failed ? FDO_ENOMEM : FDO_OK;
+}
+
+/*
+ * One query row against one slab given directly ([L][D] rows, D apart).
+ * Used to check single outputs of full-size runs without materialising
+ * the whole cache on the host.
+ */
+int fdo_attend_row(const void *q_row, const void *k_slab, const void *v_slab,
+                   int L, int D, double scale, int dtype, double *out,
+                   double *lse)
+{
+    if (D <= 0 || L < 0 || (dtype != FDO_BF16 && dtype != FDO_F32))
+        return FDO_EINVAL;
+    double *scratch = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!scratch)
+        return FDO_ENOMEM;
+    attend_row(q_row, 0, k_slab, v_slab, 0, L, D, scale, dtype, out, lse,
+               scratch);
+    free(scratch);
+    return FDO_OK;
+}
+
+/*
+ * Split/combine twin for one row.  Chunk c covers keys
+ * [c*chunk, min((c+1)*chunk, L)); chunks past L are empty and skipped.
+ * If part_out / part_lse are given they receive each chunk's normalised
+ * output ([nchunks][D]) and log-sum-exp ([nchunks]); empty chunks get
+ * out = 0 and lse = -inf there.
+ */
+int fdo_attend_row_split(const void *q_row, const void *k_slab,
+                         const void *v_slab, int L, int D, double scale,
+                         int dtype, int chunk, int nchunks, double *out,
+                         double *lse, double *part_out, double *part_lse)
+{
+    if (D <= 0 || L < 0 || chunk <= 0 || nchunks <= 0 ||
+        (dtype != FDO_BF16 && dtype != FDO_F32))
+        return FDO_EINVAL;
+    if ((long)chunk * nchunks < L)
+        return FDO_EINVAL;
+    double *scratch = malloc(sizeof(double) * (size_t)chunk);
+    double *po = malloc(sizeof(double) * (size_t)nchunks * D);
+    double *pl = malloc(sizeof(double) * (size_t)nchunks);
+    if (!scratch || !po || !pl) {
+        free(scratch);
+        free(po);
+        free(pl);
+        return FDO_ENOMEM;
+    }
+    /* Step 1: each chunk on its own, with its own log-sum-exp. */
+    for (int c = 0; c < nchunks; ++c) {
+        long lo = (long)c * chunk;
+        long n = L - lo;
+        if (n > chunk)
+            n = chunk;
+        if (n < 0)
+            n = 0;
+        attend_row(q_row, 0, k_slab, v_slab, (size_t)lo * D, (int)n, D, scale,
+                   dtype, po + (size_t)c * D, pl + c, scratch);
+    }
+    /* Step 2: merge the chunks, weighting each by exp(lse_c - max lse). */
+    double M = -INFINITY;
+    int any = 0, saw_nan = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        if ((long)c * chunk >= L)
+            continue;
+        any = 1;
+        if (isnan(pl[c]))
+            saw_nan = 1;
+        else if (pl[c] > M)
+            M = pl[c];
+    }
+    if (saw_nan)
+        M = NAN;
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (!any) {
+        *lse = -INFINITY;
+    } else {
+        double W = 0.0;
+        for (int c = 0; c < nchunks; ++c) {
+            if ((long)c * chunk >= L)
+                continue;
+            double w = exp(pl[c] - M);
+            W += w;
+            for (int d = 0; d < D; ++d)
+                out[d] += w * po[(size_t)c * D + d];
+        }
+        for (int d = 0; d < D; ++d)
+            out[d] /= W;
+        *lse = M + log(W);
+    }
+    if (part_out)
+        memcpy(part_out, po, sizeof(double) * (size_t)nchunks * D);
+    if (part_lse)
+        memcpy(part_lse, pl, sizeof(double) * (size_t)nchunks);
+    free(scratch);
+    free(po);
+    free(pl);
+    return FDO_OK;
+}
+
+/* Whole batch through the split/combine twin, chunk keys per split. */
+int fdo_decode_split(const void *q, const void *k, const void *v,
+                     const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                     int Lmax, double scale, int dtype, int chunk,
+                     int nthreads, double *out, double *lse)
+{
+    int rc = check_dims(B, Hq, Hkv, D, Lmax, dtype);
+    if (rc)
+        return rc;
+    if (chunk <= 0)
+        return FDO_EINVAL;
+    const int G = Hq / Hkv;
+    const int nchunks = (Lmax + chunk - 1) / chunk;
+    const long rows = (long)B * Hq;
+    const size_t elem = dtype == FDO_BF16 ? 2 : 4;
+    int err = 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long r = 0; r < rows; ++r) {
+        int b = (int)(r / Hq), h = (int)(r % Hq);
+        int g = h / G;
+        const char *qr = (const char *)q + ((size_t)b * Hq + h) * D * elem;
+        size_t kv = ((size_t)b * Hkv + g) * (size_t)Lmax * D * elem;
+        int e = fdo_attend_row_split(qr, (const char *)k + kv,
+                                     (const char *)v + kv,
+                                     clamp_len(seqlens, b, Lmax), D, scale,
+                                     dtype, chunk, nchunks,
+                                     out + (size_t)r * D, lse + r, NULL, NULL);
+        if (e) {
+#pragma omp atomic write
+            err = e;
+        }
+    }
+    return err;
+}

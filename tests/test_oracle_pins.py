@@ -1,0 +1,387 @@
+"""Pins for the fp64 oracle, against facts other than the oracle itself.
+
+The pages ("Flash-Decoding for long-context inference", Stanford CRFM) print
+no worked example and their attention formula was lost in extraction, so
+every pin here comes from mathematics: closed forms of softmax attention on
+constructed inputs, invariants, the split/merge identity the page's
+section "A faster attention for decoding: Flash-Decoding" relies on, a
+50-digit brute force, and a library routine (torch's fp64 attention).
+Each is chosen so that a plausible slip in the oracle -- a dropped scale, a
+base-2 log, a transposed K/V, a wrong GQA head map, an off-by-one in the
+valid length, reading the padding -- fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from long_context_decode_fd_amd import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def bf(x):
+    """Exactly representable values -> bf16 bits (asserts exactness)."""
+    x = np.asarray(x, dtype=np.float32)
+    b = wl.bf16_bits(x)
+    assert np.array_equal(wl.bf16_to_f32(b), x), "value not exact in bf16"
+    return b
+
+
+def widen(a):
+    a = np.asarray(a)
+    return (wl.bf16_to_f32(a) if a.dtype == np.uint16 else a).astype(
+        np.float64)
+
+
+def rand_bf16(rng, shape, scale=1.0):
+    return wl.bf16_bits((rng.standard_normal(shape) * scale).astype(
+        np.float32))
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_returns_its_value_row(oracle_mod, dtype):
+    # One key: softmax weight 1, so out = v0 and lse = s0 = scale*<q,k0>,
+    # with q = 2 e0, k0 = 3 e0, scale 0.5 -> s0 = 3.
+    D = 8
+    q = np.zeros(D, np.float32); q[0] = 2
+    k = np.zeros((1, D), np.float32); k[0, 0] = 3
+    v = np.arange(D, dtype=np.float32)[None] * 0.5 - 1.25
+    if dtype == "bf16":
+        q, k, v = bf(q), bf(k), bf(v)
+    out, lse = oracle_mod.attend_row(q, k, v, 1, 0.5)
+    np.testing.assert_array_equal(out, widen(v)[0])
+    assert lse == 3.0
+
+
+def test_scale_zero_gives_mean_of_values(oracle_mod):
+    rng = np.random.default_rng(11)
+    L, D = 37, 16
+    q, k, v = (rand_bf16(rng, (D,)), rand_bf16(rng, (L, D)),
+               rand_bf16(rng, (L, D)))
+    out, lse = oracle_mod.attend_row(q, k, v, L, 0.0)
+    np.testing.assert_allclose(out, widen(v).mean(axis=0), rtol=0,
+                               atol=1e-14)
+    assert abs(lse - math.log(L)) < 1e-14
+
+
+def test_identical_keys_give_mean_and_shifted_lse(oracle_mod):
+    # All keys equal k = 1.5 e1, q = -2 e1 + noise in other coords that k
+    # does not see, scale 0.25 -> every score s = 0.25 * (-3) = -0.75.
+    rng = np.random.default_rng(12)
+    L, D = 29, 32
+    q = np.zeros(D, np.float32); q[1] = -2.0
+    q[2:] = wl.bf16_to_f32(rand_bf16(rng, (D - 2,)))
+    k = np.zeros((L, D), np.float32); k[:, 1] = 1.5
+    v = rand_bf16(rng, (L, D))
+    out, lse = oracle_mod.attend_row(bf(q), bf(k), v, L, 0.25)
+    np.testing.assert_allclose(out, widen(v).mean(axis=0), rtol=0,
+                               atol=1e-14)
+    assert abs(lse - (-0.75 + math.log(L))) < 1e-13
+
+
+def test_two_keys_closed_form(oracle_mod):
+    # q = e0, k0 = 2 e0, k1 = -1 e0, scale 0.5 -> s0 = 1, s1 = -0.5.
+    # softmax of two scores: weights sigmoid(+-(s0 - s1)); lse = logaddexp.
+    D = 4
+    q = bf([1, 0, 0, 0])
+    k = bf([[2, 0, 0, 0], [-1, 0, 0, 0]])
+    v = bf([[1, 2, -3, 0.5], [3, -1, 0.25, 8]])
+    out, lse = oracle_mod.attend_row(q, k, v, 2, 0.5)
+    s0, s1 = 1.0, -0.5
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+    expect = w0 * widen(v)[0] + w1 * widen(v)[1]
+    np.testing.assert_allclose(out, expect, rtol=1e-15, atol=1e-15)
+    assert abs(lse - np.logaddexp(s0, s1)) < 1e-15
+    # K and V are not interchangeable: swapping them must change the result
+    out_sw, _ = oracle_mod.attend_row(q, v, k, 2, 0.5)
+    assert np.abs(out_sw - out).max() > 0.1
+
+
+def test_dominant_key_returns_its_row(oracle_mod):
+    # k* = c q / |q|^2-ish: s* dwarfs the others; |out - v*| is bounded by
+    # sum_{j != *} exp(s_j - s*) * max_j |v_j - v*|.
+    rng = np.random.default_rng(13)
+    L, D, star = 300, 64, 123
+    qf = wl.bf16_to_f32(rand_bf16(rng, (D,)))
+    kf = wl.bf16_to_f32(rand_bf16(rng, (L, D)))
+    kf[star] = wl.bf16_to_f32(wl.bf16_bits(qf * 4.0))
+    q, k = wl.bf16_bits(qf), wl.bf16_bits(kf)
+    v = rand_bf16(rng, (L, D))
+    scale = 1.0
+    out, lse = oracle_mod.attend_row(q, k, v, L, scale)
+    s = widen(k) @ widen(q) * scale
+    assert s.argmax() == star
+    bound = np.exp(np.delete(s, star) - s[star]).sum() * (
+        np.abs(widen(v) - widen(v)[star]).max())
+    assert bound < 1e-6
+    assert np.abs(out - widen(v)[star]).max() <= bound * 1.0000001 + 1e-15
+    assert abs(lse - s[star]) <= bound + 1e-12
+
+
+# --------------------------------------------------------------------------
+# grouped-query head map, valid lengths, special values
+
+
+def test_gqa_head_map_is_h_div_group(oracle_mod):
+    # KV head g holds V rows all equal to g+1 (and random keys), so query
+    # head h must return exactly (h // G) + 1.  The map h % Hkv would not.
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, D, L = 2, 8, 2, 8, 5
+    G = Hq // Hkv
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = np.empty((B, Hkv, L, D), np.uint16)
+    for g in range(Hkv):
+        v[:, g] = bf(np.full((L, D), g + 1.0))
+    out, _ = oracle_mod.decode(q, k, v, None, 0.3)
+    for h in range(Hq):
+        assert np.all(out[:, h] == h // G + 1)
+    assert any(h // G != h % Hkv for h in range(Hq))
+
+
+def test_batch_matches_row_function(oracle_mod):
+    rng = np.random.default_rng(15)
+    B, Hq, Hkv, D, L = 3, 4, 2, 16, 23
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    seq = np.array([23, 7, 1], np.int32)
+    out, lse = oracle_mod.decode(q, k, v, seq, 0.25)
+    for b in range(B):
+        for h in range(Hq):
+            o1, l1 = oracle_mod.attend_row(q[b, h], k[b, h // 2], v[b, h // 2],
+                                           int(seq[b]), 0.25)
+            np.testing.assert_array_equal(out[b, h], o1)
+            assert lse[b, h] == l1
+
+
+def test_padding_beyond_seqlen_is_never_read(oracle_mod):
+    rng = np.random.default_rng(16)
+    B, H, D, Lmax = 2, 2, 8, 40
+    q = rand_bf16(rng, (B, H, D))
+    k = rand_bf16(rng, (B, H, Lmax, D))
+    v = rand_bf16(rng, (B, H, Lmax, D))
+    seq = np.array([17, 40], np.int32)
+    k[0, :, 17:] = wl.BF16_NAN
+    v[0, :, 17:] = wl.BF16_NAN
+    out, lse = oracle_mod.decode(q, k, v, seq, 0.5)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    o2, l2 = oracle_mod.decode(q[:1], k[:1, :, :17].copy(),
+                               v[:1, :, :17].copy(), None, 0.5)
+    np.testing.assert_array_equal(out[:1], o2)
+    np.testing.assert_array_equal(lse[:1], l2)
+
+
+def test_seqlen_zero_and_clamping(oracle_mod):
+    rng = np.random.default_rng(17)
+    B, H, D, Lmax = 4, 1, 8, 12
+    q = rand_bf16(rng, (B, H, D))
+    k = rand_bf16(rng, (B, H, Lmax, D))
+    v = rand_bf16(rng, (B, H, Lmax, D))
+    seq = np.array([0, -5, 12, 99], np.int32)
+    out, lse = oracle_mod.decode(q, k, v, seq, 0.5)
+    assert np.all(out[0] == 0) and np.all(out[1] == 0)
+    assert lse[0, 0] == -np.inf and lse[1, 0] == -np.inf
+    full, lfull = oracle_mod.decode(q, k, v, None, 0.5)
+    np.testing.assert_array_equal(out[2:], full[2:])
+    np.testing.assert_array_equal(lse[2:], lfull[2:])
+
+
+def test_nan_inside_valid_prefix_propagates(oracle_mod):
+    rng = np.random.default_rng(18)
+    L, D = 9, 8
+    q, k, v = (rand_bf16(rng, (D,)), rand_bf16(rng, (L, D)),
+               rand_bf16(rng, (L, D)))
+    k2 = k.copy(); k2[4, 3] = wl.BF16_NAN
+    out, lse = oracle_mod.attend_row(q, k2, v, L, 0.5)
+    assert np.isnan(out).all() and math.isnan(lse)
+    v2 = v.copy(); v2[2, 5] = wl.BF16_NAN
+    out, lse = oracle_mod.attend_row(q, k, v2, L, 0.5)
+    assert np.isnan(out[5]) and np.isfinite(np.delete(out, 5)).all()
+    assert math.isfinite(lse)
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+
+def test_joint_permutation_of_rows_is_invisible(oracle_mod):
+    rng = np.random.default_rng(19)
+    L, D = 101, 32
+    q, k, v = (rand_bf16(rng, (D,)), rand_bf16(rng, (L, D)),
+               rand_bf16(rng, (L, D)))
+    perm = rng.permutation(L)
+    o1, l1 = oracle_mod.attend_row(q, k, v, L, 0.2)
+    o2, l2 = oracle_mod.attend_row(q, k[perm].copy(), v[perm].copy(), L, 0.2)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-15)
+    assert abs(l2 - l1) < 1e-13
+
+
+def test_affine_map_of_values_passes_through(oracle_mod):
+    # out(a V + c) = a out(V) + c; with V on the bf16 grid, 3 V + 0.25 is
+    # exact in fp32.
+    rng = np.random.default_rng(20)
+    L, D = 57, 16
+    q = wl.bf16_to_f32(rand_bf16(rng, (D,)))
+    k = wl.bf16_to_f32(rand_bf16(rng, (L, D)))
+    v = wl.bf16_to_f32(rand_bf16(rng, (L, D)))
+    v2 = (v * np.float32(3) + np.float32(0.25)).astype(np.float32)
+    assert np.array_equal(v2.astype(np.float64),
+                          v.astype(np.float64) * 3 + 0.25)
+    o1, l1 = oracle_mod.attend_row(q, k, v, L, 0.3)
+    o2, l2 = oracle_mod.attend_row(q, k, v2, L, 0.3)
+    np.testing.assert_allclose(o2, 3 * o1 + 0.25, rtol=1e-13, atol=1e-13)
+    assert l2 == l1
+
+
+def test_common_score_shift_moves_lse_only(oracle_mod):
+    # q = 2 e0 + (0 elsewhere); adding 1 to column 0 of every key adds
+    # scale*2*1 = 0.5 to every score: lse + 0.5, out unchanged.
+    rng = np.random.default_rng(21)
+    L, D = 45, 16
+    q = np.zeros(D, np.float32); q[0] = 2.0
+    k = wl.bf16_to_f32(rand_bf16(rng, (L, D)))
+    k2 = k.copy(); k2[:, 0] += np.float32(1.0)
+    assert np.array_equal(k2[:, 0].astype(np.float64),
+                          k[:, 0].astype(np.float64) + 1.0)
+    v = wl.bf16_to_f32(rand_bf16(rng, (L, D)))
+    o1, l1 = oracle_mod.attend_row(q, k, v, L, 0.25)
+    o2, l2 = oracle_mod.attend_row(q, k2, v, L, 0.25)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    assert abs(l2 - (l1 + 0.5)) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# the split / merge identity
+
+
+@pytest.mark.parametrize("L,chunk,extra", [
+    (1, 1, 0), (100, 1, 0), (100, 7, 0), (100, 100, 0), (100, 33, 3),
+    (100, 512, 2), (257, 64, 0), (64, 64, 5), (1000, 128, 1)])
+def test_split_and_merge_equals_unsplit(oracle_mod, L, chunk, extra):
+    rng = np.random.default_rng(1000 + L + chunk)
+    D = 32
+    q, k, v = (rand_bf16(rng, (D,)), rand_bf16(rng, (L, D), 2.0),
+               rand_bf16(rng, (L, D)))
+    n = -(-L // chunk) + extra          # extra chunks are empty
+    o1, l1 = oracle_mod.attend_row(q, k, v, L, 0.2)
+    o2, l2, po, pl = oracle_mod.attend_row_split(q, k, v, L, 0.2, chunk, n)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    assert abs(l2 - l1) < 1e-12
+    # the per-chunk lse are each chunk's own log-sum-exp; merging them with
+    # numpy's logaddexp reproduces the whole row's lse
+    live = pl[: -(-L // chunk)]
+    assert abs(np.logaddexp.reduce(live) - l1) < 1e-12
+    if extra:
+        assert np.all(pl[-extra:] == -np.inf)
+    # each chunk's output is that chunk's own exact attention
+    for c in range(-(-L // chunk)):
+        lo, hi = c * chunk, min(L, (c + 1) * chunk)
+        oc, lc = oracle_mod.attend_row(q, k[lo:hi].copy(), v[lo:hi].copy(),
+                                       hi - lo, 0.2)
+        np.testing.assert_array_equal(po[c], oc)
+        assert pl[c] == lc
+
+
+def test_split_batch_twin_matches_batch(oracle_mod):
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, D, Lmax = 3, 4, 2, 16, 70
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, Lmax, D))
+    v = rand_bf16(rng, (B, Hkv, Lmax, D))
+    seq = np.array([70, 0, 33], np.int32)
+    o1, l1 = oracle_mod.decode(q, k, v, seq, 0.3)
+    for chunk in (1, 16, 32, 64, 128):
+        o2, l2 = oracle_mod.decode_split(q, k, v, seq, 0.3, chunk)
+        np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# brute force and a library routine
+
+
+def test_mpmath_brute_force_50_digits(oracle_mod):
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(23)
+    for trial in range(6):
+        B, Hkv, G, D = 1 + trial % 2, 1 + trial % 2, 1 + trial % 3, 1 + trial
+        Hq, L = Hkv * G, 1 + 3 * trial
+        q = rand_bf16(rng, (B, Hq, D))
+        k = rand_bf16(rng, (B, Hkv, L, D), 2.0)
+        v = rand_bf16(rng, (B, Hkv, L, D))
+        scale = 0.7
+        out, lse = oracle_mod.decode(q, k, v, None, scale)
+        qf, kf, vf = widen(q), widen(k), widen(v)
+        sc = mpmath.mpf(float(np.float32(scale)))
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G
+                s = [sc * mpmath.fsum(mpmath.mpf(qf[b, h, d]) *
+                                      mpmath.mpf(kf[b, g, j, d])
+                                      for d in range(D)) for j in range(L)]
+                z = mpmath.fsum(mpmath.exp(x) for x in s)
+                for d in range(D):
+                    num = mpmath.fsum(mpmath.exp(s[j]) * mpmath.mpf(vf[b, g, j, d])
+                                      for j in range(L))
+                    assert abs(float(num / z) - out[b, h, d]) < 1e-12
+                assert abs(float(mpmath.log(z)) - lse[b, h]) < 1e-12
+
+
+def test_torch_fp64_attention_agrees(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, D, L = 2, 8, 2, 32, 77
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    scale = 1.0 / math.sqrt(D)
+    out, lse = oracle_mod.decode(q, k, v, None, scale)
+    tq = torch.from_numpy(widen(q))[:, :, None, :]            # [B,Hq,1,D]
+    tk = torch.from_numpy(widen(k)).repeat_interleave(Hq // Hkv, dim=1)
+    tv = torch.from_numpy(widen(v)).repeat_interleave(Hq // Hkv, dim=1)
+    sc = float(np.float32(scale))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv,
+                                                           scale=sc)
+    np.testing.assert_allclose(out, ref[:, :, 0].numpy(), rtol=1e-12,
+                               atol=1e-13)
+    scores = (tq @ tk.transpose(-1, -2))[:, :, 0] * sc
+    np.testing.assert_allclose(lse, torch.logsumexp(scores, -1).numpy(),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_fp32_inputs_are_used_at_full_precision(oracle_mod):
+    # fp32 values that bf16 cannot hold must not be rounded: with scale 0,
+    # out is the plain fp64 mean of the fp32 rows.
+    rng = np.random.default_rng(25)
+    L, D = 10, 8
+    q = rng.standard_normal(D).astype(np.float32)
+    k = rng.standard_normal((L, D)).astype(np.float32)
+    v = (rng.standard_normal((L, D)) * (1 + 2**-20)).astype(np.float32)
+    out, lse = oracle_mod.attend_row(q, k, v, L, 0.0)
+    np.testing.assert_allclose(out, v.astype(np.float64).mean(0), rtol=0,
+                               atol=1e-15)
+
+
+def test_oracle_snapshot_unchanged(oracle_mod):
+    # Regression guard only (written by tests/golden/make_snapshot.py from the
+    # oracle): any change to the oracle's arithmetic shows up here.
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden",
+                        "oracle_snapshot_tiny_f32.json")
+    doc = json.load(open(path))
+    w = wl.WORKLOADS[doc["workload"]]
+    q, k, v, seqlens = wl.gen_all(w)
+    out, lse = oracle_mod.decode(q, k, v, seqlens, w.scale)
+    np.testing.assert_allclose(out.ravel(), [float(x) for x in doc["out"]],
+                               rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse.ravel(), [float(x) for x in doc["lse"]],
+                               rtol=0, atol=1e-13)

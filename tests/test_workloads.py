@@ -1,0 +1,64 @@
+"""The seeded input generator: determinism, shapes, padding, bf16 rounding."""
+import numpy as np
+import pytest
+
+from long_context_decode_fd_amd import workloads as wl
+
+
+def test_bf16_rounding_is_nearest_even_like_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.4e38, -3.4e38,
+                  1e-40, np.inf, -np.inf], np.float32)])
+    ours = wl.bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy()
+    np.testing.assert_array_equal(ours, ref.view(np.uint16))
+    nan = wl.bf16_bits(np.array([np.nan], np.float32))
+    assert np.isnan(wl.bf16_to_f32(nan)).all()
+
+
+def test_generation_is_deterministic_and_slab_local():
+    w = wl.WORKLOADS["b4_mha_h32_d128_l32768_peaked"].with_(Lmax=256, B=2,
+                                                             Hq=2, Hkv=2)
+    q1, k1, v1, _ = wl.gen_all(w)
+    q2 = wl.gen_q(w)
+    k2, v2 = wl.gen_slab(w, 1, 1)
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(k1[1, 1], k2)
+    np.testing.assert_array_equal(v1[1, 1], v2)
+    assert not np.array_equal(k1[0, 0], k1[0, 1])
+
+
+def test_peaked_rows_are_exactly_scaled():
+    w = wl.WORKLOADS["b4_mha_h32_d128_l32768_peaked"].with_(Lmax=1000)
+    rows = wl.peak_rows(w, 0, 3, 1000)
+    assert rows.size == 10 and np.unique(rows).size == 10
+    plain = w.with_(peak_frac=0.0)
+    kp, _ = wl.gen_slab(w, 0, 3)
+    k0, _ = wl.gen_slab(plain, 0, 3)
+    f = wl.bf16_to_f32
+    np.testing.assert_array_equal(f(kp[rows]), f(k0[rows]) * 8)
+    mask = np.ones(1000, bool); mask[rows] = False
+    np.testing.assert_array_equal(kp[mask], k0[mask])
+
+
+def test_varlen_seqlens_and_nan_padding():
+    w = wl.WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"]
+    s = wl.gen_seqlens(w)
+    assert s.dtype == np.int32 and s.shape == (16,)
+    assert s.min() >= 1024 and s.max() <= 131072
+    small = w.with_(Lmax=64, B=2, Hq=2, Hkv=1, varlen=(8, 64))
+    sl = wl.gen_seqlens(small)
+    k, v = wl.gen_slab(small, 0, 0, sl)
+    L = int(sl[0])
+    assert np.all(k[L:] == 0xFFFF) and np.all(v[L:] == 0xFFFF)
+    assert np.isfinite(wl.bf16_to_f32(k[:L])).all()
+
+
+def test_algorithmic_bytes_of_batch1_64k():
+    w = wl.WORKLOADS["b1_gqa8_h64_d128_l65536"]
+    assert wl.algorithmic_bytes(w) == 268_468_480
+    assert wl.flops(w) == 4 * 65536 * 64 * 128
