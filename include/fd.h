@@ -1,0 +1,157 @@
+/*
+ * fd.h -- split-KV single-query decode attention (Flash-Decoding) for
+ * AMD Instinct MI355X (gfx950).  C ABI of libfd.so.
+ *
+ * The operation.  "Flash-Decoding for long-context inference" (Dao,
+ * Haziza, Massa, Sizov; Stanford CRFM blog), section "Multi-head attention
+ * for decoding": at each decoding step the single new query of every head
+ * attends to all tokens already in the KV cache.  For every batch entry b
+ * and query head h, with kv-head g = h / (Hq / Hkv) and L = seqlens[b]:
+ *
+ *     s_j      = scale * <q[b,h,:], k_cache[b,g,j,:]>      0 <= j < L
+ *     out[b,h] = sum_j softmax(s)_j * v_cache[b,g,j,:]
+ *     lse[b,h] = ln sum_j exp(s_j)                         (natural log)
+ *     L == 0  ->  out = 0, lse = -inf
+ *
+ * No mask beyond the valid length: the current token's K/V is expected to
+ * be in the cache already.
+ *
+ * How it is computed.  Same page, section "A faster attention for
+ * decoding: Flash-Decoding": the keys/values of each sequence are cut into
+ * chunks that are processed in parallel, each writing its partial output
+ * and one log-sum-exp per query row; a small final reduction rescales the
+ * chunks by their log-sum-exp and sums them.  The number of chunks is
+ * chosen for the GPU's compute-unit count so that even batch 1 fills the
+ * chip.  When one chunk per sequence already fills it, the partials are
+ * skipped and the single pass writes out/lse directly (the pages' choice
+ * between Flash-Decoding and plain FlashAttention by problem size).
+ *
+ * Layouts (all contiguous, row-major, element type `dtype` unless noted):
+ *     q        [B][Hq][D]
+ *     k_cache  [B][Hkv][Lmax][D]     head-major: each (b, g) is one slab
+ *     v_cache  [B][Hkv][Lmax][D]
+ *     seqlens  int32 [B], DEVICE memory, or NULL (= every sequence is Lmax)
+ *     out      [B][Hq][D]
+ *     lse      float32 [B][Hq]
+ * Rows j >= seqlens[b] of a slab are never read (they may hold anything,
+ * NaN included).  Pointers must be 16-byte aligned device pointers.
+ *
+ * Supported: D in {64, 128}; dtype FD_BF16 with 1 <= Hq/Hkv <= 16, or
+ * FD_F32 with 1 <= Hq/Hkv <= 16.  bf16 scores and outputs are accumulated
+ * in fp32; the bf16 output is rounded to nearest even.
+ *
+ * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
+ * passed as void* (NULL = the default stream).  The library keeps no
+ * pointer after a call returns.
+ *
+ * Errors.  Every entry point returns FD_OK or a negative FD_ERR_* code;
+ * argument checks run on the host before anything is launched, and nothing
+ * is launched when one fails.  No C++ exception crosses the ABI.
+ *
+ * Synchronisation.  Calls are asynchronous on `stream`; results are valid
+ * once the stream's work has completed.  The library never synchronises,
+ * so it cannot validate the device-side seqlens: a value outside
+ * [0, Lmax] is a caller error that the kernels clamp into that range.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_dtype {
+    FD_BF16 = 0, /* bfloat16 q/k/v/out */
+    FD_F32 = 1   /* float32 q/k/v/out */
+} fd_dtype_t;
+
+enum {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = -1, /* NULL pointer, non-positive size, Hq % Hkv,
+                                non-finite scale, misaligned pointer */
+    FD_ERR_UNSUPPORTED = -2, /* D, dtype or group size outside the list */
+    FD_ERR_WORKSPACE = -3,   /* caller workspace too small / alloc failed */
+    FD_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+};
+
+/* Kernel variant chosen for the per-chunk pass. */
+enum {
+    FD_VARIANT_AUTO = 0,
+    FD_VARIANT_MFMA = 1, /* bf16 matrix-core pass, q group padded to 16 */
+    FD_VARIANT_VALU = 2  /* vector-ALU pass (fp32, or bf16 small groups) */
+};
+
+/* What the planner decided for one problem shape (filled by fd_plan). */
+typedef struct fd_plan {
+    int num_splits;      /* chunks per sequence of length Lmax (S) */
+    int chunk;           /* keys per chunk (C), a multiple of 32 */
+    int variant;         /* FD_VARIANT_MFMA or FD_VARIANT_VALU */
+    int waves_per_block; /* 64-lane wavefronts per workgroup */
+    int grid;            /* workgroups of the per-chunk pass (upper bound
+                            when seqlens is given) */
+    int combine;         /* 1 if the log-sum-exp merge pass follows */
+    int num_cus;         /* compute units the plan was sized for */
+    size_t workspace_bytes; /* bytes of partials the plan needs */
+} fd_plan_t;
+
+/*
+ * fd_decode -- out, lse = attention(q, k_cache, v_cache) as defined above.
+ * Uses a workspace owned by the library: allocated on first use per
+ * device and grown when a larger problem needs it (that call allocates,
+ * so keep it out of graph capture).  Calls on different streams of one
+ * device must not overlap, since they share that workspace.
+ */
+int fd_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+              int Lmax, float scale, fd_dtype_t dtype, void *out, float *lse,
+              void *stream);
+
+/*
+ * fd_decode_ex -- as fd_decode, with the caller's choices:
+ *   num_splits  0 = planner's choice, else chunks per Lmax-long sequence
+ *               (clamped to [1, ceil(Lmax / 32)]); 1 disables the merge.
+ *   variant     FD_VARIANT_AUTO / _MFMA / _VALU (MFMA needs bf16).
+ *   workspace   device buffer of at least fd_workspace_bytes(...) bytes
+ *               for the same arguments, or NULL with workspace_bytes 0 to
+ *               use the library-owned one.  A caller workspace makes the
+ *               call allocation-free and free of library state.
+ */
+int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                 int Lmax, float scale, fd_dtype_t dtype, void *out,
+                 float *lse, int num_splits, int variant, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * fd_plan -- the decision fd_decode_ex would take, without launching.
+ * varlen: nonzero when seqlens will be passed (chunks are then sized for
+ * a mix of lengths).  num_cus: compute units to plan for; 0 queries the
+ * current HIP device.  Returns FD_OK or an FD_ERR_* code (plan untouched).
+ */
+int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+            int varlen, int num_splits, int variant, int num_cus,
+            fd_plan_t *plan);
+
+/*
+ * fd_workspace_bytes -- bytes of device workspace fd_decode_ex needs for
+ * these arguments on the current device (0 when no merge pass is needed).
+ * Returns 0 as well for invalid arguments; fd_plan reports why.
+ */
+size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
+                          fd_dtype_t dtype, int varlen, int num_splits,
+                          int variant);
+
+/* Static English text for a status code. */
+const char *fd_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

@@ -1,0 +1,15 @@
+"""Flash-Decoding (split-KV single-query decode attention) for MI355X.
+
+The computation lives in libfd.so (HIP kernels for gfx950 behind the C ABI
+declared in include/fd.h); this package is its Python binding plus the
+seeded synthetic workloads used by the tests and the benchmark.
+
+    from long_context_decode_fd_amd import fd_decode
+    out, lse = fd_decode(q, k_cache, v_cache, seqlens, scale)
+"""
+from ._binding import (FD_BF16, FD_ERR_HIP, FD_ERR_INVALID_ARG,  # noqa: F401
+                       FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32, FD_OK,
+                       FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
+                       LIB_PATH, FdError, fd_decode, fd_decode_ex, fd_plan,
+                       fd_status_string, fd_version, fd_workspace_bytes,
+                       load_library)

@@ -1,0 +1,206 @@
+"""ctypes binding over libfd.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this
+module checks tensor shapes/dtypes/devices, passes raw device pointers and
+the current HIP stream, and turns status codes into exceptions.  PyTorch is
+used for device memory and streams.  When libfd.so has not been built the
+calls raise; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FD_LIBRARY") or os.path.join(_PKG, "libfd.so")
+
+FD_BF16 = 0
+FD_F32 = 1
+FD_OK = 0
+FD_ERR_INVALID_ARG = -1
+FD_ERR_UNSUPPORTED = -2
+FD_ERR_WORKSPACE = -3
+FD_ERR_HIP = -4
+FD_VARIANT_AUTO = 0
+FD_VARIANT_MFMA = 1
+FD_VARIANT_VALU = 2
+
+# Every function the C header declares, with its ctypes signature.
+_vp, _i32p = ctypes.c_void_p, ctypes.c_void_p
+_ci, _cf, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class FdPlanStruct(ctypes.Structure):
+    _fields_ = [("num_splits", _ci), ("chunk", _ci), ("variant", _ci),
+                ("waves_per_block", _ci), ("grid", _ci), ("combine", _ci),
+                ("num_cus", _ci), ("workspace_bytes", _sz)]
+
+
+SIGNATURES = {
+    "fd_decode": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci, _cf,
+                        _ci, _vp, _vp, _vp]),
+    "fd_decode_ex": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci,
+                           _cf, _ci, _vp, _vp, _ci, _ci, _vp, _sz, _vp]),
+    "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                      ctypes.POINTER(FdPlanStruct)]),
+    "fd_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                                 _ci]),
+    "fd_status_string": (ctypes.c_char_p, [_ci]),
+    "fd_version": (_ci, []),
+}
+
+_lib = None
+
+
+class FdError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {code} ({fd_status_string(code)})")
+
+
+def load_library(path: str | None = None):
+    """Load libfd.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} not found: build it with "
+            "`python -m long_context_decode_fd_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fd_status_string(code: int) -> str:
+    return load_library().fd_status_string(int(code)).decode()
+
+
+def fd_version() -> int:
+    return load_library().fd_version()
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (FD_BF16, "bf16", "bfloat16"):
+        return FD_BF16
+    if dtype in (FD_F32, "f32", "fp32", "float32"):
+        return FD_F32
+    import torch
+    if dtype == torch.bfloat16:
+        return FD_BF16
+    if dtype == torch.float32:
+        return FD_F32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen=False, num_splits=0,
+            variant=FD_VARIANT_AUTO, num_cus=0) -> dict:
+    """The planner's decision (see fd.h); num_cus 0 = query the device."""
+    p = FdPlanStruct()
+    rc = load_library().fd_plan(B, Hq, Hkv, D, Lmax, _dtype_code(dtype),
+                                int(bool(varlen)), num_splits, variant,
+                                num_cus, ctypes.byref(p))
+    if rc != FD_OK:
+        raise FdError("fd_plan", rc)
+    return {f: getattr(p, f) for f, _ in FdPlanStruct._fields_}
+
+
+def fd_workspace_bytes(B, Hq, Hkv, D, Lmax, dtype, varlen=False,
+                       num_splits=0, variant=FD_VARIANT_AUTO) -> int:
+    return int(load_library().fd_workspace_bytes(
+        B, Hq, Hkv, D, Lmax, _dtype_code(dtype), int(bool(varlen)),
+        num_splits, variant))
+
+
+def _check(q, k_cache, v_cache, seqlens, out, lse):
+    import torch
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32 tensors")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D], k/v [B,Hkv,Lmax,D]")
+    B, Hq, D = q.shape
+    Bk, Hkv, Lmax, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} "
+                         f"k {tuple(k_cache.shape)}")
+    if seqlens is not None:
+        if (seqlens.dtype != torch.int32 or not seqlens.is_cuda
+                or seqlens.shape != (B,) or not seqlens.is_contiguous()):
+            raise ValueError("seqlens must be a contiguous int32 [B] "
+                             "device tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda
+            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like q")
+    if (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    return (B, Hq, Hkv, D, Lmax), out, lse
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
+                 num_splits=0, variant=FD_VARIANT_AUTO, workspace=None,
+                 stream=None):
+    """out, lse = attention(q, k_cache, v_cache) -- see fd.h.
+
+    q [B,Hq,D], k_cache/v_cache [B,Hkv,Lmax,D] (bf16 or fp32, on the GPU),
+    seqlens int32 [B] on the GPU or None, scale a float.  Returns (out, lse);
+    out/lse are allocated if not given.  workspace: a uint8 device tensor
+    of at least fd_workspace_bytes(...) bytes, or None for the library's.
+    """
+    dims, out, lse = _check(q, k_cache, v_cache, seqlens, out, lse)
+    B, Hq, Hkv, D, Lmax = dims
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
+            workspace.element_size()
+    rc = load_library().fd_decode_ex(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(),
+        B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
+        out.data_ptr(), lse.data_ptr(), int(num_splits), int(variant),
+        ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode_ex", rc)
+    return out, lse
+
+
+def fd_decode(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
+              stream=None):
+    """Same as the C fd_decode: planner's choices, library workspace."""
+    dims, out, lse = _check(q, k_cache, v_cache, seqlens, out, lse)
+    B, Hq, Hkv, D, Lmax = dims
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    rc = load_library().fd_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(),
+        B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
+        out.data_ptr(), lse.data_ptr(), _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode", rc)
+    return out, lse

@@ -1,0 +1,209 @@
+// fd_api.hip -- the C ABI of libfd.so (declared and documented in fd.h).
+//
+// Argument checks run on the host before any HIP call, so a bad call
+// returns an FD_ERR_* code without touching the device.  Then the planner
+// (fd_plan.cpp) decides chunking and kernel variant for the device's
+// compute-unit count, and the kernels are queued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "fd_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned(const void *p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Per-device compute-unit count, queried once.
+int device_cus(int *out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess ||
+        n <= 0)
+      return FD_ERR_HIP;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return FD_OK;
+}
+
+// Library-owned workspace, one per device, grown on demand.  Growing frees
+// the old buffer; hipFree waits for the device, so work still queued on
+// the old buffer completes first.
+struct OwnedWorkspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+
+int owned_workspace(size_t need, void **out) {
+  static std::mutex mu;
+  static std::vector<OwnedWorkspace> ws;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)ws.size() <= dev) ws.resize(dev + 1);
+  OwnedWorkspace &w = ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      if (hipFree(w.ptr) != hipSuccess) return FD_ERR_HIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    // Round up so that slowly growing problems do not reallocate often.
+    size_t sz = need + need / 4;
+    sz = (sz + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
+      w.ptr = nullptr;
+      return FD_ERR_WORKSPACE;
+    }
+    w.bytes = sz;
+  }
+  *out = w.ptr;
+  return FD_OK;
+}
+
+int check_pointers(const void *q, const void *k, const void *v,
+                   const int32_t *seqlens, const void *out, const float *lse,
+                   float scale) {
+  if (!q || !k || !v || !out || !lse) return FD_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out, 16) || !aligned(lse, 4))
+    return FD_ERR_INVALID_ARG;
+  if (seqlens && !aligned(seqlens, 4)) return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                 int Lmax, float scale, fd_dtype_t dtype, void *out,
+                 float *lse, int num_splits, int variant, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  int rc = check_pointers(q, k_cache, v_cache, seqlens, out, lse, scale);
+  if (rc != FD_OK) return rc;
+  rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
+  if (rc != FD_OK) return rc;
+  if (num_splits < 0 || variant < FD_VARIANT_AUTO ||
+      variant > FD_VARIANT_VALU)
+    return FD_ERR_INVALID_ARG;
+  if (workspace == nullptr && workspace_bytes != 0) return FD_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 256)) return FD_ERR_INVALID_ARG;
+
+  int ncu = 0;
+  rc = device_cus(&ncu);
+  if (rc != FD_OK) return rc;
+  fd::Plan p;
+  rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, seqlens != nullptr,
+                     num_splits, variant, ncu, &p);
+  if (rc != FD_OK) return rc;
+
+  fd::LaunchArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.scale = scale;
+  a.stream = stream;
+  if (p.combine) {
+    void *ws = workspace;
+    if (ws) {
+      if (workspace_bytes < p.ws_bytes) return FD_ERR_WORKSPACE;
+    } else {
+      rc = owned_workspace(p.ws_bytes, &ws);
+      if (rc != FD_OK) return rc;
+    }
+    const fd::WorkspaceLayout lay = fd::workspace_layout(p);
+    a.o_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                         lay.o_part_off);
+    a.lse_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                           lay.lse_part_off);
+  }
+  return fd::launch_decode(p, a) == 0 ? FD_OK : FD_ERR_HIP;
+}
+
+int fd_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+              int Lmax, float scale, fd_dtype_t dtype, void *out, float *lse,
+              void *stream) {
+  return fd_decode_ex(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax,
+                      scale, dtype, out, lse, 0, FD_VARIANT_AUTO, nullptr, 0,
+                      stream);
+}
+
+int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+            int varlen, int num_splits, int variant, int num_cus,
+            fd_plan_t *plan) {
+  if (!plan) return FD_ERR_INVALID_ARG;
+  int rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
+  if (rc != FD_OK) return rc;
+  if (num_cus < 0) return FD_ERR_INVALID_ARG;
+  if (num_cus == 0) {
+    rc = device_cus(&num_cus);
+    if (rc != FD_OK) return rc;
+  }
+  fd::Plan p;
+  rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, varlen != 0, num_splits,
+                     variant, num_cus, &p);
+  if (rc != FD_OK) return rc;
+  plan->num_splits = p.splits;
+  plan->chunk = p.chunk;
+  plan->variant = p.variant;
+  plan->waves_per_block = p.waves;
+  plan->grid = p.grid;
+  plan->combine = p.combine ? 1 : 0;
+  plan->num_cus = p.num_cus;
+  plan->workspace_bytes = p.ws_bytes;
+  return FD_OK;
+}
+
+size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
+                          fd_dtype_t dtype, int varlen, int num_splits,
+                          int variant) {
+  fd_plan_t p;
+  if (fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen, num_splits, variant, 0,
+              &p) != FD_OK)
+    return 0;
+  return p.workspace_bytes;
+}
+
+const char *fd_status_string(int status) {
+  switch (status) {
+    case FD_OK:
+      return "ok";
+    case FD_ERR_INVALID_ARG:
+      return "invalid argument (null or misaligned pointer, non-positive "
+             "size, Hq not a multiple of Hkv, or non-finite scale)";
+    case FD_ERR_UNSUPPORTED:
+      return "unsupported configuration (head dim, dtype, group size or "
+             "variant)";
+    case FD_ERR_WORKSPACE:
+      return "workspace too small or could not be allocated";
+    case FD_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int fd_version(void) { return kVersion; }
+
+}  // extern "C"

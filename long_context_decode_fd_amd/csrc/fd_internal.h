@@ -1,0 +1,60 @@
+// fd_internal.h -- declarations shared by the planner, the C ABI layer and
+// the kernels of libfd.so.  Not installed; the public contract is fd.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fd.h"
+
+namespace fd {
+
+// Keys per MFMA tile step of one wavefront, and the granularity of chunks.
+constexpr int kKeyTile = 32;
+// Largest query group (Hq / Hkv) one workgroup handles: the MFMA q-tile
+// has 16 columns.
+constexpr int kMaxGroup = 16;
+
+// Everything a launch needs, decided on the host.
+struct Plan {
+  int B, Hq, Hkv, G, D, Lmax;
+  fd_dtype_t dtype;
+  bool varlen;
+  int num_cus;
+  int variant;      // FD_VARIANT_MFMA or FD_VARIANT_VALU
+  int waves;        // wavefronts per workgroup of the per-chunk pass
+  int chunk;        // keys per chunk (multiple of kKeyTile)
+  int splits;       // ceil(Lmax / chunk)
+  int grid;         // workgroups of the per-chunk pass (upper bound)
+  bool combine;     // partials + merge pass (splits > 1)
+  size_t ws_bytes;  // partial outputs + partial lse
+};
+
+// Host-side checks of sizes/dtype shared by fd_plan and the decode calls.
+int validate_shape(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype);
+
+// Fills *p for a validated shape; requested_splits 0 = heuristic.
+int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+              bool varlen, int requested_splits, int requested_variant,
+              int num_cus, Plan *p);
+
+// Byte offsets of the two partial arrays inside a workspace.
+struct WorkspaceLayout {
+  size_t o_part_off, lse_part_off, total;
+};
+WorkspaceLayout workspace_layout(const Plan &p);
+
+// Kernel launches (fd_kernels.hip).  Return hipError_t as int.
+struct LaunchArgs {
+  const void *q, *k, *v;
+  const int32_t *seqlens;
+  void *out;
+  float *lse;
+  float *o_part;
+  float *lse_part;
+  float scale;
+  void *stream;
+};
+int launch_decode(const Plan &p, const LaunchArgs &a);
+
+}  // namespace fd

@@ -1,0 +1,152 @@
+// fd_plan.cpp -- host planner: how many chunks, how long, which kernel.
+//
+// "Flash-Decoding for long-context inference" (Stanford CRFM), section
+// "Multi-head attention for decoding": with one query per head the only
+// parallelism a plain attention kernel has is batch x heads, so at small
+// batch it occupies a sliver of the GPU; the Flash-Decoding section adds
+// the key/value sequence as a further parallel dimension, paid for by a
+// small merge step.  The shipped libraries pick between the split and the
+// unsplit kernel by problem size.  This planner makes that choice for the
+// compute-unit count of the device at hand (256 on MI355X):
+//
+//   * work units U = B * Hkv: one workgroup streams one KV-head slab range
+//     and serves all Hq / Hkv query heads of that group, so K/V are read
+//     from HBM exactly once;
+//   * aim for kBlocksPerCU workgroups per CU; split each sequence into
+//     S = ceil(target / U) chunks, each a multiple of the 32-key tile and at
+//     least kMinChunk keys (the per-workgroup prologue and the partial
+//     write, 2 * G * 4 bytes per key-row pair, must stay small next to the
+//     2 * C * D * elem bytes of K/V a chunk streams);
+//   * S == 1 means no partials and no merge pass at all;
+//   * with per-sequence lengths the mix is unknown on the host (the library
+//     never reads device memory synchronously), so chunks are sized for
+//     balance instead: kVarlenChunk keys, so that no single long sequence
+//     sets the finish time.
+//
+// The constants are this library's own (the pages give none) and the
+// result of any plan is the same attention; only speed depends on them.
+#include <algorithm>
+#include <cmath>
+
+#include "fd_internal.h"
+
+namespace fd {
+
+namespace {
+
+// Tunables (measured on MI355X; overridable at build time for sweeps).
+#ifndef FD_BLOCKS_PER_CU
+#define FD_BLOCKS_PER_CU 2
+#endif
+#ifndef FD_MIN_CHUNK
+#define FD_MIN_CHUNK 256
+#endif
+#ifndef FD_VARLEN_CHUNK
+#define FD_VARLEN_CHUNK 2048
+#endif
+#ifndef FD_MFMA_WAVES
+#define FD_MFMA_WAVES 4
+#endif
+constexpr int kBlocksPerCU = FD_BLOCKS_PER_CU;
+constexpr int kMinChunk = FD_MIN_CHUNK;
+constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
+constexpr int kMfmaWaves = FD_MFMA_WAVES;
+constexpr int kValuWaves = 4;
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+int round_up(long a, long b) { return (int)(((a + b - 1) / b) * b); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
+                   fd_dtype_t dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Lmax <= 0)
+    return FD_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FD_ERR_INVALID_ARG;
+  if (dtype != FD_BF16 && dtype != FD_F32) return FD_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return FD_ERR_UNSUPPORTED;
+  if (Hq / Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
+  // Index arithmetic below uses int for per-slab row counts and size_t for
+  // element offsets; guard the products that are computed in int.
+  if ((long)B * Hkv > (1L << 30) || (long)B * Hq > (1L << 30))
+    return FD_ERR_UNSUPPORTED;
+  return FD_OK;
+}
+
+WorkspaceLayout workspace_layout(const Plan &p) {
+  WorkspaceLayout w{0, 0, 0};
+  if (!p.combine) return w;
+  size_t rows = (size_t)p.B * p.Hq * p.splits;
+  w.o_part_off = 0;
+  w.lse_part_off = align256(rows * p.D * sizeof(float));
+  w.total = w.lse_part_off + align256(rows * sizeof(float));
+  return w;
+}
+
+int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+              bool varlen, int requested_splits, int requested_variant,
+              int num_cus, Plan *p) {
+  int rc = validate_shape(B, Hq, Hkv, D, Lmax, dtype);
+  if (rc != FD_OK) return rc;
+  if (num_cus <= 0) return FD_ERR_INVALID_ARG;
+  if (requested_splits < 0) return FD_ERR_INVALID_ARG;
+  if (requested_variant < FD_VARIANT_AUTO ||
+      requested_variant > FD_VARIANT_VALU)
+    return FD_ERR_INVALID_ARG;
+
+  Plan q{};
+  q.B = B;
+  q.Hq = Hq;
+  q.Hkv = Hkv;
+  q.G = Hq / Hkv;
+  q.D = D;
+  q.Lmax = Lmax;
+  q.dtype = dtype;
+  q.varlen = varlen;
+  q.num_cus = num_cus;
+
+  // Kernel variant: matrix cores need bf16; fp32 runs on the vector ALU.
+  if (requested_variant == FD_VARIANT_MFMA && dtype != FD_BF16)
+    return FD_ERR_UNSUPPORTED;
+  if (requested_variant != FD_VARIANT_AUTO)
+    q.variant = requested_variant;
+  else
+    q.variant = dtype == FD_BF16 ? FD_VARIANT_MFMA : FD_VARIANT_VALU;
+  // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
+  // registers; beyond 4 rows the matrix-core kernel is the one to use.
+  if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)
+    return FD_ERR_UNSUPPORTED;
+  if (q.variant == FD_VARIANT_MFMA)
+    q.waves = kMfmaWaves;
+  else
+    q.waves = q.G > 8 ? 2 : kValuWaves;  // keeps LDS of the merge <= 33 KB
+
+  const int max_splits = ceil_div(Lmax, kKeyTile);
+  const int full_chunk = round_up(Lmax, kKeyTile);
+  int chunk;
+  if (requested_splits > 0) {
+    int s = std::min(requested_splits, max_splits);
+    chunk = round_up(ceil_div(Lmax, s), kKeyTile);
+  } else if (varlen) {
+    chunk = std::min(kVarlenChunk, full_chunk);
+  } else {
+    const long units = (long)B * Hkv;
+    const long target = (long)num_cus * kBlocksPerCU;
+    int s = (int)std::max(1L, (target + units - 1) / units);
+    chunk = round_up(ceil_div(Lmax, s), kKeyTile);
+    chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
+  }
+  q.chunk = chunk;
+  q.splits = ceil_div(Lmax, chunk);
+  q.combine = q.splits > 1;
+  long grid = (long)B * Hkv * q.splits;
+  if (grid > 0x7FFFFFFFL) return FD_ERR_UNSUPPORTED;
+  q.grid = (int)grid;
+  q.ws_bytes = workspace_layout(q).total;
+  *p = q;
+  return FD_OK;
+}
+
+}  // namespace fd

@@ -150,18 +150,23 @@ def peak_rows(w: Workload, b: int, g: int, L: int) -> np.ndarray:
     return np.sort(_rng(w.seed, 3, b, g).choice(L, size=n, replace=False))
 
 
-def fill_slab(w: Workload, b: int, g: int, L: int, k_out: np.ndarray,
-              v_out: np.ndarray) -> None:
-    """Write K[b, g] and V[b, g] ([Lmax, D], storage dtype) in place."""
+def gen_slab_rows(w: Workload, b: int, g: int, L: int):
+    """The L valid rows of K[b, g] and V[b, g] ([L, D], storage dtype)."""
     D = w.D
-    assert k_out.shape == (w.Lmax, D) and v_out.shape == (w.Lmax, D)
     kx = _rng(w.seed, 1, b, g).standard_normal((L, D), dtype=np.float32)
     pr = peak_rows(w, b, g, L)
     if pr.size:
         kx[pr] *= np.float32(w.peak_mult)
     vx = _rng(w.seed, 2, b, g).standard_normal((L, D), dtype=np.float32)
-    k_out[:L] = _encode(kx, w.dtype)
-    v_out[:L] = _encode(vx, w.dtype)
+    return _encode(kx, w.dtype), _encode(vx, w.dtype)
+
+
+def fill_slab(w: Workload, b: int, g: int, L: int, k_out: np.ndarray,
+              v_out: np.ndarray) -> None:
+    """Write K[b, g] and V[b, g] ([Lmax, D], storage dtype) in place; rows
+    at or beyond L get the NaN poison."""
+    assert k_out.shape == (w.Lmax, w.D) and v_out.shape == (w.Lmax, w.D)
+    k_out[:L], v_out[:L] = gen_slab_rows(w, b, g, L)
     if L < w.Lmax:
         if w.dtype == "bf16":
             k_out[L:] = BF16_NAN

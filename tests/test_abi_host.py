@@ -1,0 +1,168 @@
+"""libfd.so on the host: it loads, exports what fd.h declares, validates
+arguments before touching the device, and plans as documented.  No GPU is
+needed (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decode_fd_amd as fd
+from long_context_decode_fd_amd import _binding as bnd
+from long_context_decode_fd_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bnd.LIB_PATH):
+        pytest.fail("libfd.so is not built; run __graft_entry__.build()")
+    return bnd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    assert names == sorted(["fd_decode", "fd_decode_ex", "fd_plan",
+                            "fd_workspace_bytes", "fd_status_string",
+                            "fd_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in bnd.SIGNATURES
+
+
+def test_status_strings_and_version(lib):
+    for code in (fd.FD_OK, fd.FD_ERR_INVALID_ARG, fd.FD_ERR_UNSUPPORTED,
+                 fd.FD_ERR_WORKSPACE, fd.FD_ERR_HIP):
+        s = fd.fd_status_string(code)
+        assert s and s != "unknown status"
+    assert fd.fd_status_string(12345) == "unknown status"
+    assert fd.fd_version() == 10000
+
+
+# Fake, never dereferenced device addresses: every call below must be
+# rejected by host-side checks before anything reaches HIP.
+A = 1 << 20
+
+
+def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
+            Lmax=64, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
+            variant=0, ws=None, ws_bytes=0):
+    return lib.fd_decode_ex(q, k, v, seqlens, B, Hq, Hkv, D, Lmax, scale,
+                            dtype, out, lse, num_splits, variant, ws,
+                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(k=None), fd.FD_ERR_INVALID_ARG),
+    (dict(v=None), fd.FD_ERR_INVALID_ARG),
+    (dict(out=None), fd.FD_ERR_INVALID_ARG),
+    (dict(lse=None), fd.FD_ERR_INVALID_ARG),
+    (dict(q=A + 8), fd.FD_ERR_INVALID_ARG),
+    (dict(k=A + 2), fd.FD_ERR_INVALID_ARG),
+    (dict(out=A + 4), fd.FD_ERR_INVALID_ARG),
+    (dict(lse=A + 2), fd.FD_ERR_INVALID_ARG),
+    (dict(seqlens=A + 1), fd.FD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fd.FD_ERR_INVALID_ARG),
+    (dict(B=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Hq=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Hkv=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(Lmax=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Hq=12, Hkv=8), fd.FD_ERR_INVALID_ARG),
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(D=256), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=7), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(variant=3), fd.FD_ERR_INVALID_ARG),
+    (dict(variant=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=64), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=A + 16, ws_bytes=1 << 20), fd.FD_ERR_INVALID_ARG),
+])
+def test_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call_ex(lib, **kw) == code
+
+
+def test_fd_decode_rejects_like_ex(lib):
+    rc = lib.fd_decode(None, A, A, None, 1, 8, 8, 128, 64, 0.1, 0, A, A, None)
+    assert rc == fd.FD_ERR_INVALID_ARG
+    rc = lib.fd_decode(A, A, A, None, 1, 8, 8, 80, 64, 0.1, 0, A, A, None)
+    assert rc == fd.FD_ERR_UNSUPPORTED
+
+
+def plan(w, varlen=None, **kw):
+    return fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                      varlen=(w.varlen is not None) if varlen is None
+                      else varlen, num_cus=256, **kw)
+
+
+def test_plans_for_the_five_workloads_on_256_cus(lib):
+    W = wl.WORKLOADS
+    # batch 1, 64k, 8 KV heads: 8 units -> 64 chunks of 1024 keys, 512 WGs
+    p = plan(W["b1_gqa8_h64_d128_l65536"])
+    assert (p["num_splits"], p["chunk"], p["grid"], p["combine"]) == \
+        (64, 1024, 512, 1)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
+    assert p["workspace_bytes"] == 64 * 64 * 128 * 4 + 64 * 64 * 4
+    # 4 x 32 MHA heads at 32k: 128 units -> 4 chunks of 8192
+    p = plan(W["b4_mha_h32_d128_l32768_peaked"])
+    assert (p["num_splits"], p["chunk"], p["grid"]) == (4, 8192, 512)
+    # 64 x 8 units already fill the chip: no split, no merge, no workspace
+    p = plan(W["b64_gqa4_h32_d128_l4096"])
+    assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == (1, 0, 0)
+    assert p["grid"] == 512
+    # var-len: balance-sized chunks over the padded length
+    p = plan(W["varlen_b16_gqa8_h64_d128_lmax131072"])
+    assert (p["chunk"], p["num_splits"], p["grid"]) == (2048, 64, 16 * 8 * 64)
+    # fp32 runs on the vector ALU
+    p = plan(W["tiny_mha_f32_b1_h8_d64_l1024"])
+    assert p["variant"] == fd.FD_VARIANT_VALU and p["chunk"] % 32 == 0
+
+
+@pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
+                                 (65536, 64), (65536, 5000), (100, 100)])
+def test_forced_splits_cover_the_sequence(lib, L, S):
+    p = fd.fd_plan(1, 8, 8, 128, L, "bf16", num_splits=S, num_cus=256)
+    C, n = p["chunk"], p["num_splits"]
+    assert C % 32 == 0 and C * n >= L and C * (n - 1) < L
+    assert n <= max(1, -(-L // 32))
+    assert p["combine"] == (n > 1)
+
+
+def test_plan_rejections(lib):
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(1, 8, 8, 128, 64, "f32", variant=fd.FD_VARIANT_MFMA,
+                   num_cus=256)
+    with pytest.raises(fd.FdError):        # bf16 vector path: G <= 4
+        fd.fd_plan(1, 64, 8, 128, 64, "bf16", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
+    assert plan(wl.WORKLOADS["b1_gqa8_h64_d128_l65536"],
+                num_splits=1)["workspace_bytes"] == 0
+
+
+def test_plan_scales_with_cu_count(lib):
+    w = wl.WORKLOADS["b1_gqa8_h64_d128_l65536"]
+    p104 = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_cus=104)
+    p256 = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_cus=256)
+    assert p104["num_splits"] < p256["num_splits"]
+
+
+def test_binding_marshals_nothing_but_pointers():
+    # The binding's table must match the header one-to-one.
+    assert set(bnd.SIGNATURES) == set(declared_functions())
+    for name, (res, args) in bnd.SIGNATURES.items():
+        for a in args:
+            assert a in (ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                         ctypes.c_size_t) or hasattr(a, "_type_"), name

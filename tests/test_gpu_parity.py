@@ -1,0 +1,225 @@
+"""GPU parity: libfd.so (through its C ABI) against the fp64 oracle.
+
+Element-by-element comparison at sizes the oracle finishes in seconds that
+still span several 32-key tiles, several chunks and a ragged tail, for all
+five workload shapes, every kernel variant and forced split counts; plus
+edge lengths, NaN padding, determinism, streams/workspaces and negative
+controls that show the comparison can fail.  The rule (tests/parity.py):
+|out - ref| <= 1e-2 or faithful bf16 rounding, |lse - ref| <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import long_context_decode_fd_amd as fd
+from long_context_decode_fd_amd import workloads as wl
+from gpu_util import dev_inputs, out_to_host, to_dev
+from parity import check_lse, check_out
+
+pytestmark = pytest.mark.gpu
+
+W = wl.WORKLOADS
+# Reduced copies of the five workloads (same heads, head dim, dtype and
+# value recipe; shorter caches): several tiles, several chunks, ragged tails.
+SMALL = {
+    "tiny_mha_f32": W["tiny_mha_f32_b1_h8_d64_l1024"],
+    "b1_gqa8": W["b1_gqa8_h64_d128_l65536"].with_(Lmax=4133),
+    "b4_mha_peaked": W["b4_mha_h32_d128_l32768_peaked"].with_(
+        B=2, Hq=8, Hkv=8, Lmax=3001),
+    "b64_gqa4": W["b64_gqa4_h32_d128_l4096"].with_(B=8, Lmax=517),
+    "varlen_gqa8": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=6, Lmax=4096, varlen=(1, 4096)),
+    "gqa8_d64": W["b1_gqa8_h64_d128_l65536"].with_(D=64, B=2, Hq=16, Hkv=2,
+                                                   Lmax=1999),
+    "gqa16_d128": W["b1_gqa8_h64_d128_l65536"].with_(B=1, Hq=32, Hkv=2,
+                                                     Lmax=777),
+    "gqa3_d128": W["b1_gqa8_h64_d128_l65536"].with_(B=2, Hq=6, Hkv=2,
+                                                    Lmax=300),
+    "f32_gqa4_d128": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
+        D=128, B=2, Hq=16, Hkv=4, Lmax=450),
+    "f32_gqa16_d64": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
+        B=1, Hq=16, Hkv=1, Lmax=300),
+}
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fd.load_library()
+    return torch
+
+
+_cache = {}
+
+
+def inputs(name, w, seqlens=None):
+    key = (name, None if seqlens is None else tuple(seqlens))
+    if key not in _cache:
+        _cache.clear()
+        _cache[key] = dev_inputs(w, seqlens=seqlens, keep_host=True)
+    return _cache[key]
+
+
+def reference(oracle_mod, w, host, seqlens, scale=None):
+    q, k, v = host
+    return oracle_mod.decode(q, k, v, seqlens,
+                             w.scale if scale is None else scale)
+
+
+def assert_parity(w, out, lse, ref_out, ref_lse, what=""):
+    ok_o, rep_o = check_out(out_to_host(out), ref_out, w.dtype)
+    ok_l, rep_l = check_lse(lse.cpu().numpy(), ref_lse)
+    print(f"{what}: out {rep_o} lse {rep_l}", flush=True)
+    assert ok_o, f"{what} out mismatch {rep_o}"
+    assert ok_l, f"{what} lse mismatch {rep_l}"
+    return rep_o, rep_l
+
+
+def variants_for(w):
+    if w.dtype == "f32":
+        return [fd.FD_VARIANT_AUTO]
+    if w.G <= 4:
+        return [fd.FD_VARIANT_MFMA, fd.FD_VARIANT_VALU]
+    return [fd.FD_VARIANT_MFMA]
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 100000])
+def test_small_workloads_match_oracle(cuda, oracle_mod, name, num_splits):
+    w = SMALL[name]
+    q, k, v, sl_dev, seqlens, host = inputs(name, w)
+    ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
+    for variant in variants_for(w):
+        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                   num_splits=num_splits, variant=variant)
+        cuda.cuda.synchronize()
+        assert_parity(w, out, lse, ref_out, ref_lse,
+                      f"{name} S={num_splits} variant={variant}")
+
+
+@pytest.mark.parametrize("G,D,dtype", [(8, 128, "bf16"), (1, 128, "bf16"),
+                                       (4, 64, "bf16"), (1, 64, "f32"),
+                                       (2, 128, "f32")])
+@pytest.mark.parametrize("num_splits", [0, 1, 4])
+def test_edge_lengths_with_nan_padding(cuda, oracle_mod, G, D, dtype,
+                                       num_splits):
+    # lengths 0, 1, a tile boundary +-1, Lmax-1, Lmax; padding is NaN
+    Hkv = 2
+    w = W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=9, Hq=Hkv * G, Hkv=Hkv, D=D, Lmax=1000, dtype=dtype,
+        varlen=(1, 1000))
+    seqlens = np.array([0, 1, 31, 32, 33, 64, 999, 1000, 517], np.int32)
+    q, k, v, sl_dev, seqlens, host = inputs(f"edge{G}{D}{dtype}", w, seqlens)
+    ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
+    assert ref_lse[0, 0] == -np.inf
+    for variant in variants_for(w):
+        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                   num_splits=num_splits, variant=variant)
+        cuda.cuda.synchronize()
+        assert_parity(w, out, lse, ref_out, ref_lse,
+                      f"edge G={G} D={D} {dtype} S={num_splits} v={variant}")
+        o = out_to_host(out)
+        assert np.all(o[0] == 0) and np.all(lse.cpu().numpy()[0] == -np.inf)
+
+
+def test_seqlens_out_of_range_are_clamped(cuda, oracle_mod):
+    w = SMALL["b1_gqa8"].with_(B=3, Lmax=300, varlen=(1, 300))
+    q, k, v, _, _, host = inputs("clamp", w, np.array([300] * 3, np.int32))
+    sl = cuda.tensor([-7, 1 << 30, 150], dtype=cuda.int32, device="cuda")
+    out, lse = fd.fd_decode(q, k, v, sl, w.scale)
+    cuda.cuda.synchronize()
+    ref_out, ref_lse = reference(oracle_mod, w, host,
+                                 np.array([0, 300, 150], np.int32))
+    assert_parity(w, out, lse, ref_out, ref_lse, "clamped seqlens")
+
+
+def test_results_are_bitwise_deterministic(cuda):
+    w = SMALL["b1_gqa8"]
+    q, k, v, sl_dev, _, _ = inputs("b1_gqa8", w)
+    runs = []
+    for _ in range(3):
+        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7)
+        cuda.cuda.synchronize()
+        runs.append((out_to_host(out).copy(), lse.cpu().numpy().copy()))
+    for o, l_ in runs[1:]:
+        assert np.array_equal(o, runs[0][0])
+        assert np.array_equal(l_.view(np.uint32), runs[0][1].view(np.uint32))
+
+
+def test_negative_controls_fail_the_comparison(cuda, oracle_mod):
+    """The comparison must reject plausible wrong answers: zeros, the GQA
+    map h % Hkv, and a missing scale (mistakes planted in the oracle's
+    inputs, on the CPU)."""
+    w = SMALL["b1_gqa8"]
+    q, k, v, sl_dev, seqlens, host = inputs("b1_gqa8", w)
+    out, lse = fd.fd_decode(q, k, v, sl_dev, w.scale)
+    cuda.cuda.synchronize()
+    o_h, l_h = out_to_host(out), lse.cpu().numpy()
+    ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
+    assert check_out(o_h, ref_out, w.dtype)[0]
+    # zeros
+    zero = np.zeros_like(o_h)
+    assert not check_out(zero, ref_out, w.dtype)[0]
+    # h % Hkv instead of h // G: permute query heads accordingly
+    qh, kh, vh = host
+    perm = [(h % w.Hkv) * w.G + h // w.Hkv for h in range(w.Hq)]
+    bad_o, bad_l = oracle_mod.decode(qh[:, perm].copy(), kh, vh, seqlens,
+                                     w.scale)
+    inv = np.argsort(perm)
+    bad_o, bad_l = bad_o[:, inv], bad_l[:, inv]
+    assert not (check_out(o_h, bad_o, w.dtype)[0]
+                and check_lse(l_h, bad_l)[0])
+    # scale dropped
+    bad_o, bad_l = oracle_mod.decode(qh, kh, vh, seqlens, 1.0)
+    assert not check_lse(l_h, bad_l)[0]
+
+
+def test_caller_workspace_and_streams(cuda, oracle_mod):
+    w = SMALL["b1_gqa8"]
+    q, k, v, sl_dev, seqlens, host = inputs("b1_gqa8", w)
+    need = fd.fd_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16",
+                                 num_splits=7)
+    p = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_splits=7)
+    assert need == p["workspace_bytes"] > 0
+    ws = cuda.empty(need, dtype=cuda.uint8, device="cuda")
+    s = cuda.cuda.Stream()
+    with cuda.cuda.stream(s):
+        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7,
+                                   workspace=ws)
+    s.synchronize()
+    ref = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7)
+    cuda.cuda.synchronize()
+    assert np.array_equal(out_to_host(out), out_to_host(ref[0]))
+    small = cuda.empty(need - 256, dtype=cuda.uint8, device="cuda")
+    with pytest.raises(fd.FdError) as e:
+        fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7,
+                        workspace=small)
+    assert e.value.code == fd.FD_ERR_WORKSPACE
+    # no merge needed -> no workspace needed
+    assert fd.fd_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16",
+                                 num_splits=1) == 0
+
+
+def test_scale_is_applied_as_given(cuda, oracle_mod):
+    w = SMALL["b4_mha_peaked"]
+    q, k, v, sl_dev, seqlens, host = inputs("b4_mha_peaked", w)
+    for scale in (0.0, 0.3, -0.05):
+        out, lse = fd.fd_decode(q, k, v, sl_dev, scale)
+        cuda.cuda.synchronize()
+        ref_out, ref_lse = reference(oracle_mod, w, host, seqlens, scale)
+        assert_parity(w, out, lse, ref_out, ref_lse, f"scale={scale}")
+
+
+def test_nan_in_valid_prefix_propagates(cuda):
+    w = SMALL["b1_gqa8"].with_(Lmax=200)
+    q, k, v, sl_dev, _, _ = inputs("nanprefix", w)
+    k2 = k.clone()
+    k2[0, 3, 17, 5] = float("nan")
+    out, lse = fd.fd_decode(q, k2, v, None, w.scale)
+    cuda.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.isnan(o[0, 3 * w.G:(3 + 1) * w.G]).all()
+    assert np.isfinite(o[0, :3 * w.G]).all()
