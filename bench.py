@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: batch 1, 64k context, one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one fd_decode call over the whole KV cache: B=1, Hq=64, Hkv=8,
+D=128, 65536 cached tokens, bf16, scale 1/sqrt(128) -- the per-chunk pass
+and, when the plan splits, the log-sum-exp merge.  Inputs are seeded
+synthetic N(0,1) values (long_context_decode_fd_amd.workloads), resident in
+HBM before timing starts.  Successive steps rotate over 4 copies of the KV
+cache (1.07 GB) so that the 256 MB Infinity Cache cannot serve a repeat of
+the previous step: each step reads its 268 MB from HBM, as a model's layers
+do in turn.  W untimed steps, then exactly K steps between two HIP events on
+the launch stream with device synchronisation on both sides.
+
+Prints one JSON line: value = algorithmic bytes per step (every K and V row
+once, q, out, lse) / step time, in GB/s; the roofline object compares the
+dominant kernel with MI355X's 8 TB/s HBM peak; cpu_baseline times the fp64
+CPU oracle on the host's cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode-attention µs/step and achieved HBM GB/s (% of peak), "
+          "batch 1 @ 64k ctx")
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+KV_COPIES = 4
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_b1_gqa8_64k.json")
+KERNEL_SRC = os.path.join(ROOT, "long_context_decode_fd_amd", "csrc",
+                          "fd_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(bytes_alg: int):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if doc.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since counters were taken"
+    return doc.get("hbm_bytes_per_launch"), doc.get("kernel")
+
+
+def cpu_baseline(w, budget_s: float):
+    """fp64 oracle over the same workload on the host's cores: whole steps,
+    repeated until ~budget_s of wall time (at least one)."""
+    import numpy as np
+    from long_context_decode_fd_amd import workloads as wl
+    from oracle import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    q, k, v, seqlens = wl.gen_all(w)
+    times = []
+    t_total = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, seqlens, w.scale, nthreads=cores)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_total >= budget_s or len(times) >= 20:
+            break
+    t = float(np.median(times))
+    nbytes = wl.algorithmic_bytes(w, seqlens)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": nbytes / t / 1e9, "unit": "GB/s", "cores": cores,
+        "kind": "oracle", "us_per_step": t * 1e6,
+        "sample": (f"{len(times)} whole step(s) of the same workload "
+                   f"(all 64 query heads x 65536 keys), median wall time; "
+                   f"fp64 C oracle, OpenMP over rows, {cores} threads"
+                   + (f", {model}" if model else "")),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for counter "
+                         "runs: HBM bytes per counter unit)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
+              "(the decode path has no multi-GPU form in this library)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import long_context_decode_fd_amd as fd
+    from long_context_decode_fd_amd import workloads as wl
+
+    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    torch.cuda.set_device(0)
+    fd.load_library()
+    log(f"[bench] workload {w.name}: generating inputs")
+    q, k, v, sl, _, _ = wl.device_inputs(w)
+    ks = [k] + [k.clone() for _ in range(KV_COPIES - 1)]
+    vs = [v] + [v.clone() for _ in range(KV_COPIES - 1)]
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    plan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                      varlen=sl is not None)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        fd.fd_decode(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl, w.scale,
+                     out=out, lse=lse, stream=stream)
+
+    log(f"[bench] plan {plan}")
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    log(f"[bench] timed {a.steps} steps: {ms * 1e3:.2f} us/step")
+
+    # Same-buffer ("hot") figure, labelled as such: repeats may hit MALL.
+    e0.record(stream)
+    for i in range(a.steps):
+        fd.fd_decode(q, k, v, sl, w.scale, out=out, lse=lse, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_hot = e0.elapsed_time(e1) / a.steps
+
+    if a.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = wl.algorithmic_bytes(w)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic, traffic_note = traffic_from_profiles(nbytes)
+    roof = {
+        "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
+        "kernel": ("whole step: per-chunk pass + merge pass" if plan["combine"]
+                   else "per-chunk pass"),
+        "bytes_per_launch": nbytes,
+        "traffic_note": traffic_note,
+    }
+    res = {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "us_per_step": ms * 1e3, "frac_of_peak": gbs / PEAK_HBM_GBS,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "seq_len": w.Lmax, "kv_copies_rotated": KV_COPIES,
+                   "num_splits": plan["num_splits"], "chunk": plan["chunk"],
+                   "grid": plan["grid"], "waves_per_block":
+                   plan["waves_per_block"], "merge_pass": bool(plan["combine"])},
+        "hot_same_buffer": {"us_per_step": ms_hot * 1e3,
+                            "GBs": nbytes / (ms_hot * 1e-3) / 1e9,
+                            "note": "one KV copy re-read every step; may be "
+                                    "served partly from the 256 MB MALL"},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

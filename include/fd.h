@@ -24,7 +24,10 @@
  * chosen for the GPU's compute-unit count so that even batch 1 fills the
  * chip.  When one chunk per sequence already fills it, the partials are
  * skipped and the single pass writes out/lse directly (the pages' choice
- * between Flash-Decoding and plain FlashAttention by problem size).
+ * between Flash-Decoding and plain FlashAttention by problem size).  The
+ * final reduction is a second, small kernel on the same stream; with
+ * FD_FLAG_FUSED_MERGE it runs inside the first launch instead, by the last
+ * workgroup to finish each (sequence, KV head) group.
  *
  * Layouts (all contiguous, row-major, element type `dtype` unless noted):
  *     q        [B][Hq][D]
@@ -77,6 +80,24 @@ enum {
     FD_ERR_HIP = -4          /* a HIP runtime call or launch failed */
 };
 
+/* Flags of fd_decode_ex / fd_plan. */
+enum {
+    /* Merge the chunks inside the per-chunk launch: the last workgroup of
+       each (b, KV head) group, found with a ticket counter, merges it.
+       Publishing partials across MI355X's eight L2s then takes an
+       agent-scope release (an L2 write-back) per workgroup, which costs
+       more than the second launch it saves; kept for callers that must
+       have a single launch. */
+    FD_FLAG_FUSED_MERGE = 1
+};
+
+/* How the chunks of a split plan are merged (fd_plan_t.merge). */
+enum {
+    FD_MERGE_NONE = 0,     /* one chunk per sequence: no partials */
+    FD_MERGE_FUSED = 1,    /* last workgroup of each group merges */
+    FD_MERGE_SEPARATE = 2  /* a second kernel merges */
+};
+
 /* Kernel variant chosen for the per-chunk pass. */
 enum {
     FD_VARIANT_AUTO = 0,
@@ -92,9 +113,13 @@ typedef struct fd_plan {
     int waves_per_block; /* 64-lane wavefronts per workgroup */
     int grid;            /* workgroups of the per-chunk pass (upper bound
                             when seqlens is given) */
-    int combine;         /* 1 if the log-sum-exp merge pass follows */
+    int combine;         /* 1 if chunks leave partials to be merged */
+    int merge;           /* FD_MERGE_NONE / _FUSED / _SEPARATE */
     int num_cus;         /* compute units the plan was sized for */
-    size_t workspace_bytes; /* bytes of partials the plan needs */
+    size_t workspace_bytes; /* tickets + partials the plan needs */
+    size_t ticket_bytes;    /* leading bytes of the workspace that hold the
+                               per-group tickets of the fused merge
+                               (0 unless FD_FLAG_FUSED_MERGE) */
 } fd_plan_t;
 
 /*
@@ -102,7 +127,9 @@ typedef struct fd_plan {
  * Uses a workspace owned by the library: allocated on first use per
  * device and grown when a larger problem needs it (that call allocates,
  * so keep it out of graph capture).  Calls on different streams of one
- * device must not overlap, since they share that workspace.
+ * device must not overlap, since they share that workspace.  Results do
+ * not depend on the order in which workgroups finish: for a given plan the
+ * output is bitwise reproducible.
  */
 int fd_decode(const void *q, const void *k_cache, const void *v_cache,
               const int32_t *seqlens, int B, int Hq, int Hkv, int D,
@@ -114,16 +141,23 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
  *   num_splits  0 = planner's choice, else chunks per Lmax-long sequence
  *               (clamped to [1, ceil(Lmax / 32)]); 1 disables the merge.
  *   variant     FD_VARIANT_AUTO / _MFMA / _VALU (MFMA needs bf16).
+ *   flags       0 or FD_FLAG_FUSED_MERGE.
  *   workspace   device buffer of at least fd_workspace_bytes(...) bytes
- *               for the same arguments, or NULL with workspace_bytes 0 to
- *               use the library-owned one.  A caller workspace makes the
- *               call allocation-free and free of library state.
+ *               for the same arguments, 256-byte aligned, or NULL with
+ *               workspace_bytes 0 to use the library-owned one.  A caller
+ *               workspace makes the call allocation-free and free of
+ *               library state.  With FD_FLAG_FUSED_MERGE its first
+ *               fd_plan_t.ticket_bytes bytes are per-group tickets that must
+ *               be zero when a call starts: zero-fill a new workspace once;
+ *               every call leaves its tickets zero again, but the rest of
+ *               the buffer holds partials, so zero-fill again before reusing
+ *               it for a fused call with a larger B * Hkv.
  */
 int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *seqlens, int B, int Hq, int Hkv, int D,
                  int Lmax, float scale, fd_dtype_t dtype, void *out,
-                 float *lse, int num_splits, int variant, void *workspace,
-                 size_t workspace_bytes, void *stream);
+                 float *lse, int num_splits, int variant, int flags,
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * fd_plan -- the decision fd_decode_ex would take, without launching.
@@ -132,7 +166,7 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
  * current HIP device.  Returns FD_OK or an FD_ERR_* code (plan untouched).
  */
 int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
-            int varlen, int num_splits, int variant, int num_cus,
+            int varlen, int num_splits, int variant, int flags, int num_cus,
             fd_plan_t *plan);
 
 /*
@@ -142,7 +176,7 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
  */
 size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
                           fd_dtype_t dtype, int varlen, int num_splits,
-                          int variant);
+                          int variant, int flags);
 
 /* Static English text for a status code. */
 const char *fd_status_string(int status);

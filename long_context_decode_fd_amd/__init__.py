@@ -8,7 +8,9 @@ seeded synthetic workloads used by the tests and the benchmark.
     out, lse = fd_decode(q, k_cache, v_cache, seqlens, scale)
 """
 from ._binding import (FD_BF16, FD_ERR_HIP, FD_ERR_INVALID_ARG,  # noqa: F401
-                       FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32, FD_OK,
+                       FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32,
+                       FD_FLAG_FUSED_MERGE, FD_MERGE_FUSED, FD_MERGE_NONE,
+                       FD_MERGE_SEPARATE, FD_OK,
                        FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
                        LIB_PATH, FdError, fd_decode, fd_decode_ex, fd_plan,
                        fd_status_string, fd_version, fd_workspace_bytes,

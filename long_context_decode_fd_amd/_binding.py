@@ -25,6 +25,10 @@ FD_ERR_HIP = -4
 FD_VARIANT_AUTO = 0
 FD_VARIANT_MFMA = 1
 FD_VARIANT_VALU = 2
+FD_FLAG_FUSED_MERGE = 1
+FD_MERGE_NONE = 0
+FD_MERGE_FUSED = 1
+FD_MERGE_SEPARATE = 2
 
 # Every function the C header declares, with its ctypes signature.
 _vp, _i32p = ctypes.c_void_p, ctypes.c_void_p
@@ -34,18 +38,20 @@ _ci, _cf, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 class FdPlanStruct(ctypes.Structure):
     _fields_ = [("num_splits", _ci), ("chunk", _ci), ("variant", _ci),
                 ("waves_per_block", _ci), ("grid", _ci), ("combine", _ci),
-                ("num_cus", _ci), ("workspace_bytes", _sz)]
+                ("merge", _ci), ("num_cus", _ci), ("workspace_bytes", _sz),
+                ("ticket_bytes", _sz)]
 
 
 SIGNATURES = {
     "fd_decode": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci, _cf,
                         _ci, _vp, _vp, _vp]),
     "fd_decode_ex": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci,
-                           _cf, _ci, _vp, _vp, _ci, _ci, _vp, _sz, _vp]),
-    "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                           _cf, _ci, _vp, _vp, _ci, _ci, _ci, _vp, _sz,
+                           _vp]),
+    "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                       ctypes.POINTER(FdPlanStruct)]),
     "fd_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
-                                 _ci]),
+                                 _ci, _ci]),
     "fd_status_string": (ctypes.c_char_p, [_ci]),
     "fd_version": (_ci, []),
 }
@@ -101,11 +107,11 @@ def _dtype_code(dtype) -> int:
 
 
 def fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen=False, num_splits=0,
-            variant=FD_VARIANT_AUTO, num_cus=0) -> dict:
+            variant=FD_VARIANT_AUTO, flags=0, num_cus=0) -> dict:
     """The planner's decision (see fd.h); num_cus 0 = query the device."""
     p = FdPlanStruct()
     rc = load_library().fd_plan(B, Hq, Hkv, D, Lmax, _dtype_code(dtype),
-                                int(bool(varlen)), num_splits, variant,
+                                int(bool(varlen)), num_splits, variant, flags,
                                 num_cus, ctypes.byref(p))
     if rc != FD_OK:
         raise FdError("fd_plan", rc)
@@ -113,10 +119,11 @@ def fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen=False, num_splits=0,
 
 
 def fd_workspace_bytes(B, Hq, Hkv, D, Lmax, dtype, varlen=False,
-                       num_splits=0, variant=FD_VARIANT_AUTO) -> int:
+                       num_splits=0, variant=FD_VARIANT_AUTO,
+                       flags=0) -> int:
     return int(load_library().fd_workspace_bytes(
         B, Hq, Hkv, D, Lmax, _dtype_code(dtype), int(bool(varlen)),
-        num_splits, variant))
+        num_splits, variant, flags))
 
 
 def _check(q, k_cache, v_cache, seqlens, out, lse):
@@ -161,14 +168,15 @@ def _stream_handle(stream, device):
 
 
 def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
-                 num_splits=0, variant=FD_VARIANT_AUTO, workspace=None,
-                 stream=None):
+                 num_splits=0, variant=FD_VARIANT_AUTO, flags=0,
+                 workspace=None, stream=None):
     """out, lse = attention(q, k_cache, v_cache) -- see fd.h.
 
     q [B,Hq,D], k_cache/v_cache [B,Hkv,Lmax,D] (bf16 or fp32, on the GPU),
     seqlens int32 [B] on the GPU or None, scale a float.  Returns (out, lse);
-    out/lse are allocated if not given.  workspace: a uint8 device tensor
-    of at least fd_workspace_bytes(...) bytes, or None for the library's.
+    out/lse are allocated if not given.  workspace: a zero-filled uint8
+    device tensor of at least fd_workspace_bytes(...) bytes (see fd.h for
+    the ticket rule), or None for the library's.
     """
     dims, out, lse = _check(q, k_cache, v_cache, seqlens, out, lse)
     B, Hq, Hkv, D, Lmax = dims
@@ -183,7 +191,7 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
         out.data_ptr(), lse.data_ptr(), int(num_splits), int(variant),
-        ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+        int(flags), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
     if rc != FD_OK:
         raise FdError("fd_decode_ex", rc)
     return out, lse

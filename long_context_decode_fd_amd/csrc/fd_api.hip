@@ -42,13 +42,19 @@ int device_cus(int *out) {
 
 // Library-owned workspace, one per device, grown on demand.  Growing frees
 // the old buffer; hipFree waits for the device, so work still queued on
-// the old buffer completes first.
+// the old buffer completes first.  The fused merge needs its leading ticket
+// bytes to be zero: calls leave their own tickets zero, and zero_bytes
+// tracks how much of the head is known to be zero (a call's partials start
+// right after its tickets, so a call with fewer groups shrinks it).  When a
+// call needs more, the head is cleared on the caller's stream first.
 struct OwnedWorkspace {
   void *ptr = nullptr;
   size_t bytes = 0;
+  size_t zero_bytes = 0;
 };
 
-int owned_workspace(size_t need, void **out) {
+int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
+                    void **out) {
   static std::mutex mu;
   static std::vector<OwnedWorkspace> ws;
   int dev = 0;
@@ -70,7 +76,14 @@ int owned_workspace(size_t need, void **out) {
       return FD_ERR_WORKSPACE;
     }
     w.bytes = sz;
+    w.zero_bytes = 0;
   }
+  if (ticket_bytes > w.zero_bytes) {
+    if (hipMemsetAsync(w.ptr, 0, ticket_bytes, stream) != hipSuccess)
+      return FD_ERR_HIP;
+  }
+  // This call's partials overwrite everything after its tickets.
+  w.zero_bytes = ticket_bytes;
   *out = w.ptr;
   return FD_OK;
 }
@@ -94,14 +107,14 @@ extern "C" {
 int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *seqlens, int B, int Hq, int Hkv, int D,
                  int Lmax, float scale, fd_dtype_t dtype, void *out,
-                 float *lse, int num_splits, int variant, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+                 float *lse, int num_splits, int variant, int flags,
+                 void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_pointers(q, k_cache, v_cache, seqlens, out, lse, scale);
   if (rc != FD_OK) return rc;
   rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
   if (num_splits < 0 || variant < FD_VARIANT_AUTO ||
-      variant > FD_VARIANT_VALU)
+      variant > FD_VARIANT_VALU || (flags & ~FD_FLAG_FUSED_MERGE))
     return FD_ERR_INVALID_ARG;
   if (workspace == nullptr && workspace_bytes != 0) return FD_ERR_INVALID_ARG;
   if (workspace && !aligned(workspace, 256)) return FD_ERR_INVALID_ARG;
@@ -111,7 +124,7 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   if (rc != FD_OK) return rc;
   fd::Plan p;
   rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, seqlens != nullptr,
-                     num_splits, variant, ncu, &p);
+                     num_splits, variant, flags, ncu, &p);
   if (rc != FD_OK) return rc;
 
   fd::LaunchArgs a{};
@@ -125,13 +138,15 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   a.stream = stream;
   if (p.combine) {
     void *ws = workspace;
+    const fd::WorkspaceLayout lay = fd::workspace_layout(p);
     if (ws) {
       if (workspace_bytes < p.ws_bytes) return FD_ERR_WORKSPACE;
     } else {
-      rc = owned_workspace(p.ws_bytes, &ws);
+      rc = owned_workspace(p.ws_bytes, lay.ticket_bytes,
+                           static_cast<hipStream_t>(stream), &ws);
       if (rc != FD_OK) return rc;
     }
-    const fd::WorkspaceLayout lay = fd::workspace_layout(p);
+    a.tickets = lay.ticket_bytes ? static_cast<int *>(ws) : nullptr;
     a.o_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                          lay.o_part_off);
     a.lse_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
@@ -145,12 +160,12 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
               int Lmax, float scale, fd_dtype_t dtype, void *out, float *lse,
               void *stream) {
   return fd_decode_ex(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax,
-                      scale, dtype, out, lse, 0, FD_VARIANT_AUTO, nullptr, 0,
-                      stream);
+                      scale, dtype, out, lse, 0, FD_VARIANT_AUTO, 0, nullptr,
+                      0, stream);
 }
 
 int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
-            int varlen, int num_splits, int variant, int num_cus,
+            int varlen, int num_splits, int variant, int flags, int num_cus,
             fd_plan_t *plan) {
   if (!plan) return FD_ERR_INVALID_ARG;
   int rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
@@ -162,7 +177,7 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   }
   fd::Plan p;
   rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, varlen != 0, num_splits,
-                     variant, num_cus, &p);
+                     variant, flags, num_cus, &p);
   if (rc != FD_OK) return rc;
   plan->num_splits = p.splits;
   plan->chunk = p.chunk;
@@ -170,17 +185,20 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   plan->waves_per_block = p.waves;
   plan->grid = p.grid;
   plan->combine = p.combine ? 1 : 0;
+  plan->merge = !p.combine ? FD_MERGE_NONE
+                           : (p.fused ? FD_MERGE_FUSED : FD_MERGE_SEPARATE);
   plan->num_cus = p.num_cus;
   plan->workspace_bytes = p.ws_bytes;
+  plan->ticket_bytes = fd::workspace_layout(p).ticket_bytes;
   return FD_OK;
 }
 
 size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
                           fd_dtype_t dtype, int varlen, int num_splits,
-                          int variant) {
+                          int variant, int flags) {
   fd_plan_t p;
-  if (fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen, num_splits, variant, 0,
-              &p) != FD_OK)
+  if (fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen, num_splits, variant, flags,
+              0, &p) != FD_OK)
     return 0;
   return p.workspace_bytes;
 }

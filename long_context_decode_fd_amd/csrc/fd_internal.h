@@ -26,8 +26,9 @@ struct Plan {
   int chunk;        // keys per chunk (multiple of kKeyTile)
   int splits;       // ceil(Lmax / chunk)
   int grid;         // workgroups of the per-chunk pass (upper bound)
-  bool combine;     // partials + merge pass (splits > 1)
-  size_t ws_bytes;  // partial outputs + partial lse
+  bool combine;     // chunks leave partials to be merged (splits > 1)
+  bool fused;       // merged by the last workgroup of each group
+  size_t ws_bytes;  // tickets + partial outputs + partial lse
 };
 
 // Host-side checks of sizes/dtype shared by fd_plan and the decode calls.
@@ -36,11 +37,13 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype);
 // Fills *p for a validated shape; requested_splits 0 = heuristic.
 int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
               bool varlen, int requested_splits, int requested_variant,
-              int num_cus, Plan *p);
+              int flags, int num_cus, Plan *p);
 
-// Byte offsets of the two partial arrays inside a workspace.
+// Byte offsets inside a workspace: the fused merge's per-group tickets
+// (int32 [B * Hkv], must be zero when a call starts; the kernels leave
+// them zero) come first, then the partial outputs and partial lse.
 struct WorkspaceLayout {
-  size_t o_part_off, lse_part_off, total;
+  size_t ticket_bytes, o_part_off, lse_part_off, total;
 };
 WorkspaceLayout workspace_layout(const Plan &p);
 
@@ -52,6 +55,7 @@ struct LaunchArgs {
   float *lse;
   float *o_part;
   float *lse_part;
+  int *tickets;
   float scale;
   void *stream;
 };

@@ -37,6 +37,22 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// K/V are streamed exactly once per call: nontemporal loads keep them from
+// displacing lines that are reused (q, partials) and measurably raise the
+// sustained read rate on MI355X.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4 t =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2 *p) {
+  const u32x2 t =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  return make_uint2(t.x, t.y);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -52,12 +68,18 @@ __device__ __forceinline__ int clamp_len(int L, int Lmax) {
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
 }
 
+// What a per-chunk workgroup does with its result.
+constexpr int kModeDirect = 0;    // one chunk per sequence: write out/lse
+constexpr int kModePartial = 1;   // write the chunk partial (merge kernel)
+constexpr int kModeFused = 2;     // partial, then the last one merges
+
 // ---------------------------------------------------------------------------
 // Work decomposition shared by the per-chunk kernels and the merge kernel.
 
 struct Work {
   int b, g, s;
   int lo, hi;  // keys [lo, hi) of slab (b, g); lo == hi only when L_b == 0
+  int nb;      // chunks of sequence b
   bool valid;
 };
 
@@ -75,7 +97,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
                           int Hkv, int Lmax, int C) {
   Work w;
   w.valid = false;
-  w.b = w.g = w.s = w.lo = w.hi = 0;
+  w.b = w.g = w.s = w.lo = w.hi = w.nb = 0;
   if (seqlens == nullptr) {
     const int S = (Lmax + C - 1) / C;
     const int per_b = S * Hkv;
@@ -87,6 +109,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
     w.g = r - w.s * Hkv;
     w.lo = w.s * C;
     w.hi = min(w.lo + C, Lmax);
+    w.nb = S;
     w.valid = true;
     return w;
   }
@@ -117,6 +140,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
       w.g = r - w.s * Hkv;
       w.lo = w.s * C;
       w.hi = max(w.lo, min(w.lo + C, Lb));
+      w.nb = chunks_of(Lb, C);
       w.valid = true;
       return w;
     }
@@ -155,7 +179,7 @@ template <int D, typename OutT>
 __device__ void merge_and_store(const float *sm_m, const float *sm_l,
                                 const float *sm_o, int nslot, int rows,
                                 int G, const Work &w, int Hq, int S,
-                                bool partial, OutT *__restrict__ out,
+                                int mode, OutT *__restrict__ out,
                                 float *__restrict__ lse,
                                 float *__restrict__ o_part,
                                 float *__restrict__ lse_part) {
@@ -178,15 +202,212 @@ __device__ void merge_and_store(const float *sm_m, const float *sm_l,
       ls = (M + log2_f(Ls)) * kLn2;
     }
     const size_t hq = (size_t)w.b * Hq + (size_t)w.g * G + h;
-    if (!partial) {
+    if (mode == kModeDirect) {
       store_out<OutT>(out + hq * D + d, o);
       if (d == 0) lse[hq] = ls;
-    } else {
+    } else if (mode == kModePartial) {
       const size_t row = hq * S + w.s;
       o_part[row * D + d] = o;
       if (d == 0) lse_part[row] = ls;
+    } else {
+      // Read by another workgroup of this launch, possibly on another XCD:
+      // device-coherent stores (written through the local L2).
+      const size_t row = hq * S + w.s;
+      __hip_atomic_store(o_part + row * D + d, o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0)
+        __hip_atomic_store(lse_part + row, ls, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused merge: the last workgroup of a (b, g) group merges its chunks.
+//
+// Every workgroup that wrote a chunk partial takes a ticket from its
+// group's counter.  The one that takes ticket nb - 1 knows that all nb
+// partials of the group are written; it merges them into out/lse exactly
+// as the separate merge pass would and puts the counter back to zero for
+// the next call.  Ordering across the eight XCDs (separate L2 caches): an
+// agent-scope release fence after the workgroup barrier and before the
+// ticket, and an agent-scope acquire fence in the last workgroup before it
+// reads the other workgroups' partials.  No workgroup ever waits for
+// another, so there is no co-residency requirement.
+//
+// The merge spreads the group's G x D outputs over the workgroup as
+// (row, 4 columns) items; when there are fewer items than threads, each
+// item's chunks are split over `slices` threads whose states meet in LDS.
+constexpr int kTailBatch = 16;
+
+// s_waitcnt with vmcnt(0) and the other counters left alone (gfx9 layout:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr unsigned kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct TailState {
+  float M, W;   // running max (natural-log units) and rescaled weight sum
+  float4 acc;   // rescaled weighted sum of 4 output columns
+};
+
+// Folds chunks s = s_first, s_first + s_step, ... of item `it` (query row
+// it / (D/4) of the group, columns 4 (it % (D/4)) ..) into a TailState,
+// kTailBatch chunks per step with all of a step's loads issued first.
+template <int D>
+__device__ TailState merge_item(const Work &w, int G, int Hq, int S, int it,
+                                int s_first, int s_step,
+                                const float *__restrict__ o_part,
+                                const float *__restrict__ lse_part) {
+  constexpr int V4 = D / 4;
+  const int h = it / V4, d4 = it - h * V4;
+  const size_t row = (size_t)w.b * Hq + (size_t)w.g * G + h;
+  const float *lp = lse_part + row * S;
+  const float *op = o_part + row * S * D + d4 * 4;
+  TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int s0 = s_first; s0 < w.nb; s0 += s_step * kTailBatch) {
+    float ls[kTailBatch];
+    float4 ov[kTailBatch];
+#pragma unroll
+    for (int j = 0; j < kTailBatch; ++j) {
+      const int s = s0 + j * s_step;
+      const int sc = s < w.nb ? s : s0;
+      ls[j] = s < w.nb ? load_coherent(lp + sc) : FD_NEG_INF;
+      const float *o4 = op + (size_t)sc * D;
+      ov[j] = make_float4(load_coherent(o4), load_coherent(o4 + 1),
+                          load_coherent(o4 + 2), load_coherent(o4 + 3));
+    }
+    float mb = ls[0];
+#pragma unroll
+    for (int j = 1; j < kTailBatch; ++j) mb = fmaxf(mb, ls[j]);
+    const float Mn = fmaxf(st.M, mb);
+    if (Mn == FD_NEG_INF) continue;
+    const float r = exp2_f((st.M - Mn) * kLog2e);
+    st.W *= r;
+    st.acc.x *= r;
+    st.acc.y *= r;
+    st.acc.z *= r;
+    st.acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < kTailBatch; ++j) {
+      const float wt = exp2_f((ls[j] - Mn) * kLog2e);
+      st.W += wt;
+      st.acc.x += wt * ov[j].x;
+      st.acc.y += wt * ov[j].y;
+      st.acc.z += wt * ov[j].z;
+      st.acc.w += wt * ov[j].w;
+    }
+    st.M = Mn;
+  }
+  return st;
+}
+
+// Writes 4 output columns of one row (and the row's lse with the first 4).
+template <int D, typename OutT>
+__device__ void store_item(const Work &w, int G, int Hq, int it, float M,
+                           float W, float4 a, OutT *__restrict__ out,
+                           float *__restrict__ lse) {
+  constexpr int V4 = D / 4;
+  const int h = it / V4, d4 = it - h * V4;
+  const size_t row = (size_t)w.b * Hq + (size_t)w.g * G + h;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = FD_NEG_INF;
+  if (M != FD_NEG_INF) {
+    o = make_float4(a.x / W, a.y / W, a.z / W, a.w / W);
+    ls = M + log2_f(W) * kLn2;
+  }
+  OutT *dst = out + row * D + d4 * 4;
+  store_out<OutT>(dst + 0, o.x);
+  store_out<OutT>(dst + 1, o.y);
+  store_out<OutT>(dst + 2, o.z);
+  store_out<OutT>(dst + 3, o.w);
+  if (d4 == 0) lse[row] = ls;
+}
+
+// Merges the nb chunk partials of group (w.b, w.g) into out/lse with the
+// whole workgroup (the fused path's last workgroup).
+template <int D, typename OutT>
+__device__ void group_merge(const Work &w, int G, int Hq, int S,
+                            const float *__restrict__ o_part,
+                            const float *__restrict__ lse_part,
+                            OutT *__restrict__ out, float *__restrict__ lse,
+                            float *scratch) {
+  constexpr int V4 = D / 4;
+  const int T = blockDim.x, tid = threadIdx.x;
+  const int items = G * V4;
+  // More items than threads: each thread merges whole items on its own.
+  // Otherwise each item's chunks are split over `slices` threads.
+  const int slices = max(1, T / items);
+  if (slices == 1) {
+    for (int it = tid; it < items; it += T) {
+      const TailState st = merge_item<D>(w, G, Hq, S, it, 0, 1, o_part,
+                                         lse_part);
+      store_item<D, OutT>(w, G, Hq, it, st.M, st.W, st.acc, out, lse);
+    }
+    return;
+  }
+  float *sM = scratch, *sW = scratch + T;
+  float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
+  TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (tid < items * slices)
+    st = merge_item<D>(w, G, Hq, S, tid % items, tid / items, slices, o_part,
+                       lse_part);
+  sM[tid] = st.M;
+  sW[tid] = st.W;
+  sA[tid] = st.acc;
+  __syncthreads();
+  if (tid < items) {
+    const int it = tid;
+    float Mt = FD_NEG_INF;
+    for (int sl = 0; sl < slices; ++sl) Mt = fmaxf(Mt, sM[sl * items + it]);
+    float Wt = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (Mt != FD_NEG_INF) {
+      for (int sl = 0; sl < slices; ++sl) {
+        const int k = sl * items + it;
+        const float r = exp2_f((sM[k] - Mt) * kLog2e);
+        Wt += r * sW[k];
+        a.x += r * sA[k].x;
+        a.y += r * sA[k].y;
+        a.z += r * sA[k].z;
+        a.w += r * sA[k].w;
+      }
+    }
+    store_item<D, OutT>(w, G, Hq, it, Mt, Wt, a, out, lse);
+  }
+}
+
+template <int D, typename OutT>
+__device__ void merge_group_if_last(const Work &w, int G, int Hq, int Hkv,
+                                    int S, const float *__restrict__ o_part,
+                                    const float *__restrict__ lse_part,
+                                    int *__restrict__ tickets,
+                                    OutT *__restrict__ out,
+                                    float *__restrict__ lse, float *scratch,
+                                    int *sm_flag) {
+  // Each thread waits until its device-coherent partial stores have
+  // completed; after the barrier all of the workgroup's partials are
+  // visible device-wide, so the relaxed ticket cannot overtake them.  (An
+  // agent-scope release fence would also write back this XCD's whole L2,
+  // once per workgroup: far too slow here.)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int *t = tickets + (size_t)w.b * Hkv + w.g;
+    const int prev = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == w.nb - 1;
+    if (last)
+      __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sm_flag = last;
+  }
+  __syncthreads();
+  if (!*sm_flag) return;
+  // The last workgroup reads the partials with device-coherent loads,
+  // issued only after its ticket came back.
+  group_merge<D, OutT>(w, G, Hq, S, o_part, lse_part, out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -249,15 +470,15 @@ __device__ __forceinline__ void mfma_tile(
     const uint16_t *p = kslab + (size_t)(k0 + r) * D + q4 * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      kr[sub][kk] = *reinterpret_cast<const uint4 *>(p + kk * 32);
+      kr[sub][kk] = load_stream(reinterpret_cast<const uint4 *>(p + kk * 32));
   }
   VT vr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int r = (i >> 2) * 16 + q4 * 4 + (i & 3);
     if (TAIL) r = min(r, valid - 1);
-    vr[i] = *reinterpret_cast<const VT *>(vslab + (size_t)(k0 + r) * D +
-                                          n16 * VW);
+    vr[i] = load_stream(
+        reinterpret_cast<const VT *>(vslab + (size_t)(k0 + r) * D + n16 * VW));
   }
 
   floatx4 sc[2];
@@ -340,13 +561,16 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     int B, int Hq, int Hkv, int G, int Lmax, int C, int S, float scale_log2,
-    int partial, uint16_t *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ o_part, float *__restrict__ lse_part) {
+    int mode, uint16_t *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part,
+    int *__restrict__ tickets) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
+  static_assert(16 * (D + 1) >= 6 * 64, "LDS reused by the fused merge");
   __shared__ float sm_m[NW * 16];
   __shared__ float sm_l[NW * 16];
-  __shared__ float sm_o[NW * 16 * (D + 1)];
+  __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
+  __shared__ int sm_flag;
 
   const Work w = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
   if (!w.valid) return;
@@ -401,7 +625,10 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
   }
   __syncthreads();
   merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, G, w, Hq, S,
-                               partial != 0, out, lse, o_part, lse_part);
+                               mode, out, lse, o_part, lse_part);
+  if (mode == kModeFused)
+    merge_group_if_last<D, uint16_t>(w, G, Hq, Hkv, S, o_part, lse_part,
+                                     tickets, out, lse, sm_o, &sm_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,18 +646,18 @@ template <>
 struct Elem<float> {
   static constexpr int kPerLane = 4;
   __device__ static void load(const float *p, float (&x)[4]) {
-    const float4 t = *reinterpret_cast<const float4 *>(p);
-    x[0] = t.x;
-    x[1] = t.y;
-    x[2] = t.z;
-    x[3] = t.w;
+    const uint4 t = load_stream(reinterpret_cast<const uint4 *>(p));
+    x[0] = __builtin_bit_cast(float, t.x);
+    x[1] = __builtin_bit_cast(float, t.y);
+    x[2] = __builtin_bit_cast(float, t.z);
+    x[3] = __builtin_bit_cast(float, t.w);
   }
 };
 template <>
 struct Elem<uint16_t> {
   static constexpr int kPerLane = 8;
   __device__ static void load(const uint16_t *p, float (&x)[8]) {
-    const uint4 t = *reinterpret_cast<const uint4 *>(p);
+    const uint4 t = load_stream(reinterpret_cast<const uint4 *>(p));
     const uint32_t d[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -444,18 +671,22 @@ template <typename T, int D, int NW, int GT>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ seqlens, int B, int Hq, int Hkv, int G,
-    int Lmax, int C, int S, float scale_log2, int partial,
+    int Lmax, int C, int S, float scale_log2, int mode,
     T *__restrict__ out, float *__restrict__ lse, float *__restrict__ o_part,
-    float *__restrict__ lse_part) {
+    float *__restrict__ lse_part, int *__restrict__ tickets) {
   constexpr int EPL = Elem<T>::kPerLane;
   constexpr int LPR = D / EPL;
   constexpr int RPW = 64 / LPR;
   constexpr int U = 4;
   constexpr int TK = U * RPW;
   constexpr int NSLOT = NW * RPW;
+  constexpr int kMergeFloats = NSLOT * GT * (D + 1);
+  constexpr int kTailFloats = 6 * NW * 64;
   __shared__ float sm_m[NSLOT * GT];
   __shared__ float sm_l[NSLOT * GT];
-  __shared__ float sm_o[NSLOT * GT * (D + 1)];
+  __shared__ __align__(16) float
+      sm_o[kMergeFloats > kTailFloats ? kMergeFloats : kTailFloats];
+  __shared__ int sm_flag;
 
   const Work w = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
   if (!w.valid) return;
@@ -557,62 +788,106 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     }
   }
   __syncthreads();
-  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, G, w, Hq, S,
-                        partial != 0, out, lse, o_part, lse_part);
+  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, G, w, Hq, S, mode, out,
+                        lse, o_part, lse_part);
+  if (mode == kModeFused)
+    merge_group_if_last<D, T>(w, G, Hq, Hkv, S, o_part, lse_part, tickets,
+                              out, lse, sm_o, &sm_flag);
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the chunks: one wavefront per (b, query head).
-// M = max_s lse_s, w_s = exp(lse_s - M), out = sum w_s o_s / sum w_s,
-// lse = M + ln sum w_s.  Summation order is fixed (s ascending), so a given
-// chunking always gives the same bits.
+// Merge pass (the default): one workgroup of kMergeWaves wavefronts per
+// (b, query head) row; wavefront w folds chunks w, w + kMergeWaves, ...
+// into a running (M, W, acc) kMergeBatch chunks at a time, all of a batch's
+// loads issued before any is used (the pass is latency-bound: a few MB).
+// Per batch: M' = max(M, max_s lse_s), r = e^(M - M'),
+//   W = r W + sum_s e^(lse_s - M'),  acc = r acc + sum_s e^(lse_s - M') o_s.
+// The wavefronts then meet in LDS the same way; out = acc / W and
+// lse = M + ln W.  Fixed order everywhere: same chunking, same bits.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 16;
+
 template <int D, typename OutT>
-__global__ __launch_bounds__(64) void combine_kernel(
+__global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
     const int32_t *__restrict__ seqlens, int Hq, int Lmax, int C, int S,
     OutT *__restrict__ out, float *__restrict__ lse) {
-  constexpr int DPL = D / 64;
+  constexpr int DPL = D / 64;  // output columns per lane
+  __shared__ float sm_M[kMergeWaves], sm_W[kMergeWaves];
+  __shared__ float sm_acc[kMergeWaves][D];
   const int row = blockIdx.x;
   const int b = row / Hq;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
   const int nb = min(S, chunks_of(L, C));
   const float *lp = lse_part + (size_t)row * S;
   const float *op = o_part + (size_t)row * S * D + lane * DPL;
 
-  float M = FD_NEG_INF;
-  for (int s = lane; s < nb; s += 64) M = fmaxf(M, lp[s]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-
-  float acc[DPL];
+  float M = FD_NEG_INF, W = 0.f, acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  float W = 0.f;
-  if (M != FD_NEG_INF) {
-    const float Ml2 = M * kLog2e;
-#pragma unroll 4
-    for (int s = 0; s < nb; ++s) {
-      const float wt = exp2_f(lp[s] * kLog2e - Ml2);
+  for (int s0 = wave; s0 < nb; s0 += kMergeWaves * kMergeBatch) {
+    float ls[kMergeBatch], ov[kMergeBatch][DPL];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int s = s0 + j * kMergeWaves;
+      const int sc = s < nb ? s : s0;
+      ls[j] = s < nb ? lp[sc] : FD_NEG_INF;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) ov[j][i] = op[(size_t)sc * D + i];
+    }
+    float mb = ls[0];
+#pragma unroll
+    for (int j = 1; j < kMergeBatch; ++j) mb = fmaxf(mb, ls[j]);
+    const float Mn = fmaxf(M, mb);
+    if (Mn == FD_NEG_INF) continue;
+    const float r = exp2_f((M - Mn) * kLog2e);
+    W *= r;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] *= r;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float wt = exp2_f((ls[j] - Mn) * kLog2e);
       W += wt;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] += wt * op[(size_t)s * D + i];
+      for (int i = 0; i < DPL; ++i) acc[i] += wt * ov[j][i];
     }
+    M = Mn;
   }
-  OutT *o = out + (size_t)row * D + lane * DPL;
-  if (M == FD_NEG_INF) {
+  if (lane == 0) {
+    sm_M[wave] = M;
+    sm_W[wave] = W;
+  }
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) store_out<OutT>(o + i, 0.f);
-    if (lane == 0) lse[row] = FD_NEG_INF;
-  } else {
+  for (int i = 0; i < DPL; ++i) sm_acc[wave][lane * DPL + i] = acc[i];
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float Mt = FD_NEG_INF;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) store_out<OutT>(o + i, acc[i] / W);
-    if (lane == 0) lse[row] = M + log2_f(W) * kLn2;
+    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sm_M[w]);
+    float o = 0.f, ls_out = FD_NEG_INF;
+    if (Mt != FD_NEG_INF) {
+      float Wt = 0.f, a = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMergeWaves; ++w) {
+        const float r = exp2_f((sm_M[w] - Mt) * kLog2e);
+        Wt += r * sm_W[w];
+        a += r * sm_acc[w][d];
+      }
+      o = a / Wt;
+      ls_out = Mt + log2_f(Wt) * kLn2;
+    }
+    store_out<OutT>(out + (size_t)row * D + d, o);
+    if (d == 0) lse[row] = ls_out;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host-side dispatch.
+
+int mode_of(const Plan &p) {
+  return !p.combine ? kModeDirect : (p.fused ? kModeFused : kModePartial);
+}
 
 template <typename T, int D, int NW>
 hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
@@ -622,7 +897,7 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
   const T *k = static_cast<const T *>(a.k);
   const T *v = static_cast<const T *>(a.v);
   T *out = static_cast<T *>(a.out);
-  const int part = p.combine ? 1 : 0;
+  const int part = mode_of(p);
   int gt = 1;
   while (gt < p.G) gt <<= 1;
 #define FD_VALU_CASE(GTV)                                                    \
@@ -630,7 +905,7 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
     hipLaunchKernelGGL((split_valu_kernel<T, D, NW, GTV>), grid, block, 0,   \
                        st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G, p.Lmax, \
                        p.chunk, p.splits, sl2, part, out, a.lse, a.o_part,    \
-                       a.lse_part);                                          \
+                       a.lse_part, a.tickets);                               \
     break;
   switch (gt) {
     FD_VALU_CASE(1)
@@ -642,14 +917,15 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
           hipLaunchKernelGGL((split_valu_kernel<T, D, NW, 8>), grid, block, 0,
                              st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G,
                              p.Lmax, p.chunk, p.splits, sl2, part, out, a.lse,
-                             a.o_part, a.lse_part);
+                             a.o_part, a.lse_part, a.tickets);
           break;
         }
         if (gt == 16) {
           hipLaunchKernelGGL((split_valu_kernel<T, D, 2, 16>), grid,
                              dim3(2 * 64), 0, st, q, k, v, a.seqlens, p.B,
                              p.Hq, p.Hkv, p.G, p.Lmax, p.chunk, p.splits, sl2,
-                             part, out, a.lse, a.o_part, a.lse_part);
+                             part, out, a.lse, a.o_part, a.lse_part,
+                             a.tickets);
           break;
         }
       }
@@ -663,7 +939,7 @@ template <int D>
 hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
                        hipStream_t st) {
   const dim3 grid(p.grid);
-  const int part = p.combine ? 1 : 0;
+  const int part = mode_of(p);
   const uint16_t *q = static_cast<const uint16_t *>(a.q);
   const uint16_t *k = static_cast<const uint16_t *>(a.k);
   const uint16_t *v = static_cast<const uint16_t *>(a.v);
@@ -673,7 +949,7 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
     hipLaunchKernelGGL((split_mfma_kernel<D, NWV>), grid, dim3(NWV * 64), 0, \
                        st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G, p.Lmax, \
                        p.chunk, p.splits, sl2, part, out, a.lse, a.o_part,    \
-                       a.lse_part);                                          \
+                       a.lse_part, a.tickets);                               \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(1)
@@ -689,9 +965,10 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
 
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Hq), dim3(64), 0,
-                     st, a.o_part, a.lse_part, a.seqlens, p.Hq, p.Lmax,
-                     p.chunk, p.splits, static_cast<OutT *>(a.out), a.lse);
+  hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Hq),
+                     dim3(kMergeWaves * 64), 0, st, a.o_part, a.lse_part,
+                     a.seqlens, p.Hq, p.Lmax, p.chunk, p.splits,
+                     static_cast<OutT *>(a.out), a.lse);
 }
 
 }  // namespace
@@ -713,7 +990,7 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   if (e != hipSuccess) return (int)e;
   e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  if (p.combine) {
+  if (p.combine && !p.fused) {
     if (p.dtype == FD_BF16) {
       if (p.D == 128)
         launch_combine<128, uint16_t>(p, a, st);

@@ -76,18 +76,19 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
 }
 
 WorkspaceLayout workspace_layout(const Plan &p) {
-  WorkspaceLayout w{0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0};
   if (!p.combine) return w;
   size_t rows = (size_t)p.B * p.Hq * p.splits;
-  w.o_part_off = 0;
-  w.lse_part_off = align256(rows * p.D * sizeof(float));
+  w.ticket_bytes = p.fused ? align256((size_t)p.B * p.Hkv * sizeof(int)) : 0;
+  w.o_part_off = w.ticket_bytes;
+  w.lse_part_off = w.o_part_off + align256(rows * p.D * sizeof(float));
   w.total = w.lse_part_off + align256(rows * sizeof(float));
   return w;
 }
 
 int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
               bool varlen, int requested_splits, int requested_variant,
-              int num_cus, Plan *p) {
+              int flags, int num_cus, Plan *p) {
   int rc = validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
   if (num_cus <= 0) return FD_ERR_INVALID_ARG;
@@ -95,6 +96,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_variant < FD_VARIANT_AUTO ||
       requested_variant > FD_VARIANT_VALU)
     return FD_ERR_INVALID_ARG;
+  if (flags & ~FD_FLAG_FUSED_MERGE) return FD_ERR_INVALID_ARG;
 
   Plan q{};
   q.B = B;
@@ -141,6 +143,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.chunk = chunk;
   q.splits = ceil_div(Lmax, chunk);
   q.combine = q.splits > 1;
+  q.fused = q.combine && (flags & FD_FLAG_FUSED_MERGE);
   long grid = (long)B * Hkv * q.splits;
   if (grid > 0x7FFFFFFFL) return FD_ERR_UNSUPPORTED;
   q.grid = (int)grid;

@@ -197,6 +197,56 @@ def gen_all(w: Workload):
     return q, k, v, seqlens
 
 
+def to_device(a: np.ndarray):
+    """Host array (uint16 bf16 bits or float32) -> torch device tensor."""
+    import torch
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+        return t.view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def device_inputs(w: Workload, seqlens=None, keep_host: bool = False):
+    """Upload a workload: (q, k, v, seqlens_dev, seqlens_host, host).
+
+    K/V are generated slab by slab on the host and copied into place; rows
+    at or beyond a sequence's length are filled with NaN bits on the
+    device.  ``host`` is (q, k, v) as host arrays when keep_host, else None.
+    """
+    import torch
+    if seqlens is None:
+        seqlens = gen_seqlens(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q_h = gen_q(w)
+    q = to_device(q_h)
+    shape = (w.B, w.Hkv, w.Lmax, w.D)
+    k = torch.empty(shape, dtype=tdt, device="cuda")
+    v = torch.empty(shape, dtype=tdt, device="cuda")
+    if seqlens is not None:
+        iv = torch.int16 if w.dtype == "bf16" else torch.int32
+        k.view(iv).fill_(-1)       # all-ones bit patterns are NaN
+        v.view(iv).fill_(-1)
+    host = None
+    if keep_host:
+        host = (q_h, np.empty(shape, w.np_dtype), np.empty(shape, w.np_dtype))
+    for b in range(w.B):
+        L = seqlen_of(w, seqlens, b)
+        for g in range(w.Hkv):
+            kr, vr = gen_slab_rows(w, b, g, L)
+            if L:
+                k[b, g, :L].copy_(to_device(kr))
+                v[b, g, :L].copy_(to_device(vr))
+            if keep_host:
+                host[1][b, g, :L], host[2][b, g, :L] = kr, vr
+                if L < w.Lmax:
+                    host[1][b, g, L:].view(np.uint8)[:] = 0xFF
+                    host[2][b, g, L:].view(np.uint8)[:] = 0xFF
+    sl_dev = None
+    if seqlens is not None:
+        sl_dev = torch.from_numpy(np.asarray(seqlens, np.int32)).to("cuda")
+    return q, k, v, sl_dev, seqlens, host
+
+
 def algorithmic_bytes(w: Workload, seqlens=None) -> int:
     """Bytes one decode step must move at minimum: every valid K and V row
     once, q, out, and the fp32 lse."""

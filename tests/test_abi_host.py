@@ -57,9 +57,9 @@ A = 1 << 20
 
 def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
             Lmax=64, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
-            variant=0, ws=None, ws_bytes=0):
+            variant=0, flags=0, ws=None, ws_bytes=0):
     return lib.fd_decode_ex(q, k, v, seqlens, B, Hq, Hkv, D, Lmax, scale,
-                            dtype, out, lse, num_splits, variant, ws,
+                            dtype, out, lse, num_splits, variant, flags, ws,
                             ws_bytes, None)
 
 
@@ -88,6 +88,8 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
     (dict(variant=3), fd.FD_ERR_INVALID_ARG),
     (dict(variant=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=2), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=-1), fd.FD_ERR_INVALID_ARG),
     (dict(ws=None, ws_bytes=64), fd.FD_ERR_INVALID_ARG),
     (dict(ws=A + 16, ws_bytes=1 << 20), fd.FD_ERR_INVALID_ARG),
 ])
@@ -96,7 +98,8 @@ def test_invalid_arguments_rejected_on_host(lib, kw, code):
 
 
 def test_fd_decode_rejects_like_ex(lib):
-    rc = lib.fd_decode(None, A, A, None, 1, 8, 8, 128, 64, 0.1, 0, A, A, None)
+    rc = lib.fd_decode(None, A, A, None, 1, 8, 8, 128, 64, 0.1, 0, A, A,
+                       None)
     assert rc == fd.FD_ERR_INVALID_ARG
     rc = lib.fd_decode(A, A, A, None, 1, 8, 8, 80, 64, 0.1, 0, A, A, None)
     assert rc == fd.FD_ERR_UNSUPPORTED
@@ -115,13 +118,19 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
     assert (p["num_splits"], p["chunk"], p["grid"], p["combine"]) == \
         (64, 1024, 512, 1)
     assert p["variant"] == fd.FD_VARIANT_MFMA
+    assert p["merge"] == fd.FD_MERGE_SEPARATE and p["ticket_bytes"] == 0
     assert p["workspace_bytes"] == 64 * 64 * 128 * 4 + 64 * 64 * 4
+    p = plan(W["b1_gqa8_h64_d128_l65536"], flags=fd.FD_FLAG_FUSED_MERGE)
+    assert p["merge"] == fd.FD_MERGE_FUSED
+    assert p["ticket_bytes"] == 256          # 8 int32 tickets, aligned
+    assert p["workspace_bytes"] == 256 + 64 * 64 * 128 * 4 + 64 * 64 * 4
     # 4 x 32 MHA heads at 32k: 128 units -> 4 chunks of 8192
     p = plan(W["b4_mha_h32_d128_l32768_peaked"])
     assert (p["num_splits"], p["chunk"], p["grid"]) == (4, 8192, 512)
     # 64 x 8 units already fill the chip: no split, no merge, no workspace
     p = plan(W["b64_gqa4_h32_d128_l4096"])
     assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == (1, 0, 0)
+    assert p["merge"] == fd.FD_MERGE_NONE
     assert p["grid"] == 512
     # var-len: balance-sized chunks over the padded length
     p = plan(W["varlen_b16_gqa8_h64_d128_lmax131072"])
@@ -148,6 +157,8 @@ def test_plan_rejections(lib):
     with pytest.raises(fd.FdError):        # bf16 vector path: G <= 4
         fd.fd_plan(1, 64, 8, 128, 64, "bf16", variant=fd.FD_VARIANT_VALU,
                    num_cus=256)
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(1, 8, 8, 128, 64, "bf16", flags=4, num_cus=256)
     assert plan(wl.WORKLOADS["b1_gqa8_h64_d128_l65536"],
                 num_splits=1)["workspace_bytes"] == 0
 

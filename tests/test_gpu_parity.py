@@ -86,6 +86,9 @@ def variants_for(w):
     return [fd.FD_VARIANT_MFMA]
 
 
+MERGES = [0, fd.FD_FLAG_FUSED_MERGE]
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 100000])
 def test_small_workloads_match_oracle(cuda, oracle_mod, name, num_splits):
@@ -93,11 +96,14 @@ def test_small_workloads_match_oracle(cuda, oracle_mod, name, num_splits):
     q, k, v, sl_dev, seqlens, host = inputs(name, w)
     ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
     for variant in variants_for(w):
-        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
-                                   num_splits=num_splits, variant=variant)
-        cuda.cuda.synchronize()
-        assert_parity(w, out, lse, ref_out, ref_lse,
-                      f"{name} S={num_splits} variant={variant}")
+        for flags in MERGES:
+            out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=num_splits, variant=variant,
+                                       flags=flags)
+            cuda.cuda.synchronize()
+            assert_parity(w, out, lse, ref_out, ref_lse,
+                          f"{name} S={num_splits} variant={variant} "
+                          f"flags={flags}")
 
 
 @pytest.mark.parametrize("G,D,dtype", [(8, 128, "bf16"), (1, 128, "bf16"),
@@ -116,13 +122,17 @@ def test_edge_lengths_with_nan_padding(cuda, oracle_mod, G, D, dtype,
     ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
     assert ref_lse[0, 0] == -np.inf
     for variant in variants_for(w):
-        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
-                                   num_splits=num_splits, variant=variant)
-        cuda.cuda.synchronize()
-        assert_parity(w, out, lse, ref_out, ref_lse,
-                      f"edge G={G} D={D} {dtype} S={num_splits} v={variant}")
-        o = out_to_host(out)
-        assert np.all(o[0] == 0) and np.all(lse.cpu().numpy()[0] == -np.inf)
+        for flags in MERGES:
+            out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=num_splits, variant=variant,
+                                       flags=flags)
+            cuda.cuda.synchronize()
+            assert_parity(w, out, lse, ref_out, ref_lse,
+                          f"edge G={G} D={D} {dtype} S={num_splits} "
+                          f"v={variant} f={flags}")
+            o = out_to_host(out)
+            assert np.all(o[0] == 0)
+            assert np.all(lse.cpu().numpy()[0] == -np.inf)
 
 
 def test_seqlens_out_of_range_are_clamped(cuda, oracle_mod):
@@ -136,17 +146,24 @@ def test_seqlens_out_of_range_are_clamped(cuda, oracle_mod):
     assert_parity(w, out, lse, ref_out, ref_lse, "clamped seqlens")
 
 
-def test_results_are_bitwise_deterministic(cuda):
-    w = SMALL["b1_gqa8"]
-    q, k, v, sl_dev, _, _ = inputs("b1_gqa8", w)
-    runs = []
-    for _ in range(3):
-        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7)
-        cuda.cuda.synchronize()
-        runs.append((out_to_host(out).copy(), lse.cpu().numpy().copy()))
-    for o, l_ in runs[1:]:
-        assert np.array_equal(o, runs[0][0])
-        assert np.array_equal(l_.view(np.uint32), runs[0][1].view(np.uint32))
+@pytest.mark.parametrize("name", ["b1_gqa8", "varlen_gqa8", "tiny_mha_f32"])
+def test_results_are_bitwise_deterministic(cuda, name):
+    """Same plan, same bits -- in particular whichever workgroup of a group
+    happens to finish last and run the fused merge."""
+    w = SMALL[name]
+    q, k, v, sl_dev, _, _ = inputs(name, w)
+    for flags in MERGES:
+        runs = []
+        for _ in range(4):
+            out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=7, flags=flags)
+            cuda.cuda.synchronize()
+            runs.append((out_to_host(out).copy(), lse.cpu().numpy().copy()))
+        for o, l_ in runs[1:]:
+            assert np.array_equal(o.view(np.uint16),
+                                  runs[0][0].view(np.uint16))
+            assert np.array_equal(l_.view(np.uint32),
+                                  runs[0][1].view(np.uint32))
 
 
 def test_negative_controls_fail_the_comparison(cuda, oracle_mod):
@@ -180,22 +197,34 @@ def test_negative_controls_fail_the_comparison(cuda, oracle_mod):
 def test_caller_workspace_and_streams(cuda, oracle_mod):
     w = SMALL["b1_gqa8"]
     q, k, v, sl_dev, seqlens, host = inputs("b1_gqa8", w)
+    F = fd.FD_FLAG_FUSED_MERGE
     need = fd.fd_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16",
-                                 num_splits=7)
-    p = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_splits=7)
-    assert need == p["workspace_bytes"] > 0
-    ws = cuda.empty(need, dtype=cuda.uint8, device="cuda")
+                                 num_splits=7, flags=F)
+    p = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_splits=7,
+                   flags=F)
+    assert need == p["workspace_bytes"] > 0 and p["ticket_bytes"] > 0
+    ws = cuda.zeros(need, dtype=cuda.uint8, device="cuda")
     s = cuda.cuda.Stream()
-    with cuda.cuda.stream(s):
-        out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7,
-                                   workspace=ws)
-    s.synchronize()
-    ref = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7)
-    cuda.cuda.synchronize()
-    assert np.array_equal(out_to_host(out), out_to_host(ref[0]))
-    small = cuda.empty(need - 256, dtype=cuda.uint8, device="cuda")
+    for flags in (0, F):
+        with cuda.cuda.stream(s):
+            out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=7, flags=flags,
+                                       workspace=ws)
+        s.synchronize()
+        ref = fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7,
+                              flags=flags)
+        cuda.cuda.synchronize()
+        assert np.array_equal(out_to_host(out), out_to_host(ref[0]))
+        if flags == 0:
+            # a separate-merge call keeps partials from byte 0 on: zero the
+            # ticket region again before the fused call (fd.h's rule)
+            ws[:p["ticket_bytes"]].zero_()
+        else:
+            # the fused merge leaves its tickets at zero for the next call
+            assert int(ws[:p["ticket_bytes"]].count_nonzero()) == 0
+    small = cuda.zeros(need - 256, dtype=cuda.uint8, device="cuda")
     with pytest.raises(fd.FdError) as e:
-        fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7,
+        fd.fd_decode_ex(q, k, v, sl_dev, w.scale, num_splits=7, flags=F,
                         workspace=small)
     assert e.value.code == fd.FD_ERR_WORKSPACE
     # no merge needed -> no workspace needed
@@ -223,3 +252,59 @@ def test_nan_in_valid_prefix_propagates(cuda):
     o = out.float().cpu().numpy()
     assert np.isnan(o[0, 3 * w.G:(3 + 1) * w.G]).all()
     assert np.isfinite(o[0, :3 * w.G]).all()
+
+
+def test_owned_workspace_across_shapes(cuda, oracle_mod):
+    """The library's own workspace is reused across shapes whose ticket
+    regions grow and shrink (stale partials must never be read as
+    tickets)."""
+    seq = [("b1_gqa8", SMALL["b1_gqa8"]),
+           ("b64_gqa4_split", SMALL["b64_gqa4"]),
+           ("b1_gqa8", SMALL["b1_gqa8"]),
+           ("varlen_gqa8", SMALL["varlen_gqa8"]),
+           ("b64_gqa4_split", SMALL["b64_gqa4"])]
+    for name, w in seq:
+        q, k, v, sl_dev, seqlens, host = inputs(name, w)
+        ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
+        for _ in range(2):
+            out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=5,
+                                       flags=fd.FD_FLAG_FUSED_MERGE)
+            cuda.cuda.synchronize()
+            assert_parity(w, out, lse, ref_out, ref_lse, f"reuse {name}")
+
+
+@pytest.mark.parametrize("name,S", [("b1_gqa8_h64_d128_l65536", 64),
+                                    ("b1_gqa8_h64_d128_l65536", 32),
+                                    ("varlen_b16_gqa8_h64_d128_lmax131072",
+                                     0)])
+def test_fused_merge_never_reads_stale_partials(cuda, name, S):
+    """Alternate two different inputs of the full size on the same
+    workspace: a partial of the previous call read by the fused merge would
+    move that row's lse by O(0.1).  Every fused result must agree with the
+    separate-merge result up to rounding (different summation order)."""
+    wa = W[name]
+    wb = wa.with_(seed=wa.seed + 100)
+    ins = []
+    for w in (wa, wb):
+        q, k, v, sl, _, _ = dev_inputs(w)
+        ins.append((q, k, v, sl))
+    refs = []
+    for q, k, v, sl in ins:
+        o, l_ = fd.fd_decode_ex(q, k, v, sl, wa.scale, num_splits=S)
+        cuda.cuda.synchronize()
+        refs.append((o.float().cpu().numpy(), l_.cpu().numpy()))
+    assert np.abs(refs[0][1] - refs[1][1]).max() > 0.05
+    out = cuda.empty_like(ins[0][0])
+    lse = cuda.empty((wa.B, wa.Hq), dtype=cuda.float32, device="cuda")
+    for it in range(40):
+        i = it % 2
+        q, k, v, sl = ins[i]
+        fd.fd_decode_ex(q, k, v, sl, wa.scale, out=out, lse=lse,
+                        num_splits=S, flags=fd.FD_FLAG_FUSED_MERGE)
+        if it % 4 < 2:       # also back-to-back launches without a sync
+            cuda.cuda.synchronize()
+            dl = np.abs(lse.cpu().numpy() - refs[i][1]).max()
+            do = np.abs(out.float().cpu().numpy() - refs[i][0]).max()
+            assert dl < 1e-4 and do < 2e-3, (it, dl, do)
+    cuda.cuda.synchronize()
