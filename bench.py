@@ -48,7 +48,7 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(bytes_alg: int):
+def traffic_from_profiles():
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
     counter runs, if they were taken on the current kernel source."""
     try:
@@ -61,9 +61,13 @@ def traffic_from_profiles(bytes_alg: int):
     return doc.get("hbm_bytes_per_launch"), doc.get("kernel")
 
 
+SAMPLE_KV_BYTES = 1 << 30     # host-side K/V of the CPU baseline's sample
+
+
 def cpu_baseline(w, budget_s: float):
-    """fp64 oracle over the same workload on the host's cores: whole steps,
-    repeated until ~budget_s of wall time (at least one)."""
+    """fp64 oracle over the same workload on the host's cores: whole steps
+    of the first batch entries whose K/V fit SAMPLE_KV_BYTES (all of them
+    for the batch-1 workloads), repeated until ~budget_s of wall time."""
     import numpy as np
     from long_context_decode_fd_amd import workloads as wl
     from oracle import oracle
@@ -71,7 +75,13 @@ def cpu_baseline(w, budget_s: float):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    q, k, v, seqlens = wl.gen_all(w)
+    per_b = 2 * w.Hkv * w.Lmax * w.D * w.elem_bytes
+    nb = max(1, min(w.B, SAMPLE_KV_BYTES // per_b))
+    # The generator's streams are per slab, and q / seqlens are drawn in
+    # batch order, so the first nb entries of the workload are exactly the
+    # workload with B = nb.
+    ws = w.with_(B=nb)
+    q, k, v, seqlens = wl.gen_all(ws)
     times = []
     t_total = time.perf_counter()
     while True:
@@ -81,7 +91,7 @@ def cpu_baseline(w, budget_s: float):
         if time.perf_counter() - t_total >= budget_s or len(times) >= 20:
             break
     t = float(np.median(times))
-    nbytes = wl.algorithmic_bytes(w, seqlens)
+    nbytes = wl.algorithmic_bytes(ws, seqlens)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -94,10 +104,11 @@ def cpu_baseline(w, budget_s: float):
     return {
         "value": nbytes / t / 1e9, "unit": "GB/s", "cores": cores,
         "kind": "oracle", "us_per_step": t * 1e6,
-        "sample": (f"{len(times)} whole step(s) of the same workload "
-                   f"(all 64 query heads x 65536 keys), median wall time; "
-                   f"fp64 C oracle, OpenMP over rows, {cores} threads"
-                   + (f", {model}" if model else "")),
+        "sample": (f"{len(times)} run(s) over batch entries 0..{nb - 1} of "
+                   f"{w.B} (all {w.Hq} query heads, same inputs as the GPU "
+                   f"run), median wall time, rate = their algorithmic bytes "
+                   f"/ time; fp64 C oracle, OpenMP over rows, {cores} "
+                   f"threads" + (f", {model}" if model else "")),
     }
 
 
@@ -108,6 +119,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--workload", default=None,
+                    help="another workload of long_context_decode_fd_amd."
+                         "workloads (default: the batch-1 64k one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -122,7 +136,7 @@ def main(argv=None):
     import long_context_decode_fd_amd as fd
     from long_context_decode_fd_amd import workloads as wl
 
-    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    w = wl.WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
     torch.cuda.set_device(0)
     fd.load_library()
     log(f"[bench] workload {w.name}: generating inputs")
@@ -162,6 +176,30 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_hot = e0.elapsed_time(e1) / a.steps
 
+    # Dominant kernel on its own: the per-chunk pass of the same plan
+    # (fd_decode_partials), K launches back to back between two HIP events
+    # on the launch stream, then one merge to leave out/lse consistent.
+    pplan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                       varlen=sl is not None, flags=fd.FD_FLAG_PARTIALS)
+    assert (pplan["num_splits"], pplan["chunk"], pplan["grid"]) == \
+        (plan["num_splits"], plan["chunk"], plan["grid"])
+    ws = torch.zeros(pplan["workspace_bytes"], dtype=torch.uint8,
+                     device="cuda")
+    for i in range(a.warmup):
+        fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl,
+                              w.scale, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl,
+                              w.scale, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_avg_ms = e0.elapsed_time(e1) / a.steps
+    fd.fd_merge_partials(sl, w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype, ws,
+                         out, lse, stream=stream)
+    torch.cuda.synchronize()
+
     if a.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -170,15 +208,28 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    nbytes = wl.algorithmic_bytes(w)
+    nbytes = wl.algorithmic_bytes(w, wl.gen_seqlens(w))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    traffic, traffic_note = traffic_from_profiles(nbytes)
+    # The per-chunk pass must read every K/V row and q once; out/lse are the
+    # merge pass's.
+    kbytes = nbytes - (w.B * w.Hq * w.D * w.elem_bytes + 4 * w.B * w.Hq)
+    split_kernel = (f"split_mfma_kernel<{w.D}, {plan['waves_per_block']}>"
+                    if plan["variant"] == fd.FD_VARIANT_MFMA else
+                    f"split_valu_kernel<{w.dtype}, {w.D}>")
+    kgbs = kbytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic, traffic_note = (traffic_from_profiles()
+                             if w.name == wl.BENCH_WORKLOAD
+                             else (None, "counters taken for the batch-1 "
+                                         "64k workload only"))
     roof = {
-        "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
-        "kernel": ("whole step: per-chunk pass + merge pass" if plan["combine"]
-                   else "per-chunk pass"),
-        "bytes_per_launch": nbytes,
+        "bound": "hbm", "achieved": kgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": kgbs / PEAK_HBM_GBS, "traffic": traffic,
+        "kernel": f"{split_kernel} (per-chunk pass)",
+        "bytes_per_launch": kbytes,
+        "avg_launch_us": kern_avg_ms * 1e3,
+        "timing": f"{a.steps} back-to-back launches of the per-chunk pass "
+                  "(fd_decode_partials, same plan) between two HIP events on "
+                  f"the launch stream, KV rotated over {KV_COPIES} copies",
         "traffic_note": traffic_note,
     }
     res = {
@@ -186,8 +237,8 @@ def main(argv=None):
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
         "us_per_step": ms * 1e3, "frac_of_peak": gbs / PEAK_HBM_GBS,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 q/K/V)",
+        "dtype": w.dtype,
+        "data": f"synthetic (seeded N(0,1) {w.dtype} q/K/V)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "seq_len": w.Lmax, "kv_copies_rotated": KV_COPIES,
                    "num_splits": plan["num_splits"], "chunk": plan["chunk"],

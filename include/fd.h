@@ -88,7 +88,10 @@ enum {
        agent-scope release (an L2 write-back) per workgroup, which costs
        more than the second launch it saves; kept for callers that must
        have a single launch. */
-    FD_FLAG_FUSED_MERGE = 1
+    FD_FLAG_FUSED_MERGE = 1,
+    /* Always leave per-chunk partials, even when one chunk per sequence
+       would do (the plan fd_decode_partials / fd_merge_partials use). */
+    FD_FLAG_PARTIALS = 2
 };
 
 /* How the chunks of a split plan are merged (fd_plan_t.merge). */
@@ -120,6 +123,13 @@ typedef struct fd_plan {
     size_t ticket_bytes;    /* leading bytes of the workspace that hold the
                                per-group tickets of the fused merge
                                (0 unless FD_FLAG_FUSED_MERGE) */
+    size_t o_part_offset;   /* byte offset of the partial outputs:
+                               float32 [B][Hq][num_splits][D], each chunk's
+                               own softmax-normalised output */
+    size_t lse_part_offset; /* byte offset of the partial log-sum-exps:
+                               float32 [B][Hq][num_splits], natural log;
+                               chunk s of sequence b exists iff
+                               s < max(1, ceil(seqlens[b] / chunk)) */
 } fd_plan_t;
 
 /*
@@ -158,6 +168,31 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int Lmax, float scale, fd_dtype_t dtype, void *out,
                  float *lse, int num_splits, int variant, int flags,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fd_decode_partials / fd_merge_partials -- the two phases of a split decode
+ * as separate calls: the parallel pass over the chunks, and the log-sum-exp
+ * reduction (the two steps of the Flash-Decoding section), for callers that
+ * schedule or time them apart, or merge partials gathered elsewhere.
+ * Both plan with FD_FLAG_PARTIALS added to `flags`, so partials exist even
+ * for one chunk per sequence; use fd_plan / fd_workspace_bytes with that
+ * flag for the layout and size of `workspace` (a caller buffer, required).
+ * fd_merge_partials must get the same sizes, seqlens, num_splits, variant
+ * and flags as the fd_decode_partials call that filled the workspace, and
+ * run after it (same stream, or ordered by the caller).
+ */
+int fd_decode_partials(const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *seqlens, int B,
+                       int Hq, int Hkv, int D, int Lmax, float scale,
+                       fd_dtype_t dtype, int num_splits, int variant,
+                       int flags, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                      int Lmax, fd_dtype_t dtype, int num_splits, int variant,
+                      int flags, const void *workspace,
+                      size_t workspace_bytes, void *out, float *lse,
+                      void *stream);
 
 /*
  * fd_plan -- the decision fd_decode_ex would take, without launching.

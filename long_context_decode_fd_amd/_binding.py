@@ -26,6 +26,7 @@ FD_VARIANT_AUTO = 0
 FD_VARIANT_MFMA = 1
 FD_VARIANT_VALU = 2
 FD_FLAG_FUSED_MERGE = 1
+FD_FLAG_PARTIALS = 2
 FD_MERGE_NONE = 0
 FD_MERGE_FUSED = 1
 FD_MERGE_SEPARATE = 2
@@ -39,7 +40,8 @@ class FdPlanStruct(ctypes.Structure):
     _fields_ = [("num_splits", _ci), ("chunk", _ci), ("variant", _ci),
                 ("waves_per_block", _ci), ("grid", _ci), ("combine", _ci),
                 ("merge", _ci), ("num_cus", _ci), ("workspace_bytes", _sz),
-                ("ticket_bytes", _sz)]
+                ("ticket_bytes", _sz), ("o_part_offset", _sz),
+                ("lse_part_offset", _sz)]
 
 
 SIGNATURES = {
@@ -48,6 +50,11 @@ SIGNATURES = {
     "fd_decode_ex": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci,
                            _cf, _ci, _vp, _vp, _ci, _ci, _ci, _vp, _sz,
                            _vp]),
+    "fd_decode_partials": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
+                                 _ci, _cf, _ci, _ci, _ci, _ci, _vp, _sz,
+                                 _vp]),
+    "fd_merge_partials": (_ci, [_i32p, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                                _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
     "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                       ctypes.POINTER(FdPlanStruct)]),
     "fd_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
@@ -126,7 +133,7 @@ def fd_workspace_bytes(B, Hq, Hkv, D, Lmax, dtype, varlen=False,
         num_splits, variant, flags))
 
 
-def _check(q, k_cache, v_cache, seqlens, out, lse):
+def _check(q, k_cache, v_cache, seqlens, out, lse, need_out=True):
     import torch
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q/k/v must be bfloat16 or float32 tensors")
@@ -147,6 +154,8 @@ def _check(q, k_cache, v_cache, seqlens, out, lse):
                 or seqlens.shape != (B,) or not seqlens.is_contiguous()):
             raise ValueError("seqlens must be a contiguous int32 [B] "
                              "device tensor")
+    if not need_out:
+        return (B, Hq, Hkv, D, Lmax), None, None
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -212,3 +221,51 @@ def fd_decode(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
     if rc != FD_OK:
         raise FdError("fd_decode", rc)
     return out, lse
+
+
+def _ws(workspace):
+    if workspace is None:
+        raise ValueError("the phase calls need a caller workspace tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def fd_decode_partials(q, k_cache, v_cache, seqlens, scale, workspace,
+                       num_splits=0, variant=FD_VARIANT_AUTO, flags=0,
+                       stream=None):
+    """Chunk phase only: partials into `workspace` (see fd.h)."""
+    dims, _, _ = _check(q, k_cache, v_cache, seqlens, None, None,
+                        need_out=False)
+    B, Hq, Hkv, D, Lmax = dims
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    ws_ptr, ws_bytes = _ws(workspace)
+    rc = load_library().fd_decode_partials(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(),
+        B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
+        int(num_splits), int(variant), int(flags), ws_ptr, ws_bytes,
+        _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode_partials", rc)
+
+
+def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
+                      lse, num_splits=0, variant=FD_VARIANT_AUTO, flags=0,
+                      stream=None):
+    """Merge phase only: out/lse from the partials in `workspace`."""
+    import torch
+    tdt = torch.bfloat16 if _dtype_code(dtype) == FD_BF16 else torch.float32
+    if (out.shape != (B, Hq, D) or out.dtype != tdt or not out.is_cuda
+            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [B,Hq,D] device tensor")
+    if (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    ws_ptr, ws_bytes = _ws(workspace)
+    rc = load_library().fd_merge_partials(
+        None if seqlens is None else seqlens.data_ptr(), B, Hq, Hkv, D, Lmax,
+        _dtype_code(dtype), int(num_splits), int(variant), int(flags),
+        ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
+        _stream_handle(stream, out.device))
+    if rc != FD_OK:
+        raise FdError("fd_merge_partials", rc)

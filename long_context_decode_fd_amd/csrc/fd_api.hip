@@ -88,36 +88,39 @@ int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
   return FD_OK;
 }
 
-int check_pointers(const void *q, const void *k, const void *v,
-                   const int32_t *seqlens, const void *out, const float *lse,
-                   float scale) {
-  if (!q || !k || !v || !out || !lse) return FD_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-      !aligned(out, 16) || !aligned(lse, 4))
-    return FD_ERR_INVALID_ARG;
+
+// Shared body of fd_decode_ex and the two phase calls.  q/k/v may be null
+// only when the chunk phase is not requested; out/lse only when the merge
+// phase is not requested.
+int run(const void *q, const void *k_cache, const void *v_cache,
+        const int32_t *seqlens, int B, int Hq, int Hkv, int D, int Lmax,
+        float scale, fd_dtype_t dtype, void *out, float *lse, int num_splits,
+        int variant, int flags, void *workspace, size_t workspace_bytes,
+        void *stream, int phases) {
+  const bool chunks = phases & fd::kPhaseChunks;
+  const bool merge = phases & fd::kPhaseMerge;
+  if (chunks) {
+    if (!q || !k_cache || !v_cache) return FD_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+      return FD_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  }
+  if (merge) {
+    if (!out || !lse) return FD_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(lse, 4)) return FD_ERR_INVALID_ARG;
+  }
   if (seqlens && !aligned(seqlens, 4)) return FD_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
-  return FD_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
-                 const int32_t *seqlens, int B, int Hq, int Hkv, int D,
-                 int Lmax, float scale, fd_dtype_t dtype, void *out,
-                 float *lse, int num_splits, int variant, int flags,
-                 void *workspace, size_t workspace_bytes, void *stream) {
-  int rc = check_pointers(q, k_cache, v_cache, seqlens, out, lse, scale);
-  if (rc != FD_OK) return rc;
-  rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
+  int rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
   if (num_splits < 0 || variant < FD_VARIANT_AUTO ||
-      variant > FD_VARIANT_VALU || (flags & ~FD_FLAG_FUSED_MERGE))
+      variant > FD_VARIANT_VALU ||
+      (flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_PARTIALS)))
     return FD_ERR_INVALID_ARG;
   if (workspace == nullptr && workspace_bytes != 0) return FD_ERR_INVALID_ARG;
   if (workspace && !aligned(workspace, 256)) return FD_ERR_INVALID_ARG;
+  // The phase calls exchange partials through the caller's workspace.
+  if (phases != (fd::kPhaseChunks | fd::kPhaseMerge) && !workspace)
+    return FD_ERR_INVALID_ARG;
 
   int ncu = 0;
   rc = device_cus(&ncu);
@@ -126,6 +129,8 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, seqlens != nullptr,
                      num_splits, variant, flags, ncu, &p);
   if (rc != FD_OK) return rc;
+  if (phases != (fd::kPhaseChunks | fd::kPhaseMerge) && p.fused)
+    return FD_ERR_INVALID_ARG;  // the fused merge has no separate phase
 
   fd::LaunchArgs a{};
   a.q = q;
@@ -136,6 +141,7 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   a.lse = lse;
   a.scale = scale;
   a.stream = stream;
+  a.phases = phases;
   if (p.combine) {
     void *ws = workspace;
     const fd::WorkspaceLayout lay = fd::workspace_layout(p);
@@ -155,6 +161,20 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   return fd::launch_decode(p, a) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                 int Lmax, float scale, fd_dtype_t dtype, void *out,
+                 float *lse, int num_splits, int variant, int flags,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
+             out, lse, num_splits, variant, flags, workspace, workspace_bytes,
+             stream, fd::kPhaseChunks | fd::kPhaseMerge);
+}
+
 int fd_decode(const void *q, const void *k_cache, const void *v_cache,
               const int32_t *seqlens, int B, int Hq, int Hkv, int D,
               int Lmax, float scale, fd_dtype_t dtype, void *out, float *lse,
@@ -162,6 +182,28 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
   return fd_decode_ex(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax,
                       scale, dtype, out, lse, 0, FD_VARIANT_AUTO, 0, nullptr,
                       0, stream);
+}
+
+int fd_decode_partials(const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *seqlens, int B,
+                       int Hq, int Hkv, int D, int Lmax, float scale,
+                       fd_dtype_t dtype, int num_splits, int variant,
+                       int flags, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
+             nullptr, nullptr, num_splits, variant, flags | FD_FLAG_PARTIALS,
+             workspace, workspace_bytes, stream, fd::kPhaseChunks);
+}
+
+int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
+                      int Lmax, fd_dtype_t dtype, int num_splits, int variant,
+                      int flags, const void *workspace,
+                      size_t workspace_bytes, void *out, float *lse,
+                      void *stream) {
+  return run(nullptr, nullptr, nullptr, seqlens, B, Hq, Hkv, D, Lmax, 0.f,
+             dtype, out, lse, num_splits, variant, flags | FD_FLAG_PARTIALS,
+             const_cast<void *>(workspace), workspace_bytes, stream,
+             fd::kPhaseMerge);
 }
 
 int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
@@ -179,6 +221,7 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, varlen != 0, num_splits,
                      variant, flags, num_cus, &p);
   if (rc != FD_OK) return rc;
+  const fd::WorkspaceLayout lay = fd::workspace_layout(p);
   plan->num_splits = p.splits;
   plan->chunk = p.chunk;
   plan->variant = p.variant;
@@ -189,7 +232,9 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
                            : (p.fused ? FD_MERGE_FUSED : FD_MERGE_SEPARATE);
   plan->num_cus = p.num_cus;
   plan->workspace_bytes = p.ws_bytes;
-  plan->ticket_bytes = fd::workspace_layout(p).ticket_bytes;
+  plan->ticket_bytes = lay.ticket_bytes;
+  plan->o_part_offset = p.combine ? lay.o_part_off : 0;
+  plan->lse_part_offset = p.combine ? lay.lse_part_off : 0;
   return FD_OK;
 }
 

@@ -58,7 +58,10 @@ struct LaunchArgs {
   int *tickets;
   float scale;
   void *stream;
+  int phases;  // kPhaseChunks | kPhaseMerge
 };
+constexpr int kPhaseChunks = 1;
+constexpr int kPhaseMerge = 2;
 int launch_decode(const Plan &p, const LaunchArgs &a);
 
 }  // namespace fd

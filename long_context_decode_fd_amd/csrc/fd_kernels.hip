@@ -976,8 +976,10 @@ void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
 int launch_decode(const Plan &p, const LaunchArgs &a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float sl2 = a.scale * kLog2e;
-  hipError_t e;
-  if (p.variant == FD_VARIANT_MFMA) {
+  hipError_t e = hipSuccess;
+  if (!(a.phases & kPhaseChunks)) {
+    // merge only
+  } else if (p.variant == FD_VARIANT_MFMA) {
     e = p.D == 128 ? launch_mfma<128>(p, a, sl2, st)
                    : launch_mfma<64>(p, a, sl2, st);
   } else if (p.dtype == FD_BF16) {
@@ -990,7 +992,7 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   if (e != hipSuccess) return (int)e;
   e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  if (p.combine && !p.fused) {
+  if ((a.phases & kPhaseMerge) && p.combine && !p.fused) {
     if (p.dtype == FD_BF16) {
       if (p.D == 128)
         launch_combine<128, uint16_t>(p, a, st);

@@ -96,7 +96,8 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_variant < FD_VARIANT_AUTO ||
       requested_variant > FD_VARIANT_VALU)
     return FD_ERR_INVALID_ARG;
-  if (flags & ~FD_FLAG_FUSED_MERGE) return FD_ERR_INVALID_ARG;
+  if (flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_PARTIALS))
+    return FD_ERR_INVALID_ARG;
 
   Plan q{};
   q.B = B;
@@ -142,7 +143,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   }
   q.chunk = chunk;
   q.splits = ceil_div(Lmax, chunk);
-  q.combine = q.splits > 1;
+  q.combine = q.splits > 1 || (flags & FD_FLAG_PARTIALS);
   q.fused = q.combine && (flags & FD_FLAG_FUSED_MERGE);
   long grid = (long)B * Hkv * q.splits;
   if (grid > 0x7FFFFFFFL) return FD_ERR_UNSUPPORTED;

@@ -27,7 +27,8 @@ def sample_rows(w: wl.Workload, seqlens, n: int, seed: int = 0):
     if seqlens is not None:
         rows.add((int(np.argmin(seqlens)), 0))
         rows.add((int(np.argmax(seqlens)), w.Hq // 2))
-    while len(rows) < n + 2:
+    target = min(len(rows) + n, w.B * w.Hq)
+    while len(rows) < target:
         rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq))))
     return sorted(rows)
 

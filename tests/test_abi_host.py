@@ -32,7 +32,8 @@ def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     assert names == sorted(["fd_decode", "fd_decode_ex", "fd_plan",
                             "fd_workspace_bytes", "fd_status_string",
-                            "fd_version"])
+                            "fd_version", "fd_decode_partials",
+                            "fd_merge_partials"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -88,7 +89,7 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
     (dict(variant=3), fd.FD_ERR_INVALID_ARG),
     (dict(variant=-1), fd.FD_ERR_INVALID_ARG),
-    (dict(flags=2), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=4), fd.FD_ERR_INVALID_ARG),
     (dict(flags=-1), fd.FD_ERR_INVALID_ARG),
     (dict(ws=None, ws_bytes=64), fd.FD_ERR_INVALID_ARG),
     (dict(ws=A + 16, ws_bytes=1 << 20), fd.FD_ERR_INVALID_ARG),
@@ -103,6 +104,41 @@ def test_fd_decode_rejects_like_ex(lib):
     assert rc == fd.FD_ERR_INVALID_ARG
     rc = lib.fd_decode(A, A, A, None, 1, 8, 8, 80, 64, 0.1, 0, A, A, None)
     assert rc == fd.FD_ERR_UNSUPPORTED
+
+
+def test_phase_calls_reject_on_host(lib):
+    P = lib.fd_decode_partials
+    M = lib.fd_merge_partials
+    ok = dict(B=1, Hq=8, Hkv=8, D=128, Lmax=64)
+    # chunk phase: needs q/k/v and a caller workspace, no fused merge
+    assert P(None, A, A, None, 1, 8, 8, 128, 64, 0.1, 0, 0, 0, 0, A, 4096,
+             None) == fd.FD_ERR_INVALID_ARG
+    assert P(A, A, A, None, 1, 8, 8, 128, 64, 0.1, 0, 0, 0, 0, None, 0,
+             None) == fd.FD_ERR_INVALID_ARG
+    assert P(A, A, A, None, 1, 8, 8, 128, 64, float("nan"), 0, 0, 0, 0, A,
+             4096, None) == fd.FD_ERR_INVALID_ARG
+    assert P(A, A, A, None, 1, 8, 8, 96, 64, 0.1, 0, 0, 0, 0, A, 4096,
+             None) == fd.FD_ERR_UNSUPPORTED
+    # merge phase: needs out/lse and the workspace
+    assert M(None, 1, 8, 8, 128, 64, 0, 0, 0, 0, A, 4096, None, A,
+             None) == fd.FD_ERR_INVALID_ARG
+    assert M(None, 1, 8, 8, 128, 64, 0, 0, 0, 0, None, 0, A, A,
+             None) == fd.FD_ERR_INVALID_ARG
+    assert M(None, 1, 8, 8, 128, 64, 0, 0, 0, 4, A, 4096, A, A,
+             None) == fd.FD_ERR_INVALID_ARG
+    assert ok
+
+
+def test_partials_flag_plans_partials_for_one_chunk(lib):
+    p = fd.fd_plan(64, 32, 8, 128, 4096, "bf16", num_cus=256)
+    assert p["combine"] == 0 and p["workspace_bytes"] == 0
+    p = fd.fd_plan(64, 32, 8, 128, 4096, "bf16", num_cus=256,
+                   flags=fd.FD_FLAG_PARTIALS)
+    assert p["combine"] == 1 and p["num_splits"] == 1
+    rows = 64 * 32
+    assert p["o_part_offset"] == 0
+    assert p["lse_part_offset"] == rows * 128 * 4
+    assert p["workspace_bytes"] == rows * 128 * 4 + rows * 4
 
 
 def plan(w, varlen=None, **kw):
@@ -158,7 +194,7 @@ def test_plan_rejections(lib):
         fd.fd_plan(1, 64, 8, 128, 64, "bf16", variant=fd.FD_VARIANT_VALU,
                    num_cus=256)
     with pytest.raises(fd.FdError):
-        fd.fd_plan(1, 8, 8, 128, 64, "bf16", flags=4, num_cus=256)
+        fd.fd_plan(1, 8, 8, 128, 64, "bf16", flags=8, num_cus=256)
     assert plan(wl.WORKLOADS["b1_gqa8_h64_d128_l65536"],
                 num_splits=1)["workspace_bytes"] == 0
 

@@ -308,3 +308,59 @@ def test_fused_merge_never_reads_stale_partials(cuda, name, S):
             do = np.abs(out.float().cpu().numpy() - refs[i][0]).max()
             assert dl < 1e-4 and do < 2e-3, (it, dl, do)
     cuda.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,num_splits", [("b1_gqa8", 7), ("b1_gqa8", 1),
+                                             ("varlen_gqa8", 0),
+                                             ("b4_mha_peaked", 3),
+                                             ("tiny_mha_f32", 4),
+                                             ("gqa8_d64", 5)])
+def test_phase_calls_and_chunk_partials(cuda, oracle_mod, name, num_splits):
+    """fd_decode_partials leaves, for every existing chunk, that chunk's own
+    normalised attention output and log-sum-exp (checked against the
+    oracle's split twin with the same chunk length); fd_merge_partials then
+    gives the same bits as the one-call path with the same plan."""
+    w = SMALL[name]
+    q, k, v, sl_dev, seqlens, host = inputs(name, w)
+    P = fd.FD_FLAG_PARTIALS
+    plan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                      varlen=sl_dev is not None, num_splits=num_splits,
+                      flags=P)
+    S, C = plan["num_splits"], plan["chunk"]
+    ws = cuda.zeros(plan["workspace_bytes"], dtype=cuda.uint8,
+                    device="cuda")
+    fd.fd_decode_partials(q, k, v, sl_dev, w.scale, ws,
+                          num_splits=num_splits)
+    out = cuda.empty_like(q)
+    lse = cuda.empty((w.B, w.Hq), dtype=cuda.float32, device="cuda")
+    fd.fd_merge_partials(sl_dev, w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype, ws,
+                         out, lse, num_splits=num_splits)
+    one_out, one_lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
+                                       num_splits=num_splits, flags=P)
+    cuda.cuda.synchronize()
+    assert np.array_equal(out_to_host(out).view(np.uint16),
+                          out_to_host(one_out).view(np.uint16))
+    assert np.array_equal(lse.cpu().numpy(), one_lse.cpu().numpy())
+    ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"phases {name}")
+
+    o_off, l_off = plan["o_part_offset"], plan["lse_part_offset"]
+    wsh = ws.cpu().numpy()
+    o_part = wsh[o_off:o_off + w.B * w.Hq * S * w.D * 4].view(
+        np.float32).reshape(w.B, w.Hq, S, w.D)
+    l_part = wsh[l_off:l_off + w.B * w.Hq * S * 4].view(
+        np.float32).reshape(w.B, w.Hq, S)
+    qh, kh, vh = host
+    for b in range(w.B):
+        L = wl.seqlen_of(w, seqlens, b)
+        nb = max(1, -(-L // C))
+        for h in range(0, w.Hq, max(1, w.Hq // 4)):
+            g = h // w.G
+            _, _, po, pl = oracle_mod.attend_row_split(
+                qh[b, h], kh[b, g], vh[b, g], L, w.scale, C, nb)
+            np.testing.assert_allclose(o_part[b, h, :nb], po, rtol=0,
+                                       atol=2e-3)
+            fin = np.isfinite(pl)
+            assert np.array_equal(fin, np.isfinite(l_part[b, h, :nb]))
+            np.testing.assert_allclose(l_part[b, h, :nb][fin], pl[fin],
+                                       rtol=0, atol=1e-3)

@@ -62,3 +62,19 @@ def test_algorithmic_bytes_of_batch1_64k():
     w = wl.WORKLOADS["b1_gqa8_h64_d128_l65536"]
     assert wl.algorithmic_bytes(w) == 268_468_480
     assert wl.flops(w) == 4 * 65536 * 64 * 128
+
+
+def test_first_batch_entries_are_the_smaller_workload():
+    # bench.py's CPU baseline times the first entries of a large batch as
+    # the same workload with a smaller B: that must give identical inputs.
+    w = wl.WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        Lmax=512, Hq=8, varlen=(8, 512))
+    ws = w.with_(B=3)
+    np.testing.assert_array_equal(wl.gen_seqlens(w)[:3], wl.gen_seqlens(ws))
+    np.testing.assert_array_equal(wl.gen_q(w)[:3], wl.gen_q(ws))
+    sl = wl.gen_seqlens(w)
+    for b in range(3):
+        k1, v1 = wl.gen_slab(w, b, 1, sl)
+        k2, v2 = wl.gen_slab(ws, b, 1, wl.gen_seqlens(ws))
+        np.testing.assert_array_equal(k1, k2)
+        np.testing.assert_array_equal(v1, v2)
