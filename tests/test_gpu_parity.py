@@ -206,6 +206,8 @@ def test_caller_workspace_and_streams(cuda, oracle_mod):
     ws = cuda.zeros(need, dtype=cuda.uint8, device="cuda")
     s = cuda.cuda.Stream()
     for flags in (0, F):
+        # the workspace was filled on the default stream: order it first
+        s.wait_stream(cuda.cuda.current_stream())
         with cuda.cuda.stream(s):
             out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
                                        num_splits=7, flags=flags,
