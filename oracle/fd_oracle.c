@@ -25,6 +25,17 @@
  * seqlens (optional) gives the valid prefix of each sequence; rows at or
  * beyond it are never read.  A seqlen outside [0, Lmax] is clamped.
  *
+ * Two cache variants the pages point to (a note on the Flash-Decoding
+ * search-result page that frameworks store the KV cache very differently,
+ * and that decoding may process several new query tokens at once, as in
+ * speculative decoding):
+ *   paged:       K, V [num_pages][page_size][Hkv][D]; row j of sequence b
+ *                lives in page block_table[b][j / page_size], token
+ *                j % page_size.  Same definition over the same rows.
+ *   multi-query: q [B][Tq][Hq][D] holds the Tq newest tokens of each
+ *                sequence, whose K/V are the last Tq rows of its cache;
+ *                query t sees rows j < seqlens[b] - (Tq - 1 - t) (causal).
+ *
  * The split/combine twin follows the section "A faster attention for
  * decoding: Flash-Decoding" of the same page: the keys/values are cut into
  * contiguous chunks, each chunk's attention is computed on its own together
@@ -62,15 +73,16 @@ static double load_elem(const void *base, size_t idx, int dtype)
 }
 
 /*
- * One query row against L rows of one KV slab.  q_off / kv_off are element
- * offsets into q and into k/v; rows of the slab are D elements apart.
- * scratch must hold L doubles.  Two exact passes: scores and their max,
- * then the exp-weighted sums.
+ * One query row against L rows of K/V.  q_off is the element offset of the
+ * query in q.  Row j starts at element row_off[j] of k and v, or, when
+ * row_off is NULL, at kv_off + j * D (a contiguous slab).  scratch must hold
+ * L doubles.  Two exact passes: scores and their max, then the exp-weighted
+ * sums.
  */
 static void attend_row(const void *q, size_t q_off, const void *k,
-                       const void *v, size_t kv_off, int L, int D,
-                       double scale, int dtype, double *out, double *lse,
-                       double *scratch)
+                       const void *v, size_t kv_off, const size_t *row_off,
+                       int L, int D, double scale, int dtype, double *out,
+                       double *lse, double *scratch)
 {
     if (L <= 0) {
         for (int d = 0; d < D; ++d)
@@ -81,10 +93,10 @@ static void attend_row(const void *q, size_t q_off, const void *k,
     double m = -INFINITY;
     int saw_nan = 0;
     for (int j = 0; j < L; ++j) {
+        const size_t r = row_off ? row_off[j] : kv_off + (size_t)j * D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += load_elem(q, q_off + d, dtype) *
-                   load_elem(k, kv_off + (size_t)j * D + d, dtype);
+            dot += load_elem(q, q_off + d, dtype) * load_elem(k, r + d, dtype);
         double s = scale * dot;
         scratch[j] = s;
         if (isnan(s))
@@ -98,10 +110,11 @@ static void attend_row(const void *q, size_t q_off, const void *k,
     for (int d = 0; d < D; ++d)
         out[d] = 0.0;
     for (int j = 0; j < L; ++j) {
+        const size_t r = row_off ? row_off[j] : kv_off + (size_t)j * D;
         double p = exp(scratch[j] - m);
         l += p;
         for (int d = 0; d < D; ++d)
-            out[d] += p * load_elem(v, kv_off + (size_t)j * D + d, dtype);
+            out[d] += p * load_elem(v, r + d, dtype);
     }
     for (int d = 0; d < D; ++d)
         out[d] /= l;
@@ -163,8 +176,9 @@ int fdo_decode(const void *q, const void *k, const void *v,
             int g = h / G;
             size_t q_off = ((size_t)b * Hq + h) * D;
             size_t kv_off = ((size_t)b * Hkv + g) * (size_t)Lmax * D;
-            attend_row(q, q_off, k, v, kv_off, clamp_len(seqlens, b, Lmax), D,
-                       scale, dtype, out + (size_t)r * D, lse + r, scratch);
+            attend_row(q, q_off, k, v, kv_off, NULL,
+                       clamp_len(seqlens, b, Lmax), D, scale, dtype,
+                       out + (size_t)r * D, lse + r, scratch);
         }
         free(scratch);
     }
@@ -185,8 +199,8 @@ int fdo_attend_row(const void *q_row, const void *k_slab, const void *v_slab,
     double *scratch = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
     if (!scratch)
         return FDO_ENOMEM;
-    attend_row(q_row, 0, k_slab, v_slab, 0, L, D, scale, dtype, out, lse,
-               scratch);
+    attend_row(q_row, 0, k_slab, v_slab, 0, NULL, L, D, scale, dtype, out,
+               lse, scratch);
     free(scratch);
     return FDO_OK;
 }
@@ -225,8 +239,8 @@ int fdo_attend_row_split(const void *q_row, const void *k_slab,
             n = chunk;
         if (n < 0)
             n = 0;
-        attend_row(q_row, 0, k_slab, v_slab, (size_t)lo * D, (int)n, D, scale,
-                   dtype, po + (size_t)c * D, pl + c, scratch);
+        attend_row(q_row, 0, k_slab, v_slab, (size_t)lo * D, NULL, (int)n, D,
+                   scale, dtype, po + (size_t)c * D, pl + c, scratch);
     }
     /* Step 2: merge the chunks, weighting each by exp(lse_c - max lse). */
     double M = -INFINITY;
@@ -305,4 +319,113 @@ int fdo_decode_split(const void *q, const void *k, const void *v,
         }
     }
     return err;
+}
+
+/*
+ * Paged cache: K, V [num_pages][page_size][Hkv][D], block_table
+ * [B][max_pages].  Row j of (b, kv-head g) starts at element
+ * ((block_table[b][j / page_size] * page_size + j % page_size) * Hkv + g) * D.
+ * seqlens is required; a length beyond max_pages * page_size is clamped, and
+ * a page index outside [0, num_pages) is an error (FDO_EINVAL).
+ */
+int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                     const int32_t *block_table, int max_pages, int page_size,
+                     int num_pages, const int32_t *seqlens, int B, int Hq,
+                     int Hkv, int D, double scale, int dtype, int nthreads,
+                     double *out, double *lse)
+{
+    if (max_pages <= 0 || page_size <= 0 || num_pages <= 0 || !seqlens)
+        return FDO_EINVAL;
+    const int Lcap = max_pages * page_size;
+    int rc = check_dims(B, Hq, Hkv, D, Lcap, dtype);
+    if (rc)
+        return rc;
+    for (int b = 0; b < B; ++b) {
+        int L = clamp_len(seqlens, b, Lcap);
+        for (int p = 0; p < (L + page_size - 1) / page_size; ++p) {
+            int pg = block_table[(size_t)b * max_pages + p];
+            if (pg < 0 || pg >= num_pages)
+                return FDO_EINVAL;
+        }
+    }
+    const int G = Hq / Hkv;
+    const long rows = (long)B * Hq;
+    int failed = 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)Lcap);
+        size_t *roff = malloc(sizeof(size_t) * (size_t)Lcap);
+        if (!scratch || !roff) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < rows; ++r) {
+            if (!scratch || !roff)
+                continue;
+            int b = (int)(r / Hq), h = (int)(r % Hq);
+            int g = h / G;
+            int L = clamp_len(seqlens, b, Lcap);
+            for (int j = 0; j < L; ++j) {
+                size_t pg = (size_t)block_table[(size_t)b * max_pages +
+                                                j / page_size];
+                roff[j] = ((pg * page_size + (size_t)(j % page_size)) * Hkv +
+                           g) * (size_t)D;
+            }
+            attend_row(q, ((size_t)b * Hq + h) * D, k_pages, v_pages, 0, roff,
+                       L, D, scale, dtype, out + (size_t)r * D, lse + r,
+                       scratch);
+        }
+        free(scratch);
+        free(roff);
+    }
+    return failed ? FDO_ENOMEM : FDO_OK;
+}
+
+/*
+ * Multi-query decode: q, out [B][Tq][Hq][D], lse [B][Tq][Hq].  The Tq query
+ * tokens are the newest Tq tokens of the sequence (already in the cache);
+ * query t sees rows j < seqlens[b] - (Tq - 1 - t), clamped at 0.
+ */
+int fdo_decode_multiquery(const void *q, const void *k, const void *v,
+                          const int32_t *seqlens, int B, int Tq, int Hq,
+                          int Hkv, int D, int Lmax, double scale, int dtype,
+                          int nthreads, double *out, double *lse)
+{
+    int rc = check_dims(B, Hq, Hkv, D, Lmax, dtype);
+    if (rc)
+        return rc;
+    if (Tq <= 0)
+        return FDO_EINVAL;
+    const int G = Hq / Hkv;
+    const long rows = (long)B * Tq * Hq;
+    int failed = 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)Lmax);
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < rows; ++r) {
+            if (!scratch)
+                continue;
+            int b = (int)(r / ((long)Tq * Hq));
+            int t = (int)((r / Hq) % Tq), h = (int)(r % Hq);
+            int g = h / G;
+            int L = clamp_len(seqlens, b, Lmax) - (Tq - 1 - t);
+            if (L < 0)
+                L = 0;
+            size_t kv_off = ((size_t)b * Hkv + g) * (size_t)Lmax * D;
+            attend_row(q, (size_t)r * D, k, v, kv_off, NULL, L, D, scale,
+                       dtype, out + (size_t)r * D, lse + r, scratch);
+        }
+        free(scratch);
+    }
+    return failed ? FDO_ENOMEM : FDO_OK;
 }

@@ -10,6 +10,10 @@ cache, as described in "Flash-Decoding for long-context inference"
 ``*_split`` functions follow that page's section "A faster attention for
 decoding: Flash-Decoding" (chunk the keys/values, attend per chunk with one
 log-sum-exp per row and chunk, merge the chunks by their log-sum-exp).
+``decode_paged`` reads the same rows through a page table and
+``decode_multiquery`` attends several newest tokens per sequence causally
+(the Flash-Decoding search-result page notes both cache layouts that differ
+between frameworks and decoding several query tokens at once).
 
 Arrays: bf16 tensors are passed as ``numpy.uint16`` bit patterns, fp32 as
 ``numpy.float32``.  Shapes: q [B, Hq, D], k/v [B, Hkv, Lmax, D], seqlens
@@ -44,6 +48,12 @@ def _bind(path: str):
     lib.fdo_attend_row_split.argtypes = [vp, vp, vp, ci, ci, cd, ci, ci, ci,
                                          dp, dp, dp, dp]
     lib.fdo_attend_row_split.restype = ci
+    lib.fdo_decode_paged.argtypes = [vp, vp, vp, i32p, ci, ci, ci, i32p, ci,
+                                     ci, ci, ci, cd, ci, ci, dp, dp]
+    lib.fdo_decode_paged.restype = ci
+    lib.fdo_decode_multiquery.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci,
+                                          ci, ci, cd, ci, ci, dp, dp]
+    lib.fdo_decode_multiquery.restype = ci
     return lib
 
 
@@ -159,6 +169,52 @@ def attend_row_split(q_row, k_slab, v_slab, L: int, scale, chunk: int,
     return out, float(lse[0]), po, pl
 
 
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
+                 nthreads: int = 0, _lib_override=None):
+    """Exact attention over a paged cache.  k_pages/v_pages
+    [num_pages, page_size, Hkv, D]; block_table int32 [B, max_pages];
+    seqlens int32 [B] (required)."""
+    q, k_pages, v_pages = _c(q), _c(k_pages), _c(v_pages)
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    assert Dk == D and v_pages.shape == k_pages.shape
+    bt = _c(np.asarray(block_table, dtype=np.int32))
+    assert bt.shape[0] == B
+    sl = _c(np.asarray(seqlens, dtype=np.int32))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    lib = _lib_override or _load()
+    rc = lib.fdo_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages),
+                              _ptr(bt), bt.shape[1], page_size, num_pages,
+                              _ptr(sl), B, Hq, Hkv, D, _scale(scale), dt,
+                              int(nthreads), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"fdo_decode_paged failed with {rc}")
+    return out, lse
+
+
+def decode_multiquery(q, k, v, seqlens, scale, nthreads: int = 0,
+                      _lib_override=None):
+    """Exact causal attention of Tq new query tokens per sequence.
+    q [B, Tq, Hq, D]; k/v [B, Hkv, Lmax, D]; returns out [B, Tq, Hq, D],
+    lse [B, Tq, Hq]."""
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    B, Tq, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k.shape
+    sl = None if seqlens is None else _c(np.asarray(seqlens, dtype=np.int32))
+    out = np.empty((B, Tq, Hq, D), dtype=np.float64)
+    lse = np.empty((B, Tq, Hq), dtype=np.float64)
+    lib = _lib_override or _load()
+    rc = lib.fdo_decode_multiquery(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), B,
+                                   Tq, Hq, Hkv, D, Lmax, _scale(scale), dt,
+                                   int(nthreads), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"fdo_decode_multiquery failed with {rc}")
+    return out, lse
+
+
 class Variant:
     """The same API bound to another build of fd_oracle.c (used by the
     mutation tests, which compile deliberately broken copies)."""
@@ -177,3 +233,9 @@ class Variant:
 
     def attend_row_split(self, *a, **kw):
         return attend_row_split(*a, _lib_override=self._l, **kw)
+
+    def decode_paged(self, *a, **kw):
+        return decode_paged(*a, _lib_override=self._l, **kw)
+
+    def decode_multiquery(self, *a, **kw):
+        return decode_multiquery(*a, _lib_override=self._l, **kw)

@@ -25,23 +25,35 @@ MUTANTS = [
     ("gqa_map_h_mod_hkv", "int g = h / G;", "int g = h % Hkv;"),
     ("q_row_from_kv_head", "size_t q_off = ((size_t)b * Hq + h) * D;",
      "size_t q_off = ((size_t)b * Hq + g) * D;"),
-    ("k_and_v_swapped",
-     "load_elem(k, kv_off + (size_t)j * D + d, dtype)",
-     "load_elem(v, kv_off + (size_t)j * D + d, dtype)"),
+    ("k_and_v_swapped", "load_elem(k, r + d, dtype)",
+     "load_elem(v, r + d, dtype)"),
     ("exp_sign_flipped", "double p = exp(scratch[j] - m);",
      "double p = exp(m - scratch[j]);"),
     ("not_normalised", "        out[d] /= l;\n", "\n"),
-    ("last_key_dropped", "for (int j = 0; j < L; ++j) {\n        double p",
-     "for (int j = 0; j < L - 1; ++j) {\n        double p"),
+    ("last_key_dropped",
+     "for (int j = 0; j < L; ++j) {\n        const size_t r = row_off ? "
+     "row_off[j] : kv_off + (size_t)j * D;\n        double p",
+     "for (int j = 0; j < L - 1; ++j) {\n        const size_t r = row_off ? "
+     "row_off[j] : kv_off + (size_t)j * D;\n        double p"),
     ("seqlens_ignored", "    if (!seqlens)\n        return Lmax;",
      "    return Lmax;"),
     ("merge_weight_sign", "double w = exp(pl[c] - M);",
      "double w = exp(M - pl[c]);"),
     ("merge_not_normalised", "            out[d] /= W;\n", "\n"),
     ("merge_lse_no_max", "*lse = M + log(W);", "*lse = log(W);"),
-    ("chunk_offset_in_rows", "(size_t)lo * D, (int)n", "(size_t)lo, (int)n"),
+    ("chunk_offset_in_rows", "(size_t)lo * D, NULL", "(size_t)lo, NULL"),
     ("chunk_tail_dropped", "        if (n > chunk)\n            n = chunk;",
      "        if (n > chunk || n < chunk)\n            n = chunk < n ? chunk : n - 1;"),
+    ("paged_token_index", "(size_t)(j % page_size)) * Hkv +",
+     "(size_t)(j / page_size)) * Hkv +"),
+    ("paged_head_ignored", "                           g) * (size_t)D;",
+     "                           0) * (size_t)D;"),
+    ("paged_page_of_token_zero", "                                j / page_size];",
+     "                                0];"),
+    ("multiquery_not_causal", "- (Tq - 1 - t);", "- 0;"),
+    ("multiquery_causal_reversed", "- (Tq - 1 - t);", "- t;"),
+    ("multiquery_q_row", "attend_row(q, (size_t)r * D, k, v, kv_off",
+     "attend_row(q, (size_t)(r % Hq) * D, k, v, kv_off"),
 ]
 
 PINS = [
@@ -64,6 +76,11 @@ PINS = [
     (pins.test_split_batch_twin_matches_batch, ()),
     (pins.test_torch_fp64_attention_agrees, ()),
     (pins.test_mpmath_brute_force_50_digits, ()),
+    (pins.test_paged_equals_contiguous_after_scatter, (32,)),
+    (pins.test_paged_equals_contiguous_after_scatter, (64,)),
+    (pins.test_multiquery_single_token_is_decode, ()),
+    (pins.test_multiquery_identical_keys_closed_form, ()),
+    (pins.test_multiquery_query_never_sees_later_tokens, ()),
 ]
 
 

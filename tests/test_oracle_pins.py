@@ -370,6 +370,99 @@ def test_fp32_inputs_are_used_at_full_precision(oracle_mod):
                                atol=1e-15)
 
 
+# --------------------------------------------------------------------------
+# paged cache and multi-query decode
+
+
+def scatter_to_pages(k, v, seqlens, page_size, rng, extra_pages=3):
+    """Contiguous [B, Hkv, L, D] -> a shuffled page pool [P, page, Hkv, D]
+    (unused and spare pages filled with NaN) and its block table."""
+    B, Hkv, L, D = k.shape
+    maxp = -(-L // page_size)
+    n = B * maxp + extra_pages
+    perm = rng.permutation(n)
+    nan = wl.BF16_NAN if k.dtype == np.uint16 else np.float32(np.nan)
+    kp = np.full((n, page_size, Hkv, D), nan, dtype=k.dtype)
+    vp = np.full((n, page_size, Hkv, D), nan, dtype=k.dtype)
+    bt = np.zeros((B, maxp), np.int32)
+    for b in range(B):
+        for p in range(maxp):
+            pg = int(perm[b * maxp + p])
+            bt[b, p] = pg
+            lo, hi = p * page_size, min(L, (p + 1) * page_size, int(seqlens[b]))
+            if hi > lo:
+                kp[pg, :hi - lo] = k[b, :, lo:hi].transpose(1, 0, 2)
+                vp[pg, :hi - lo] = v[b, :, lo:hi].transpose(1, 0, 2)
+    return kp, vp, bt
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 16])
+def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size):
+    # Same rows, same order: a shuffled page pool must give the contiguous
+    # result bit for bit, with NaN in every byte the pages do not own.
+    rng = np.random.default_rng(30 + page_size)
+    B, Hq, Hkv, D, L = 3, 8, 2, 16, 150
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    seq = np.array([150, 1, 97], np.int32)
+    kp, vp, bt = scatter_to_pages(k, v, seq, page_size, rng)
+    o1, l1 = oracle_mod.decode(q, k, v, seq, 0.3)
+    o2, l2 = oracle_mod.decode_paged(q, kp, vp, bt, seq, 0.3)
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(l2, l1)
+
+
+def test_multiquery_single_token_is_decode(oracle_mod):
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, D, L = 2, 6, 3, 8, 40
+    q = rand_bf16(rng, (B, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    seq = np.array([40, 17], np.int32)
+    o1, l1 = oracle_mod.decode(q, k, v, seq, 0.5)
+    o2, l2 = oracle_mod.decode_multiquery(q[:, None].copy(), k, v, seq, 0.5)
+    np.testing.assert_array_equal(o2[:, 0], o1)
+    np.testing.assert_array_equal(l2[:, 0], l1)
+
+
+def test_multiquery_identical_keys_closed_form(oracle_mod):
+    # All keys equal: each query t returns the mean of the V rows it sees,
+    # rows 0 .. L - Tq + t, and lse = s + ln(count).
+    rng = np.random.default_rng(32)
+    B, Tq, Hq, Hkv, D, L = 1, 4, 2, 1, 8, 20
+    q = np.zeros((B, Tq, Hq, D), np.float32); q[..., 0] = 1.0
+    k = np.zeros((B, Hkv, L, D), np.float32); k[..., 0] = 0.5
+    v = wl.bf16_to_f32(rand_bf16(rng, (B, Hkv, L, D)))
+    out, lse = oracle_mod.decode_multiquery(q, k, v, None, 2.0)
+    for t in range(Tq):
+        n = L - (Tq - 1 - t)
+        np.testing.assert_allclose(out[0, t, 0], v[0, 0, :n].astype(
+            np.float64).mean(0), rtol=0, atol=1e-14)
+        assert abs(lse[0, t, 1] - (1.0 + math.log(n))) < 1e-13
+
+
+def test_multiquery_query_never_sees_later_tokens(oracle_mod):
+    # Poison the rows of the later new tokens: query 0 must not change; the
+    # last query sees the poison.
+    rng = np.random.default_rng(33)
+    B, Tq, Hq, Hkv, D, L = 2, 3, 4, 2, 8, 30
+    q = rand_bf16(rng, (B, Tq, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    seq = np.array([30, 12], np.int32)
+    o1, l1 = oracle_mod.decode_multiquery(q, k, v, seq, 0.4)
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        n = int(seq[b]) - (Tq - 1)
+        k2[b, :, n:seq[b]] = wl.BF16_NAN
+        v2[b, :, n:seq[b]] = wl.BF16_NAN
+    o2, l2 = oracle_mod.decode_multiquery(q, k2, v2, seq, 0.4)
+    np.testing.assert_array_equal(o2[:, 0], o1[:, 0])
+    np.testing.assert_array_equal(l2[:, 0], l1[:, 0])
+    assert np.isnan(l2[:, Tq - 1]).all()
+
+
 def test_oracle_snapshot_unchanged(oracle_mod):
     # Regression guard only (written by tests/golden/make_snapshot.py from the
     # oracle): any change to the oracle's arithmetic shows up here.
