@@ -17,6 +17,11 @@ Prints one JSON line: value = algorithmic bytes per step (every K and V row
 once, q, out, lse) / step time, in GB/s; the roofline object compares the
 dominant kernel with MI355X's 8 TB/s HBM peak; cpu_baseline times the fp64
 CPU oracle on the host's cores over the same workload.
+
+--workload picks another workload of long_context_decode_fd_amd.workloads,
+including the paged-cache (fd_decode_paged) and multi-token
+(fd_decode_multiquery) ones; for those the roofline object covers the whole
+step, since their per-chunk pass has no separate phase call.
 """
 from __future__ import annotations
 
@@ -79,14 +84,30 @@ def cpu_baseline(w, budget_s: float):
     nb = max(1, min(w.B, SAMPLE_KV_BYTES // per_b))
     # The generator's streams are per slab, and q / seqlens are drawn in
     # batch order, so the first nb entries of the workload are exactly the
-    # workload with B = nb.
+    # workload with B = nb (a paged sample gets its own page table).
     ws = w.with_(B=nb)
     q, k, v, seqlens = wl.gen_all(ws)
+    if w.page_size:
+        seqlens = wl.paged_seqlens(ws, seqlens)
+        bt = wl.gen_block_table(ws)
+        kp, vp = wl.scatter_pages(ws, k, v, bt, seqlens)
+        del k, v
+
+        def run():
+            oracle.decode_paged(q, kp, vp, bt, seqlens, w.scale,
+                                nthreads=cores)
+    elif w.Tq > 1:
+        def run():
+            oracle.decode_multiquery(q, k, v, seqlens, w.scale,
+                                     nthreads=cores)
+    else:
+        def run():
+            oracle.decode(q, k, v, seqlens, w.scale, nthreads=cores)
     times = []
     t_total = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.decode(q, k, v, seqlens, w.scale, nthreads=cores)
+        run()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_total >= budget_s or len(times) >= 20:
             break
@@ -108,7 +129,9 @@ def cpu_baseline(w, budget_s: float):
                    f"{w.B} (all {w.Hq} query heads, same inputs as the GPU "
                    f"run), median wall time, rate = their algorithmic bytes "
                    f"/ time; fp64 C oracle, OpenMP over rows, {cores} "
-                   f"threads" + (f", {model}" if model else "")),
+                   f"threads" + (f", {model}" if model else "")
+                   + ("; the sample's own page table" if w.page_size
+                      else "")),
     }
 
 
@@ -136,22 +159,39 @@ def main(argv=None):
     import long_context_decode_fd_amd as fd
     from long_context_decode_fd_amd import workloads as wl
 
-    w = wl.WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
+    w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
+    kind = ("paged" if w.page_size else
+            "multiquery" if w.Tq > 1 else "decode")
     torch.cuda.set_device(0)
     fd.load_library()
-    log(f"[bench] workload {w.name}: generating inputs")
-    q, k, v, sl, _, _ = wl.device_inputs(w)
+    log(f"[bench] workload {w.name} ({kind}): generating inputs")
+    stream = torch.cuda.current_stream()
+    if kind == "paged":
+        q, k, v, bt, sl, seqlens, _ = wl.device_paged_inputs(w)
+        plan = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D,
+                             w.max_pages * w.page_size, w.dtype, paged=True)
+    else:
+        q, k, v, sl, seqlens, _ = wl.device_inputs(w)
+        plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                             varlen=sl is not None)
     ks = [k] + [k.clone() for _ in range(KV_COPIES - 1)]
     vs = [v] + [v.clone() for _ in range(KV_COPIES - 1)]
     out = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    plan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
-                      varlen=sl is not None)
-    stream = torch.cuda.current_stream()
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+    def call(kk, vv):
+        if kind == "paged":
+            fd.fd_decode_paged(q, kk, vv, bt, sl, w.scale, out=out, lse=lse,
+                               stream=stream)
+        elif kind == "multiquery":
+            fd.fd_decode_multiquery(q, kk, vv, sl, w.scale, out=out, lse=lse,
+                                    stream=stream)
+        else:
+            fd.fd_decode(q, kk, vv, sl, w.scale, out=out, lse=lse,
+                         stream=stream)
 
     def step(i):
-        fd.fd_decode(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl, w.scale,
-                     out=out, lse=lse, stream=stream)
+        call(ks[i % KV_COPIES], vs[i % KV_COPIES])
 
     log(f"[bench] plan {plan}")
     for i in range(a.warmup):
@@ -171,34 +211,37 @@ def main(argv=None):
     # Same-buffer ("hot") figure, labelled as such: repeats may hit MALL.
     e0.record(stream)
     for i in range(a.steps):
-        fd.fd_decode(q, k, v, sl, w.scale, out=out, lse=lse, stream=stream)
+        call(k, v)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_hot = e0.elapsed_time(e1) / a.steps
 
-    # Dominant kernel on its own: the per-chunk pass of the same plan
-    # (fd_decode_partials), K launches back to back between two HIP events
-    # on the launch stream, then one merge to leave out/lse consistent.
-    pplan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
-                       varlen=sl is not None, flags=fd.FD_FLAG_PARTIALS)
-    assert (pplan["num_splits"], pplan["chunk"], pplan["grid"]) == \
-        (plan["num_splits"], plan["chunk"], plan["grid"])
-    ws = torch.zeros(pplan["workspace_bytes"], dtype=torch.uint8,
-                     device="cuda")
-    for i in range(a.warmup):
-        fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl,
-                              w.scale, ws, stream=stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(a.steps):
-        fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl,
-                              w.scale, ws, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kern_avg_ms = e0.elapsed_time(e1) / a.steps
-    fd.fd_merge_partials(sl, w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype, ws,
-                         out, lse, stream=stream)
-    torch.cuda.synchronize()
+    kern_avg_ms = None
+    if kind == "decode":
+        # Dominant kernel on its own: the per-chunk pass of the same plan
+        # (fd_decode_partials), K launches back to back between two HIP
+        # events on the launch stream, then one merge to leave out/lse
+        # consistent.
+        pplan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                           varlen=sl is not None, flags=fd.FD_FLAG_PARTIALS)
+        assert (pplan["num_splits"], pplan["chunk"], pplan["grid"]) == \
+            (plan["num_splits"], plan["chunk"], plan["grid"])
+        ws = torch.zeros(pplan["workspace_bytes"], dtype=torch.uint8,
+                         device="cuda")
+        for i in range(a.warmup):
+            fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
+                                  sl, w.scale, ws, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
+                                  sl, w.scale, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern_avg_ms = e0.elapsed_time(e1) / a.steps
+        fd.fd_merge_partials(sl, w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype, ws,
+                             out, lse, stream=stream)
+        torch.cuda.synchronize()
 
     if a.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -208,30 +251,45 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    nbytes = wl.algorithmic_bytes(w, wl.gen_seqlens(w))
+    nbytes = wl.algorithmic_bytes(w, seqlens)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    # The per-chunk pass must read every K/V row and q once; out/lse are the
-    # merge pass's.
-    kbytes = nbytes - (w.B * w.Hq * w.D * w.elem_bytes + 4 * w.B * w.Hq)
-    split_kernel = (f"split_mfma_kernel<{w.D}, {plan['waves_per_block']}>"
+    split_kernel = (f"split_mfma_kernel<{w.D}, {plan['waves_per_block']}, "
+                    f"{'paged' if kind == 'paged' else 'contiguous'}>"
                     if plan["variant"] == fd.FD_VARIANT_MFMA else
                     f"split_valu_kernel<{w.dtype}, {w.D}>")
-    kgbs = kbytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic, traffic_note = (traffic_from_profiles()
-                             if w.name == wl.BENCH_WORKLOAD
-                             else (None, "counters taken for the batch-1 "
-                                         "64k workload only"))
-    roof = {
-        "bound": "hbm", "achieved": kgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": kgbs / PEAK_HBM_GBS, "traffic": traffic,
-        "kernel": f"{split_kernel} (per-chunk pass)",
-        "bytes_per_launch": kbytes,
-        "avg_launch_us": kern_avg_ms * 1e3,
-        "timing": f"{a.steps} back-to-back launches of the per-chunk pass "
-                  "(fd_decode_partials, same plan) between two HIP events on "
-                  f"the launch stream, KV rotated over {KV_COPIES} copies",
-        "traffic_note": traffic_note,
-    }
+    if kern_avg_ms is not None:
+        # The per-chunk pass must read every K/V row and q once; out/lse
+        # are the merge pass's.
+        kbytes = nbytes - (w.B * w.Hq * w.D * w.elem_bytes + 4 * w.B * w.Hq)
+        kgbs = kbytes / (kern_avg_ms * 1e-3) / 1e9
+        traffic, traffic_note = (traffic_from_profiles()
+                                 if w.name == wl.BENCH_WORKLOAD
+                                 else (None, "counters taken for the batch-1 "
+                                             "64k workload only"))
+        roof = {
+            "bound": "hbm", "achieved": kgbs, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": kgbs / PEAK_HBM_GBS, "traffic": traffic,
+            "kernel": f"{split_kernel} (per-chunk pass)",
+            "bytes_per_launch": kbytes,
+            "avg_launch_us": kern_avg_ms * 1e3,
+            "timing": f"{a.steps} back-to-back launches of the per-chunk "
+                      "pass (fd_decode_partials, same plan) between two HIP "
+                      f"events on the launch stream, KV rotated over "
+                      f"{KV_COPIES} copies",
+            "traffic_note": traffic_note,
+        }
+    else:
+        roof = {
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "kernel": f"{split_kernel} + merge (whole step)",
+            "bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3,
+            "timing": f"{a.steps} whole steps between two HIP events on the "
+                      f"launch stream, KV rotated over {KV_COPIES} copies; "
+                      "this layout has no separate per-chunk phase call",
+            "traffic_note": "counters taken for the batch-1 64k workload "
+                            "only",
+        }
     res = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
@@ -239,8 +297,10 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype,
         "data": f"synthetic (seeded N(0,1) {w.dtype} q/K/V)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "D": w.D, "seq_len": w.Lmax, "kv_copies_rotated": KV_COPIES,
+        "config": {"workload": w.name, "call": "fd_decode" if kind == "decode"
+                   else f"fd_decode_{kind}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "seq_len": w.Lmax, "Tq": w.Tq,
+                   "page_size": w.page_size, "kv_copies_rotated": KV_COPIES,
                    "num_splits": plan["num_splits"], "chunk": plan["chunk"],
                    "grid": plan["grid"], "waves_per_block":
                    plan["waves_per_block"], "merge_pass": bool(plan["combine"])},

@@ -205,6 +205,70 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
             fd_plan_t *plan);
 
 /*
+ * fd_decode_paged -- the same attention over a paged KV cache.  The
+ * "flash decoding" search-result page (a note on decode kernels for
+ * serving) observes that frameworks store the KV cache in very different
+ * ways; vLLM-style paging is the common one: fixed-size pages in a shared
+ * pool and a per-sequence table of page indices.
+ *     k_pages, v_pages  [num_pages][page_size][Hkv][D]   (dtype)
+ *     block_table       int32 [B][max_pages], DEVICE memory
+ *     seqlens           int32 [B], DEVICE memory, REQUIRED
+ *     q, out, lse       as for fd_decode
+ * Token j < L = clamp(seqlens[b], 0, max_pages * page_size) of sequence b,
+ * KV head g, is row ((block_table[b][j / page_size] * page_size
+ * + j % page_size) * Hkv + g) * D of each pool; the result is fd_decode's
+ * over those rows.  Only the first ceil(L / page_size) table entries of a
+ * sequence are read, and only rows below L of its last page.
+ * page_size must be a multiple of 16 (FD_ERR_UNSUPPORTED otherwise),
+ * max_pages * page_size and num_pages * page_size at most INT_MAX.  A
+ * table entry outside [0, num_pages) is a caller error that the kernel
+ * clamps into that range (never a read outside the pools).
+ * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Hq/Hkv <= 16.
+ * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
+ * tokens; FD_FLAG_FUSED_MERGE allowed).  Workspace: the library-owned one,
+ * as for fd_decode.
+ */
+int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *block_table, int max_pages, int page_size,
+                    int num_pages, const int32_t *seqlens, int B, int Hq,
+                    int Hkv, int D, float scale, fd_dtype_t dtype, void *out,
+                    float *lse, int num_splits, int flags, void *stream);
+
+/*
+ * fd_decode_multiquery -- Tq new query tokens per sequence at once (the
+ * same search-result note: multi-turn chat and speculative decoding give
+ * several query vectors per step, which raises the work per byte read).
+ * The Tq tokens are the newest of each sequence and their K/V are already
+ * the last Tq rows of the cache; attention among them is causal:
+ *     q, out   [B][Tq][Hq][D]      lse  float32 [B][Tq][Hq]
+ *     k_cache, v_cache, seqlens    as for fd_decode
+ * Query token t < Tq of sequence b sees keys j < L - (Tq - 1 - t), with
+ * L = clamp(seqlens[b], 0, Lmax) (NULL seqlens: L = Lmax); a token that
+ * sees no key gets out = 0, lse = -inf.  Tq = 1 is fd_decode.
+ * The keys a token must not see (j in [L - Tq + 1, L)) are still loaded
+ * for the tile and weighted by exactly 0: their V rows must be finite.
+ * bf16 only, 1 <= Tq * Hq/Hkv <= 16 (all query rows of a KV head share
+ * one 16-column matrix-core tile).  num_splits, flags and the workspace
+ * as for fd_decode_paged.
+ */
+int fd_decode_multiquery(const void *q, const void *k_cache,
+                         const void *v_cache, const int32_t *seqlens, int B,
+                         int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
+                         fd_dtype_t dtype, void *out, float *lse,
+                         int num_splits, int flags, void *stream);
+
+/*
+ * fd_plan_ex -- fd_plan for the calls above: Tq query tokens per sequence
+ * (1 for fd_decode / fd_decode_paged), paged nonzero for a paged cache
+ * (then Lmax = max_pages * page_size and seqlens are implied).  The
+ * partial layouts gain the token index: o_part [B][Tq][Hq][S][D], lse_part
+ * [B][Tq][Hq][S].
+ */
+int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
+               fd_dtype_t dtype, int varlen, int paged, int num_splits,
+               int variant, int flags, int num_cus, fd_plan_t *plan);
+
+/*
  * fd_workspace_bytes -- bytes of device workspace fd_decode_ex needs for
  * these arguments on the current device (0 when no merge pass is needed).
  * Returns 0 as well for invalid arguments; fd_plan reports why.

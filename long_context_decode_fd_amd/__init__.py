@@ -14,6 +14,7 @@ from ._binding import (FD_BF16, FD_ERR_HIP, FD_ERR_INVALID_ARG,  # noqa: F401
                        FD_MERGE_SEPARATE, FD_OK,
                        FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
                        LIB_PATH, FdError, fd_decode, fd_decode_ex,
+                       fd_decode_multiquery, fd_decode_paged,
                        fd_decode_partials, fd_merge_partials, fd_plan,
-                       fd_status_string, fd_version, fd_workspace_bytes,
-                       load_library)
+                       fd_plan_ex, fd_status_string, fd_version,
+                       fd_workspace_bytes, load_library)

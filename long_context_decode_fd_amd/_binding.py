@@ -55,8 +55,16 @@ SIGNATURES = {
                                  _vp]),
     "fd_merge_partials": (_ci, [_i32p, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                 _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
+    "fd_decode_paged": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _i32p,
+                              _ci, _ci, _ci, _ci, _cf, _ci, _vp, _vp, _ci,
+                              _ci, _vp]),
+    "fd_decode_multiquery": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
+                                   _ci, _ci, _cf, _ci, _vp, _vp, _ci, _ci,
+                                   _vp]),
     "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                       ctypes.POINTER(FdPlanStruct)]),
+    "fd_plan_ex": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                         _ci, _ci, _ci, ctypes.POINTER(FdPlanStruct)]),
     "fd_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                  _ci, _ci]),
     "fd_status_string": (ctypes.c_char_p, [_ci]),
@@ -122,6 +130,20 @@ def fd_plan(B, Hq, Hkv, D, Lmax, dtype, varlen=False, num_splits=0,
                                 num_cus, ctypes.byref(p))
     if rc != FD_OK:
         raise FdError("fd_plan", rc)
+    return {f: getattr(p, f) for f, _ in FdPlanStruct._fields_}
+
+
+def fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, dtype, varlen=False, paged=False,
+               num_splits=0, variant=FD_VARIANT_AUTO, flags=0,
+               num_cus=0) -> dict:
+    """The plan of fd_decode_multiquery (Tq tokens) / fd_decode_paged."""
+    p = FdPlanStruct()
+    rc = load_library().fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, _dtype_code(dtype),
+                                   int(bool(varlen)), int(bool(paged)),
+                                   num_splits, variant, flags, num_cus,
+                                   ctypes.byref(p))
+    if rc != FD_OK:
+        raise FdError("fd_plan_ex", rc)
     return {f: getattr(p, f) for f, _ in FdPlanStruct._fields_}
 
 
@@ -269,3 +291,96 @@ def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
         _stream_handle(stream, out.device))
     if rc != FD_OK:
         raise FdError("fd_merge_partials", rc)
+
+
+def _device_tensor(name, t, dtype, shape=None):
+    import torch
+    if (not isinstance(t, torch.Tensor) or not t.is_cuda
+            or not t.is_contiguous() or t.dtype != dtype
+            or (shape is not None and tuple(t.shape) != tuple(shape))):
+        want = "" if shape is None else f" {list(shape)}"
+        raise ValueError(f"{name} must be a contiguous {dtype}{want} "
+                         "device tensor")
+
+
+def _out_lse(out, lse, shape, lse_shape, dtype, device):
+    import torch
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=device)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=device)
+    _device_tensor("out", out, dtype, shape)
+    _device_tensor("lse", lse, torch.float32, lse_shape)
+    return out, lse
+
+
+def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
+                    out=None, lse=None, num_splits=0, flags=0, stream=None):
+    """Decode attention over a paged KV cache -- see fd.h.
+
+    q [B,Hq,D] bf16; k_pages/v_pages [num_pages,page_size,Hkv,D] bf16;
+    block_table int32 [B,max_pages]; seqlens int32 [B] (required); all on
+    the GPU.  Returns (out [B,Hq,D], lse [B,Hq]).
+    """
+    import torch
+    if q.dim() != 3 or k_pages.dim() != 4:
+        raise ValueError("expected q [B,Hq,D], k/v [num_pages,page_size,"
+                         "Hkv,D]")
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError(f"head dim mismatch q {D} vs pages {Dk}")
+    _device_tensor("q", q, q.dtype)
+    _device_tensor("k_pages", k_pages, q.dtype)
+    _device_tensor("v_pages", v_pages, q.dtype, k_pages.shape)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    _device_tensor("block_table", block_table, torch.int32)
+    _device_tensor("seqlens", seqlens, torch.int32, (B,))
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    out, lse = _out_lse(out, lse, (B, Hq, D), (B, Hq), q.dtype, q.device)
+    rc = load_library().fd_decode_paged(
+        q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+        block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
+        seqlens.data_ptr(), B, Hq, Hkv, D, float(scale),
+        _dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
+        int(num_splits), int(flags), _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode_paged", rc)
+    return out, lse
+
+
+def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
+                         lse=None, num_splits=0, flags=0, stream=None):
+    """Tq causal query tokens per sequence -- see fd.h.
+
+    q [B,Tq,Hq,D] bf16; k_cache/v_cache [B,Hkv,Lmax,D]; seqlens int32 [B]
+    on the GPU or None.  Returns (out [B,Tq,Hq,D], lse [B,Tq,Hq]).
+    """
+    import torch
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("expected q [B,Tq,Hq,D], k/v [B,Hkv,Lmax,D]")
+    B, Tq, Hq, D = q.shape
+    Bk, Hkv, Lmax, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} "
+                         f"k {tuple(k_cache.shape)}")
+    _device_tensor("q", q, q.dtype)
+    _device_tensor("k_cache", k_cache, q.dtype)
+    _device_tensor("v_cache", v_cache, q.dtype, k_cache.shape)
+    if seqlens is not None:
+        _device_tensor("seqlens", seqlens, torch.int32, (B,))
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    out, lse = _out_lse(out, lse, (B, Tq, Hq, D), (B, Tq, Hq), q.dtype,
+                        q.device)
+    rc = load_library().fd_decode_multiquery(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(), B, Tq, Hq, Hkv, D,
+        Lmax, float(scale), _dtype_code(q.dtype), out.data_ptr(),
+        lse.data_ptr(), int(num_splits), int(flags),
+        _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode_multiquery", rc)
+    return out, lse

@@ -6,6 +6,7 @@
 // compute-unit count, and the kernels are queued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -89,14 +90,33 @@ int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
 }
 
 
-// Shared body of fd_decode_ex and the two phase calls.  q/k/v may be null
-// only when the chunk phase is not requested; out/lse only when the merge
-// phase is not requested.
+// Checks of the paged-cache arguments; returns the block table's capacity
+// in tokens (max_pages * page_size) through *cap.
+int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int *cap) {
+  if (!pk.block_table || !seqlens) return FD_ERR_INVALID_ARG;
+  if (!aligned(pk.block_table, 4)) return FD_ERR_INVALID_ARG;
+  if (pk.max_pages <= 0 || pk.page_size <= 0 || pk.num_pages <= 0)
+    return FD_ERR_INVALID_ARG;
+  // A 16-key half tile must lie inside one page.
+  if (pk.page_size % 16 != 0) return FD_ERR_UNSUPPORTED;
+  // Token counts and pool rows are computed in int.
+  if ((long)pk.max_pages * pk.page_size > INT_MAX ||
+      (long)pk.num_pages * pk.page_size > INT_MAX)
+    return FD_ERR_UNSUPPORTED;
+  *cap = pk.max_pages * pk.page_size;
+  return FD_OK;
+}
+
+// Shared body of every decode entry point.  q/k/v may be null only when
+// the chunk phase is not requested; out/lse only when the merge phase is
+// not requested.  ex selects several query tokens and/or a paged cache
+// (pk; then Lmax is the block table's capacity).
 int run(const void *q, const void *k_cache, const void *v_cache,
         const int32_t *seqlens, int B, int Hq, int Hkv, int D, int Lmax,
         float scale, fd_dtype_t dtype, void *out, float *lse, int num_splits,
         int variant, int flags, void *workspace, size_t workspace_bytes,
-        void *stream, int phases) {
+        void *stream, int phases, fd::Extra ex = fd::Extra(),
+        fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0}) {
   const bool chunks = phases & fd::kPhaseChunks;
   const bool merge = phases & fd::kPhaseMerge;
   if (chunks) {
@@ -122,12 +142,17 @@ int run(const void *q, const void *k_cache, const void *v_cache,
   if (phases != (fd::kPhaseChunks | fd::kPhaseMerge) && !workspace)
     return FD_ERR_INVALID_ARG;
 
+  // Every remaining check is the planner's: run it once for them before
+  // the first HIP call, then for the device's compute-unit count.
+  fd::Plan p;
+  rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, seqlens != nullptr,
+                     num_splits, variant, flags, 1, &p, ex);
+  if (rc != FD_OK) return rc;
   int ncu = 0;
   rc = device_cus(&ncu);
   if (rc != FD_OK) return rc;
-  fd::Plan p;
   rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, seqlens != nullptr,
-                     num_splits, variant, flags, ncu, &p);
+                     num_splits, variant, flags, ncu, &p, ex);
   if (rc != FD_OK) return rc;
   if (phases != (fd::kPhaseChunks | fd::kPhaseMerge) && p.fused)
     return FD_ERR_INVALID_ARG;  // the fused merge has no separate phase
@@ -137,6 +162,7 @@ int run(const void *q, const void *k_cache, const void *v_cache,
   a.k = k_cache;
   a.v = v_cache;
   a.seqlens = seqlens;
+  a.paged = pk;
   a.out = out;
   a.lse = lse;
   a.scale = scale;
@@ -206,20 +232,55 @@ int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
              fd::kPhaseMerge);
 }
 
-int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
-            int varlen, int num_splits, int variant, int flags, int num_cus,
-            fd_plan_t *plan) {
-  if (!plan) return FD_ERR_INVALID_ARG;
-  int rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
+int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *block_table, int max_pages, int page_size,
+                    int num_pages, const int32_t *seqlens, int B, int Hq,
+                    int Hkv, int D, float scale, fd_dtype_t dtype, void *out,
+                    float *lse, int num_splits, int flags, void *stream) {
+  const fd::PagedKV pk{block_table, max_pages, page_size, num_pages};
+  int cap = 0;
+  const int rc = check_paged(pk, seqlens, &cap);
   if (rc != FD_OK) return rc;
-  if (num_cus < 0) return FD_ERR_INVALID_ARG;
+  fd::Extra ex;
+  ex.paged = true;
+  return run(q, k_pages, v_pages, seqlens, B, Hq, Hkv, D, cap, scale, dtype,
+             out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
+             fd::kPhaseChunks | fd::kPhaseMerge, ex, pk);
+}
+
+int fd_decode_multiquery(const void *q, const void *k_cache,
+                         const void *v_cache, const int32_t *seqlens, int B,
+                         int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
+                         fd_dtype_t dtype, void *out, float *lse,
+                         int num_splits, int flags, void *stream) {
+  if (Tq <= 0) return FD_ERR_INVALID_ARG;
+  if (dtype != FD_BF16) return FD_ERR_UNSUPPORTED;  // also for Tq == 1
+  fd::Extra ex;
+  ex.Tq = Tq;
+  return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
+             out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
+             fd::kPhaseChunks | fd::kPhaseMerge, ex);
+}
+
+int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
+               fd_dtype_t dtype, int varlen, int paged, int num_splits,
+               int variant, int flags, int num_cus, fd_plan_t *plan) {
+  if (!plan) return FD_ERR_INVALID_ARG;
+  if (num_cus < 0 || Tq <= 0) return FD_ERR_INVALID_ARG;
+  fd::Extra ex;
+  ex.Tq = Tq;
+  ex.paged = paged != 0;
+  const bool vl = varlen != 0 || ex.paged;
+  fd::Plan p;
+  int rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, vl, num_splits, variant,
+                         flags, 1, &p, ex);
+  if (rc != FD_OK) return rc;
   if (num_cus == 0) {
     rc = device_cus(&num_cus);
     if (rc != FD_OK) return rc;
   }
-  fd::Plan p;
-  rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, varlen != 0, num_splits,
-                     variant, flags, num_cus, &p);
+  rc = fd::make_plan(B, Hq, Hkv, D, Lmax, dtype, vl, num_splits, variant,
+                     flags, num_cus, &p, ex);
   if (rc != FD_OK) return rc;
   const fd::WorkspaceLayout lay = fd::workspace_layout(p);
   plan->num_splits = p.splits;
@@ -236,6 +297,13 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   plan->o_part_offset = p.combine ? lay.o_part_off : 0;
   plan->lse_part_offset = p.combine ? lay.lse_part_off : 0;
   return FD_OK;
+}
+
+int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+            int varlen, int num_splits, int variant, int flags, int num_cus,
+            fd_plan_t *plan) {
+  return fd_plan_ex(B, 1, Hq, Hkv, D, Lmax, dtype, varlen, 0, num_splits,
+                    variant, flags, num_cus, plan);
 }
 
 size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,

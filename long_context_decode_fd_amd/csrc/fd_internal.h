@@ -17,9 +17,11 @@ constexpr int kMaxGroup = 16;
 
 // Everything a launch needs, decided on the host.
 struct Plan {
-  int B, Hq, Hkv, G, D, Lmax;
+  int B, Hq, Hkv, G, D, Lmax;  // paged cache: Lmax = max_pages * page_size
+  int Tq;                       // new query tokens per sequence (1: decode)
   fd_dtype_t dtype;
   bool varlen;
+  bool paged;
   int num_cus;
   int variant;      // FD_VARIANT_MFMA or FD_VARIANT_VALU
   int waves;        // wavefronts per workgroup of the per-chunk pass
@@ -34,10 +36,16 @@ struct Plan {
 // Host-side checks of sizes/dtype shared by fd_plan and the decode calls.
 int validate_shape(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype);
 
+// Cache layout and query count beyond the plain decode call.
+struct Extra {
+  int Tq = 1;          // query tokens per sequence
+  bool paged = false;  // K/V in pages behind a block table
+};
+
 // Fills *p for a validated shape; requested_splits 0 = heuristic.
 int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
               bool varlen, int requested_splits, int requested_variant,
-              int flags, int num_cus, Plan *p);
+              int flags, int num_cus, Plan *p, Extra extra = Extra());
 
 // Byte offsets inside a workspace: the fused merge's per-group tickets
 // (int32 [B * Hkv], must be zero when a call starts; the kernels leave
@@ -47,10 +55,18 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout workspace_layout(const Plan &p);
 
+// Paged K/V: pool [num_pages][page_size][Hkv][D] per tensor; token j of
+// sequence b sits in page block_table[b][j / page_size], row j % page_size.
+struct PagedKV {
+  const int32_t *block_table;
+  int max_pages, page_size, num_pages;
+};
+
 // Kernel launches (fd_kernels.hip).  Return hipError_t as int.
 struct LaunchArgs {
   const void *q, *k, *v;
   const int32_t *seqlens;
+  PagedKV paged;  // used when the plan is paged
   void *out;
   float *lse;
   float *o_part;

@@ -79,6 +79,7 @@ constexpr int kModeFused = 2;     // partial, then the last one merges
 struct Work {
   int b, g, s;
   int lo, hi;  // keys [lo, hi) of slab (b, g); lo == hi only when L_b == 0
+  int L;       // clamped length of sequence b
   int nb;      // chunks of sequence b
   bool valid;
 };
@@ -97,7 +98,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
                           int Hkv, int Lmax, int C) {
   Work w;
   w.valid = false;
-  w.b = w.g = w.s = w.lo = w.hi = w.nb = 0;
+  w.b = w.g = w.s = w.lo = w.hi = w.L = w.nb = 0;
   if (seqlens == nullptr) {
     const int S = (Lmax + C - 1) / C;
     const int per_b = S * Hkv;
@@ -109,6 +110,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
     w.g = r - w.s * Hkv;
     w.lo = w.s * C;
     w.hi = min(w.lo + C, Lmax);
+    w.L = Lmax;
     w.nb = S;
     w.valid = true;
     return w;
@@ -140,6 +142,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
       w.g = r - w.s * Hkv;
       w.lo = w.s * C;
       w.hi = max(w.lo, min(w.lo + C, Lb));
+      w.L = Lb;
       w.nb = chunks_of(Lb, C);
       w.valid = true;
       return w;
@@ -147,6 +150,15 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
     base += total;
   }
   return w;
+}
+
+// Query rows served by the workgroup of (b, g): column c < G * Tq of the
+// q-tile is new token t = c / G and query head g * G + c % G.  q, out and
+// the partials are laid out [B][Tq][Hq] (Tq = 1: [B][Hq]).
+__device__ __forceinline__ size_t row_of(const Work &w, int G, int Hq, int Tq,
+                                         int c) {
+  const int t = c / G, h = c - t * G;
+  return ((size_t)w.b * Tq + t) * Hq + (size_t)w.g * G + h;
 }
 
 // ---------------------------------------------------------------------------
@@ -178,12 +190,12 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 template <int D, typename OutT>
 __device__ void merge_and_store(const float *sm_m, const float *sm_l,
                                 const float *sm_o, int nslot, int rows,
-                                int G, const Work &w, int Hq, int S,
+                                int G, int Tq, const Work &w, int Hq, int S,
                                 int mode, OutT *__restrict__ out,
                                 float *__restrict__ lse,
                                 float *__restrict__ o_part,
                                 float *__restrict__ lse_part) {
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < G * Tq * D; idx += blockDim.x) {
     const int h = idx / D, d = idx - h * D;
     float M = FD_NEG_INF;
     for (int sl = 0; sl < nslot; ++sl) M = fmaxf(M, sm_m[sl * rows + h]);
@@ -201,7 +213,7 @@ __device__ void merge_and_store(const float *sm_m, const float *sm_l,
       o = O / Ls;
       ls = (M + log2_f(Ls)) * kLn2;
     }
-    const size_t hq = (size_t)w.b * Hq + (size_t)w.g * G + h;
+    const size_t hq = row_of(w, G, Hq, Tq, h);
     if (mode == kModeDirect) {
       store_out<OutT>(out + hq * D + d, o);
       if (d == 0) lse[hq] = ls;
@@ -253,17 +265,17 @@ struct TailState {
   float4 acc;   // rescaled weighted sum of 4 output columns
 };
 
-// Folds chunks s = s_first, s_first + s_step, ... of item `it` (query row
-// it / (D/4) of the group, columns 4 (it % (D/4)) ..) into a TailState,
+// Folds chunks s = s_first, s_first + s_step, ... of item `it` (q-tile
+// column it / (D/4), output columns 4 (it % (D/4)) ..) into a TailState,
 // kTailBatch chunks per step with all of a step's loads issued first.
 template <int D>
-__device__ TailState merge_item(const Work &w, int G, int Hq, int S, int it,
-                                int s_first, int s_step,
+__device__ TailState merge_item(const Work &w, int G, int Tq, int Hq, int S,
+                                int it, int s_first, int s_step,
                                 const float *__restrict__ o_part,
                                 const float *__restrict__ lse_part) {
   constexpr int V4 = D / 4;
   const int h = it / V4, d4 = it - h * V4;
-  const size_t row = (size_t)w.b * Hq + (size_t)w.g * G + h;
+  const size_t row = row_of(w, G, Hq, Tq, h);
   const float *lp = lse_part + row * S;
   const float *op = o_part + row * S * D + d4 * 4;
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -306,12 +318,12 @@ __device__ TailState merge_item(const Work &w, int G, int Hq, int S, int it,
 
 // Writes 4 output columns of one row (and the row's lse with the first 4).
 template <int D, typename OutT>
-__device__ void store_item(const Work &w, int G, int Hq, int it, float M,
-                           float W, float4 a, OutT *__restrict__ out,
+__device__ void store_item(const Work &w, int G, int Tq, int Hq, int it,
+                           float M, float W, float4 a, OutT *__restrict__ out,
                            float *__restrict__ lse) {
   constexpr int V4 = D / 4;
   const int h = it / V4, d4 = it - h * V4;
-  const size_t row = (size_t)w.b * Hq + (size_t)w.g * G + h;
+  const size_t row = row_of(w, G, Hq, Tq, h);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float ls = FD_NEG_INF;
   if (M != FD_NEG_INF) {
@@ -329,22 +341,22 @@ __device__ void store_item(const Work &w, int G, int Hq, int it, float M,
 // Merges the nb chunk partials of group (w.b, w.g) into out/lse with the
 // whole workgroup (the fused path's last workgroup).
 template <int D, typename OutT>
-__device__ void group_merge(const Work &w, int G, int Hq, int S,
+__device__ void group_merge(const Work &w, int G, int Tq, int Hq, int S,
                             const float *__restrict__ o_part,
                             const float *__restrict__ lse_part,
                             OutT *__restrict__ out, float *__restrict__ lse,
                             float *scratch) {
   constexpr int V4 = D / 4;
   const int T = blockDim.x, tid = threadIdx.x;
-  const int items = G * V4;
+  const int items = G * Tq * V4;
   // More items than threads: each thread merges whole items on its own.
   // Otherwise each item's chunks are split over `slices` threads.
   const int slices = max(1, T / items);
   if (slices == 1) {
     for (int it = tid; it < items; it += T) {
-      const TailState st = merge_item<D>(w, G, Hq, S, it, 0, 1, o_part,
+      const TailState st = merge_item<D>(w, G, Tq, Hq, S, it, 0, 1, o_part,
                                          lse_part);
-      store_item<D, OutT>(w, G, Hq, it, st.M, st.W, st.acc, out, lse);
+      store_item<D, OutT>(w, G, Tq, Hq, it, st.M, st.W, st.acc, out, lse);
     }
     return;
   }
@@ -352,8 +364,8 @@ __device__ void group_merge(const Work &w, int G, int Hq, int S,
   float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   if (tid < items * slices)
-    st = merge_item<D>(w, G, Hq, S, tid % items, tid / items, slices, o_part,
-                       lse_part);
+    st = merge_item<D>(w, G, Tq, Hq, S, tid % items, tid / items, slices,
+                       o_part, lse_part);
   sM[tid] = st.M;
   sW[tid] = st.W;
   sA[tid] = st.acc;
@@ -375,13 +387,14 @@ __device__ void group_merge(const Work &w, int G, int Hq, int S,
         a.w += r * sA[k].w;
       }
     }
-    store_item<D, OutT>(w, G, Hq, it, Mt, Wt, a, out, lse);
+    store_item<D, OutT>(w, G, Tq, Hq, it, Mt, Wt, a, out, lse);
   }
 }
 
 template <int D, typename OutT>
-__device__ void merge_group_if_last(const Work &w, int G, int Hq, int Hkv,
-                                    int S, const float *__restrict__ o_part,
+__device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
+                                    int Hkv, int S,
+                                    const float *__restrict__ o_part,
                                     const float *__restrict__ lse_part,
                                     int *__restrict__ tickets,
                                     OutT *__restrict__ out,
@@ -407,7 +420,7 @@ __device__ void merge_group_if_last(const Work &w, int G, int Hq, int Hkv,
   if (!*sm_flag) return;
   // The last workgroup reads the partials with device-coherent loads,
   // issued only after its ticket came back.
-  group_merge<D, OutT>(w, G, Hq, S, o_part, lse_part, out, lse, scratch);
+  group_merge<D, OutT>(w, G, Tq, Hq, S, o_part, lse_part, out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -453,11 +466,44 @@ __device__ __forceinline__ uint32_t dword_of<4>(const uint2 &v, int i) {
   return i == 0 ? v.x : v.y;
 }
 
-template <int D, bool TAIL>
+// Where the key rows of a tile live.  Contiguous cache: row r of the tile
+// starting at key k0 is k[(k0 + r) * D].  Paged cache: the tile's two
+// 16-key halves each lie inside one page, at h0 / h1, rows rs = Hkv * D
+// elements apart.
+template <int D, bool PAGED>
+struct TileRows;
+template <int D>
+struct TileRows<D, false> {
+  const uint16_t *k, *v;  // slab (b, g)
+  int k0;
+  __device__ const uint16_t *krow(int r) const {
+    return k + (size_t)(k0 + r) * D;
+  }
+  __device__ const uint16_t *vrow(int r) const {
+    return v + (size_t)(k0 + r) * D;
+  }
+};
+template <int D>
+struct TileRows<D, true> {
+  const uint16_t *k0h, *k1h, *v0h, *v1h;
+  size_t rs;
+  __device__ const uint16_t *krow(int r) const {
+    return (r < 16 ? k0h : k1h) + (size_t)(r & 15) * rs;
+  }
+  __device__ const uint16_t *vrow(int r) const {
+    return (r < 16 ? v0h : v1h) + (size_t)(r & 15) * rs;
+  }
+};
+
+// One 32-key tile of one wavefront.  TAIL tiles load only their first
+// `valid` rows (others re-read the last valid one and the V rows are
+// zeroed) and give keys at or beyond the lane's `lim` a score of -inf;
+// full tiles need neither.
+template <int D, bool TAIL, typename Rows>
 __device__ __forceinline__ void mfma_tile(
-    const uint16_t *__restrict__ kslab, const uint16_t *__restrict__ vslab,
-    int k0, int valid, int n16, int q4, const bf16x8 (&qop)[D / 32],
-    float scale_log2, floatx4 (&acc)[D / 16], float &m, float &l) {
+    const Rows &rows, int valid, int lim, int n16, int q4,
+    const bf16x8 (&qop)[D / 32], float scale_log2, floatx4 (&acc)[D / 16],
+    float &m, float &l) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   typedef typename VecOf<VW>::type VT;
@@ -467,7 +513,7 @@ __device__ __forceinline__ void mfma_tile(
   for (int sub = 0; sub < 2; ++sub) {
     int r = sub * 16 + n16;
     if (TAIL) r = min(r, valid - 1);
-    const uint16_t *p = kslab + (size_t)(k0 + r) * D + q4 * 8;
+    const uint16_t *p = rows.krow(r) + q4 * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       kr[sub][kk] = load_stream(reinterpret_cast<const uint4 *>(p + kk * 32));
@@ -478,7 +524,7 @@ __device__ __forceinline__ void mfma_tile(
     int r = (i >> 2) * 16 + q4 * 4 + (i & 3);
     if (TAIL) r = min(r, valid - 1);
     vr[i] = load_stream(
-        reinterpret_cast<const VT *>(vslab + (size_t)(k0 + r) * D + n16 * VW));
+        reinterpret_cast<const VT *>(rows.vrow(r) + n16 * VW));
   }
 
   floatx4 sc[2];
@@ -497,7 +543,7 @@ __device__ __forceinline__ void mfma_tile(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float x = sc[sub][j] * scale_log2;
-      if (TAIL && sub * 16 + q4 * 4 + j >= valid) x = FD_NEG_INF;
+      if (TAIL && sub * 16 + q4 * 4 + j >= lim) x = FD_NEG_INF;
       s[sub * 4 + j] = x;
     }
   float mt = s[0];
@@ -556,14 +602,34 @@ __device__ __forceinline__ void mfma_tile(
                                                      0, 0);
 }
 
-template <int D, int NW>
+// Paged cache: the pool row (page * page_size + offset in page) of the
+// first key of each 16-key half of this wavefront's tiles it0 .. it0 + 31
+// (lane 2 j + h: half h of tile it0 + j).  Halves at or beyond the chunk
+// end read nothing and give row 0; page indices are clamped into the pool,
+// so no entry of the table can make a load leave the K/V buffers.
+__device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
+                                         int wave, int nw, int it0,
+                                         int lane) {
+  const int t = wave + (it0 + (lane >> 1)) * nw;
+  const int key = w.lo + t * kKeyTile + (lane & 1) * 16;
+  if (key >= w.hi) return 0;
+  const int j = key / pk.page_size;
+  int pg = pk.block_table[(size_t)w.b * pk.max_pages + j];
+  pg = min(max(pg, 0), pk.num_pages - 1);
+  return pg * pk.page_size + (key - j * pk.page_size);
+}
+
+// PAGED: K/V in a page pool behind a block table.  CAUSAL: Tq > 1 new
+// tokens per sequence, each column with its own key limit (a separate
+// instantiation keeps the single-token loop exactly as simple as before).
+template <int D, int NW, bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
-    int B, int Hq, int Hkv, int G, int Lmax, int C, int S, float scale_log2,
-    int mode, uint16_t *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ o_part, float *__restrict__ lse_part,
-    int *__restrict__ tickets) {
+    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
+    float scale_log2, int mode, uint16_t *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ o_part,
+    float *__restrict__ lse_part, int *__restrict__ tickets) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   static_assert(16 * (D + 1) >= 6 * 64, "LDS reused by the fused merge");
@@ -576,12 +642,12 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
   if (!w.valid) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, q4 = lane >> 4;
+  const int ncol = G * Tq;
 
   bf16x8 qop[KK];
   {
-    const bool live = n16 < G;
-    const uint16_t *qr = q + ((size_t)w.b * Hq + (size_t)w.g * G +
-                              (live ? n16 : 0)) * D + q4 * 8;
+    const bool live = n16 < ncol;
+    const uint16_t *qr = q + row_of(w, G, Hq, Tq, live ? n16 : 0) * D + q4 * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 t = live ? *reinterpret_cast<const uint4 *>(qr + kk * 32)
@@ -589,9 +655,14 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
       qop[kk] = __builtin_bit_cast(bf16x8, t);
     }
   }
+  // Causal limit among the Tq new tokens (the newest Tq keys of the
+  // sequence): column c, token t = c / G, sees keys below L - (Tq - 1 - t).
+  // Tiles wholly below the first token's limit need no mask.
+  const int hi_col = min(w.hi, w.L - (Tq - 1 - n16 / G));
+  const int hi_all = min(w.hi, w.L - (Tq - 1));
+
   const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
-  const uint16_t *kslab = kc + slab;
-  const uint16_t *vslab = vc + slab;
+  const size_t head = (size_t)w.g * D;
 
   floatx4 acc[VW];
 #pragma unroll
@@ -599,20 +670,38 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
   float m = FD_NEG_INF, l = 0.f;
 
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
-  for (int t = wave; t < ntiles; t += NW) {
+  int prow = 0;
+  for (int t = wave, it = 0; t < ntiles; t += NW, ++it) {
     const int k0 = w.lo + t * kKeyTile;
+    TileRows<D, PAGED> rows;
+    if constexpr (PAGED) {
+      const int slot = it & 31;
+      if (slot == 0) prow = page_rows(pk, w, wave, NW, it, lane);
+      const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
+      const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
+      rows.rs = (size_t)Hkv * D;
+      rows.k0h = kc + (size_t)r0 * rows.rs + head;
+      rows.k1h = kc + (size_t)r1 * rows.rs + head;
+      rows.v0h = vc + (size_t)r0 * rows.rs + head;
+      rows.v1h = vc + (size_t)r1 * rows.rs + head;
+    } else {
+      rows.k = kc + slab;
+      rows.v = vc + slab;
+      rows.k0 = k0;
+    }
     const int valid = min(kKeyTile, w.hi - k0);
-    if (valid == kKeyTile)
-      mfma_tile<D, false>(kslab, vslab, k0, valid, n16, q4, qop, scale_log2,
+    const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
+    if (full)
+      mfma_tile<D, false>(rows, kKeyTile, kKeyTile, n16, q4, qop, scale_log2,
                           acc, m, l);
     else
-      mfma_tile<D, true>(kslab, vslab, k0, valid, n16, q4, qop, scale_log2,
-                         acc, m, l);
+      mfma_tile<D, true>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16, q4,
+                         qop, scale_log2, acc, m, l);
   }
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (n16 < G) {
+  if (n16 < ncol) {
     if (q4 == 0) {
       sm_m[wave * 16 + n16] = m;
       sm_l[wave * 16 + n16] = l;
@@ -624,10 +713,10 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
       for (int j = 0; j < 4; ++j) o[(q4 * 4 + j) * VW + e] = acc[e][j];
   }
   __syncthreads();
-  merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, G, w, Hq, S,
+  merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, G, Tq, w, Hq, S,
                                mode, out, lse, o_part, lse_part);
   if (mode == kModeFused)
-    merge_group_if_last<D, uint16_t>(w, G, Hq, Hkv, S, o_part, lse_part,
+    merge_group_if_last<D, uint16_t>(w, G, Tq, Hq, Hkv, S, o_part, lse_part,
                                      tickets, out, lse, sm_o, &sm_flag);
 }
 
@@ -788,16 +877,16 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     }
   }
   __syncthreads();
-  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, G, w, Hq, S, mode, out,
-                        lse, o_part, lse_part);
+  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, G, 1, w, Hq, S, mode,
+                        out, lse, o_part, lse_part);
   if (mode == kModeFused)
-    merge_group_if_last<D, T>(w, G, Hq, Hkv, S, o_part, lse_part, tickets,
+    merge_group_if_last<D, T>(w, G, 1, Hq, Hkv, S, o_part, lse_part, tickets,
                               out, lse, sm_o, &sm_flag);
 }
 
 // ---------------------------------------------------------------------------
 // Merge pass (the default): one workgroup of kMergeWaves wavefronts per
-// (b, query head) row; wavefront w folds chunks w, w + kMergeWaves, ...
+// query row (b, token, head); wavefront w folds chunks w, w + kMergeWaves, ...
 // into a running (M, W, acc) kMergeBatch chunks at a time, all of a batch's
 // loads issued before any is used (the pass is latency-bound: a few MB).
 // Per batch: M' = max(M, max_s lse_s), r = e^(M - M'),
@@ -810,13 +899,13 @@ constexpr int kMergeBatch = 16;
 template <int D, typename OutT>
 __global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
-    const int32_t *__restrict__ seqlens, int Hq, int Lmax, int C, int S,
-    OutT *__restrict__ out, float *__restrict__ lse) {
+    const int32_t *__restrict__ seqlens, int rows_per_b, int Lmax, int C,
+    int S, OutT *__restrict__ out, float *__restrict__ lse) {
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float sm_M[kMergeWaves], sm_W[kMergeWaves];
   __shared__ float sm_acc[kMergeWaves][D];
   const int row = blockIdx.x;
-  const int b = row / Hq;
+  const int b = row / rows_per_b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
   const int nb = min(S, chunks_of(L, C));
@@ -935,7 +1024,7 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
   return hipSuccess;
 }
 
-template <int D>
+template <int D, bool PAGED, bool CAUSAL>
 hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
                        hipStream_t st) {
   const dim3 grid(p.grid);
@@ -946,10 +1035,11 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   uint16_t *out = static_cast<uint16_t *>(a.out);
 #define FD_MFMA_CASE(NWV)                                                    \
   case NWV:                                                                  \
-    hipLaunchKernelGGL((split_mfma_kernel<D, NWV>), grid, dim3(NWV * 64), 0, \
-                       st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G, p.Lmax, \
-                       p.chunk, p.splits, sl2, part, out, a.lse, a.o_part,    \
-                       a.lse_part, a.tickets);                               \
+    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL>), grid,     \
+                       dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
+                       p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk,         \
+                       p.splits, sl2, part, out, a.lse, a.o_part, a.lse_part, \
+                       a.tickets);                                           \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(1)
@@ -965,9 +1055,9 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
 
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Hq),
+  hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Tq * p.Hq),
                      dim3(kMergeWaves * 64), 0, st, a.o_part, a.lse_part,
-                     a.seqlens, p.Hq, p.Lmax, p.chunk, p.splits,
+                     a.seqlens, p.Tq * p.Hq, p.Lmax, p.chunk, p.splits,
                      static_cast<OutT *>(a.out), a.lse);
 }
 
@@ -980,8 +1070,19 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   if (!(a.phases & kPhaseChunks)) {
     // merge only
   } else if (p.variant == FD_VARIANT_MFMA) {
-    e = p.D == 128 ? launch_mfma<128>(p, a, sl2, st)
-                   : launch_mfma<64>(p, a, sl2, st);
+    const bool causal = p.Tq > 1;
+    if (p.D == 128)
+      e = p.paged ? (causal ? launch_mfma<128, true, true>(p, a, sl2, st)
+                            : launch_mfma<128, true, false>(p, a, sl2, st))
+                  : (causal ? launch_mfma<128, false, true>(p, a, sl2, st)
+                            : launch_mfma<128, false, false>(p, a, sl2, st));
+    else
+      e = p.paged ? (causal ? launch_mfma<64, true, true>(p, a, sl2, st)
+                            : launch_mfma<64, true, false>(p, a, sl2, st))
+                  : (causal ? launch_mfma<64, false, true>(p, a, sl2, st)
+                            : launch_mfma<64, false, false>(p, a, sl2, st));
+  } else if (p.paged || p.Tq != 1) {
+    e = hipErrorInvalidValue;  // the planner sends these to the MFMA kernel
   } else if (p.dtype == FD_BF16) {
     e = p.D == 128 ? launch_valu<uint16_t, 128, 4>(p, a, sl2, st)
                    : launch_valu<uint16_t, 64, 4>(p, a, sl2, st);

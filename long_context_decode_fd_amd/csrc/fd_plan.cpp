@@ -19,9 +19,10 @@
 //     2 * C * D * elem bytes of K/V a chunk streams);
 //   * S == 1 means no partials and no merge pass at all;
 //   * with per-sequence lengths the mix is unknown on the host (the library
-//     never reads device memory synchronously), so chunks are sized for
-//     balance instead: kVarlenChunk keys, so that no single long sequence
-//     sets the finish time.
+//     never reads device memory synchronously), so chunks are also capped
+//     at kVarlenChunk keys, so that no single long sequence sets the finish
+//     time.  A paged cache always comes with per-sequence lengths; its
+//     Lmax is the block table's capacity, max_pages * page_size.
 //
 // The constants are this library's own (the pages give none) and the
 // result of any plan is the same attention; only speed depends on them.
@@ -78,7 +79,7 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
 WorkspaceLayout workspace_layout(const Plan &p) {
   WorkspaceLayout w{0, 0, 0, 0};
   if (!p.combine) return w;
-  size_t rows = (size_t)p.B * p.Hq * p.splits;
+  size_t rows = (size_t)p.B * p.Tq * p.Hq * p.splits;
   w.ticket_bytes = p.fused ? align256((size_t)p.B * p.Hkv * sizeof(int)) : 0;
   w.o_part_off = w.ticket_bytes;
   w.lse_part_off = w.o_part_off + align256(rows * p.D * sizeof(float));
@@ -88,9 +89,19 @@ WorkspaceLayout workspace_layout(const Plan &p) {
 
 int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
               bool varlen, int requested_splits, int requested_variant,
-              int flags, int num_cus, Plan *p) {
+              int flags, int num_cus, Plan *p, Extra extra) {
   int rc = validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
+  if (extra.Tq < 1) return FD_ERR_INVALID_ARG;
+  // Several new tokens or a paged cache: the matrix-core kernel only, with
+  // all G * Tq query rows of a KV head in its 16-column q-tile.
+  const bool general = extra.Tq > 1 || extra.paged;
+  if (general) {
+    if (dtype != FD_BF16 || requested_variant == FD_VARIANT_VALU)
+      return FD_ERR_UNSUPPORTED;
+    if ((long)(Hq / Hkv) * extra.Tq > kMaxGroup) return FD_ERR_UNSUPPORTED;
+    if ((long)B * Hq * extra.Tq > (1L << 30)) return FD_ERR_UNSUPPORTED;
+  }
   if (num_cus <= 0) return FD_ERR_INVALID_ARG;
   if (requested_splits < 0) return FD_ERR_INVALID_ARG;
   if (requested_variant < FD_VARIANT_AUTO ||
@@ -106,8 +117,10 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.G = Hq / Hkv;
   q.D = D;
   q.Lmax = Lmax;
+  q.Tq = extra.Tq;
   q.dtype = dtype;
   q.varlen = varlen;
+  q.paged = extra.paged;
   q.num_cus = num_cus;
 
   // Kernel variant: matrix cores need bf16; fp32 runs on the vector ALU.
@@ -132,14 +145,15 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_splits > 0) {
     int s = std::min(requested_splits, max_splits);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
-  } else if (varlen) {
-    chunk = std::min(kVarlenChunk, full_chunk);
   } else {
     const long units = (long)B * Hkv;
     const long target = (long)num_cus * kBlocksPerCU;
     int s = (int)std::max(1L, (target + units - 1) / units);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
     chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
+    // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
+    // than the even split would make it were every sequence full.
+    if (varlen) chunk = std::min(chunk, kVarlenChunk);
   }
   q.chunk = chunk;
   q.splits = ceil_div(Lmax, chunk);

@@ -13,14 +13,20 @@ serving.  The pages name no dataset; everything is synthetic.
 Recipe (every stream is an independent PCG64 seeded from
 ``SeedSequence(seed, spawn_key=...)`` so any one slab can be rebuilt alone):
 
-* q           spawn_key (0,)        standard normal float32 -> dtype
+* q           spawn_key (0,)        standard normal float32 -> dtype,
+                                     [B, Hq, D] ([B, Tq, Hq, D] if Tq > 1)
 * seqlens     spawn_key (4,)        u ~ U[0,1): floor(lo * (hi/lo)**u), <= hi
+* pages       spawn_key (5,)        paged cache: the pool holds
+                                     B * max_pages + spare pages; the block
+                                     table is a random permutation's first
+                                     B * max_pages entries
 * K[b, g]     spawn_key (1, b, g)   standard normal float32 rows [0, L_b)
 * V[b, g]     spawn_key (2, b, g)   standard normal float32 rows [0, L_b)
 * peaks[b, g] spawn_key (3, b, g)   ceil(frac * L_b) distinct rows of K
                                      multiplied by ``peak_mult`` (exact)
 * rows >= L_b of a padded slab hold NaN (bf16 0xFFFF, fp32 0xFFFFFFFF) so
-  that a kernel reading past the valid prefix is caught.
+  that a kernel reading past the valid prefix is caught; so do the unused
+  rows of a sequence's last page and every spare page of a paged pool.
 
 bf16 values are produced by rounding float32 to nearest-even on the bit
 pattern and are handled as ``numpy.uint16`` arrays throughout.
@@ -49,6 +55,8 @@ class Workload:
     peak_frac: float = 0.0
     peak_mult: float = 8.0
     varlen: tuple | None = None   # (lo, hi) for log-uniform seqlens
+    Tq: int = 1                   # new query tokens per sequence
+    page_size: int = 0            # > 0: K/V in a paged pool
     note: str = field(default="", compare=False)
 
     @property
@@ -66,6 +74,15 @@ class Workload:
     @property
     def np_dtype(self):
         return np.uint16 if self.dtype == "bf16" else np.float32
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.Lmax // self.page_size)
+
+    @property
+    def num_pages(self) -> int:
+        n = self.B * self.max_pages
+        return n + 2 + n // 16          # a few spare pages stay unused
 
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
@@ -97,6 +114,27 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 BENCH_WORKLOAD = "b1_gqa8_h64_d128_l65536"
+
+# The same data behind the two cache layouts / query counts beyond plain
+# decode: a vLLM-style paged pool, and several causal new tokens.
+EXTRA_WORKLOADS = {
+    w.name: w for w in [
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="paged_p64_b1_gqa8_h64_d128_l65536", page_size=64,
+            note="batch-1 64k decode from 64-token pages"),
+        WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+            name="paged_p16_varlen_b16_gqa8_h64_d128_lmax131072",
+            page_size=16,
+            note="variable-length batch from 16-token pages"),
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="mq2_b1_gqa8_h64_d128_l65536", Tq=2,
+            note="two causal new tokens, batch-1 64k (16 q-tile columns)"),
+        WORKLOADS["b64_gqa4_h32_d128_l4096"].with_(
+            name="mq4_b64_gqa4_h32_d128_l4096", Tq=4,
+            note="four causal new tokens, batch 64 at 4k"),
+    ]
+}
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -138,8 +176,45 @@ def seqlen_of(w: Workload, seqlens, b: int) -> int:
 
 
 def gen_q(w: Workload) -> np.ndarray:
-    x = _rng(w.seed, 0).standard_normal((w.B, w.Hq, w.D), dtype=np.float32)
+    shape = ((w.B, w.Hq, w.D) if w.Tq == 1 else (w.B, w.Tq, w.Hq, w.D))
+    x = _rng(w.seed, 0).standard_normal(shape, dtype=np.float32)
     return _encode(x, w.dtype)
+
+
+def paged_seqlens(w: Workload, seqlens=None) -> np.ndarray:
+    """A paged call always takes lengths: the workload's, else Lmax."""
+    if seqlens is None:
+        seqlens = gen_seqlens(w)
+    if seqlens is None:
+        seqlens = np.full(w.B, w.Lmax, np.int32)
+    return np.asarray(seqlens, np.int32)
+
+
+def gen_block_table(w: Workload) -> np.ndarray:
+    """int32 [B, max_pages]: distinct pool pages in random order."""
+    perm = _rng(w.seed, 5).permutation(w.num_pages)
+    return perm[:w.B * w.max_pages].reshape(w.B, w.max_pages).astype(
+        np.int32)
+
+
+def scatter_pages(w: Workload, k: np.ndarray, v: np.ndarray,
+                  block_table: np.ndarray, seqlens):
+    """Host pools [num_pages, page_size, Hkv, D] holding rows [0, L_b) of
+    the contiguous k/v [B, Hkv, Lmax, D]; every other row is NaN."""
+    P = w.page_size
+    shape = (w.num_pages, P, w.Hkv, w.D)
+    kp = np.empty(shape, w.np_dtype)
+    vp = np.empty(shape, w.np_dtype)
+    kp.view(np.uint8)[:] = 0xFF
+    vp.view(np.uint8)[:] = 0xFF
+    for b in range(w.B):
+        L = min(int(seqlens[b]), w.Lmax)
+        for j in range(-(-L // P)):
+            n = min(P, L - j * P)
+            pg = block_table[b, j]
+            kp[pg, :n] = k[b, :, j * P:j * P + n].transpose(1, 0, 2)
+            vp[pg, :n] = v[b, :, j * P:j * P + n].transpose(1, 0, 2)
+    return kp, vp
 
 
 def peak_rows(w: Workload, b: int, g: int, L: int) -> np.ndarray:
@@ -197,16 +272,17 @@ def gen_all(w: Workload):
     return q, k, v, seqlens
 
 
-def to_device(a: np.ndarray):
+def to_device(a: np.ndarray, device: str = "cuda"):
     """Host array (uint16 bf16 bits or float32) -> torch device tensor."""
     import torch
     if a.dtype == np.uint16:
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
-        return t.view(torch.bfloat16).to("cuda")
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        return t.view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def device_inputs(w: Workload, seqlens=None, keep_host: bool = False):
+def device_inputs(w: Workload, seqlens=None, keep_host: bool = False,
+                  device: str = "cuda"):
     """Upload a workload: (q, k, v, seqlens_dev, seqlens_host, host).
 
     K/V are generated slab by slab on the host and copied into place; rows
@@ -218,10 +294,10 @@ def device_inputs(w: Workload, seqlens=None, keep_host: bool = False):
         seqlens = gen_seqlens(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q_h = gen_q(w)
-    q = to_device(q_h)
+    q = to_device(q_h, device)
     shape = (w.B, w.Hkv, w.Lmax, w.D)
-    k = torch.empty(shape, dtype=tdt, device="cuda")
-    v = torch.empty(shape, dtype=tdt, device="cuda")
+    k = torch.empty(shape, dtype=tdt, device=device)
+    v = torch.empty(shape, dtype=tdt, device=device)
     if seqlens is not None:
         iv = torch.int16 if w.dtype == "bf16" else torch.int32
         k.view(iv).fill_(-1)       # all-ones bit patterns are NaN
@@ -234,8 +310,8 @@ def device_inputs(w: Workload, seqlens=None, keep_host: bool = False):
         for g in range(w.Hkv):
             kr, vr = gen_slab_rows(w, b, g, L)
             if L:
-                k[b, g, :L].copy_(to_device(kr))
-                v[b, g, :L].copy_(to_device(vr))
+                k[b, g, :L].copy_(to_device(kr, device))
+                v[b, g, :L].copy_(to_device(vr, device))
             if keep_host:
                 host[1][b, g, :L], host[2][b, g, :L] = kr, vr
                 if L < w.Lmax:
@@ -243,21 +319,61 @@ def device_inputs(w: Workload, seqlens=None, keep_host: bool = False):
                     host[2][b, g, L:].view(np.uint8)[:] = 0xFF
     sl_dev = None
     if seqlens is not None:
-        sl_dev = torch.from_numpy(np.asarray(seqlens, np.int32)).to("cuda")
+        sl_dev = torch.from_numpy(np.asarray(seqlens, np.int32)).to(device)
     return q, k, v, sl_dev, seqlens, host
+
+
+def device_paged_inputs(w: Workload, seqlens=None, device: str = "cuda"):
+    """Upload a paged workload: (q, k_pages, v_pages, block_table_dev,
+    seqlens_dev, seqlens_host, block_table_host).
+
+    The contiguous cache of ``device_inputs`` is scattered into the pool on
+    the device (rows past a length and spare pages hold NaN bits), then
+    released.
+    """
+    import torch
+    seqlens = paged_seqlens(w, seqlens)
+    q, k, v, sl_dev, _, _ = device_inputs(w, seqlens=seqlens, device=device)
+    bt = gen_block_table(w)
+    P, mp = w.page_size, w.max_pages
+    iv = torch.int16 if w.dtype == "bf16" else torch.int32
+    pools = []
+    for src in (k, v):
+        pool = torch.empty((w.num_pages, P, w.Hkv, w.D), dtype=src.dtype,
+                           device=device)
+        pool.view(iv).fill_(-1)
+        pad = mp * P - w.Lmax
+        if pad:
+            src = torch.nn.functional.pad(src.view(iv), (0, 0, 0, pad),
+                                          value=-1).view(src.dtype)
+        # [B, Hkv, mp, P, D] -> [B * mp, P, Hkv, D], page j of sequence b
+        pages = src.view(w.B, w.Hkv, mp, P, w.D).permute(0, 2, 3, 1, 4)
+        idx = torch.from_numpy(bt.reshape(-1).astype(np.int64)).to(device)
+        pool.view(iv).index_copy_(0, idx, pages.reshape(
+            w.B * mp, P, w.Hkv, w.D).view(iv))
+        pools.append(pool)
+    del k, v
+    bt_dev = torch.from_numpy(bt).to(device)
+    return q, pools[0], pools[1], bt_dev, sl_dev, seqlens, bt
 
 
 def algorithmic_bytes(w: Workload, seqlens=None) -> int:
     """Bytes one decode step must move at minimum: every valid K and V row
-    once, q, out, and the fp32 lse."""
+    once, q, out, and the fp32 lse (Tq rows of each per sequence and head),
+    plus, for a paged cache, the block-table entries of the valid pages."""
     eb = w.elem_bytes
-    rows = (w.Lmax * w.B if seqlens is None
-            else int(np.sum(np.clip(seqlens, 0, w.Lmax))))
+    Ls = (np.full(w.B, w.Lmax) if seqlens is None
+          else np.clip(np.asarray(seqlens, np.int64), 0, w.Lmax))
+    rows = int(np.sum(Ls))
     kv = 2 * rows * w.Hkv * w.D * eb
-    return kv + 2 * w.B * w.Hq * w.D * eb + 4 * w.B * w.Hq
+    qo = w.Tq * (2 * w.B * w.Hq * w.D * eb + 4 * w.B * w.Hq)
+    table = 0
+    if w.page_size:
+        table = 4 * int(np.sum(-(-Ls // w.page_size)))
+    return kv + qo + table
 
 
 def flops(w: Workload, seqlens=None) -> int:
     rows = (w.Lmax * w.B if seqlens is None
             else int(np.sum(np.clip(seqlens, 0, w.Lmax))))
-    return 4 * rows * w.Hq * w.D
+    return 4 * rows * w.Hq * w.D * w.Tq

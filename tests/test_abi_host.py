@@ -33,7 +33,8 @@ def test_header_declares_the_documented_entry_points():
     assert names == sorted(["fd_decode", "fd_decode_ex", "fd_plan",
                             "fd_workspace_bytes", "fd_status_string",
                             "fd_version", "fd_decode_partials",
-                            "fd_merge_partials"])
+                            "fd_merge_partials", "fd_decode_paged",
+                            "fd_decode_multiquery", "fd_plan_ex"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -213,3 +214,94 @@ def test_binding_marshals_nothing_but_pointers():
         for a in args:
             assert a in (ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
                          ctypes.c_size_t) or hasattr(a, "_type_"), name
+
+
+def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
+               num_pages=8, seqlens=A, B=1, Hq=8, Hkv=8, D=128, scale=0.1,
+               dtype=0, out=A, lse=A, num_splits=0, flags=0):
+    return lib.fd_decode_paged(q, k, v, bt, max_pages, page_size, num_pages,
+                               seqlens, B, Hq, Hkv, D, scale, dtype, out, lse,
+                               num_splits, flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), fd.FD_ERR_INVALID_ARG),
+    (dict(bt=A + 2), fd.FD_ERR_INVALID_ARG),
+    (dict(seqlens=None), fd.FD_ERR_INVALID_ARG),   # required when paged
+    (dict(max_pages=0), fd.FD_ERR_INVALID_ARG),
+    (dict(page_size=0), fd.FD_ERR_INVALID_ARG),
+    (dict(num_pages=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(page_size=24), fd.FD_ERR_UNSUPPORTED),   # not a multiple of 16
+    (dict(page_size=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(max_pages=1 << 26, page_size=64), fd.FD_ERR_UNSUPPORTED),
+    (dict(num_pages=1 << 26, page_size=64), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),        # bf16 only
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(k=A + 8), fd.FD_ERR_INVALID_ARG),
+    (dict(lse=None), fd.FD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=4), fd.FD_ERR_INVALID_ARG),
+    (dict(num_splits=-2), fd.FD_ERR_INVALID_ARG),
+    (dict(B=0), fd.FD_ERR_INVALID_ARG),
+])
+def test_paged_arguments_rejected_on_host(lib, kw, code):
+    assert call_paged(lib, **kw) == code
+
+
+def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
+            D=128, Lmax=64, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
+            flags=0):
+    return lib.fd_decode_multiquery(q, k, v, seqlens, B, Tq, Hq, Hkv, D, Lmax,
+                                    scale, dtype, out, lse, num_splits, flags,
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Tq=-3), fd.FD_ERR_INVALID_ARG),
+    (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 17 columns
+    (dict(Tq=5, Hq=32, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 4 x 5 = 20
+    (dict(Tq=2, Hq=64, Hkv=4), fd.FD_ERR_UNSUPPORTED),   # G alone is 16
+    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),
+    (dict(Tq=1, dtype=1), fd.FD_ERR_UNSUPPORTED),
+    (dict(B=1 << 20, Tq=16, Hq=128, Hkv=128), fd.FD_ERR_UNSUPPORTED),
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(seqlens=A + 1), fd.FD_ERR_INVALID_ARG),
+    (dict(D=80), fd.FD_ERR_UNSUPPORTED),
+    (dict(Lmax=0), fd.FD_ERR_INVALID_ARG),
+])
+def test_multiquery_arguments_rejected_on_host(lib, kw, code):
+    assert call_mq(lib, **kw) == code
+
+
+def test_plan_ex_for_several_tokens_and_pages(lib):
+    w = wl.WORKLOADS["b1_gqa8_h64_d128_l65536"]
+    base = plan(w)
+    # one token: identical to fd_plan
+    p1 = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_cus=256)
+    assert p1 == base
+    # Tq tokens: same chunks and grid, Tq times the partial rows
+    p2 = fd.fd_plan_ex(w.B, 2, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", num_cus=256)
+    assert (p2["num_splits"], p2["chunk"], p2["grid"]) == \
+        (base["num_splits"], base["chunk"], base["grid"])
+    rows = w.B * 2 * w.Hq * p2["num_splits"]
+    assert p2["lse_part_offset"] == rows * w.D * 4
+    assert p2["workspace_bytes"] == rows * w.D * 4 + rows * 4
+    # paged: per-sequence lengths are implied; the even split still
+    # applies when it is finer than the var-len cap
+    pp = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", paged=True,
+                       num_cus=256)
+    assert (pp["chunk"], pp["num_splits"]) == (1024, 64)
+    pv = fd.fd_plan_ex(16, 1, 64, 8, 128, 131072, "bf16", paged=True,
+                       num_cus=256)
+    assert pv["chunk"] == 2048
+    for kw in (dict(Tq=3, Hq=64, Hkv=8), dict(Tq=2, dtype="f32"),
+               dict(Tq=1, dtype="f32", paged=True),
+               dict(Tq=2, variant=fd.FD_VARIANT_VALU), dict(Tq=0)):
+        args = dict(B=1, Tq=1, Hq=8, Hkv=8, D=128, Lmax=4096, dtype="bf16",
+                    num_cus=256)
+        args.update(kw)
+        with pytest.raises(fd.FdError):
+            fd.fd_plan_ex(**args)

@@ -78,3 +78,55 @@ def test_first_batch_entries_are_the_smaller_workload():
         k2, v2 = wl.gen_slab(ws, b, 1, wl.gen_seqlens(ws))
         np.testing.assert_array_equal(k1, k2)
         np.testing.assert_array_equal(v1, v2)
+
+
+@pytest.mark.parametrize("P,sls", [(16, [100, 0, 37]), (64, [200, 200, 65]),
+                                   (48, [1, 144, 150])])
+def test_page_pools_hold_each_row_once_and_nan_elsewhere(P, sls):
+    torch = pytest.importorskip("torch")
+    w = wl.Workload("pages", B=3, Hq=4, Hkv=2, D=64, Lmax=200,
+                    dtype="bf16", seed=9, page_size=P)
+    sl = np.array(sls, np.int32)
+    bt = wl.gen_block_table(w)
+    assert bt.shape == (3, w.max_pages)
+    assert np.unique(bt).size == bt.size and bt.min() >= 0
+    assert bt.max() < w.num_pages and w.num_pages > bt.size
+    q, k, v, _ = wl.gen_all(w.with_(varlen=None))
+    for b in range(3):              # rows past the length are NaN bits
+        k[b, :, sl[b]:] = wl.BF16_NAN
+        v[b, :, sl[b]:] = wl.BF16_NAN
+    kp, vp = wl.scatter_pages(w, k, v, bt, sl)
+    owned = np.zeros(w.num_pages * P, bool)
+    for b in range(3):
+        for j in range(int(sl[b])):
+            r = bt[b, j // P] * P + j % P
+            np.testing.assert_array_equal(kp.reshape(-1, 2, 64)[r], k[b, :, j])
+            np.testing.assert_array_equal(vp.reshape(-1, 2, 64)[r], v[b, :, j])
+            owned[r] = True
+    assert np.all(kp.reshape(-1, 2, 64)[~owned] == wl.BF16_NAN)
+    assert np.all(vp.reshape(-1, 2, 64)[~owned] == wl.BF16_NAN)
+    # the torch scatter (used on the device for large pools) agrees
+    qd, kd, vd, btd, sld, sl2, bt2 = wl.device_paged_inputs(w, sl,
+                                                            device="cpu")
+    np.testing.assert_array_equal(bt2, bt)
+    np.testing.assert_array_equal(btd.numpy(), bt)
+    np.testing.assert_array_equal(sld.numpy(), sl)
+    np.testing.assert_array_equal(
+        kd.view(torch.int16).numpy().view(np.uint16), kp)
+    np.testing.assert_array_equal(
+        vd.view(torch.int16).numpy().view(np.uint16), vp)
+    np.testing.assert_array_equal(
+        qd.view(torch.int16).numpy().view(np.uint16), q)
+
+
+def test_multi_token_queries_extend_the_q_stream():
+    w = wl.EXTRA_WORKLOADS["mq4_b64_gqa4_h32_d128_l4096"]
+    q = wl.gen_q(w)
+    assert q.shape == (64, 4, 32, 128)
+    one = wl.gen_q(w.with_(Tq=1))
+    assert one.shape == (64, 32, 128)
+    # the first B*Hq*D draws are the single-token q
+    np.testing.assert_array_equal(q.reshape(-1)[:one.size], one.reshape(-1))
+    base = wl.WORKLOADS["b64_gqa4_h32_d128_l4096"]
+    assert wl.algorithmic_bytes(w) - wl.algorithmic_bytes(base) == \
+        3 * (2 * 64 * 32 * 128 * 2 + 4 * 64 * 32)
