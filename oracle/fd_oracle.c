@@ -29,9 +29,12 @@
  * search-result page that frameworks store the KV cache very differently,
  * and that decoding may process several new query tokens at once, as in
  * speculative decoding):
- *   paged:       K, V [num_pages][page_size][Hkv][D]; row j of sequence b
- *                lives in page block_table[b][j / page_size], token
- *                j % page_size.  Same definition over the same rows.
+ *   paged:       row j of sequence b lives in page block_table[b][j /
+ *                page_size], token j % page_size, of a page pool laid out
+ *                token-major, K, V [num_pages][page_size][Hkv][D], or
+ *                head-major, K, V [num_pages][Hkv][page_size][D] (two of
+ *                the ways frameworks store it).  Same definition over the
+ *                same rows.
  *   multi-query: q [B][Tq][Hq][D] holds the Tq newest tokens of each
  *                sequence, whose K/V are the last Tq rows of its cache;
  *                query t sees rows j < seqlens[b] - (Tq - 1 - t) (causal).
@@ -322,19 +325,24 @@ int fdo_decode_split(const void *q, const void *k, const void *v,
 }
 
 /*
- * Paged cache: K, V [num_pages][page_size][Hkv][D], block_table
- * [B][max_pages].  Row j of (b, kv-head g) starts at element
- * ((block_table[b][j / page_size] * page_size + j % page_size) * Hkv + g) * D.
+ * Paged cache, block_table [B][max_pages].  With pg = block_table[b][j /
+ * page_size] and t = j % page_size, row j of (b, kv-head g) starts at element
+ *   token-major (head_major = 0), K, V [num_pages][page_size][Hkv][D]:
+ *       ((pg * page_size + t) * Hkv + g) * D
+ *   head-major  (head_major = 1), K, V [num_pages][Hkv][page_size][D]:
+ *       ((pg * Hkv + g) * page_size + t) * D
  * seqlens is required; a length beyond max_pages * page_size is clamped, and
  * a page index outside [0, num_pages) is an error (FDO_EINVAL).
  */
 int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                      const int32_t *block_table, int max_pages, int page_size,
-                     int num_pages, const int32_t *seqlens, int B, int Hq,
-                     int Hkv, int D, double scale, int dtype, int nthreads,
-                     double *out, double *lse)
+                     int num_pages, int head_major, const int32_t *seqlens,
+                     int B, int Hq, int Hkv, int D, double scale, int dtype,
+                     int nthreads, double *out, double *lse)
 {
     if (max_pages <= 0 || page_size <= 0 || num_pages <= 0 || !seqlens)
+        return FDO_EINVAL;
+    if (head_major != 0 && head_major != 1)
         return FDO_EINVAL;
     const int Lcap = max_pages * page_size;
     int rc = check_dims(B, Hq, Hkv, D, Lcap, dtype);
@@ -371,8 +379,11 @@ int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
             for (int j = 0; j < L; ++j) {
                 size_t pg = (size_t)block_table[(size_t)b * max_pages +
                                                 j / page_size];
-                roff[j] = ((pg * page_size + (size_t)(j % page_size)) * Hkv +
-                           g) * (size_t)D;
+                size_t t = (size_t)(j % page_size);
+                if (head_major)
+                    roff[j] = ((pg * Hkv + g) * page_size + t) * (size_t)D;
+                else
+                    roff[j] = ((pg * page_size + t) * Hkv + g) * (size_t)D;
             }
             attend_row(q, ((size_t)b * Hq + h) * D, k_pages, v_pages, 0, roff,
                        L, D, scale, dtype, out + (size_t)r * D, lse + r,

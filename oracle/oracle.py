@@ -48,8 +48,8 @@ def _bind(path: str):
     lib.fdo_attend_row_split.argtypes = [vp, vp, vp, ci, ci, cd, ci, ci, ci,
                                          dp, dp, dp, dp]
     lib.fdo_attend_row_split.restype = ci
-    lib.fdo_decode_paged.argtypes = [vp, vp, vp, i32p, ci, ci, ci, i32p, ci,
-                                     ci, ci, ci, cd, ci, ci, dp, dp]
+    lib.fdo_decode_paged.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci, i32p,
+                                     ci, ci, ci, ci, cd, ci, ci, dp, dp]
     lib.fdo_decode_paged.restype = ci
     lib.fdo_decode_multiquery.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci,
                                           ci, ci, cd, ci, ci, dp, dp]
@@ -170,14 +170,19 @@ def attend_row_split(q_row, k_slab, v_slab, L: int, scale, chunk: int,
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
-                 nthreads: int = 0, _lib_override=None):
+                 head_major: bool = False, nthreads: int = 0,
+                 _lib_override=None):
     """Exact attention over a paged cache.  k_pages/v_pages
-    [num_pages, page_size, Hkv, D]; block_table int32 [B, max_pages];
-    seqlens int32 [B] (required)."""
+    [num_pages, page_size, Hkv, D] (token-major) or [num_pages, Hkv,
+    page_size, D] (head_major); block_table int32 [B, max_pages]; seqlens
+    int32 [B] (required)."""
     q, k_pages, v_pages = _c(q), _c(k_pages), _c(v_pages)
     dt = _dtype_code(q)
     B, Hq, D = q.shape
-    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if head_major:
+        num_pages, Hkv, page_size, Dk = k_pages.shape
+    else:
+        num_pages, page_size, Hkv, Dk = k_pages.shape
     assert Dk == D and v_pages.shape == k_pages.shape
     bt = _c(np.asarray(block_table, dtype=np.int32))
     assert bt.shape[0] == B
@@ -187,7 +192,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     lib = _lib_override or _load()
     rc = lib.fdo_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages),
                               _ptr(bt), bt.shape[1], page_size, num_pages,
-                              _ptr(sl), B, Hq, Hkv, D, _scale(scale), dt,
+                              int(bool(head_major)), _ptr(sl), B, Hq, Hkv, D,
+                              _scale(scale), dt,
                               int(nthreads), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"fdo_decode_paged failed with {rc}")

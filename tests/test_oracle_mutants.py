@@ -44,10 +44,14 @@ MUTANTS = [
     ("chunk_offset_in_rows", "(size_t)lo * D, NULL", "(size_t)lo, NULL"),
     ("chunk_tail_dropped", "        if (n > chunk)\n            n = chunk;",
      "        if (n > chunk || n < chunk)\n            n = chunk < n ? chunk : n - 1;"),
-    ("paged_token_index", "(size_t)(j % page_size)) * Hkv +",
-     "(size_t)(j / page_size)) * Hkv +"),
-    ("paged_head_ignored", "                           g) * (size_t)D;",
-     "                           0) * (size_t)D;"),
+    ("paged_token_index", "size_t t = (size_t)(j % page_size);",
+     "size_t t = (size_t)(j / page_size);"),
+    ("paged_head_ignored", "((pg * page_size + t) * Hkv + g)",
+     "((pg * page_size + t) * Hkv + 0)"),
+    ("paged_head_major_ignored", "if (head_major)\n                    roff",
+     "if (0)\n                    roff"),
+    ("paged_head_major_wrong_head", "((pg * Hkv + g) * page_size + t)",
+     "((pg * Hkv + (Hkv - 1 - g)) * page_size + t)"),
     ("paged_page_of_token_zero", "                                j / page_size];",
      "                                0];"),
     ("multiquery_not_causal", "- (Tq - 1 - t);", "- 0;"),
@@ -76,8 +80,9 @@ PINS = [
     (pins.test_split_batch_twin_matches_batch, ()),
     (pins.test_torch_fp64_attention_agrees, ()),
     (pins.test_mpmath_brute_force_50_digits, ()),
-    (pins.test_paged_equals_contiguous_after_scatter, (32,)),
-    (pins.test_paged_equals_contiguous_after_scatter, (64,)),
+    (pins.test_paged_equals_contiguous_after_scatter, (32, False)),
+    (pins.test_paged_equals_contiguous_after_scatter, (64, False)),
+    (pins.test_paged_equals_contiguous_after_scatter, (32, True)),
     (pins.test_multiquery_single_token_is_decode, ()),
     (pins.test_multiquery_identical_keys_closed_form, ()),
     (pins.test_multiquery_query_never_sees_later_tokens, ()),

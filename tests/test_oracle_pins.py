@@ -374,30 +374,41 @@ def test_fp32_inputs_are_used_at_full_precision(oracle_mod):
 # paged cache and multi-query decode
 
 
-def scatter_to_pages(k, v, seqlens, page_size, rng, extra_pages=3):
-    """Contiguous [B, Hkv, L, D] -> a shuffled page pool [P, page, Hkv, D]
-    (unused and spare pages filled with NaN) and its block table."""
+def scatter_to_pages(k, v, seqlens, page_size, rng, extra_pages=3,
+                     head_major=False):
+    """Contiguous [B, Hkv, L, D] -> a shuffled page pool, token-major
+    [n, page, Hkv, D] or head-major [n, Hkv, page, D] (unused and spare
+    pages filled with NaN), and its block table."""
     B, Hkv, L, D = k.shape
     maxp = -(-L // page_size)
     n = B * maxp + extra_pages
     perm = rng.permutation(n)
     nan = wl.BF16_NAN if k.dtype == np.uint16 else np.float32(np.nan)
-    kp = np.full((n, page_size, Hkv, D), nan, dtype=k.dtype)
-    vp = np.full((n, page_size, Hkv, D), nan, dtype=k.dtype)
+    shape = (n, Hkv, page_size, D) if head_major else (n, page_size, Hkv, D)
+    kp = np.full(shape, nan, dtype=k.dtype)
+    vp = np.full(shape, nan, dtype=k.dtype)
     bt = np.zeros((B, maxp), np.int32)
     for b in range(B):
         for p in range(maxp):
             pg = int(perm[b * maxp + p])
             bt[b, p] = pg
             lo, hi = p * page_size, min(L, (p + 1) * page_size, int(seqlens[b]))
-            if hi > lo:
+            if hi <= lo:
+                continue
+            if head_major:
+                kp[pg, :, :hi - lo] = k[b, :, lo:hi]
+                vp[pg, :, :hi - lo] = v[b, :, lo:hi]
+            else:
                 kp[pg, :hi - lo] = k[b, :, lo:hi].transpose(1, 0, 2)
                 vp[pg, :hi - lo] = v[b, :, lo:hi].transpose(1, 0, 2)
     return kp, vp, bt
 
 
-@pytest.mark.parametrize("page_size", [32, 64, 16])
-def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size):
+@pytest.mark.parametrize("page_size,head_major", [(32, False), (64, False),
+                                                  (16, False), (32, True),
+                                                  (48, True)])
+def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size,
+                                               head_major):
     # Same rows, same order: a shuffled page pool must give the contiguous
     # result bit for bit, with NaN in every byte the pages do not own.
     rng = np.random.default_rng(30 + page_size)
@@ -406,11 +417,19 @@ def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size):
     k = rand_bf16(rng, (B, Hkv, L, D))
     v = rand_bf16(rng, (B, Hkv, L, D))
     seq = np.array([150, 1, 97], np.int32)
-    kp, vp, bt = scatter_to_pages(k, v, seq, page_size, rng)
+    kp, vp, bt = scatter_to_pages(k, v, seq, page_size, rng,
+                                  head_major=head_major)
     o1, l1 = oracle_mod.decode(q, k, v, seq, 0.3)
-    o2, l2 = oracle_mod.decode_paged(q, kp, vp, bt, seq, 0.3)
+    o2, l2 = oracle_mod.decode_paged(q, kp, vp, bt, seq, 0.3,
+                                     head_major=head_major)
     np.testing.assert_array_equal(o2, o1)
     np.testing.assert_array_equal(l2, l1)
+    # the other layout's reading of the same bytes is a different cache
+    o3, _ = oracle_mod.decode_paged(
+        q, kp.reshape(kp.shape[0], kp.shape[2], kp.shape[1], D), vp.reshape(
+            vp.shape[0], vp.shape[2], vp.shape[1], D), bt, seq, 0.3,
+        head_major=not head_major)
+    assert not np.array_equal(np.nan_to_num(o3), o1)
 
 
 def test_multiquery_single_token_is_decode(oracle_mod):
