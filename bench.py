@@ -182,7 +182,7 @@ def main(argv=None):
     def call(kk, vv):
         if kind == "paged":
             fd.fd_decode_paged(q, kk, vv, bt, sl, w.scale, out=out, lse=lse,
-                               stream=stream)
+                               head_major=w.head_major, stream=stream)
         elif kind == "multiquery":
             fd.fd_decode_multiquery(q, kk, vv, sl, w.scale, out=out, lse=lse,
                                     stream=stream)
@@ -300,7 +300,10 @@ def main(argv=None):
         "config": {"workload": w.name, "call": "fd_decode" if kind == "decode"
                    else f"fd_decode_{kind}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "seq_len": w.Lmax, "Tq": w.Tq,
-                   "page_size": w.page_size, "kv_copies_rotated": KV_COPIES,
+                   "page_size": w.page_size,
+                   "page_layout": ("head-major" if w.head_major else
+                                   "token-major") if w.page_size else None,
+                   "kv_copies_rotated": KV_COPIES,
                    "num_splits": plan["num_splits"], "chunk": plan["chunk"],
                    "grid": plan["grid"], "waves_per_block":
                    plan["waves_per_block"], "merge_pass": bool(plan["combine"])},

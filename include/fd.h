@@ -204,25 +204,36 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
             int varlen, int num_splits, int variant, int flags, int num_cus,
             fd_plan_t *plan);
 
+/* Page-pool layouts of fd_decode_paged. */
+enum {
+    FD_PAGES_TOKEN_MAJOR = 0, /* [num_pages][page_size][Hkv][D] */
+    FD_PAGES_HEAD_MAJOR = 1   /* [num_pages][Hkv][page_size][D] */
+};
+
 /*
  * fd_decode_paged -- the same attention over a paged KV cache.  The
  * "flash decoding" search-result page (a note on decode kernels for
  * serving) observes that frameworks store the KV cache in very different
  * ways; vLLM-style paging is the common one: fixed-size pages in a shared
  * pool and a per-sequence table of page indices.
- *     k_pages, v_pages  [num_pages][page_size][Hkv][D]   (dtype)
+ *     k_pages, v_pages  pools of num_pages pages (dtype), `layout`:
+ *         FD_PAGES_TOKEN_MAJOR  [num_pages][page_size][Hkv][D]
+ *         FD_PAGES_HEAD_MAJOR   [num_pages][Hkv][page_size][D]
  *     block_table       int32 [B][max_pages], DEVICE memory
  *     seqlens           int32 [B], DEVICE memory, REQUIRED
  *     q, out, lse       as for fd_decode
  * Token j < L = clamp(seqlens[b], 0, max_pages * page_size) of sequence b,
- * KV head g, is row ((block_table[b][j / page_size] * page_size
- * + j % page_size) * Hkv + g) * D of each pool; the result is fd_decode's
- * over those rows.  Only the first ceil(L / page_size) table entries of a
- * sequence are read, and only rows below L of its last page.
- * page_size must be a multiple of 16 (FD_ERR_UNSUPPORTED otherwise),
- * max_pages * page_size and num_pages * page_size at most INT_MAX.  A
- * table entry outside [0, num_pages) is a caller error that the kernel
- * clamps into that range (never a read outside the pools).
+ * KV head g, is in page pg = block_table[b][j / page_size] at t = j %
+ * page_size: row ((pg * page_size + t) * Hkv + g) * D token-major,
+ * ((pg * Hkv + g) * page_size + t) * D head-major; the result is
+ * fd_decode's over those rows.  Head-major pages keep each head's rows of
+ * a page together and stream faster on MI355X.  Only the first
+ * ceil(L / page_size) table entries of a sequence are read, and only rows
+ * below L of its last page.  page_size must be a multiple of 16
+ * (FD_ERR_UNSUPPORTED otherwise), max_pages * page_size and num_pages *
+ * page_size * Hkv at most INT_MAX.  A table entry outside [0, num_pages)
+ * is a caller error that the kernel clamps into that range (never a read
+ * outside the pools).
  * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Hq/Hkv <= 16.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
  * tokens; FD_FLAG_FUSED_MERGE allowed).  Workspace: the library-owned one,
@@ -230,9 +241,10 @@ int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
  */
 int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     const int32_t *block_table, int max_pages, int page_size,
-                    int num_pages, const int32_t *seqlens, int B, int Hq,
-                    int Hkv, int D, float scale, fd_dtype_t dtype, void *out,
-                    float *lse, int num_splits, int flags, void *stream);
+                    int num_pages, int layout, const int32_t *seqlens, int B,
+                    int Hq, int Hkv, int D, float scale, fd_dtype_t dtype,
+                    void *out, float *lse, int num_splits, int flags,
+                    void *stream);
 
 /*
  * fd_decode_multiquery -- Tq new query tokens per sequence at once (the

@@ -30,6 +30,8 @@ FD_FLAG_PARTIALS = 2
 FD_MERGE_NONE = 0
 FD_MERGE_FUSED = 1
 FD_MERGE_SEPARATE = 2
+FD_PAGES_TOKEN_MAJOR = 0
+FD_PAGES_HEAD_MAJOR = 1
 
 # Every function the C header declares, with its ctypes signature.
 _vp, _i32p = ctypes.c_void_p, ctypes.c_void_p
@@ -55,9 +57,9 @@ SIGNATURES = {
                                  _vp]),
     "fd_merge_partials": (_ci, [_i32p, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                 _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
-    "fd_decode_paged": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _i32p,
-                              _ci, _ci, _ci, _ci, _cf, _ci, _vp, _vp, _ci,
-                              _ci, _vp]),
+    "fd_decode_paged": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
+                              _i32p, _ci, _ci, _ci, _ci, _cf, _ci, _vp, _vp,
+                              _ci, _ci, _vp]),
     "fd_decode_multiquery": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                                    _ci, _ci, _cf, _ci, _vp, _vp, _ci, _ci,
                                    _vp]),
@@ -315,19 +317,23 @@ def _out_lse(out, lse, shape, lse_shape, dtype, device):
 
 
 def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
-                    out=None, lse=None, num_splits=0, flags=0, stream=None):
+                    out=None, lse=None, num_splits=0, flags=0,
+                    head_major=False, stream=None):
     """Decode attention over a paged KV cache -- see fd.h.
 
-    q [B,Hq,D] bf16; k_pages/v_pages [num_pages,page_size,Hkv,D] bf16;
+    q [B,Hq,D] bf16; k_pages/v_pages [num_pages,page_size,Hkv,D] bf16
+    (token-major) or [num_pages,Hkv,page_size,D] (head_major);
     block_table int32 [B,max_pages]; seqlens int32 [B] (required); all on
     the GPU.  Returns (out [B,Hq,D], lse [B,Hq]).
     """
     import torch
     if q.dim() != 3 or k_pages.dim() != 4:
-        raise ValueError("expected q [B,Hq,D], k/v [num_pages,page_size,"
-                         "Hkv,D]")
+        raise ValueError("expected q [B,Hq,D], 4-d page pools")
     B, Hq, D = q.shape
-    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if head_major:
+        num_pages, Hkv, page_size, Dk = k_pages.shape
+    else:
+        num_pages, page_size, Hkv, Dk = k_pages.shape
     if Dk != D:
         raise ValueError(f"head dim mismatch q {D} vs pages {Dk}")
     _device_tensor("q", q, q.dtype)
@@ -343,6 +349,7 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     rc = load_library().fd_decode_paged(
         q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
+        FD_PAGES_HEAD_MAJOR if head_major else FD_PAGES_TOKEN_MAJOR,
         seqlens.data_ptr(), B, Hq, Hkv, D, float(scale),
         _dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
         int(num_splits), int(flags), _stream_handle(stream, q.device))

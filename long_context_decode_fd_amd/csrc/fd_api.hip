@@ -92,16 +92,20 @@ int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
 
 // Checks of the paged-cache arguments; returns the block table's capacity
 // in tokens (max_pages * page_size) through *cap.
-int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int *cap) {
+int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int Hkv,
+                int *cap) {
   if (!pk.block_table || !seqlens) return FD_ERR_INVALID_ARG;
   if (!aligned(pk.block_table, 4)) return FD_ERR_INVALID_ARG;
   if (pk.max_pages <= 0 || pk.page_size <= 0 || pk.num_pages <= 0)
     return FD_ERR_INVALID_ARG;
+  if (pk.head_major != FD_PAGES_TOKEN_MAJOR &&
+      pk.head_major != FD_PAGES_HEAD_MAJOR)
+    return FD_ERR_INVALID_ARG;
   // A 16-key half tile must lie inside one page.
   if (pk.page_size % 16 != 0) return FD_ERR_UNSUPPORTED;
-  // Token counts and pool rows are computed in int.
+  // Token counts and D-element pool rows are computed in int.
   if ((long)pk.max_pages * pk.page_size > INT_MAX ||
-      (long)pk.num_pages * pk.page_size > INT_MAX)
+      (long)pk.num_pages * pk.page_size * (Hkv > 0 ? Hkv : 1) > INT_MAX)
     return FD_ERR_UNSUPPORTED;
   *cap = pk.max_pages * pk.page_size;
   return FD_OK;
@@ -116,7 +120,7 @@ int run(const void *q, const void *k_cache, const void *v_cache,
         float scale, fd_dtype_t dtype, void *out, float *lse, int num_splits,
         int variant, int flags, void *workspace, size_t workspace_bytes,
         void *stream, int phases, fd::Extra ex = fd::Extra(),
-        fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0}) {
+        fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0, 0}) {
   const bool chunks = phases & fd::kPhaseChunks;
   const bool merge = phases & fd::kPhaseMerge;
   if (chunks) {
@@ -234,12 +238,13 @@ int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
 
 int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     const int32_t *block_table, int max_pages, int page_size,
-                    int num_pages, const int32_t *seqlens, int B, int Hq,
-                    int Hkv, int D, float scale, fd_dtype_t dtype, void *out,
-                    float *lse, int num_splits, int flags, void *stream) {
-  const fd::PagedKV pk{block_table, max_pages, page_size, num_pages};
+                    int num_pages, int layout, const int32_t *seqlens, int B,
+                    int Hq, int Hkv, int D, float scale, fd_dtype_t dtype,
+                    void *out, float *lse, int num_splits, int flags,
+                    void *stream) {
+  const fd::PagedKV pk{block_table, max_pages, page_size, num_pages, layout};
   int cap = 0;
-  const int rc = check_paged(pk, seqlens, &cap);
+  const int rc = check_paged(pk, seqlens, Hkv, &cap);
   if (rc != FD_OK) return rc;
   fd::Extra ex;
   ex.paged = true;

@@ -55,11 +55,13 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout workspace_layout(const Plan &p);
 
-// Paged K/V: pool [num_pages][page_size][Hkv][D] per tensor; token j of
-// sequence b sits in page block_table[b][j / page_size], row j % page_size.
+// Paged K/V: token j of sequence b sits in page block_table[b][j /
+// page_size], at t = j % page_size; pools [num_pages][page_size][Hkv][D]
+// (token-major) or [num_pages][Hkv][page_size][D] (head_major).
 struct PagedKV {
   const int32_t *block_table;
   int max_pages, page_size, num_pages;
+  int head_major;
 };
 
 // Kernel launches (fd_kernels.hip).  Return hipError_t as int.

@@ -468,12 +468,13 @@ __device__ __forceinline__ uint32_t dword_of<4>(const uint2 &v, int i) {
 
 // Where the key rows of a tile live.  Contiguous cache: row r of the tile
 // starting at key k0 is k[(k0 + r) * D].  Paged cache: the tile's two
-// 16-key halves each lie inside one page, at h0 / h1, rows rs = Hkv * D
-// elements apart.
+// 16-key halves each lie inside one page, at h0 / h1, rows rs elements
+// apart (Hkv * D token-major, D head-major).
 template <int D, bool PAGED>
 struct TileRows;
 template <int D>
 struct TileRows<D, false> {
+  static constexpr bool kPaged = false;
   const uint16_t *k, *v;  // slab (b, g)
   int k0;
   __device__ const uint16_t *krow(int r) const {
@@ -485,6 +486,7 @@ struct TileRows<D, false> {
 };
 template <int D>
 struct TileRows<D, true> {
+  static constexpr bool kPaged = true;
   const uint16_t *k0h, *k1h, *v0h, *v1h;
   size_t rs;
   __device__ const uint16_t *krow(int r) const {
@@ -577,6 +579,10 @@ __device__ __forceinline__ void mfma_tile(
     for (int i = 0; i < 8; ++i)
       if ((i >> 2) * 16 + q4 * 4 + (i & 3) >= valid) vr[i] = VT{};
   }
+  // Paged tiles: left alone, the scheduler hoists the V regrouping (which
+  // waits for every V load) above the softmax; keeping it here lets the
+  // exponentials overlap the V loads, as the contiguous loop does by itself.
+  if constexpr (Rows::kPaged) __builtin_amdgcn_sched_barrier(0);
   bf16x8 vt[VW];
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
@@ -602,13 +608,15 @@ __device__ __forceinline__ void mfma_tile(
                                                      0, 0);
 }
 
-// Paged cache: the pool row (page * page_size + offset in page) of the
-// first key of each 16-key half of this wavefront's tiles it0 .. it0 + 31
-// (lane 2 j + h: half h of tile it0 + j).  Halves at or beyond the chunk
-// end read nothing and give row 0; page indices are clamped into the pool,
-// so no entry of the table can make a load leave the K/V buffers.
+// Paged cache: for the first key of each 16-key half of this wavefront's
+// tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
+// of its D-element row of KV head g in the pool: (page * page_size + t) *
+// Hkv + g token-major, (page * Hkv + g) * page_size + t head-major, with t
+// the key's place in its page.  Halves at or beyond the chunk end read
+// nothing and give 0; page indices are clamped into the pool, so no entry
+// of the table can make a load leave the K/V buffers.
 __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
-                                         int wave, int nw, int it0,
+                                         int Hkv, int wave, int nw, int it0,
                                          int lane) {
   const int t = wave + (it0 + (lane >> 1)) * nw;
   const int key = w.lo + t * kKeyTile + (lane & 1) * 16;
@@ -616,7 +624,9 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
   const int j = key / pk.page_size;
   int pg = pk.block_table[(size_t)w.b * pk.max_pages + j];
   pg = min(max(pg, 0), pk.num_pages - 1);
-  return pg * pk.page_size + (key - j * pk.page_size);
+  const int off = key - j * pk.page_size;
+  return pk.head_major ? (pg * Hkv + w.g) * pk.page_size + off
+                       : (pg * pk.page_size + off) * Hkv + w.g;
 }
 
 // PAGED: K/V in a page pool behind a block table.  CAUSAL: Tq > 1 new
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
   const int hi_all = min(w.hi, w.L - (Tq - 1));
 
   const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
-  const size_t head = (size_t)w.g * D;
+  const size_t prs = pk.head_major ? (size_t)D : (size_t)Hkv * D;
 
   floatx4 acc[VW];
 #pragma unroll
@@ -676,14 +686,14 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
     TileRows<D, PAGED> rows;
     if constexpr (PAGED) {
       const int slot = it & 31;
-      if (slot == 0) prow = page_rows(pk, w, wave, NW, it, lane);
+      if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
       const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
       const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
-      rows.rs = (size_t)Hkv * D;
-      rows.k0h = kc + (size_t)r0 * rows.rs + head;
-      rows.k1h = kc + (size_t)r1 * rows.rs + head;
-      rows.v0h = vc + (size_t)r0 * rows.rs + head;
-      rows.v1h = vc + (size_t)r1 * rows.rs + head;
+      rows.rs = prs;
+      rows.k0h = kc + (size_t)r0 * D;
+      rows.k1h = kc + (size_t)r1 * D;
+      rows.v0h = vc + (size_t)r0 * D;
+      rows.v1h = vc + (size_t)r1 * D;
     } else {
       rows.k = kc + slab;
       rows.v = vc + slab;

@@ -57,6 +57,7 @@ class Workload:
     varlen: tuple | None = None   # (lo, hi) for log-uniform seqlens
     Tq: int = 1                   # new query tokens per sequence
     page_size: int = 0            # > 0: K/V in a paged pool
+    head_major: bool = False      # pages [Hkv][t][D], else [t][Hkv][D]
     note: str = field(default="", compare=False)
 
     @property
@@ -122,6 +123,10 @@ EXTRA_WORKLOADS = {
         WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
             name="paged_p64_b1_gqa8_h64_d128_l65536", page_size=64,
             note="batch-1 64k decode from 64-token pages"),
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="paged_hm_p64_b1_gqa8_h64_d128_l65536", page_size=64,
+            head_major=True,
+            note="batch-1 64k decode from 64-token head-major pages"),
         WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
             name="paged_p16_varlen_b16_gqa8_h64_d128_lmax131072",
             page_size=16,
@@ -199,10 +204,12 @@ def gen_block_table(w: Workload) -> np.ndarray:
 
 def scatter_pages(w: Workload, k: np.ndarray, v: np.ndarray,
                   block_table: np.ndarray, seqlens):
-    """Host pools [num_pages, page_size, Hkv, D] holding rows [0, L_b) of
-    the contiguous k/v [B, Hkv, Lmax, D]; every other row is NaN."""
+    """Host pools [num_pages, page_size, Hkv, D] ([num_pages, Hkv,
+    page_size, D] when head_major) holding rows [0, L_b) of the contiguous
+    k/v [B, Hkv, Lmax, D]; every other row is NaN."""
     P = w.page_size
-    shape = (w.num_pages, P, w.Hkv, w.D)
+    shape = ((w.num_pages, w.Hkv, P, w.D) if w.head_major
+             else (w.num_pages, P, w.Hkv, w.D))
     kp = np.empty(shape, w.np_dtype)
     vp = np.empty(shape, w.np_dtype)
     kp.view(np.uint8)[:] = 0xFF
@@ -212,8 +219,12 @@ def scatter_pages(w: Workload, k: np.ndarray, v: np.ndarray,
         for j in range(-(-L // P)):
             n = min(P, L - j * P)
             pg = block_table[b, j]
-            kp[pg, :n] = k[b, :, j * P:j * P + n].transpose(1, 0, 2)
-            vp[pg, :n] = v[b, :, j * P:j * P + n].transpose(1, 0, 2)
+            if w.head_major:
+                kp[pg, :, :n] = k[b, :, j * P:j * P + n]
+                vp[pg, :, :n] = v[b, :, j * P:j * P + n]
+            else:
+                kp[pg, :n] = k[b, :, j * P:j * P + n].transpose(1, 0, 2)
+                vp[pg, :n] = v[b, :, j * P:j * P + n].transpose(1, 0, 2)
     return kp, vp
 
 
@@ -339,18 +350,21 @@ def device_paged_inputs(w: Workload, seqlens=None, device: str = "cuda"):
     iv = torch.int16 if w.dtype == "bf16" else torch.int32
     pools = []
     for src in (k, v):
-        pool = torch.empty((w.num_pages, P, w.Hkv, w.D), dtype=src.dtype,
-                           device=device)
+        shape = ((w.num_pages, w.Hkv, P, w.D) if w.head_major
+                 else (w.num_pages, P, w.Hkv, w.D))
+        pool = torch.empty(shape, dtype=src.dtype, device=device)
         pool.view(iv).fill_(-1)
         pad = mp * P - w.Lmax
         if pad:
             src = torch.nn.functional.pad(src.view(iv), (0, 0, 0, pad),
                                           value=-1).view(src.dtype)
-        # [B, Hkv, mp, P, D] -> [B * mp, P, Hkv, D], page j of sequence b
-        pages = src.view(w.B, w.Hkv, mp, P, w.D).permute(0, 2, 3, 1, 4)
+        # [B, Hkv, mp, P, D] -> [B * mp, P, Hkv, D] (or [B * mp, Hkv, P,
+        # D]), page j of sequence b
+        pages = src.view(w.B, w.Hkv, mp, P, w.D).permute(
+            (0, 2, 1, 3, 4) if w.head_major else (0, 2, 3, 1, 4))
         idx = torch.from_numpy(bt.reshape(-1).astype(np.int64)).to(device)
         pool.view(iv).index_copy_(0, idx, pages.reshape(
-            w.B * mp, P, w.Hkv, w.D).view(iv))
+            (w.B * mp,) + shape[1:]).view(iv))
         pools.append(pool)
     del k, v
     bt_dev = torch.from_numpy(bt).to(device)

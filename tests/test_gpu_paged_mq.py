@@ -85,45 +85,53 @@ PAGED_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("hm", [False, True], ids=["token_major",
+                                                   "head_major"])
 @pytest.mark.parametrize("shape", PAGED_SHAPES,
                          ids=[f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_D{s[3]}_L{s[4]}"
                               f"_P{s[5]}" for s in PAGED_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (5, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags):
+def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm):
     B, Hq, Hkv, D, L, P, sls = shape
     w = wl.Workload("paged_case", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=L,
-                    dtype="bf16", seed=40 + P, page_size=P)
+                    dtype="bf16", seed=40 + P, page_size=P, head_major=hm)
     seqlens = np.array(sls, np.int32)
     (q, kp, vp, bt, sl), (qd, kd, vd, btd, sld) = paged_case(torch, w,
                                                              seqlens)
-    _note(f"{shape} splits={splits} flags={flags} pages={w.num_pages}")
+    _note(f"{shape} hm={hm} splits={splits} flags={flags} "
+          f"pages={w.num_pages}")
     out, lse = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale,
-                                  num_splits=splits, flags=flags)
+                                  num_splits=splits, flags=flags,
+                                  head_major=hm)
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle_mod.decode_paged(q, kp, vp, bt, sl, w.scale)
-    _assert_parity(out, lse, ref_o, ref_l, f"paged {shape}")
+    ref_o, ref_l = oracle_mod.decode_paged(q, kp, vp, bt, sl, w.scale,
+                                           head_major=hm)
+    _assert_parity(out, lse, ref_o, ref_l, f"paged {shape} hm={hm}")
 
 
-def test_paged_table_entries_past_the_length_are_not_read(torch):
+@pytest.mark.parametrize("hm", [False, True])
+def test_paged_table_entries_past_the_length_are_not_read(torch, hm):
     w = wl.Workload("paged_tail", B=3, Hq=16, Hkv=2, D=128, Lmax=1024,
-                    dtype="bf16", seed=47, page_size=64)
+                    dtype="bf16", seed=47, page_size=64, head_major=hm)
     seqlens = np.array([1024, 300, 0], np.int32)
     _, (qd, kd, vd, btd, sld) = paged_case(torch, w, seqlens)
     _, (_, _, _, btd2, _) = paged_case(torch, w, seqlens,
                                        table_fill=w.num_pages + 12345)
     _note("table entries past the length: out of range values")
-    o1, l1 = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale)
-    o2, l2 = fd.fd_decode_paged(qd, kd, vd, btd2, sld, w.scale)
+    o1, l1 = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale, head_major=hm)
+    o2, l2 = fd.fd_decode_paged(qd, kd, vd, btd2, sld, w.scale,
+                                head_major=hm)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
 
 
-def test_paged_equals_contiguous_bitwise(torch):
+@pytest.mark.parametrize("hm", [False, True])
+def test_paged_equals_contiguous_bitwise(torch, hm):
     # Same lengths, so the same plan; the pool holds the same rows.
     w = wl.Workload("paged_vs_contig", B=4, Hq=32, Hkv=4, D=128, Lmax=3072,
-                    dtype="bf16", seed=48, page_size=32)
+                    dtype="bf16", seed=48, page_size=32, head_major=hm)
     seqlens = np.array([3072, 2048, 777, 5], np.int32)
     (q, k_unused, _, _, _), (qd, kd, vd, btd, sld) = paged_case(
         torch, w, seqlens)
@@ -131,7 +139,7 @@ def test_paged_equals_contiguous_bitwise(torch):
     kc, vc = to_dev(k), to_dev(v)
     for splits in (0, 3):
         po, pl = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale,
-                                    num_splits=splits)
+                                    num_splits=splits, head_major=hm)
         co, cl = fd.fd_decode_ex(qd, kc, vc, sld, w.scale,
                                  num_splits=splits)
         torch.cuda.synchronize()
@@ -139,14 +147,17 @@ def test_paged_equals_contiguous_bitwise(torch):
         assert torch.equal(pl, cl)
 
 
-def test_paged_full_size_64k(torch, oracle_mod):
+@pytest.mark.parametrize("name", ["paged_p64_b1_gqa8_h64_d128_l65536",
+                                  "paged_hm_p64_b1_gqa8_h64_d128_l65536"])
+def test_paged_full_size_64k(torch, oracle_mod, name):
     """The 64k batch-1 shape from 64-token pages, in the benchmark's launch
     configuration: bit-identical to the contiguous call, sampled rows
     against the oracle."""
-    w = wl.EXTRA_WORKLOADS["paged_p64_b1_gqa8_h64_d128_l65536"]
+    w = wl.EXTRA_WORKLOADS[name]
     _note(f"{w.name}: generating")
     q, kp, vp, btd, sld, seqlens, bt = wl.device_paged_inputs(w)
-    out, lse = fd.fd_decode_paged(q, kp, vp, btd, sld, w.scale)
+    out, lse = fd.fd_decode_paged(q, kp, vp, btd, sld, w.scale,
+                                  head_major=w.head_major)
     torch.cuda.synchronize()
     del kp, vp
     _, k, v, _, _, _ = wl.device_inputs(w.with_(page_size=0),

@@ -80,12 +80,13 @@ def test_first_batch_entries_are_the_smaller_workload():
         np.testing.assert_array_equal(v1, v2)
 
 
+@pytest.mark.parametrize("hm", [False, True])
 @pytest.mark.parametrize("P,sls", [(16, [100, 0, 37]), (64, [200, 200, 65]),
                                    (48, [1, 144, 150])])
-def test_page_pools_hold_each_row_once_and_nan_elsewhere(P, sls):
+def test_page_pools_hold_each_row_once_and_nan_elsewhere(P, sls, hm):
     torch = pytest.importorskip("torch")
     w = wl.Workload("pages", B=3, Hq=4, Hkv=2, D=64, Lmax=200,
-                    dtype="bf16", seed=9, page_size=P)
+                    dtype="bf16", seed=9, page_size=P, head_major=hm)
     sl = np.array(sls, np.int32)
     bt = wl.gen_block_table(w)
     assert bt.shape == (3, w.max_pages)
@@ -96,15 +97,19 @@ def test_page_pools_hold_each_row_once_and_nan_elsewhere(P, sls):
         k[b, :, sl[b]:] = wl.BF16_NAN
         v[b, :, sl[b]:] = wl.BF16_NAN
     kp, vp = wl.scatter_pages(w, k, v, bt, sl)
-    owned = np.zeros(w.num_pages * P, bool)
+    owned = np.zeros(w.num_pages * P * 2, bool)
     for b in range(3):
         for j in range(int(sl[b])):
-            r = bt[b, j // P] * P + j % P
-            np.testing.assert_array_equal(kp.reshape(-1, 2, 64)[r], k[b, :, j])
-            np.testing.assert_array_equal(vp.reshape(-1, 2, 64)[r], v[b, :, j])
-            owned[r] = True
-    assert np.all(kp.reshape(-1, 2, 64)[~owned] == wl.BF16_NAN)
-    assert np.all(vp.reshape(-1, 2, 64)[~owned] == wl.BF16_NAN)
+            pg, t = bt[b, j // P], j % P
+            for g in range(2):
+                r = (pg * 2 + g) * P + t if hm else (pg * P + t) * 2 + g
+                np.testing.assert_array_equal(kp.reshape(-1, 64)[r],
+                                              k[b, g, j])
+                np.testing.assert_array_equal(vp.reshape(-1, 64)[r],
+                                              v[b, g, j])
+                owned[r] = True
+    assert np.all(kp.reshape(-1, 64)[~owned] == wl.BF16_NAN)
+    assert np.all(vp.reshape(-1, 64)[~owned] == wl.BF16_NAN)
     # the torch scatter (used on the device for large pools) agrees
     qd, kd, vd, btd, sld, sl2, bt2 = wl.device_paged_inputs(w, sl,
                                                             device="cpu")
