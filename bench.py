@@ -145,6 +145,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=None,
                     help="another workload of long_context_decode_fd_amd."
                          "workloads (default: the batch-1 64k one)")
+    ap.add_argument("--unified-max", type=float, default=None, metavar="PHI",
+                    help="time fd_decode_unified_max with this phi instead "
+                         "of fd_decode (contiguous single-token workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -161,7 +164,8 @@ def main(argv=None):
 
     w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
     kind = ("paged" if w.page_size else
-            "multiquery" if w.Tq > 1 else "decode")
+            "multiquery" if w.Tq > 1 else
+            "unified_max" if a.unified_max is not None else "decode")
     torch.cuda.set_device(0)
     fd.load_library()
     log(f"[bench] workload {w.name} ({kind}): generating inputs")
@@ -173,7 +177,9 @@ def main(argv=None):
     else:
         q, k, v, sl, seqlens, _ = wl.device_inputs(w)
         plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
-                             varlen=sl is not None)
+                             varlen=sl is not None,
+                             flags=fd.FD_FLAG_UNIFIED_MAX
+                             if kind == "unified_max" else 0)
     ks = [k] + [k.clone() for _ in range(KV_COPIES - 1)]
     vs = [v] + [v.clone() for _ in range(KV_COPIES - 1)]
     out = torch.empty_like(q)
@@ -186,6 +192,9 @@ def main(argv=None):
         elif kind == "multiquery":
             fd.fd_decode_multiquery(q, kk, vv, sl, w.scale, out=out, lse=lse,
                                     stream=stream)
+        elif kind == "unified_max":
+            fd.fd_decode_unified_max(q, kk, vv, sl, w.scale, a.unified_max,
+                                     out=out, lse=lse, stream=stream)
         else:
             fd.fd_decode(q, kk, vv, sl, w.scale, out=out, lse=lse,
                          stream=stream)
@@ -254,7 +263,8 @@ def main(argv=None):
     nbytes = wl.algorithmic_bytes(w, seqlens)
     gbs = nbytes / (ms * 1e-3) / 1e9
     split_kernel = (f"split_mfma_kernel<{w.D}, {plan['waves_per_block']}, "
-                    f"{'paged' if kind == 'paged' else 'contiguous'}>"
+                    f"{'paged' if kind == 'paged' else 'contiguous'}"
+                    f"{', unified max' if kind == 'unified_max' else ''}>"
                     if plan["variant"] == fd.FD_VARIANT_MFMA else
                     f"split_valu_kernel<{w.dtype}, {w.D}>")
     if kern_avg_ms is not None:
@@ -300,7 +310,7 @@ def main(argv=None):
         "config": {"workload": w.name, "call": "fd_decode" if kind == "decode"
                    else f"fd_decode_{kind}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "seq_len": w.Lmax, "Tq": w.Tq,
-                   "page_size": w.page_size,
+                   "page_size": w.page_size, "unified_max_phi": a.unified_max,
                    "page_layout": ("head-major" if w.head_major else
                                    "token-major") if w.page_size else None,
                    "kv_copies_rotated": KV_COPIES,

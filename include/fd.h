@@ -91,7 +91,10 @@ enum {
     FD_FLAG_FUSED_MERGE = 1,
     /* Always leave per-chunk partials, even when one chunk per sequence
        would do (the plan fd_decode_partials / fd_merge_partials use). */
-    FD_FLAG_PARTIALS = 2
+    FD_FLAG_PARTIALS = 2,
+    /* Unified-maximum softmax (fd_decode_unified_max sets it; fd_plan and
+       fd_plan_ex accept it; other calls reject it). */
+    FD_FLAG_UNIFIED_MAX = 4
 };
 
 /* How the chunks of a split plan are merged (fd_plan_t.merge). */
@@ -268,6 +271,32 @@ int fd_decode_multiquery(const void *q, const void *k_cache,
                          int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
                          fd_dtype_t dtype, void *out, float *lse,
                          int num_splits, int flags, void *stream);
+
+/*
+ * fd_decode_unified_max -- fd_decode_ex computed with FlashDecoding++'s
+ * asynchronised softmax ("FlashDecoding++: Faster Large Language Model
+ * Inference on GPUs", summarised on the "flash decoding" search-result
+ * page, which names the cost it removes: partial softmax results that
+ * must be synchronised with each other).  Each chunk takes its
+ * exponentials against one fixed estimate phi of the row maximum instead
+ * of a running maximum, so tiles need no cross-lane maximum and no
+ * rescaling of their sums.  phi is in the units of lse (natural log of
+ * the scaled score), chosen by the caller from the model's score range
+ * (0 suits unit-variance scores).  Fallback: when some row of a chunk
+ * has scores beyond phi +- 64 ln 2 (where 2^x would lose range), that
+ * chunk is recomputed with the running maximum, giving exactly the
+ * fd_decode_ex result for it; either way the result is the same
+ * attention within the usual rounding.  Contiguous cache, one token per
+ * sequence, bf16 only (FD_ERR_UNSUPPORTED otherwise).  phi must be finite.
+ * num_splits, flags (FD_FLAG_FUSED_MERGE), workspace: as for
+ * fd_decode_ex; plan with FD_FLAG_UNIFIED_MAX for the workspace size.
+ */
+int fd_decode_unified_max(const void *q, const void *k_cache,
+                          const void *v_cache, const int32_t *seqlens, int B,
+                          int Hq, int Hkv, int D, int Lmax, float scale,
+                          fd_dtype_t dtype, void *out, float *lse, float phi,
+                          int num_splits, int flags, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * fd_plan_ex -- fd_plan for the calls above: Tq query tokens per sequence

@@ -9,13 +9,15 @@ seeded synthetic workloads used by the tests and the benchmark.
 """
 from ._binding import (FD_BF16, FD_ERR_HIP, FD_ERR_INVALID_ARG,  # noqa: F401
                        FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32,
-                       FD_FLAG_FUSED_MERGE, FD_FLAG_PARTIALS, FD_MERGE_FUSED,
+                       FD_FLAG_FUSED_MERGE, FD_FLAG_PARTIALS,
+                       FD_FLAG_UNIFIED_MAX, FD_MERGE_FUSED,
                        FD_MERGE_NONE,
                        FD_MERGE_SEPARATE, FD_OK, FD_PAGES_HEAD_MAJOR,
                        FD_PAGES_TOKEN_MAJOR,
                        FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
                        LIB_PATH, FdError, fd_decode, fd_decode_ex,
                        fd_decode_multiquery, fd_decode_paged,
+                       fd_decode_unified_max,
                        fd_decode_partials, fd_merge_partials, fd_plan,
                        fd_plan_ex, fd_status_string, fd_version,
                        fd_workspace_bytes, load_library)

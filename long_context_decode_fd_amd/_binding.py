@@ -27,6 +27,7 @@ FD_VARIANT_MFMA = 1
 FD_VARIANT_VALU = 2
 FD_FLAG_FUSED_MERGE = 1
 FD_FLAG_PARTIALS = 2
+FD_FLAG_UNIFIED_MAX = 4
 FD_MERGE_NONE = 0
 FD_MERGE_FUSED = 1
 FD_MERGE_SEPARATE = 2
@@ -63,6 +64,9 @@ SIGNATURES = {
     "fd_decode_multiquery": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                                    _ci, _ci, _cf, _ci, _vp, _vp, _ci, _ci,
                                    _vp]),
+    "fd_decode_unified_max": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci,
+                                    _ci, _ci, _cf, _ci, _vp, _vp, _cf, _ci,
+                                    _ci, _vp, _sz, _vp]),
     "fd_plan": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                       ctypes.POINTER(FdPlanStruct)]),
     "fd_plan_ex": (_ci, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
@@ -227,6 +231,30 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
         int(flags), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
     if rc != FD_OK:
         raise FdError("fd_decode_ex", rc)
+    return out, lse
+
+
+def fd_decode_unified_max(q, k_cache, v_cache, seqlens, scale, phi,
+                          out=None, lse=None, num_splits=0, flags=0,
+                          workspace=None, stream=None):
+    """fd_decode_ex with the unified-maximum softmax against phi (natural
+    log units of the scaled score) -- see fd.h."""
+    dims, out, lse = _check(q, k_cache, v_cache, seqlens, out, lse)
+    B, Hq, Hkv, D, Lmax = dims
+    if not math.isfinite(float(scale)) or not math.isfinite(float(phi)):
+        raise ValueError("scale and phi must be finite")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
+            workspace.element_size()
+    rc = load_library().fd_decode_unified_max(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(),
+        B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
+        out.data_ptr(), lse.data_ptr(), float(phi), int(num_splits),
+        int(flags), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    if rc != FD_OK:
+        raise FdError("fd_decode_unified_max", rc)
     return out, lse
 
 

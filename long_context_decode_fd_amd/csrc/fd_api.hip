@@ -120,7 +120,8 @@ int run(const void *q, const void *k_cache, const void *v_cache,
         float scale, fd_dtype_t dtype, void *out, float *lse, int num_splits,
         int variant, int flags, void *workspace, size_t workspace_bytes,
         void *stream, int phases, fd::Extra ex = fd::Extra(),
-        fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0, 0}) {
+        fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0, 0},
+        float unified_max = 0.f) {
   const bool chunks = phases & fd::kPhaseChunks;
   const bool merge = phases & fd::kPhaseMerge;
   if (chunks) {
@@ -137,8 +138,9 @@ int run(const void *q, const void *k_cache, const void *v_cache,
   int rc = fd::validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
   if (num_splits < 0 || variant < FD_VARIANT_AUTO ||
-      variant > FD_VARIANT_VALU ||
-      (flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_PARTIALS)))
+      variant > FD_VARIANT_VALU || (flags & ~fd::kKnownFlags))
+    return FD_ERR_INVALID_ARG;
+  if ((flags & FD_FLAG_UNIFIED_MAX) && !std::isfinite(unified_max))
     return FD_ERR_INVALID_ARG;
   if (workspace == nullptr && workspace_bytes != 0) return FD_ERR_INVALID_ARG;
   if (workspace && !aligned(workspace, 256)) return FD_ERR_INVALID_ARG;
@@ -170,6 +172,7 @@ int run(const void *q, const void *k_cache, const void *v_cache,
   a.out = out;
   a.lse = lse;
   a.scale = scale;
+  a.unified_max = unified_max;
   a.stream = stream;
   a.phases = phases;
   if (p.combine) {
@@ -200,6 +203,7 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int Lmax, float scale, fd_dtype_t dtype, void *out,
                  float *lse, int num_splits, int variant, int flags,
                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (flags & FD_FLAG_UNIFIED_MAX) return FD_ERR_INVALID_ARG;  // needs phi
   return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
              out, lse, num_splits, variant, flags, workspace, workspace_bytes,
              stream, fd::kPhaseChunks | fd::kPhaseMerge);
@@ -220,6 +224,7 @@ int fd_decode_partials(const void *q, const void *k_cache,
                        fd_dtype_t dtype, int num_splits, int variant,
                        int flags, void *workspace, size_t workspace_bytes,
                        void *stream) {
+  if (flags & FD_FLAG_UNIFIED_MAX) return FD_ERR_INVALID_ARG;
   return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
              nullptr, nullptr, num_splits, variant, flags | FD_FLAG_PARTIALS,
              workspace, workspace_bytes, stream, fd::kPhaseChunks);
@@ -230,6 +235,7 @@ int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
                       int flags, const void *workspace,
                       size_t workspace_bytes, void *out, float *lse,
                       void *stream) {
+  if (flags & FD_FLAG_UNIFIED_MAX) return FD_ERR_INVALID_ARG;
   return run(nullptr, nullptr, nullptr, seqlens, B, Hq, Hkv, D, Lmax, 0.f,
              dtype, out, lse, num_splits, variant, flags | FD_FLAG_PARTIALS,
              const_cast<void *>(workspace), workspace_bytes, stream,
@@ -242,6 +248,7 @@ int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int Hq, int Hkv, int D, float scale, fd_dtype_t dtype,
                     void *out, float *lse, int num_splits, int flags,
                     void *stream) {
+  if (flags & FD_FLAG_UNIFIED_MAX) return FD_ERR_INVALID_ARG;
   const fd::PagedKV pk{block_table, max_pages, page_size, num_pages, layout};
   int cap = 0;
   const int rc = check_paged(pk, seqlens, Hkv, &cap);
@@ -258,13 +265,26 @@ int fd_decode_multiquery(const void *q, const void *k_cache,
                          int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
                          fd_dtype_t dtype, void *out, float *lse,
                          int num_splits, int flags, void *stream) {
-  if (Tq <= 0) return FD_ERR_INVALID_ARG;
+  if (Tq <= 0 || (flags & FD_FLAG_UNIFIED_MAX)) return FD_ERR_INVALID_ARG;
   if (dtype != FD_BF16) return FD_ERR_UNSUPPORTED;  // also for Tq == 1
   fd::Extra ex;
   ex.Tq = Tq;
   return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
              out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
              fd::kPhaseChunks | fd::kPhaseMerge, ex);
+}
+
+int fd_decode_unified_max(const void *q, const void *k_cache,
+                          const void *v_cache, const int32_t *seqlens, int B,
+                          int Hq, int Hkv, int D, int Lmax, float scale,
+                          fd_dtype_t dtype, void *out, float *lse, float phi,
+                          int num_splits, int flags, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
+             out, lse, num_splits, FD_VARIANT_AUTO,
+             flags | FD_FLAG_UNIFIED_MAX, workspace, workspace_bytes, stream,
+             fd::kPhaseChunks | fd::kPhaseMerge, fd::Extra(),
+             fd::PagedKV{nullptr, 0, 0, 0, 0}, phi);
 }
 
 int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,

@@ -22,6 +22,7 @@ struct Plan {
   fd_dtype_t dtype;
   bool varlen;
   bool paged;
+  bool unified;     // unified-maximum softmax (FD_FLAG_UNIFIED_MAX)
   int num_cus;
   int variant;      // FD_VARIANT_MFMA or FD_VARIANT_VALU
   int waves;        // wavefronts per workgroup of the per-chunk pass
@@ -41,6 +42,10 @@ struct Extra {
   int Tq = 1;          // query tokens per sequence
   bool paged = false;  // K/V in pages behind a block table
 };
+
+// Flags the planner accepts (the public ones of fd.h).
+constexpr int kKnownFlags =
+    FD_FLAG_FUSED_MERGE | FD_FLAG_PARTIALS | FD_FLAG_UNIFIED_MAX;
 
 // Fills *p for a validated shape; requested_splits 0 = heuristic.
 int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
@@ -75,6 +80,7 @@ struct LaunchArgs {
   float *lse_part;
   int *tickets;
   float scale;
+  float unified_max;  // phi (natural-log units of the scaled score)
   void *stream;
   int phases;  // kPhaseChunks | kPhaseMerge
 };

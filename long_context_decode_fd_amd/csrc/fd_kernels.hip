@@ -501,11 +501,17 @@ struct TileRows<D, true> {
 // `valid` rows (others re-read the last valid one and the V rows are
 // zeroed) and give keys at or beyond the lane's `lim` a score of -inf;
 // full tiles need neither.
-template <int D, bool TAIL, typename Rows>
+//
+// UNI (unified maximum): the exponentials are taken against the fixed
+// phi2 instead of the column's running maximum, so there is no
+// cross-lane maximum, no rescale of l and acc, and m only records the
+// lane's largest x = score - phi2 for the range check that follows the
+// chunk.
+template <int D, bool TAIL, bool UNI, typename Rows>
 __device__ __forceinline__ void mfma_tile(
     const Rows &rows, int valid, int lim, int n16, int q4,
-    const bf16x8 (&qop)[D / 32], float scale_log2, floatx4 (&acc)[D / 16],
-    float &m, float &l) {
+    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
+    floatx4 (&acc)[D / 16], float &m, float &l) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   typedef typename VecOf<VW>::type VT;
@@ -544,18 +550,23 @@ __device__ __forceinline__ void mfma_tile(
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float x = sc[sub][j] * scale_log2;
+      float x = UNI ? sc[sub][j] * scale_log2 - phi2 : sc[sub][j] * scale_log2;
       if (TAIL && sub * 16 + q4 * 4 + j >= lim) x = FD_NEG_INF;
       s[sub * 4 + j] = x;
     }
   float mt = s[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mt = fmaxf(mt, s[i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float mn = fmaxf(m, mt);
-  const float mref = mn == FD_NEG_INF ? 0.f : mn;
-  const float alpha = exp2_f(m - mref);
+  float mref = 0.f, alpha = 1.f, mn;
+  if (UNI) {
+    mn = fmaxf(m, mt);
+  } else {
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mn = fmaxf(m, mt);
+    mref = mn == FD_NEG_INF ? 0.f : mn;
+    alpha = exp2_f(m - mref);
+  }
 
   // P enters the matrix cores as an exact-to-2^-17 pair of bf16 operands
   // (hi = bf16(p), lo = bf16(p - hi)); the running sum uses fp32 p.
@@ -569,20 +580,25 @@ __device__ __forceinline__ void mfma_tile(
     p_lo[i] = (__bf16)(p - (float)hi);
     psum += p;
   }
-  l = l * alpha + psum;
   m = mn;
+  if (UNI) {
+    l += psum;
+  } else {
+    l = l * alpha + psum;
 #pragma unroll
-  for (int e = 0; e < VW; ++e) acc[e] *= alpha;
+    for (int e = 0; e < VW; ++e) acc[e] *= alpha;
+  }
 
   if (TAIL) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if ((i >> 2) * 16 + q4 * 4 + (i & 3) >= valid) vr[i] = VT{};
   }
-  // Paged tiles: left alone, the scheduler hoists the V regrouping (which
-  // waits for every V load) above the softmax; keeping it here lets the
-  // exponentials overlap the V loads, as the contiguous loop does by itself.
-  if constexpr (Rows::kPaged) __builtin_amdgcn_sched_barrier(0);
+  // Paged and unified-maximum tiles: left alone, the scheduler hoists the V
+  // regrouping (which waits for every V load) above the softmax; keeping it
+  // here lets the exponentials overlap the V loads, as the contiguous loop
+  // does by itself.
+  if constexpr (Rows::kPaged || UNI) __builtin_amdgcn_sched_barrier(0);
   bf16x8 vt[VW];
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
@@ -629,15 +645,69 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
                        : (pg * pk.page_size + off) * Hkv + w.g;
 }
 
+// The tiles of a chunk, wavefront `wave` taking tiles wave, wave + NW, ...
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
+__device__ __forceinline__ void chunk_tiles(
+    const Work &w, const PagedKV &pk, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
+    int hi_all, int hi_col, int wave, int lane, int n16, int q4,
+    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
+    floatx4 (&acc)[D / 16], float &m, float &l) {
+  const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
+  int prow = 0;
+  for (int t = wave, it = 0; t < ntiles; t += NW, ++it) {
+    const int k0 = w.lo + t * kKeyTile;
+    TileRows<D, PAGED> rows;
+    if constexpr (PAGED) {
+      const int slot = it & 31;
+      if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
+      const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
+      const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
+      rows.rs = prs;
+      rows.k0h = kc + (size_t)r0 * D;
+      rows.k1h = kc + (size_t)r1 * D;
+      rows.v0h = vc + (size_t)r0 * D;
+      rows.v1h = vc + (size_t)r1 * D;
+    } else {
+      rows.k = kc + slab;
+      rows.v = vc + slab;
+      rows.k0 = k0;
+    }
+    const int valid = min(kKeyTile, w.hi - k0);
+    const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
+    // The unified-maximum loop takes one (masked) tile body: with a branch
+    // the compiler moves its accumulators out of the matrix-core registers
+    // and back on every tile.
+    if (UNI)
+      mfma_tile<D, true, UNI>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16,
+                              q4, qop, scale_log2, phi2, acc, m, l);
+    else if (full)
+      mfma_tile<D, false, UNI>(rows, kKeyTile, kKeyTile, n16, q4, qop,
+                               scale_log2, phi2, acc, m, l);
+    else
+      mfma_tile<D, true, UNI>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16,
+                              q4, qop, scale_log2, phi2, acc, m, l);
+  }
+}
+
+// Unified maximum: a chunk column whose largest score - phi lies outside
+// +-kUniRange (log2 units) is recomputed exactly.  Inside it, 2^x neither
+// overflows (sums of up to 2^31 terms of at most 2^64) nor loses the
+// terms that matter (the largest is at least 2^-64, far above fp32's
+// smallest normal).
+constexpr float kUniRange = 64.f;
+
 // PAGED: K/V in a page pool behind a block table.  CAUSAL: Tq > 1 new
 // tokens per sequence, each column with its own key limit (a separate
 // instantiation keeps the single-token loop exactly as simple as before).
-template <int D, int NW, bool PAGED, bool CAUSAL>
+// UNI: unified-maximum softmax against phi2 (log2 units of the scaled
+// score) with an exact fallback.
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
 __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, int mode, uint16_t *__restrict__ out,
+    float scale_log2, float phi2, int mode, uint16_t *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
   constexpr int KK = D / 32;
@@ -679,34 +749,35 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
   for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = FD_NEG_INF, l = 0.f;
 
-  const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
-  int prow = 0;
-  for (int t = wave, it = 0; t < ntiles; t += NW, ++it) {
-    const int k0 = w.lo + t * kKeyTile;
-    TileRows<D, PAGED> rows;
-    if constexpr (PAGED) {
-      const int slot = it & 31;
-      if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
-      const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
-      const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
-      rows.rs = prs;
-      rows.k0h = kc + (size_t)r0 * D;
-      rows.k1h = kc + (size_t)r1 * D;
-      rows.v0h = vc + (size_t)r0 * D;
-      rows.v1h = vc + (size_t)r1 * D;
+  if constexpr (UNI) {
+    // Unified maximum (FlashDecoding++): one pass against phi2.  If a
+    // column's largest x = score - phi2 leaves [-kUniRange, kUniRange] the
+    // fixed reference risks overflow or lost precision, and the whole
+    // workgroup recomputes the chunk with the running maximum.
+    chunk_tiles<D, NW, PAGED, CAUSAL, true>(w, pk, kc, vc, slab, prs, Hkv,
+                                            hi_all, hi_col, wave, lane, n16,
+                                            q4, qop, scale_log2, phi2, acc,
+                                            m, l);
+    float xm = fmaxf(m, __shfl_xor(m, 16, 64));
+    xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
+    const bool bad = xm != FD_NEG_INF && !(xm >= -kUniRange && xm <= kUniRange);
+    if (__syncthreads_or(bad)) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m = FD_NEG_INF;
+      l = 0.f;
+      chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
+                                               hi_all, hi_col, wave, lane,
+                                               n16, q4, qop, scale_log2, 0.f,
+                                               acc, m, l);
     } else {
-      rows.k = kc + slab;
-      rows.v = vc + slab;
-      rows.k0 = k0;
+      m = xm == FD_NEG_INF ? FD_NEG_INF : phi2;
     }
-    const int valid = min(kKeyTile, w.hi - k0);
-    const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
-    if (full)
-      mfma_tile<D, false>(rows, kKeyTile, kKeyTile, n16, q4, qop, scale_log2,
-                          acc, m, l);
-    else
-      mfma_tile<D, true>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16, q4,
-                         qop, scale_log2, acc, m, l);
+  } else {
+    chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
+                                             hi_all, hi_col, wave, lane, n16,
+                                             q4, qop, scale_log2, 0.f, acc, m,
+                                             l);
   }
 
   l += __shfl_xor(l, 16, 64);
@@ -1034,9 +1105,10 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
   return hipSuccess;
 }
 
-template <int D, bool PAGED, bool CAUSAL>
+template <int D, bool PAGED, bool CAUSAL, bool UNI = false>
 hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
                        hipStream_t st) {
+  const float phi2 = a.unified_max * kLog2e;
   const dim3 grid(p.grid);
   const int part = mode_of(p);
   const uint16_t *q = static_cast<const uint16_t *>(a.q);
@@ -1045,11 +1117,11 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   uint16_t *out = static_cast<uint16_t *>(a.out);
 #define FD_MFMA_CASE(NWV)                                                    \
   case NWV:                                                                  \
-    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL>), grid,     \
+    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI>), grid,\
                        dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
                        p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk,         \
-                       p.splits, sl2, part, out, a.lse, a.o_part, a.lse_part, \
-                       a.tickets);                                           \
+                       p.splits, sl2, phi2, part, out, a.lse, a.o_part,      \
+                       a.lse_part, a.tickets);                               \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(1)
@@ -1079,6 +1151,11 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   hipError_t e = hipSuccess;
   if (!(a.phases & kPhaseChunks)) {
     // merge only
+  } else if (p.variant == FD_VARIANT_MFMA && p.unified) {
+    // the planner allows the unified maximum for contiguous single-token
+    // decode only
+    e = p.D == 128 ? launch_mfma<128, false, false, true>(p, a, sl2, st)
+                   : launch_mfma<64, false, false, true>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA) {
     const bool causal = p.Tq > 1;
     if (p.D == 128)

@@ -107,8 +107,13 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_variant < FD_VARIANT_AUTO ||
       requested_variant > FD_VARIANT_VALU)
     return FD_ERR_INVALID_ARG;
-  if (flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_PARTIALS))
-    return FD_ERR_INVALID_ARG;
+  if (flags & ~kKnownFlags) return FD_ERR_INVALID_ARG;
+  // The unified maximum (FlashDecoding++) is built for the bf16
+  // matrix-core pass over a contiguous cache, one token per sequence.
+  const bool unified = flags & FD_FLAG_UNIFIED_MAX;
+  if (unified && (dtype != FD_BF16 || general ||
+                  requested_variant == FD_VARIANT_VALU))
+    return FD_ERR_UNSUPPORTED;
 
   Plan q{};
   q.B = B;
@@ -121,6 +126,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.dtype = dtype;
   q.varlen = varlen;
   q.paged = extra.paged;
+  q.unified = unified;
   q.num_cus = num_cus;
 
   // Kernel variant: matrix cores need bf16; fp32 runs on the vector ALU.

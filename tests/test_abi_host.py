@@ -34,7 +34,8 @@ def test_header_declares_the_documented_entry_points():
                             "fd_workspace_bytes", "fd_status_string",
                             "fd_version", "fd_decode_partials",
                             "fd_merge_partials", "fd_decode_paged",
-                            "fd_decode_multiquery", "fd_plan_ex"])
+                            "fd_decode_multiquery", "fd_plan_ex",
+                            "fd_decode_unified_max"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -90,7 +91,8 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
     (dict(variant=3), fd.FD_ERR_INVALID_ARG),
     (dict(variant=-1), fd.FD_ERR_INVALID_ARG),
-    (dict(flags=4), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=4), fd.FD_ERR_INVALID_ARG),     # unified max needs phi
+    (dict(flags=8), fd.FD_ERR_INVALID_ARG),
     (dict(flags=-1), fd.FD_ERR_INVALID_ARG),
     (dict(ws=None, ws_bytes=64), fd.FD_ERR_INVALID_ARG),
     (dict(ws=A + 16, ws_bytes=1 << 20), fd.FD_ERR_INVALID_ARG),
@@ -247,6 +249,7 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(lse=None), fd.FD_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
     (dict(flags=4), fd.FD_ERR_INVALID_ARG),
+    (dict(flags=8), fd.FD_ERR_INVALID_ARG),
     (dict(num_splits=-2), fd.FD_ERR_INVALID_ARG),
     (dict(B=0), fd.FD_ERR_INVALID_ARG),
 ])
@@ -275,6 +278,7 @@ def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
     (dict(seqlens=A + 1), fd.FD_ERR_INVALID_ARG),
     (dict(D=80), fd.FD_ERR_UNSUPPORTED),
     (dict(Lmax=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Tq=1, flags=4), fd.FD_ERR_INVALID_ARG),   # unified max: own call
 ])
 def test_multiquery_arguments_rejected_on_host(lib, kw, code):
     assert call_mq(lib, **kw) == code
@@ -309,3 +313,43 @@ def test_plan_ex_for_several_tokens_and_pages(lib):
         args.update(kw)
         with pytest.raises(fd.FdError):
             fd.fd_plan_ex(**args)
+
+
+def call_uni(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
+             Lmax=64, scale=0.1, dtype=0, out=A, lse=A, phi=0.0,
+             num_splits=0, flags=0, ws=None, ws_bytes=0):
+    return lib.fd_decode_unified_max(q, k, v, seqlens, B, Hq, Hkv, D, Lmax,
+                                     scale, dtype, out, lse, phi, num_splits,
+                                     flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(phi=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(phi=float("inf")), fd.FD_ERR_INVALID_ARG),
+    (dict(phi=-float("inf")), fd.FD_ERR_INVALID_ARG),
+    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),          # bf16 only
+    (dict(q=None), fd.FD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(flags=2 | 8), fd.FD_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=A + 8, ws_bytes=4096), fd.FD_ERR_INVALID_ARG),
+])
+def test_unified_max_arguments_rejected_on_host(lib, kw, code):
+    assert call_uni(lib, **kw) == code
+
+
+def test_unified_max_plans_like_the_exact_pass(lib):
+    w = wl.WORKLOADS["b1_gqa8_h64_d128_l65536"]
+    base = plan(w)
+    uni = plan(w, flags=fd.FD_FLAG_UNIFIED_MAX)
+    assert uni == base
+    with pytest.raises(fd.FdError):
+        plan(wl.WORKLOADS["tiny_mha_f32_b1_h8_d64_l1024"],
+             flags=fd.FD_FLAG_UNIFIED_MAX)
+    with pytest.raises(fd.FdError):
+        fd.fd_plan_ex(1, 2, 8, 8, 128, 4096, "bf16",
+                      flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
+    with pytest.raises(fd.FdError):
+        fd.fd_plan_ex(1, 1, 8, 8, 128, 4096, "bf16", paged=True,
+                      flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
