@@ -15,8 +15,10 @@ the launch stream with device synchronisation on both sides.
 
 Prints one JSON line: value = algorithmic bytes per step (every K and V row
 once, q, out, lse) / step time, in GB/s; the roofline object compares the
-dominant kernel with MI355X's 8 TB/s HBM peak; cpu_baseline times the fp64
-CPU oracle on the host's cores over the same workload.
+dominant kernel with MI355X's 8 TB/s HBM peak (and, as frac_of_stream_ceiling,
+with stream_read_ceiling: a plain streaming read of the same number of bytes,
+measured in the same run); cpu_baseline times the fp64 CPU oracle on the
+host's cores over the same workload.
 
 --workload picks another workload of long_context_decode_fd_amd.workloads,
 including the paged-cache (fd_decode_paged) and multi-token
@@ -46,6 +48,50 @@ KERNEL_SRC = os.path.join(ROOT, "long_context_decode_fd_amd", "csrc",
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def stream_ceiling(torch, nbytes: int, steps: int, warmup: int, stream):
+    """Practical HBM read ceiling: libfdprobe.so's plain streaming read of
+    nbytes, rotating over KV_COPIES buffers like the decode steps, timed
+    the same way (HIP events on the launch stream)."""
+    import ctypes
+    from long_context_decode_fd_amd import build as lib_build
+    if not os.path.exists(lib_build.PROBE_LIB):
+        raise RuntimeError(f"{lib_build.PROBE_LIB} not built: run "
+                           "python -m long_context_decode_fd_amd.build")
+    lib = ctypes.CDLL(lib_build.PROBE_LIB)
+    lib.fdp_stream_read.restype = ctypes.c_int
+    lib.fdp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    n = nbytes // 16 * 16
+    bufs = [torch.full((n,), 1 + i, dtype=torch.uint8, device="cuda")
+            for i in range(KV_COPIES)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h = ctypes.c_void_p(stream.cuda_stream)
+
+    def rd(i):
+        rc = lib.fdp_stream_read(bufs[i % KV_COPIES].data_ptr(), n,
+                                 sink.data_ptr(), 256, h)
+        if rc != 0:
+            raise RuntimeError(f"fdp_stream_read failed: {rc}")
+
+    for i in range(warmup):
+        rd(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        rd(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    del bufs
+    return {"GBs": n / (us * 1e-6) / 1e9, "us": us, "bytes": n,
+            "kernel": "stream_read (long_context_decode_fd_amd/csrc/"
+                      "fd_probe.hip), 256 workgroups, 16-byte nontemporal "
+                      f"loads, {KV_COPIES} rotated buffers"}
 
 
 def kernel_source_hash() -> str:
@@ -252,6 +298,10 @@ def main(argv=None):
                              out, lse, stream=stream)
         torch.cuda.synchronize()
 
+    ceiling = stream_ceiling(torch, wl.algorithmic_bytes(w, seqlens), a.steps,
+                             a.warmup, stream)
+    log(f"[bench] streaming-read ceiling {ceiling['GBs']:.0f} GB/s")
+
     if a.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -322,7 +372,9 @@ def main(argv=None):
                             "note": "one KV copy re-read every step; may be "
                                     "served partly from the 256 MB MALL"},
         "roofline": roof,
+        "stream_read_ceiling": ceiling,
     }
+    roof["frac_of_stream_ceiling"] = roof["achieved"] / ceiling["GBs"]
     if not a.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)

@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfd.so")
 SOURCES = ["fd_api.hip", "fd_kernels.hip", "fd_plan.cpp"]
+# The benchmark's streaming-read helper (not part of the decode path).
+PROBE_LIB = os.path.join(PKG, "libfdprobe.so")
+PROBE_SOURCES = ["fd_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -26,14 +29,15 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(out: str = LIB, defines=(), verbose: bool = False) -> str:
+def build(out: str = LIB, defines=(), verbose: bool = False,
+          sources=SOURCES) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
            "-shared", "-Wall", "-I", INCLUDE, "-I", CSRC,
            # no packed-fp32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument"]
     cmd += [f"-D{d}" for d in defines]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -49,6 +53,8 @@ def main(argv=None):
     ap.add_argument("-q", action="store_true")
     a = ap.parse_args(argv)
     print(build(a.o, a.defines, verbose=not a.q))
+    if a.o == LIB:
+        print(build(PROBE_LIB, verbose=not a.q, sources=PROBE_SOURCES))
 
 
 if __name__ == "__main__":
