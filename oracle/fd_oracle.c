@@ -333,14 +333,19 @@ int fdo_decode_split(const void *q, const void *k, const void *v,
  *       ((pg * Hkv + g) * page_size + t) * D
  * seqlens is required; a length beyond max_pages * page_size is clamped, and
  * a page index outside [0, num_pages) is an error (FDO_EINVAL).
+ * Tq new tokens per sequence, as in fdo_decode_multiquery: q, out
+ * [B][Tq][Hq][D], lse [B][Tq][Hq]; token t sees the first
+ * L - (Tq - 1 - t) of the sequence's rows (Tq = 1: plain decode).
  */
 int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                      const int32_t *block_table, int max_pages, int page_size,
                      int num_pages, int head_major, const int32_t *seqlens,
-                     int B, int Hq, int Hkv, int D, double scale, int dtype,
-                     int nthreads, double *out, double *lse)
+                     int B, int Tq, int Hq, int Hkv, int D, double scale,
+                     int dtype, int nthreads, double *out, double *lse)
 {
     if (max_pages <= 0 || page_size <= 0 || num_pages <= 0 || !seqlens)
+        return FDO_EINVAL;
+    if (Tq <= 0)
         return FDO_EINVAL;
     if (head_major != 0 && head_major != 1)
         return FDO_EINVAL;
@@ -357,7 +362,7 @@ int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
         }
     }
     const int G = Hq / Hkv;
-    const long rows = (long)B * Hq;
+    const long rows = (long)B * Tq * Hq;
     int failed = 0;
     if (nthreads <= 0)
         nthreads = omp_get_max_threads();
@@ -373,9 +378,14 @@ int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
         for (long r = 0; r < rows; ++r) {
             if (!scratch || !roff)
                 continue;
-            int b = (int)(r / Hq), h = (int)(r % Hq);
+            int b = (int)(r / ((long)Tq * Hq)), h = (int)(r % Hq);
+            int tok = (int)((r / Hq) % Tq);
             int g = h / G;
             int L = clamp_len(seqlens, b, Lcap);
+            /* causal among the new tokens: later ones' rows are not seen */
+            L -= Tq - 1 - tok;
+            if (L < 0)
+                L = 0;
             for (int j = 0; j < L; ++j) {
                 size_t pg = (size_t)block_table[(size_t)b * max_pages +
                                                 j / page_size];
@@ -385,9 +395,8 @@ int fdo_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                 else
                     roff[j] = ((pg * page_size + t) * Hkv + g) * (size_t)D;
             }
-            attend_row(q, ((size_t)b * Hq + h) * D, k_pages, v_pages, 0, roff,
-                       L, D, scale, dtype, out + (size_t)r * D, lse + r,
-                       scratch);
+            attend_row(q, (size_t)r * D, k_pages, v_pages, 0, roff, L, D,
+                       scale, dtype, out + (size_t)r * D, lse + r, scratch);
         }
         free(scratch);
         free(roff);

@@ -49,7 +49,7 @@ def _bind(path: str):
                                          dp, dp, dp, dp]
     lib.fdo_attend_row_split.restype = ci
     lib.fdo_decode_paged.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci, i32p,
-                                     ci, ci, ci, ci, cd, ci, ci, dp, dp]
+                                     ci, ci, ci, ci, ci, cd, ci, ci, dp, dp]
     lib.fdo_decode_paged.restype = ci
     lib.fdo_decode_multiquery.argtypes = [vp, vp, vp, i32p, ci, ci, ci, ci,
                                           ci, ci, cd, ci, ci, dp, dp]
@@ -175,10 +175,14 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     """Exact attention over a paged cache.  k_pages/v_pages
     [num_pages, page_size, Hkv, D] (token-major) or [num_pages, Hkv,
     page_size, D] (head_major); block_table int32 [B, max_pages]; seqlens
-    int32 [B] (required)."""
+    int32 [B] (required).  q [B, Hq, D], or [B, Tq, Hq, D] for Tq causal
+    new tokens (out and lse then carry the Tq axis too)."""
     q, k_pages, v_pages = _c(q), _c(k_pages), _c(v_pages)
     dt = _dtype_code(q)
-    B, Hq, D = q.shape
+    if q.ndim == 4:
+        B, Tq, Hq, D = q.shape
+    else:
+        (B, Hq, D), Tq = q.shape, 1
     if head_major:
         num_pages, Hkv, page_size, Dk = k_pages.shape
     else:
@@ -187,13 +191,13 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     bt = _c(np.asarray(block_table, dtype=np.int32))
     assert bt.shape[0] == B
     sl = _c(np.asarray(seqlens, dtype=np.int32))
-    out = np.empty((B, Hq, D), dtype=np.float64)
-    lse = np.empty((B, Hq), dtype=np.float64)
+    out = np.empty(q.shape, dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
     lib = _lib_override or _load()
     rc = lib.fdo_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages),
                               _ptr(bt), bt.shape[1], page_size, num_pages,
-                              int(bool(head_major)), _ptr(sl), B, Hq, Hkv, D,
-                              _scale(scale), dt,
+                              int(bool(head_major)), _ptr(sl), B, Tq, Hq, Hkv,
+                              D, _scale(scale), dt,
                               int(nthreads), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"fdo_decode_paged failed with {rc}")

@@ -55,6 +55,11 @@ MUTANTS = [
     ("paged_page_of_token_zero", "                                j / page_size];",
      "                                0];"),
     ("multiquery_not_causal", "- (Tq - 1 - t);", "- 0;"),
+    ("paged_multiquery_not_causal", "L -= Tq - 1 - tok;", "L -= 0;"),
+    ("paged_multiquery_token_ignored", "int tok = (int)((r / Hq) % Tq);",
+     "int tok = Tq - 1;"),
+    ("paged_multiquery_q_row", "attend_row(q, (size_t)r * D, k_pages",
+     "attend_row(q, (size_t)(r % ((long)Tq * Hq) % Hq) * D, k_pages"),
     ("multiquery_causal_reversed", "- (Tq - 1 - t);", "- t;"),
     ("multiquery_q_row", "attend_row(q, (size_t)r * D, k, v, kv_off",
      "attend_row(q, (size_t)(r % Hq) * D, k, v, kv_off"),
@@ -83,6 +88,7 @@ PINS = [
     (pins.test_paged_equals_contiguous_after_scatter, (32, False)),
     (pins.test_paged_equals_contiguous_after_scatter, (64, False)),
     (pins.test_paged_equals_contiguous_after_scatter, (32, True)),
+    (pins.test_paged_multiquery_equals_contiguous_after_scatter, (False,)),
     (pins.test_multiquery_single_token_is_decode, ()),
     (pins.test_multiquery_identical_keys_closed_form, ()),
     (pins.test_multiquery_query_never_sees_later_tokens, ()),

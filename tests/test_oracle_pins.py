@@ -432,6 +432,26 @@ def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size,
     assert not np.array_equal(np.nan_to_num(o3), o1)
 
 
+@pytest.mark.parametrize("head_major", [False, True])
+def test_paged_multiquery_equals_contiguous_after_scatter(oracle_mod,
+                                                        head_major):
+    # Several new tokens over a shuffled page pool: the contiguous
+    # multi-token oracle's result bit for bit, token by token.
+    rng = np.random.default_rng(34)
+    B, Tq, Hq, Hkv, D, L, P = 3, 3, 4, 2, 16, 130, 32
+    q = rand_bf16(rng, (B, Tq, Hq, D))
+    k = rand_bf16(rng, (B, Hkv, L, D))
+    v = rand_bf16(rng, (B, Hkv, L, D))
+    seq = np.array([130, 2, 65], np.int32)
+    kp, vp, bt = scatter_to_pages(k, v, seq, P, rng, head_major=head_major)
+    o1, l1 = oracle_mod.decode_multiquery(q, k, v, seq, 0.3)
+    o2, l2 = oracle_mod.decode_paged(q, kp, vp, bt, seq, 0.3,
+                                     head_major=head_major)
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(l2, l1)
+    assert np.isinf(l1[1, 0]).all()          # length 2 < Tq: token 0 sees none
+
+
 def test_multiquery_single_token_is_decode(oracle_mod):
     rng = np.random.default_rng(31)
     B, Hq, Hkv, D, L = 2, 6, 3, 8, 40
