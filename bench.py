@@ -218,7 +218,7 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     if kind == "paged":
         q, k, v, bt, sl, seqlens, _ = wl.device_paged_inputs(w)
-        plan = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D,
+        plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D,
                              w.max_pages * w.page_size, w.dtype, paged=True)
     else:
         q, k, v, sl, seqlens, _ = wl.device_inputs(w)

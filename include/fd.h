@@ -224,7 +224,9 @@ enum {
  *         FD_PAGES_HEAD_MAJOR   [num_pages][Hkv][page_size][D]
  *     block_table       int32 [B][max_pages], DEVICE memory
  *     seqlens           int32 [B], DEVICE memory, REQUIRED
- *     q, out, lse       as for fd_decode
+ *     q, out, lse       as for fd_decode when Tq = 1; for Tq > 1 causal new
+ *                       tokens per sequence as for fd_decode_multiquery:
+ *                       q, out [B][Tq][Hq][D], lse [B][Tq][Hq]
  * Token j < L = clamp(seqlens[b], 0, max_pages * page_size) of sequence b,
  * KV head g, is in page pg = block_table[b][j / page_size] at t = j %
  * page_size: row ((pg * page_size + t) * Hkv + g) * D token-major,
@@ -237,7 +239,7 @@ enum {
  * page_size * Hkv at most INT_MAX.  A table entry outside [0, num_pages)
  * is a caller error that the kernel clamps into that range (never a read
  * outside the pools).
- * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Hq/Hkv <= 16.
+ * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Tq * Hq/Hkv <= 16.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
  * tokens; FD_FLAG_FUSED_MERGE allowed).  Workspace: the library-owned one,
  * as for fd_decode.
@@ -245,9 +247,9 @@ enum {
 int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     const int32_t *block_table, int max_pages, int page_size,
                     int num_pages, int layout, const int32_t *seqlens, int B,
-                    int Hq, int Hkv, int D, float scale, fd_dtype_t dtype,
-                    void *out, float *lse, int num_splits, int flags,
-                    void *stream);
+                    int Tq, int Hq, int Hkv, int D, float scale,
+                    fd_dtype_t dtype, void *out, float *lse, int num_splits,
+                    int flags, void *stream);
 
 /*
  * fd_decode_multiquery -- Tq new query tokens per sequence at once (the
@@ -300,7 +302,7 @@ int fd_decode_unified_max(const void *q, const void *k_cache,
 
 /*
  * fd_plan_ex -- fd_plan for the calls above: Tq query tokens per sequence
- * (1 for fd_decode / fd_decode_paged), paged nonzero for a paged cache
+ * (1 for fd_decode), paged nonzero for a paged cache
  * (then Lmax = max_pages * page_size and seqlens are implied).  The
  * partial layouts gain the token index: o_part [B][Tq][Hq][S][D], lse_part
  * [B][Tq][Hq][S].

@@ -59,8 +59,8 @@ SIGNATURES = {
     "fd_merge_partials": (_ci, [_i32p, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                 _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
     "fd_decode_paged": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
-                              _i32p, _ci, _ci, _ci, _ci, _cf, _ci, _vp, _vp,
-                              _ci, _ci, _vp]),
+                              _i32p, _ci, _ci, _ci, _ci, _ci, _cf, _ci, _vp,
+                              _vp, _ci, _ci, _vp]),
     "fd_decode_multiquery": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                                    _ci, _ci, _cf, _ci, _vp, _vp, _ci, _ci,
                                    _vp]),
@@ -349,15 +349,20 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
                     head_major=False, stream=None):
     """Decode attention over a paged KV cache -- see fd.h.
 
-    q [B,Hq,D] bf16; k_pages/v_pages [num_pages,page_size,Hkv,D] bf16
-    (token-major) or [num_pages,Hkv,page_size,D] (head_major);
-    block_table int32 [B,max_pages]; seqlens int32 [B] (required); all on
-    the GPU.  Returns (out [B,Hq,D], lse [B,Hq]).
+    q [B,Hq,D] bf16, or [B,Tq,Hq,D] for Tq causal new tokens;
+    k_pages/v_pages [num_pages,page_size,Hkv,D] bf16 (token-major) or
+    [num_pages,Hkv,page_size,D] (head_major); block_table int32
+    [B,max_pages]; seqlens int32 [B] (required); all on the GPU.  Returns
+    (out, lse) shaped like q and q without its last axis.
     """
     import torch
-    if q.dim() != 3 or k_pages.dim() != 4:
-        raise ValueError("expected q [B,Hq,D], 4-d page pools")
-    B, Hq, D = q.shape
+    if q.dim() not in (3, 4) or k_pages.dim() != 4:
+        raise ValueError("expected q [B,Hq,D] or [B,Tq,Hq,D], 4-d page "
+                         "pools")
+    if q.dim() == 4:
+        B, Tq, Hq, D = q.shape
+    else:
+        (B, Hq, D), Tq = q.shape, 1
     if head_major:
         num_pages, Hkv, page_size, Dk = k_pages.shape
     else:
@@ -373,12 +378,13 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     _device_tensor("seqlens", seqlens, torch.int32, (B,))
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
-    out, lse = _out_lse(out, lse, (B, Hq, D), (B, Hq), q.dtype, q.device)
+    out, lse = _out_lse(out, lse, tuple(q.shape), tuple(q.shape[:-1]),
+                        q.dtype, q.device)
     rc = load_library().fd_decode_paged(
         q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
         FD_PAGES_HEAD_MAJOR if head_major else FD_PAGES_TOKEN_MAJOR,
-        seqlens.data_ptr(), B, Hq, Hkv, D, float(scale),
+        seqlens.data_ptr(), B, Tq, Hq, Hkv, D, float(scale),
         _dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
         int(num_splits), int(flags), _stream_handle(stream, q.device))
     if rc != FD_OK:

@@ -245,16 +245,17 @@ int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
 int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     const int32_t *block_table, int max_pages, int page_size,
                     int num_pages, int layout, const int32_t *seqlens, int B,
-                    int Hq, int Hkv, int D, float scale, fd_dtype_t dtype,
-                    void *out, float *lse, int num_splits, int flags,
-                    void *stream) {
-  if (flags & FD_FLAG_UNIFIED_MAX) return FD_ERR_INVALID_ARG;
+                    int Tq, int Hq, int Hkv, int D, float scale,
+                    fd_dtype_t dtype, void *out, float *lse, int num_splits,
+                    int flags, void *stream) {
+  if (Tq <= 0 || (flags & FD_FLAG_UNIFIED_MAX)) return FD_ERR_INVALID_ARG;
   const fd::PagedKV pk{block_table, max_pages, page_size, num_pages, layout};
   int cap = 0;
   const int rc = check_paged(pk, seqlens, Hkv, &cap);
   if (rc != FD_OK) return rc;
   fd::Extra ex;
   ex.paged = true;
+  ex.Tq = Tq;
   return run(q, k_pages, v_pages, seqlens, B, Hq, Hkv, D, cap, scale, dtype,
              out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
              fd::kPhaseChunks | fd::kPhaseMerge, ex, pk);

@@ -127,6 +127,10 @@ EXTRA_WORKLOADS = {
             name="paged_hm_p64_b1_gqa8_h64_d128_l65536", page_size=64,
             head_major=True,
             note="batch-1 64k decode from 64-token head-major pages"),
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="paged_hm_p64_mq2_b1_gqa8_h64_d128_l65536", page_size=64,
+            head_major=True, Tq=2,
+            note="two causal new tokens over 64-token head-major pages"),
         WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
             name="paged_p16_varlen_b16_gqa8_h64_d128_lmax131072",
             page_size=16,

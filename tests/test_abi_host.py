@@ -219,11 +219,12 @@ def test_binding_marshals_nothing_but_pointers():
 
 
 def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
-               num_pages=8, layout=0, seqlens=A, B=1, Hq=8, Hkv=8, D=128,
-               scale=0.1, dtype=0, out=A, lse=A, num_splits=0, flags=0):
+               num_pages=8, layout=0, seqlens=A, B=1, Tq=1, Hq=8, Hkv=8,
+               D=128, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
+               flags=0):
     return lib.fd_decode_paged(q, k, v, bt, max_pages, page_size, num_pages,
-                               layout, seqlens, B, Hq, Hkv, D, scale, dtype,
-                               out, lse, num_splits, flags, None)
+                               layout, seqlens, B, Tq, Hq, Hkv, D, scale,
+                               dtype, out, lse, num_splits, flags, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -241,6 +242,9 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(layout=2), fd.FD_ERR_INVALID_ARG),
     (dict(layout=-1), fd.FD_ERR_INVALID_ARG),
     (dict(layout=1, page_size=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Tq=3, Hq=48, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 6 x 3 = 18 rows
+    (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),
     (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),        # bf16 only
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),

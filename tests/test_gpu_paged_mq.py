@@ -178,6 +178,68 @@ def test_paged_full_size_64k(torch, oracle_mod, name):
     assert o_h.shape == (1, 64, 128) and l_h.shape == (1, 64)
 
 
+PAGED_MQ_SHAPES = [
+    # (B, Tq, Hq, Hkv, D, Lmax, page_size, seqlens)
+    (3, 2, 16, 2, 128, 1000, 32, [1000, 517, 1]),
+    (2, 4, 16, 4, 128, 700, 16, [700, 3]),
+    (2, 3, 8, 8, 64, 640, 64, [641, 64]),
+    (1, 16, 4, 4, 128, 9000, 48, [8999]),
+]
+
+
+@pytest.mark.parametrize("hm", [False, True], ids=["token_major",
+                                                   "head_major"])
+@pytest.mark.parametrize("shape", PAGED_MQ_SHAPES,
+                         ids=[f"B{s[0]}_Tq{s[1]}_Hq{s[2]}_Hkv{s[3]}_D{s[4]}"
+                              f"_L{s[5]}_P{s[6]}" for s in PAGED_MQ_SHAPES])
+@pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (7, 0),
+                                          (0, fd.FD_FLAG_FUSED_MERGE)])
+def test_paged_multiquery_matches_oracle(torch, oracle_mod, shape, splits,
+                                         flags, hm):
+    B, Tq, Hq, Hkv, D, L, P, sls = shape
+    w = wl.Workload("paged_mq_case", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=L,
+                    dtype="bf16", seed=80 + Tq, page_size=P, head_major=hm,
+                    Tq=Tq)
+    seqlens = np.array(sls, np.int32)
+    (q, kp, vp, bt, sl), (qd, kd, vd, btd, sld) = paged_case(torch, w,
+                                                             seqlens)
+    _note(f"paged mq {shape} hm={hm} splits={splits} flags={flags}")
+    out, lse = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale,
+                                  num_splits=splits, flags=flags,
+                                  head_major=hm)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mod.decode_paged(q, kp, vp, bt, sl, w.scale,
+                                           head_major=hm)
+    _assert_parity(out, lse, ref_o, ref_l, f"paged mq {shape} hm={hm}")
+
+
+def test_paged_multiquery_full_size_equals_contiguous(torch, oracle_mod):
+    """Two new tokens over 64-token head-major pages at batch-1 64k: bit
+    for bit the contiguous multi-token call on the same rows (same plan),
+    sampled rows against the oracle."""
+    w = wl.EXTRA_WORKLOADS["paged_hm_p64_mq2_b1_gqa8_h64_d128_l65536"]
+    _note(f"{w.name}: generating")
+    q, kp, vp, btd, sld, seqlens, _ = wl.device_paged_inputs(w)
+    out, lse = fd.fd_decode_paged(q, kp, vp, btd, sld, w.scale,
+                                  head_major=True)
+    torch.cuda.synchronize()
+    del kp, vp
+    _, k, v, _, _, _ = wl.device_inputs(w.with_(page_size=0),
+                                        seqlens=seqlens)
+    co, cl = fd.fd_decode_multiquery(q, k, v, sld, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), co.view(torch.int16))
+    assert torch.equal(lse, cl)
+    qh = wl.gen_q(w)
+    for b, t, h in [(0, 0, 0), (0, 1, 63), (0, 0, 17), (0, 1, 40)]:
+        L = int(seqlens[b])
+        kr, vr = wl.gen_slab_rows(w, b, h // w.G, L)
+        ro, rl = oracle_mod.attend_row(qh[b, t, h], kr, vr,
+                                       L - (w.Tq - 1 - t), w.scale)
+        _assert_parity(out[b, t, h], lse[b, t, h:h + 1], ro, np.array([rl]),
+                       f"{w.name} row {(b, t, h)}")
+
+
 # ---------------------------------------------------------------------------
 # Several causal new tokens.
 
