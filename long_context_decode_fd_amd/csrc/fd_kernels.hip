@@ -977,15 +977,29 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
 constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 16;
 
+// Workgroups are dealt to MI355X's eight XCDs round robin (id % 8).  When
+// Hkv is a multiple of 8, every chunk of kv-head g ran on XCD g % 8 (the
+// chunk pass's ids are ... * Hkv + g), so the merge of a query row of that
+// head is given an id on the same XCD: workgroup 8 k + x takes the k-th
+// row, in row order, among the rows of kv-heads g with g % 8 == x.
+// Otherwise ids are rows.  Either way it is a permutation of the rows.
+__device__ __forceinline__ int merge_row(int id, int G, int Hkv) {
+  if (Hkv % 8 != 0) return id;
+  const int x = id % 8, k = id / 8, per = Hkv / 8;
+  const int hh = k % G, g1 = (k / G) % per, bt = k / G / per;
+  return (bt * Hkv + 8 * g1 + x) * G + hh;
+}
+
 template <int D, typename OutT>
 __global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
-    const int32_t *__restrict__ seqlens, int rows_per_b, int Lmax, int C,
-    int S, OutT *__restrict__ out, float *__restrict__ lse) {
+    const int32_t *__restrict__ seqlens, int rows_per_b, int G, int Hkv,
+    int Lmax, int C, int S, OutT *__restrict__ out,
+    float *__restrict__ lse) {
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float sm_M[kMergeWaves], sm_W[kMergeWaves];
   __shared__ float sm_acc[kMergeWaves][D];
-  const int row = blockIdx.x;
+  const int row = merge_row(blockIdx.x, G, Hkv);
   const int b = row / rows_per_b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
@@ -1139,8 +1153,8 @@ template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Tq * p.Hq),
                      dim3(kMergeWaves * 64), 0, st, a.o_part, a.lse_part,
-                     a.seqlens, p.Tq * p.Hq, p.Lmax, p.chunk, p.splits,
-                     static_cast<OutT *>(a.out), a.lse);
+                     a.seqlens, p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk,
+                     p.splits, static_cast<OutT *>(a.out), a.lse);
 }
 
 }  // namespace
