@@ -697,6 +697,86 @@ __device__ __forceinline__ void chunk_tiles(
 // smallest normal).
 constexpr float kUniRange = 64.f;
 
+// End of a chunk in the matrix-core kernel (direct and partial modes): the
+// wavefronts' states are merged with one weight per (wavefront, column):
+// each wavefront publishes its column maxima m and sums l; every lane then
+// forms M = max m, W = sum 2^(m - M) l and its own scale 2^(m - M) / W;
+// wavefronts 1.. park their scaled accumulators in LDS as 16-byte vectors
+// and wavefront 0 adds them, in wavefront order, to its own and stores its
+// lane's contiguous run of output columns, (q4 * 4 + j) * VW + e, with
+// vector stores.  A column that saw no key gets out 0 and lse -inf.
+template <int D, int NW>
+__device__ __forceinline__ void wave_merge_store(
+    float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
+    int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
+    const Work &w, int G, int Tq, int Hq, int S, int mode,
+    uint16_t *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part) {
+  constexpr int VW = D / 16;
+  constexpr int V4 = VW / 4;  // float4 per (lane, j)
+  if (q4 == 0) {
+    sm_m[wave * 16 + n16] = m;
+    sm_l[wave * 16 + n16] = l;
+  }
+  __syncthreads();
+  float M = FD_NEG_INF;
+#pragma unroll
+  for (int sl = 0; sl < NW; ++sl) M = fmaxf(M, sm_m[sl * 16 + n16]);
+  float W = 0.f;
+  if (M != FD_NEG_INF) {
+#pragma unroll
+    for (int sl = 0; sl < NW; ++sl)
+      W += exp2_f(sm_m[sl * 16 + n16] - M) * sm_l[sl * 16 + n16];
+  }
+  const float own = M == FD_NEG_INF ? 0.f : exp2_f(m - M) / W;
+  float4 *park = reinterpret_cast<float4 *>(sm_o);
+  if (NW > 1 && wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < V4; ++e4)
+        park[(((wave - 1) * 4 + j) * V4 + e4) * 64 + lane] = make_float4(
+            acc[4 * e4][j] * own, acc[4 * e4 + 1][j] * own,
+            acc[4 * e4 + 2][j] * own, acc[4 * e4 + 3][j] * own);
+  }
+  __syncthreads();
+  if (wave != 0 || n16 >= ncol) return;
+  const size_t row = row_of(w, G, Hq, Tq, n16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int e4 = 0; e4 < V4; ++e4) {
+      float4 o = make_float4(acc[4 * e4][j] * own, acc[4 * e4 + 1][j] * own,
+                             acc[4 * e4 + 2][j] * own,
+                             acc[4 * e4 + 3][j] * own);
+#pragma unroll
+      for (int sl = 1; sl < NW; ++sl) {
+        const float4 p = park[(((sl - 1) * 4 + j) * V4 + e4) * 64 + lane];
+        o.x += p.x;
+        o.y += p.y;
+        o.z += p.z;
+        o.w += p.w;
+      }
+      const int d0 = (q4 * 4 + j) * VW + 4 * e4;
+      if (mode == kModeDirect) {
+        uint2 bits;
+        bits.x = (uint32_t)to_bf16_bits(o.x) | ((uint32_t)to_bf16_bits(o.y) << 16);
+        bits.y = (uint32_t)to_bf16_bits(o.z) | ((uint32_t)to_bf16_bits(o.w) << 16);
+        *reinterpret_cast<uint2 *>(out + row * D + d0) = bits;
+      } else {
+        *reinterpret_cast<float4 *>(o_part + (row * S + w.s) * D + d0) = o;
+      }
+    }
+  }
+  if (q4 == 0) {
+    const float ls = M == FD_NEG_INF ? FD_NEG_INF : (M + log2_f(W)) * kLn2;
+    if (mode == kModeDirect)
+      lse[row] = ls;
+    else
+      lse_part[row * S + w.s] = ls;
+  }
+}
+
 // PAGED: K/V in a page pool behind a block table.  CAUSAL: Tq > 1 new
 // tokens per sequence, each column with its own key limit (a separate
 // instantiation keeps the single-token loop exactly as simple as before).
@@ -782,6 +862,12 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
+  if (mode != kModeFused) {
+    wave_merge_store<D, NW>(sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l,
+                            acc, w, G, Tq, Hq, S, mode, out, lse, o_part,
+                            lse_part);
+    return;
+  }
   if (n16 < ncol) {
     if (q4 == 0) {
       sm_m[wave * 16 + n16] = m;
