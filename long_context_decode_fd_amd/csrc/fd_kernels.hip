@@ -698,13 +698,13 @@ __device__ __forceinline__ void chunk_tiles(
 constexpr float kUniRange = 64.f;
 
 // End of a chunk in the matrix-core kernel (direct and partial modes): the
-// wavefronts' states are merged with one weight per (wavefront, column):
-// each wavefront publishes its column maxima m and sums l; every lane then
-// forms M = max m, W = sum 2^(m - M) l and its own scale 2^(m - M) / W;
-// wavefronts 1.. park their scaled accumulators in LDS as 16-byte vectors
-// and wavefront 0 adds them, in wavefront order, to its own and stores its
-// lane's contiguous run of output columns, (q4 * 4 + j) * VW + e, with
-// vector stores.  A column that saw no key gets out 0 and lse -inf.
+// wavefronts' states are merged with one weight per (wavefront, column).
+// Every wavefront publishes its column maxima m and sums l, and wavefronts
+// 1.. park their accumulators in LDS as 16-byte vectors; after one barrier
+// wavefront 0 alone forms M = max m, W = sum 2^(m - M) l and the weights
+// 2^(m - M) / W, adds the weighted accumulators in wavefront order and
+// stores its lane's contiguous run of output columns, (q4 * 4 + j) * VW + e,
+// with vector stores.  A column that saw no key gets out 0 and lse -inf.
 template <int D, int NW>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
@@ -718,17 +718,6 @@ __device__ __forceinline__ void wave_merge_store(
     sm_m[wave * 16 + n16] = m;
     sm_l[wave * 16 + n16] = l;
   }
-  __syncthreads();
-  float M = FD_NEG_INF;
-#pragma unroll
-  for (int sl = 0; sl < NW; ++sl) M = fmaxf(M, sm_m[sl * 16 + n16]);
-  float W = 0.f;
-  if (M != FD_NEG_INF) {
-#pragma unroll
-    for (int sl = 0; sl < NW; ++sl)
-      W += exp2_f(sm_m[sl * 16 + n16] - M) * sm_l[sl * 16 + n16];
-  }
-  const float own = M == FD_NEG_INF ? 0.f : exp2_f(m - M) / W;
   float4 *park = reinterpret_cast<float4 *>(sm_o);
   if (NW > 1 && wave > 0) {
 #pragma unroll
@@ -736,26 +725,42 @@ __device__ __forceinline__ void wave_merge_store(
 #pragma unroll
       for (int e4 = 0; e4 < V4; ++e4)
         park[(((wave - 1) * 4 + j) * V4 + e4) * 64 + lane] = make_float4(
-            acc[4 * e4][j] * own, acc[4 * e4 + 1][j] * own,
-            acc[4 * e4 + 2][j] * own, acc[4 * e4 + 3][j] * own);
+            acc[4 * e4][j], acc[4 * e4 + 1][j], acc[4 * e4 + 2][j],
+            acc[4 * e4 + 3][j]);
   }
   __syncthreads();
   if (wave != 0 || n16 >= ncol) return;
+  float ms[NW], wt[NW];
+  float M = FD_NEG_INF;
+#pragma unroll
+  for (int sl = 0; sl < NW; ++sl) {
+    ms[sl] = sm_m[sl * 16 + n16];
+    M = fmaxf(M, ms[sl]);
+  }
+  float W = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < NW; ++sl) {
+    wt[sl] = M == FD_NEG_INF ? 0.f : exp2_f(ms[sl] - M);
+    W += wt[sl] * sm_l[sl * 16 + n16];
+  }
+  const float inv = M == FD_NEG_INF ? 0.f : 1.f / W;
+#pragma unroll
+  for (int sl = 0; sl < NW; ++sl) wt[sl] *= inv;
   const size_t row = row_of(w, G, Hq, Tq, n16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int e4 = 0; e4 < V4; ++e4) {
-      float4 o = make_float4(acc[4 * e4][j] * own, acc[4 * e4 + 1][j] * own,
-                             acc[4 * e4 + 2][j] * own,
-                             acc[4 * e4 + 3][j] * own);
+      float4 o = make_float4(acc[4 * e4][j] * wt[0], acc[4 * e4 + 1][j] * wt[0],
+                             acc[4 * e4 + 2][j] * wt[0],
+                             acc[4 * e4 + 3][j] * wt[0]);
 #pragma unroll
       for (int sl = 1; sl < NW; ++sl) {
         const float4 p = park[(((sl - 1) * 4 + j) * V4 + e4) * 64 + lane];
-        o.x += p.x;
-        o.y += p.y;
-        o.z += p.z;
-        o.w += p.w;
+        o.x += p.x * wt[sl];
+        o.y += p.y * wt[sl];
+        o.z += p.z * wt[sl];
+        o.w += p.w * wt[sl];
       }
       const int d0 = (q4 * 4 + j) * VW + 4 * e4;
       if (mode == kModeDirect) {
