@@ -159,7 +159,8 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
  *               for the same arguments, 256-byte aligned, or NULL with
  *               workspace_bytes 0 to use the library-owned one.  A caller
  *               workspace makes the call allocation-free and free of
- *               library state.  With FD_FLAG_FUSED_MERGE its first
+ *               library state, so it can be captured in a HIP graph and
+ *               replayed (it queues kernels only; no memset, no copy).  With FD_FLAG_FUSED_MERGE its first
  *               fd_plan_t.ticket_bytes bytes are per-group tickets that must
  *               be zero when a call starts: zero-fill a new workspace once;
  *               every call leaves its tickets zero again, but the rest of
