@@ -25,8 +25,14 @@
 //   * the wavefronts of a workgroup take interleaved tiles and merge their
 //     (max, sum, accumulator) states through LDS at the end, so a chunk
 //     writes one partial per query row;
+//   * the same kernel, by template switches, reads the tiles from a paged
+//     pool through a block table, serves several causal new tokens per
+//     sequence (their query rows share the 16-column q-tile), or takes the
+//     unified-maximum softmax of FlashDecoding++ with an exact fallback;
 //   * fp32 (and bf16 tiny groups) run a vector-ALU kernel with 16-byte
-//     loads per lane and shuffle reductions of the dot products.
+//     loads per lane and shuffle reductions of the dot products;
+//   * a second, small kernel merges the chunk partials of every query row
+//     (or, opt-in, the last workgroup of each group merges them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -180,7 +186,8 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the workgroup's softmax states and the chunk's store.
+// Merge of the workgroup's softmax states and the chunk's store (the
+// vector-ALU kernel, and the matrix-core kernel under the fused merge).
 //
 // Slot sl holds, for query row h of the group: running max m (log2 units of
 // the scaled score), running sum l, and the unnormalised accumulator
