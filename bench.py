@@ -95,8 +95,16 @@ def stream_ceiling(torch, nbytes: int, steps: int, warmup: int, stream):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with comments and whitespace
+    removed: counters stay valid across comment-only edits and become
+    stale with any change of the code."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = "".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles():
