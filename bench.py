@@ -10,8 +10,9 @@ synthetic N(0,1) values (long_context_decode_fd_amd.workloads), resident in
 HBM before timing starts.  Successive steps rotate over 4 copies of the KV
 cache (1.07 GB) so that the 256 MB Infinity Cache cannot serve a repeat of
 the previous step: each step reads its 268 MB from HBM, as a model's layers
-do in turn.  W untimed steps, then exactly K steps between two HIP events on
-the launch stream with device synchronisation on both sides.
+do in turn.  W untimed steps (continued until at least 50 ms of warm-up, the
+count reported as warmup_steps_run), then exactly K steps between two HIP
+events on the launch stream with device synchronisation on both sides.
 
 Prints one JSON line: value = algorithmic bytes per step (every K and V row
 once, q, out, lse) / step time, in GB/s; the roofline object compares the
@@ -48,6 +49,29 @@ KERNEL_SRC = os.path.join(ROOT, "long_context_decode_fd_amd", "csrc",
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Untimed warm-up runs at least this long whatever W is: MI355X reaches its
+# steady step time only after some milliseconds of continuous work (20
+# steps: 47.8 us/step; 200 or more: 46.5).
+MIN_WARMUP_S = 0.05
+
+
+def warm_up(torch, fn, steps: int) -> int:
+    """Runs fn(i) for `steps` steps, then more until MIN_WARMUP_S of
+    device time has passed; returns the number of steps run."""
+    i = 0
+    t0 = time.perf_counter()
+    while i < steps:
+        fn(i)
+        i += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(50):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
 
 
 def stream_ceiling(torch, nbytes: int, steps: int, warmup: int, stream):
@@ -194,7 +218,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--workload", default=None,
@@ -258,9 +282,7 @@ def main(argv=None):
         call(ks[i % KV_COPIES], vs[i % KV_COPIES])
 
     log(f"[bench] plan {plan}")
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warmup_run = warm_up(torch, step, a.warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -271,6 +293,19 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
     log(f"[bench] timed {a.steps} steps: {ms * 1e3:.2f} us/step")
+
+    # Spread of the step time: BLOCKS more blocks of BLOCK_STEPS rotated
+    # steps, each between two HIP events; median and min of their means.
+    BLOCKS, BLOCK_STEPS = 10, 20
+    block_us = []
+    for blk in range(BLOCKS):
+        e0.record(stream)
+        for i in range(BLOCK_STEPS):
+            step(blk * BLOCK_STEPS + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        block_us.append(e0.elapsed_time(e1) / BLOCK_STEPS * 1e3)
+    block_us.sort()
 
     # Same-buffer ("hot") figure, labelled as such: repeats may hit MALL.
     e0.record(stream)
@@ -292,10 +327,9 @@ def main(argv=None):
             (plan["num_splits"], plan["chunk"], plan["grid"])
         ws = torch.zeros(pplan["workspace_bytes"], dtype=torch.uint8,
                          device="cuda")
-        for i in range(a.warmup):
-            fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
-                                  sl, w.scale, ws, stream=stream)
-        torch.cuda.synchronize()
+        warm_up(torch, lambda i: fd.fd_decode_partials(
+            q, ks[i % KV_COPIES], vs[i % KV_COPIES], sl, w.scale, ws,
+            stream=stream), a.warmup)
         e0.record(stream)
         for i in range(a.steps):
             fd.fd_decode_partials(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
@@ -361,7 +395,8 @@ def main(argv=None):
         }
     res = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "steps": a.steps, "warmup": a.warmup,
+        "warmup_steps_run": warmup_run, "ms_per_step": ms,
         "us_per_step": ms * 1e3, "frac_of_peak": gbs / PEAK_HBM_GBS,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype,
@@ -376,6 +411,11 @@ def main(argv=None):
                    "num_splits": plan["num_splits"], "chunk": plan["chunk"],
                    "grid": plan["grid"], "waves_per_block":
                    plan["waves_per_block"], "merge_pass": bool(plan["combine"])},
+        "step_spread": {"blocks": BLOCKS, "steps_per_block": BLOCK_STEPS,
+                        "median_us": block_us[BLOCKS // 2],
+                        "min_us": block_us[0], "max_us": block_us[-1],
+                        "note": "means of separately timed blocks of "
+                                "rotated steps, after the timed region"},
         "hot_same_buffer": {"us_per_step": ms_hot * 1e3,
                             "GBs": nbytes / (ms_hot * 1e-3) / 1e9,
                             "note": "one KV copy re-read every step; may be "
