@@ -504,26 +504,23 @@ struct TileRows<D, true> {
   }
 };
 
-// One 32-key tile of one wavefront.  TAIL tiles load only their first
-// `valid` rows (others re-read the last valid one and the V rows are
-// zeroed) and give keys at or beyond the lane's `lim` a score of -inf;
-// full tiles need neither.
+// One 32-key tile of one wavefront, in three parts: the K loads, the V
+// loads, and the math on both (mfma_tile runs them in that order; the
+// plain contiguous loop issues the next tile's K before this tile's math).
+// TAIL tiles load only their first `valid` rows (others re-read the last
+// valid one and the V rows are zeroed) and give keys at or beyond the
+// lane's `lim` a score of -inf; full tiles need neither.
 //
 // UNI (unified maximum): the exponentials are taken against the fixed
 // phi2 instead of the column's running maximum, so there is no
 // cross-lane maximum, no rescale of l and acc, and m only records the
 // lane's largest x = score - phi2 for the range check that follows the
 // chunk.
-template <int D, bool TAIL, bool UNI, typename Rows>
-__device__ __forceinline__ void mfma_tile(
-    const Rows &rows, int valid, int lim, int n16, int q4,
-    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
-    floatx4 (&acc)[D / 16], float &m, float &l) {
+template <int D, bool TAIL, typename Rows>
+__device__ __forceinline__ void tile_load_k(const Rows &rows, int valid,
+                                            int n16, int q4,
+                                            uint4 (&kr)[2][D / 32]) {
   constexpr int KK = D / 32;
-  constexpr int VW = D / 16;
-  typedef typename VecOf<VW>::type VT;
-
-  uint4 kr[2][KK];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     int r = sub * 16 + n16;
@@ -533,7 +530,14 @@ __device__ __forceinline__ void mfma_tile(
     for (int kk = 0; kk < KK; ++kk)
       kr[sub][kk] = load_stream(reinterpret_cast<const uint4 *>(p + kk * 32));
   }
-  VT vr[8];
+}
+
+template <int D, bool TAIL, typename Rows>
+__device__ __forceinline__ void tile_load_v(
+    const Rows &rows, int valid, int n16, int q4,
+    typename VecOf<D / 16>::type (&vr)[8]) {
+  constexpr int VW = D / 16;
+  typedef typename VecOf<VW>::type VT;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int r = (i >> 2) * 16 + q4 * 4 + (i & 3);
@@ -541,7 +545,17 @@ __device__ __forceinline__ void mfma_tile(
     vr[i] = load_stream(
         reinterpret_cast<const VT *>(rows.vrow(r) + n16 * VW));
   }
+}
 
+template <int D, bool TAIL, bool UNI, bool PAGED_ROWS>
+__device__ __forceinline__ void tile_compute(
+    const uint4 (&kr)[2][D / 32], typename VecOf<D / 16>::type (&vr)[8],
+    int valid, int lim, int n16, int q4, const bf16x8 (&qop)[D / 32],
+    float scale_log2, float phi2, floatx4 (&acc)[D / 16], float &m,
+    float &l) {
+  constexpr int KK = D / 32;
+  constexpr int VW = D / 16;
+  typedef typename VecOf<VW>::type VT;
   floatx4 sc[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -605,7 +619,7 @@ __device__ __forceinline__ void mfma_tile(
   // regrouping (which waits for every V load) above the softmax; keeping it
   // here lets the exponentials overlap the V loads, as the contiguous loop
   // does by itself.
-  if constexpr (Rows::kPaged || UNI) __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PAGED_ROWS || UNI) __builtin_amdgcn_sched_barrier(0);
   bf16x8 vt[VW];
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
@@ -631,6 +645,19 @@ __device__ __forceinline__ void mfma_tile(
                                                      0, 0);
 }
 
+template <int D, bool TAIL, bool UNI, typename Rows>
+__device__ __forceinline__ void mfma_tile(
+    const Rows &rows, int valid, int lim, int n16, int q4,
+    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
+    floatx4 (&acc)[D / 16], float &m, float &l) {
+  uint4 kr[2][D / 32];
+  typename VecOf<D / 16>::type vr[8];
+  tile_load_k<D, TAIL>(rows, valid, n16, q4, kr);
+  tile_load_v<D, TAIL>(rows, valid, n16, q4, vr);
+  tile_compute<D, TAIL, UNI, Rows::kPaged>(kr, vr, valid, lim, n16, q4, qop,
+                                           scale_log2, phi2, acc, m, l);
+}
+
 // Paged cache: for the first key of each 16-key half of this wavefront's
 // tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
 // of its D-element row of KV head g in the pool: (page * page_size + t) *
@@ -652,6 +679,16 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
                        : (pg * pk.page_size + off) * Hkv + w.g;
 }
 
+// The plain contiguous loop loads K one tile ahead (chunk_tiles below).
+template <bool PAGED, bool CAUSAL, bool UNI>
+constexpr bool kPrefetchK = !PAGED && !CAUSAL && !UNI;
+
+// Contiguous non-causal kernels (the prefetching loop and the unified
+// maximum's two loops) are held to two workgroups per CU: left free, the
+// compiler spends registers until only one wavefront fits per SIMD.
+template <bool PAGED, bool CAUSAL>
+constexpr int kMinBlocks = (!PAGED && !CAUSAL) ? 2 : 1;
+
 // The tiles of a chunk, wavefront `wave` taking tiles wave, wave + NW, ...
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
 __device__ __forceinline__ void chunk_tiles(
@@ -661,6 +698,48 @@ __device__ __forceinline__ void chunk_tiles(
     const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
     floatx4 (&acc)[D / 16], float &m, float &l) {
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
+  if constexpr (kPrefetchK<PAGED, CAUSAL, UNI>) {
+    // K of the next tile is loaded while this tile computes: per tile, V of
+    // this tile, then K of the next, then the math on this tile's K.  Every
+    // tile but a wavefront's last is full (only the chunk's last tile can
+    // be short); loads clamp rows to the valid count without branching.
+    int t = wave;
+    if (t >= ntiles) return;
+    TileRows<D, false> rows;
+    rows.k = kc + slab;
+    rows.v = vc + slab;
+    uint4 kr[2][D / 32];
+    rows.k0 = w.lo + t * kKeyTile;
+    tile_load_k<D, true>(rows, min(kKeyTile, w.hi - rows.k0), n16, q4, kr);
+    for (; t + NW < ntiles; t += NW) {
+      rows.k0 = w.lo + t * kKeyTile;
+      typename VecOf<D / 16>::type vr[8];
+      tile_load_v<D, false>(rows, kKeyTile, n16, q4, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      uint4 kn[2][D / 32];
+      TileRows<D, false> rn = rows;
+      rn.k0 = rows.k0 + NW * kKeyTile;
+      tile_load_k<D, true>(rn, min(kKeyTile, w.hi - rn.k0), n16, q4, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_compute<D, false, false, false>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                           qop, scale_log2, phi2, acc, m, l);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) kr[sub][kk] = kn[sub][kk];
+    }
+    rows.k0 = w.lo + t * kKeyTile;
+    const int valid = min(kKeyTile, w.hi - rows.k0);
+    typename VecOf<D / 16>::type vr[8];
+    tile_load_v<D, true>(rows, valid, n16, q4, vr);
+    if (valid == kKeyTile)
+      tile_compute<D, false, false, false>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                           qop, scale_log2, phi2, acc, m, l);
+    else
+      tile_compute<D, true, false, false>(kr, vr, valid, valid, n16, q4, qop,
+                                          scale_log2, phi2, acc, m, l);
+    return;
+  }
   int prow = 0;
   for (int t = wave, it = 0; t < ntiles; t += NW, ++it) {
     const int k0 = w.lo + t * kKeyTile;
@@ -795,7 +874,8 @@ __device__ __forceinline__ void wave_merge_store(
 // UNI: unified-maximum softmax against phi2 (log2 units of the scaled
 // score) with an exact fallback.
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
-__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, (kMinBlocks<PAGED, CAUSAL>))
+void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
