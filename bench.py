@@ -151,7 +151,8 @@ def cpu_baseline(w, budget_s: float):
     """fp64 oracle over the same workload on the host's cores: whole steps
     of the first batch entries whose K/V fit SAMPLE_KV_BYTES (all of them
     for the batch-1 workloads), repeated until ~budget_s of wall time (at
-    least one run); the rate is taken from the median run."""
+    least one run); the rate is taken from the median run.  A one-thread
+    time of the same sample (at most 3 runs or ~budget_s / 4) is added."""
     import numpy as np
     from long_context_decode_fd_amd import workloads as wl
     from oracle import oracle
@@ -172,25 +173,30 @@ def cpu_baseline(w, budget_s: float):
         kp, vp = wl.scatter_pages(ws, k, v, bt, seqlens)
         del k, v
 
-        def run():
-            oracle.decode_paged(q, kp, vp, bt, seqlens, w.scale,
-                                nthreads=cores)
+        def run(n):
+            oracle.decode_paged(q, kp, vp, bt, seqlens, w.scale, nthreads=n)
     elif w.Tq > 1:
-        def run():
-            oracle.decode_multiquery(q, k, v, seqlens, w.scale,
-                                     nthreads=cores)
+        def run(n):
+            oracle.decode_multiquery(q, k, v, seqlens, w.scale, nthreads=n)
     else:
-        def run():
-            oracle.decode(q, k, v, seqlens, w.scale, nthreads=cores)
-    times = []
-    t_total = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        run()
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_total >= budget_s or len(times) >= 1000:
-            break
+        def run(n):
+            oracle.decode(q, k, v, seqlens, w.scale, nthreads=n)
+
+    def timed(n, budget, max_runs):
+        ts = []
+        t_total = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            run(n)
+            ts.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_total >= budget or len(ts) >= max_runs:
+                return ts
+
+    times = timed(cores, budget_s, 1000)
     t = float(np.median(times))
+    # one thread as well (per-core figure), a few runs at most
+    times1 = timed(1, budget_s / 4, 3)
+    t1 = float(np.median(times1))
     nbytes = wl.algorithmic_bytes(ws, seqlens)
     model = ""
     try:
@@ -204,6 +210,8 @@ def cpu_baseline(w, budget_s: float):
     return {
         "value": nbytes / t / 1e9, "unit": "GB/s", "cores": cores,
         "kind": "oracle", "us_per_step": t * 1e6,
+        "one_thread": {"us_per_step": t1 * 1e6,
+                       "value": nbytes / t1 / 1e9, "runs": len(times1)},
         "sample": (f"{len(times)} run(s) over batch entries 0..{nb - 1} of "
                    f"{w.B} (all {w.Hq} query heads, same inputs as the GPU "
                    f"run), median wall time, rate = their algorithmic bytes "
