@@ -505,8 +505,8 @@ struct TileRows<D, true> {
 };
 
 // One 32-key tile of one wavefront, in three parts: the K loads, the V
-// loads, and the math on both (mfma_tile runs them in that order; the
-// plain contiguous loop issues the next tile's K before this tile's math).
+// loads, and the math on both (the tile loop issues the next tile's K
+// between this tile's V loads and its math).
 // TAIL tiles load only their first `valid` rows (others re-read the last
 // valid one and the V rows are zeroed) and give keys at or beyond the
 // lane's `lim` a score of -inf; full tiles need neither.
@@ -645,19 +645,6 @@ __device__ __forceinline__ void tile_compute(
                                                      0, 0);
 }
 
-template <int D, bool TAIL, bool UNI, typename Rows>
-__device__ __forceinline__ void mfma_tile(
-    const Rows &rows, int valid, int lim, int n16, int q4,
-    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
-    floatx4 (&acc)[D / 16], float &m, float &l) {
-  uint4 kr[2][D / 32];
-  typename VecOf<D / 16>::type vr[8];
-  tile_load_k<D, TAIL>(rows, valid, n16, q4, kr);
-  tile_load_v<D, TAIL>(rows, valid, n16, q4, vr);
-  tile_compute<D, TAIL, UNI, Rows::kPaged>(kr, vr, valid, lim, n16, q4, qop,
-                                           scale_log2, phi2, acc, m, l);
-}
-
 // Paged cache: for the first key of each 16-key half of this wavefront's
 // tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
 // of its D-element row of KV head g in the pool: (page * page_size + t) *
@@ -679,17 +666,47 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
                        : (pg * pk.page_size + off) * Hkv + w.g;
 }
 
-// The plain contiguous loop loads K one tile ahead (chunk_tiles below).
-template <bool PAGED, bool CAUSAL, bool UNI>
-constexpr bool kPrefetchK = !PAGED && !CAUSAL && !UNI;
+// Rows of the tile starting at key k0, wavefront iteration `it`: a slab
+// offset, or two page-resident halves read from the staged page rows
+// (restaged every 32 iterations).
+template <int D, int NW, bool PAGED>
+__device__ __forceinline__ TileRows<D, PAGED> tile_rows(
+    const PagedKV &pk, const Work &w, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
+    int wave, int lane, int k0, int it, int &prow) {
+  TileRows<D, PAGED> rows;
+  if constexpr (PAGED) {
+    const int slot = it & 31;
+    if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
+    const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
+    const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
+    rows.rs = prs;
+    rows.k0h = kc + (size_t)r0 * D;
+    rows.k1h = kc + (size_t)r1 * D;
+    rows.v0h = vc + (size_t)r0 * D;
+    rows.v1h = vc + (size_t)r1 * D;
+  } else {
+    rows.k = kc + slab;
+    rows.v = vc + slab;
+    rows.k0 = k0;
+  }
+  return rows;
+}
 
-// Contiguous non-causal kernels (the prefetching loop and the unified
-// maximum's two loops) are held to two workgroups per CU: left free, the
-// compiler spends registers until only one wavefront fits per SIMD.
-template <bool PAGED, bool CAUSAL>
-constexpr int kMinBlocks = (!PAGED && !CAUSAL) ? 2 : 1;
+// The per-chunk kernel is held to two workgroups per CU (one of eight
+// wavefronts): left free, the compiler spends the registers of the K tile
+// loaded ahead until only one wavefront fits per SIMD.
+template <int NW>
+constexpr int kBlocksPerCU = NW >= 8 ? 1 : 2;
 
 // The tiles of a chunk, wavefront `wave` taking tiles wave, wave + NW, ...
+// K of the next tile is loaded while this tile computes: per tile, V of
+// this tile, then K of the next, then the math on this tile's K.  Every
+// tile but a wavefront's last is full: only the chunk's last tile can be
+// short, and the causal limits of several new tokens (at most 15 keys
+// apart) cut into the chunk's last two tiles only, which with two or more
+// wavefronts are both some wavefront's last.  Loads clamp rows to the valid
+// count without branching.
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
 __device__ __forceinline__ void chunk_tiles(
     const Work &w, const PagedKV &pk, const uint16_t *__restrict__ kc,
@@ -697,83 +714,48 @@ __device__ __forceinline__ void chunk_tiles(
     int hi_all, int hi_col, int wave, int lane, int n16, int q4,
     const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
     floatx4 (&acc)[D / 16], float &m, float &l) {
+  static_assert(NW >= 2, "the loop relies on two or more wavefronts");
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
-  if constexpr (kPrefetchK<PAGED, CAUSAL, UNI>) {
-    // K of the next tile is loaded while this tile computes: per tile, V of
-    // this tile, then K of the next, then the math on this tile's K.  Every
-    // tile but a wavefront's last is full (only the chunk's last tile can
-    // be short); loads clamp rows to the valid count without branching.
-    int t = wave;
-    if (t >= ntiles) return;
-    TileRows<D, false> rows;
-    rows.k = kc + slab;
-    rows.v = vc + slab;
-    uint4 kr[2][D / 32];
-    rows.k0 = w.lo + t * kKeyTile;
-    tile_load_k<D, true>(rows, min(kKeyTile, w.hi - rows.k0), n16, q4, kr);
-    for (; t + NW < ntiles; t += NW) {
-      rows.k0 = w.lo + t * kKeyTile;
-      typename VecOf<D / 16>::type vr[8];
-      tile_load_v<D, false>(rows, kKeyTile, n16, q4, vr);
-      __builtin_amdgcn_sched_barrier(0);
-      uint4 kn[2][D / 32];
-      TileRows<D, false> rn = rows;
-      rn.k0 = rows.k0 + NW * kKeyTile;
-      tile_load_k<D, true>(rn, min(kKeyTile, w.hi - rn.k0), n16, q4, kn);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_compute<D, false, false, false>(kr, vr, kKeyTile, kKeyTile, n16, q4,
-                                           qop, scale_log2, phi2, acc, m, l);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) kr[sub][kk] = kn[sub][kk];
-    }
-    rows.k0 = w.lo + t * kKeyTile;
-    const int valid = min(kKeyTile, w.hi - rows.k0);
-    typename VecOf<D / 16>::type vr[8];
-    tile_load_v<D, true>(rows, valid, n16, q4, vr);
-    if (valid == kKeyTile)
-      tile_compute<D, false, false, false>(kr, vr, kKeyTile, kKeyTile, n16, q4,
-                                           qop, scale_log2, phi2, acc, m, l);
-    else
-      tile_compute<D, true, false, false>(kr, vr, valid, valid, n16, q4, qop,
-                                          scale_log2, phi2, acc, m, l);
-    return;
-  }
+  int t = wave;
+  if (t >= ntiles) return;
   int prow = 0;
-  for (int t = wave, it = 0; t < ntiles; t += NW, ++it) {
-    const int k0 = w.lo + t * kKeyTile;
-    TileRows<D, PAGED> rows;
-    if constexpr (PAGED) {
-      const int slot = it & 31;
-      if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
-      const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
-      const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
-      rows.rs = prs;
-      rows.k0h = kc + (size_t)r0 * D;
-      rows.k1h = kc + (size_t)r1 * D;
-      rows.v0h = vc + (size_t)r0 * D;
-      rows.v1h = vc + (size_t)r1 * D;
-    } else {
-      rows.k = kc + slab;
-      rows.v = vc + slab;
-      rows.k0 = k0;
-    }
-    const int valid = min(kKeyTile, w.hi - k0);
-    const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
-    // The unified-maximum loop takes one (masked) tile body: with a branch
-    // the compiler moves its accumulators out of the matrix-core registers
-    // and back on every tile.
-    if (UNI)
-      mfma_tile<D, true, UNI>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16,
-                              q4, qop, scale_log2, phi2, acc, m, l);
-    else if (full)
-      mfma_tile<D, false, UNI>(rows, kKeyTile, kKeyTile, n16, q4, qop,
-                               scale_log2, phi2, acc, m, l);
-    else
-      mfma_tile<D, true, UNI>(rows, valid, CAUSAL ? hi_col - k0 : valid, n16,
-                              q4, qop, scale_log2, phi2, acc, m, l);
+  TileRows<D, PAGED> cur =
+      tile_rows<D, NW, PAGED>(pk, w, kc, vc, slab, prs, Hkv, wave, lane,
+                              w.lo + t * kKeyTile, 0, prow);
+  uint4 kr[2][D / 32];
+  tile_load_k<D, true>(cur, min(kKeyTile, w.hi - (w.lo + t * kKeyTile)),
+                       n16, q4, kr);
+  int it = 0;
+  for (; t + NW < ntiles; t += NW, ++it) {
+    typename VecOf<D / 16>::type vr[8];
+    tile_load_v<D, false>(cur, kKeyTile, n16, q4, vr);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kn0 = w.lo + (t + NW) * kKeyTile;
+    TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
+        pk, w, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+    uint4 kn[2][D / 32];
+    tile_load_k<D, true>(nxt, min(kKeyTile, w.hi - kn0), n16, q4, kn);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                       qop, scale_log2, phi2, acc, m, l);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) kr[sub][kk] = kn[sub][kk];
+    cur = nxt;
   }
+  const int k0 = w.lo + t * kKeyTile;
+  const int valid = min(kKeyTile, w.hi - k0);
+  const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
+  typename VecOf<D / 16>::type vr[8];
+  tile_load_v<D, true>(cur, valid, n16, q4, vr);
+  if (full)
+    tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                       qop, scale_log2, phi2, acc, m, l);
+  else
+    tile_compute<D, true, UNI, PAGED>(kr, vr, valid,
+                                      CAUSAL ? hi_col - k0 : valid, n16, q4,
+                                      qop, scale_log2, phi2, acc, m, l);
 }
 
 // Unified maximum: a chunk column whose largest score - phi lies outside
@@ -874,7 +856,7 @@ __device__ __forceinline__ void wave_merge_store(
 // UNI: unified-maximum softmax against phi2 (log2 units of the scaled
 // score) with an exact fallback.
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
-__global__ __launch_bounds__(NW * 64, (kMinBlocks<PAGED, CAUSAL>))
+__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
 void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
@@ -1316,7 +1298,6 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
                        a.lse_part, a.tickets);                               \
     break;
   switch (p.waves) {
-    FD_MFMA_CASE(1)
     FD_MFMA_CASE(2)
     FD_MFMA_CASE(4)
     FD_MFMA_CASE(8)

@@ -52,6 +52,8 @@ constexpr int kBlocksPerCU = FD_BLOCKS_PER_CU;
 constexpr int kMinChunk = FD_MIN_CHUNK;
 constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
 constexpr int kMfmaWaves = FD_MFMA_WAVES;
+static_assert(kMfmaWaves == 2 || kMfmaWaves == 4 || kMfmaWaves == 8,
+              "the matrix-core kernel is built for 2, 4 or 8 wavefronts");
 constexpr int kValuWaves = 4;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
