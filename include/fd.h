@@ -117,8 +117,11 @@ typedef struct fd_plan {
     int chunk;           /* keys per chunk (C), a multiple of 32 */
     int variant;         /* FD_VARIANT_MFMA or FD_VARIANT_VALU */
     int waves_per_block; /* 64-lane wavefronts per workgroup */
-    int grid;            /* workgroups of the per-chunk pass (upper bound
-                            when seqlens is given) */
+    int grid;            /* workgroups of the per-chunk pass; with seqlens
+                            the chunk count is an upper bound, and the
+                            matrix-core pass launches max(half of it, 8
+                            per CU), workgroup i taking chunks i and
+                            i + grid */
     int combine;         /* 1 if chunks leave partials to be merged */
     int merge;           /* FD_MERGE_NONE / _FUSED / _SEPARATE */
     int num_cus;         /* compute units the plan was sized for */

@@ -96,10 +96,14 @@ __device__ __forceinline__ int chunks_of(int L, int C) {
   return max(1, (L + C - 1) / C);
 }
 
-// Workgroup id -> (b, g, s).  Ids run over the chunks that exist, sequence
-// by sequence, chunk-major, KV head fastest: id = (prefix_b + s) * Hkv + g.
-// With per-sequence lengths the prefix over sequences is a wavefront scan
-// of the seqlens (every wavefront does it; it is a few dozen instructions).
+// Work id -> (b, g, s).  Equal lengths: ids run over the chunks sequence by
+// sequence, chunk-major, KV head fastest: id = (b * S + s) * Hkv + g.
+// Per-sequence lengths: first every full chunk (C keys) in that order, then
+// each sequence's short last chunk, longest first (ties by sequence), so
+// that the chunks dispatched last are the shortest; the prefix over the
+// sequences is a wavefront scan of the seqlens (a few dozen instructions
+// per wavefront), and the ranking of the last chunks a loop over the
+// wavefront's 64 lanes (sequences beyond 64 keep their natural order).
 __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
                           int Hkv, int Lmax, int C) {
   Work w;
@@ -122,13 +126,14 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
     return w;
   }
   const int lane = threadIdx.x & 63;
+  // Pass 1: the full chunks (C keys), sequence by sequence.
   int base = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
     int L = 0, blocks = 0;
     if (b < B) {
       L = clamp_len(seqlens[b], Lmax);
-      blocks = chunks_of(L, C) * Hkv;
+      blocks = (L / C) * Hkv;
     }
     int incl = blocks;
 #pragma unroll
@@ -147,13 +152,56 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
       w.s = r / Hkv;
       w.g = r - w.s * Hkv;
       w.lo = w.s * C;
-      w.hi = max(w.lo, min(w.lo + C, Lb));
+      w.hi = w.lo + C;
       w.L = Lb;
       w.nb = chunks_of(Lb, C);
       w.valid = true;
       return w;
     }
     base += total;
+  }
+  // Pass 2: each sequence's last chunk when it is short (or the empty chunk
+  // of a length-0 sequence), longest first, so the work dispatched last is
+  // the shortest.
+  const int r = bid - base;
+  const int j = r / Hkv;
+  for (int b0 = 0, done = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    int L = 0, rem = 0;
+    bool has = false;
+    if (b < B) {
+      L = clamp_len(seqlens[b], Lmax);
+      rem = L % C;
+      has = rem != 0 || L == 0;
+    }
+    const unsigned long long hv = __ballot(has);
+    const int cnt = __popcll(hv);
+    if (j < done + cnt) {
+      int rank = 0;  // among this batch's last chunks: longer first, then b
+      if (B <= 64) {
+#pragma unroll 8
+        for (int o = 0; o < 64; ++o) {
+          const int ro = __shfl(rem, o, 64);
+          const bool ho = (hv >> o) & 1ull;
+          rank += (ho && (ro > rem || (ro == rem && o < lane))) ? 1 : 0;
+        }
+      } else {
+        rank = __popcll(hv & ((1ull << lane) - 1ull));
+      }
+      const unsigned long long hit = __ballot(has && rank == j - done);
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int Lb = __shfl(L, src, 64);
+      w.b = b0 + src;
+      w.s = Lb / C;
+      w.g = r - j * Hkv;
+      w.lo = w.s * C;
+      w.hi = Lb;
+      w.L = Lb;
+      w.nb = chunks_of(Lb, C);
+      w.valid = true;
+      return w;
+    }
+    done += cnt;
   }
   return w;
 }
@@ -850,15 +898,16 @@ __device__ __forceinline__ void wave_merge_store(
   }
 }
 
-// PAGED: K/V in a page pool behind a block table.  CAUSAL: Tq > 1 new
-// tokens per sequence, each column with its own key limit (a separate
-// instantiation keeps the single-token loop exactly as simple as before).
+// One chunk of the matrix-core per-chunk pass (the kernel below runs one or
+// two).  PAGED: K/V in a page pool behind a block table.  CAUSAL:
+// Tq > 1 new tokens per sequence, each column with its own key limit (a
+// separate instantiation keeps the single-token loop exactly as simple as
+// before).
 // UNI: unified-maximum softmax against phi2 (log2 units of the scaled
 // score) with an exact fallback.
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
-__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
-void split_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+__device__ __forceinline__ void chunk_pass(
+    const Work &w, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
     float scale_log2, float phi2, int mode, uint16_t *__restrict__ out,
@@ -872,8 +921,6 @@ void split_mfma_kernel(
   __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
   __shared__ int sm_flag;
 
-  const Work w = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
-  if (!w.valid) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int ncol = G * Tq;
@@ -959,6 +1006,38 @@ void split_mfma_kernel(
   if (mode == kModeFused)
     merge_group_if_last<D, uint16_t>(w, G, Tq, Hq, Hkv, S, o_part, lse_part,
                                      tickets, out, lse, sm_o, &sm_flag);
+}
+
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
+__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
+void split_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
+    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
+    float scale_log2, float phi2, int mode, uint16_t *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ o_part,
+    float *__restrict__ lse_part, int *__restrict__ tickets) {
+  // With per-sequence lengths the grid can be as small as half the work
+  // list's upper bound: workgroup i takes chunk i and then, if it exists,
+  // chunk i + gridDim.x.  (Written out twice rather than as a loop: around
+  // a loop the compiler keeps lane offsets live through the tile loop and
+  // spills.)
+  const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
+  if (!w0.valid) return;
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w0, q, kc, vc, seqlens, pk, B, Hq,
+                                        Hkv, G, Tq, Lmax, C, S, scale_log2,
+                                        phi2, mode, out, lse, o_part,
+                                        lse_part, tickets);
+  // Equal lengths, or a grid that covers the upper bound: one chunk each.
+  const long id1 = (long)blockIdx.x + gridDim.x;
+  if (seqlens == nullptr || id1 >= (long)B * Hkv * S) return;
+  const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C);
+  if (!w1.valid) return;
+  __syncthreads();  // the second chunk reuses the LDS
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w1, q, kc, vc, seqlens, pk, B, Hq,
+                                        Hkv, G, Tq, Lmax, C, S, scale_log2,
+                                        phi2, mode, out, lse, o_part,
+                                        lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------

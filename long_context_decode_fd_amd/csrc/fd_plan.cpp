@@ -51,6 +51,7 @@ namespace {
 constexpr int kBlocksPerCU = FD_BLOCKS_PER_CU;
 constexpr int kMinChunk = FD_MIN_CHUNK;
 constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
+constexpr int kGridPerCU = 8;
 constexpr int kMfmaWaves = FD_MFMA_WAVES;
 static_assert(kMfmaWaves == 2 || kMfmaWaves == 4 || kMfmaWaves == 8,
               "the matrix-core kernel is built for 2, 4 or 8 wavefronts");
@@ -169,6 +170,13 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.fused = q.combine && (flags & FD_FLAG_FUSED_MERGE);
   long grid = (long)B * Hkv * q.splits;
   if (grid > 0x7FFFFFFFL) return FD_ERR_UNSUPPORTED;
+  // Per-sequence lengths: the chunk count is only an upper bound (every
+  // sequence at Lmax), and each workgroup of the matrix-core kernel can take
+  // two chunks, so launch max(half the bound, kGridPerCU per CU): enough for
+  // the hardware to deal typical batches one chunk per workgroup, with
+  // fewer empty workgroups at the end of the dispatch.
+  if (varlen && q.variant == FD_VARIANT_MFMA)
+    grid = std::min(grid, std::max((grid + 1) / 2, (long)num_cus * kGridPerCU));
   q.grid = (int)grid;
   q.ws_bytes = workspace_layout(q).total;
   *p = q;
