@@ -11,11 +11,14 @@
 // possible.
 //
 // MI355X mapping (our own design; the page's kernel targets A100):
-//   * one workgroup per (sequence b, KV head g, chunk s); it serves all
-//     G = Hq / Hkv query heads of KV head g, so each K/V byte leaves HBM
-//     once;
+//   * one workgroup per (sequence b, KV head g, chunk s) -- with
+//     per-sequence lengths a workgroup may take a second chunk, and the
+//     chunk list puts each sequence's short last chunk after every full
+//     one; a workgroup serves all G = Hq / Hkv query heads of KV head g,
+//     so each K/V byte leaves HBM once;
 //   * bf16: each 64-lane wavefront streams 32-key tiles straight from HBM
-//     into registers in the operand layout of v_mfma_f32_16x16x32_bf16 and
+//     into registers in the operand layout of v_mfma_f32_16x16x32_bf16,
+//     the next tile's K in flight while the current tile computes, and
 //     computes S^T = K Q^T (16 keys x 16 padded heads per MFMA) and
 //     O^T += V^T P^T; the accumulator's column is the query head, so each
 //     lane rescales only its own head's accumulators;

@@ -21,8 +21,11 @@
 //   * with per-sequence lengths the mix is unknown on the host (the library
 //     never reads device memory synchronously), so chunks are also capped
 //     at kVarlenChunk keys, so that no single long sequence sets the finish
-//     time.  A paged cache always comes with per-sequence lengths; its
-//     Lmax is the block table's capacity, max_pages * page_size.
+//     time, and the grid is cut to max(half the chunk count's upper bound,
+//     kGridPerCU per CU): the matrix-core kernel lets a workgroup take a
+//     second chunk, and most of the bound is usually empty.  A paged cache
+//     always comes with per-sequence lengths; its Lmax is the block table's
+//     capacity, max_pages * page_size.
 //
 // The constants are this library's own (the pages give none) and the
 // result of any plan is the same attention; only speed depends on them.
