@@ -1208,16 +1208,19 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge pass (the default): one workgroup of kMergeWaves wavefronts per
-// query row (b, token, head); wavefront w folds chunks w, w + kMergeWaves, ...
-// into a running (M, W, acc) kMergeBatch chunks at a time, all of a batch's
-// loads issued before any is used (the pass is latency-bound: a few MB).
+// Merge pass (the default): for every query row (b, token, head),
+// workgroups of MW wavefronts, one per block of 64 * CPL output columns;
+// wavefront w folds chunks w, w + MW, ... into a running (M, W, acc), MB
+// chunks at a time, all of a batch's loads issued before any is used (the
+// pass is latency-bound: a few MB).
 // Per batch: M' = max(M, max_s lse_s), r = e^(M - M'),
 //   W = r W + sum_s e^(lse_s - M'),  acc = r acc + sum_s e^(lse_s - M') o_s.
 // The wavefronts then meet in LDS the same way; out = acc / W and
 // lse = M + ln W.  Fixed order everywhere: same chunking, same bits.
-constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 16;
+// Two shapes (launch_combine): fewer rows than CUs (batch 1: 64 rows) get
+// D / 64 workgroups of eight wavefronts per row, one column per lane and
+// eight chunks in flight per wavefront; many rows get one workgroup of four
+// wavefronts per row, D / 64 columns per lane, sixteen chunks in flight.
 
 // Workgroups are dealt to MI355X's eight XCDs round robin (id % 8).  When
 // Hkv is a multiple of 8, every chunk of kv-head g ran on XCD g % 8 (the
@@ -1232,51 +1235,53 @@ __device__ __forceinline__ int merge_row(int id, int G, int Hkv) {
   return (bt * Hkv + 8 * g1 + x) * G + hh;
 }
 
-template <int D, typename OutT>
-__global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
+template <int D, typename OutT, int CPL, int MW, int MB>
+__global__ __launch_bounds__(MW * 64) void combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
     const int32_t *__restrict__ seqlens, int rows_per_b, int G, int Hkv,
     int Lmax, int C, int S, OutT *__restrict__ out,
     float *__restrict__ lse) {
-  constexpr int DPL = D / 64;  // output columns per lane
-  __shared__ float sm_M[kMergeWaves], sm_W[kMergeWaves];
-  __shared__ float sm_acc[kMergeWaves][D];
+  constexpr int COLS = 64 * CPL;  // output columns of this workgroup
+  static_assert(D % COLS == 0, "column blocks tile the head dimension");
+  __shared__ float sm_M[MW], sm_W[MW];
+  __shared__ float sm_acc[MW][COLS];
   const int row = merge_row(blockIdx.x, G, Hkv);
+  const int c0 = blockIdx.y * COLS;
   const int b = row / rows_per_b;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
   const int nb = min(S, chunks_of(L, C));
   const float *lp = lse_part + (size_t)row * S;
-  const float *op = o_part + (size_t)row * S * D + lane * DPL;
+  const float *op = o_part + (size_t)row * S * D + c0 + lane * CPL;
 
-  float M = FD_NEG_INF, W = 0.f, acc[DPL];
+  float M = FD_NEG_INF, W = 0.f, acc[CPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  for (int s0 = wave; s0 < nb; s0 += kMergeWaves * kMergeBatch) {
-    float ls[kMergeBatch], ov[kMergeBatch][DPL];
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+  for (int s0 = wave; s0 < nb; s0 += MW * MB) {
+    float ls[MB], ov[MB][CPL];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int s = s0 + j * kMergeWaves;
+    for (int j = 0; j < MB; ++j) {
+      const int s = s0 + j * MW;
       const int sc = s < nb ? s : s0;
       ls[j] = s < nb ? lp[sc] : FD_NEG_INF;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) ov[j][i] = op[(size_t)sc * D + i];
+      for (int i = 0; i < CPL; ++i) ov[j][i] = op[(size_t)sc * D + i];
     }
     float mb = ls[0];
 #pragma unroll
-    for (int j = 1; j < kMergeBatch; ++j) mb = fmaxf(mb, ls[j]);
+    for (int j = 1; j < MB; ++j) mb = fmaxf(mb, ls[j]);
     const float Mn = fmaxf(M, mb);
     if (Mn == FD_NEG_INF) continue;
     const float r = exp2_f((M - Mn) * kLog2e);
     W *= r;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] *= r;
+    for (int i = 0; i < CPL; ++i) acc[i] *= r;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
+    for (int j = 0; j < MB; ++j) {
       const float wt = exp2_f((ls[j] - Mn) * kLog2e);
       W += wt;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] += wt * ov[j][i];
+      for (int i = 0; i < CPL; ++i) acc[i] += wt * ov[j][i];
     }
     M = Mn;
   }
@@ -1285,17 +1290,17 @@ __global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
     sm_W[wave] = W;
   }
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) sm_acc[wave][lane * DPL + i] = acc[i];
+  for (int i = 0; i < CPL; ++i) sm_acc[wave][lane * CPL + i] = acc[i];
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  for (int d = threadIdx.x; d < COLS; d += blockDim.x) {
     float Mt = FD_NEG_INF;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sm_M[w]);
+    for (int w = 0; w < MW; ++w) Mt = fmaxf(Mt, sm_M[w]);
     float o = 0.f, ls_out = FD_NEG_INF;
     if (Mt != FD_NEG_INF) {
       float Wt = 0.f, a = 0.f;
 #pragma unroll
-      for (int w = 0; w < kMergeWaves; ++w) {
+      for (int w = 0; w < MW; ++w) {
         const float r = exp2_f((sm_M[w] - Mt) * kLog2e);
         Wt += r * sm_W[w];
         a += r * sm_acc[w][d];
@@ -1303,8 +1308,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void combine_kernel(
       o = a / Wt;
       ls_out = Mt + log2_f(Wt) * kLn2;
     }
-    store_out<OutT>(out + (size_t)row * D + d, o);
-    if (d == 0) lse[row] = ls_out;
+    store_out<OutT>(out + (size_t)row * D + c0 + d, o);
+    if (c0 + d == 0) lse[row] = ls_out;
   }
 }
 
@@ -1392,10 +1397,17 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
 
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<D, OutT>), dim3(p.B * p.Tq * p.Hq),
-                     dim3(kMergeWaves * 64), 0, st, a.o_part, a.lse_part,
-                     a.seqlens, p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk,
-                     p.splits, static_cast<OutT *>(a.out), a.lse);
+  const int rows = p.B * p.Tq * p.Hq;
+  if (rows < p.num_cus)
+    hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 8, 8>), dim3(rows, D / 64),
+                       dim3(8 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
+                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
+                       static_cast<OutT *>(a.out), a.lse);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, OutT, D / 64, 4, 16>), dim3(rows),
+                       dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
+                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
+                       static_cast<OutT *>(a.out), a.lse);
 }
 
 }  // namespace
