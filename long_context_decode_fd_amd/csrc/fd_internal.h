@@ -29,6 +29,7 @@ struct Plan {
   int chunk;        // keys per chunk (multiple of kKeyTile)
   int splits;       // ceil(Lmax / chunk)
   int grid;         // workgroups of the per-chunk pass (upper bound)
+  bool direct;      // with seqlens: chunk ids map straight to (b, s, g)
   bool combine;     // chunks leave partials to be merged (splits > 1)
   bool fused;       // merged by the last workgroup of each group
   size_t ws_bytes;  // tickets + partial outputs + partial lse

@@ -99,33 +99,38 @@ __device__ __forceinline__ int chunks_of(int L, int C) {
   return max(1, (L + C - 1) / C);
 }
 
-// Work id -> (b, g, s).  Equal lengths: ids run over the chunks sequence by
-// sequence, chunk-major, KV head fastest: id = (b * S + s) * Hkv + g.
-// Per-sequence lengths: first every full chunk (C keys) in that order, then
+// Work id -> (b, g, s).  Equal lengths, or a grid that covers every chunk
+// id any lengths could need (direct): ids run over the chunks sequence by
+// sequence, chunk-major, KV head fastest: id = (b * S + s) * Hkv + g, and
+// only seqlens[b] is read (one load with a workgroup-uniform address; ids
+// past the sequence's chunks do nothing).
+// Otherwise (per-sequence lengths, smaller grid): first every full chunk
+// (C keys) in that order, then
 // each sequence's short last chunk, longest first (ties by sequence), so
 // that the chunks dispatched last are the shortest; the prefix over the
 // sequences is a wavefront scan of the seqlens (a few dozen instructions
 // per wavefront), and the ranking of the last chunks a loop over the
 // wavefront's 64 lanes (sequences beyond 64 keep their natural order).
 __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
-                          int Hkv, int Lmax, int C) {
+                          int Hkv, int Lmax, int C, bool direct) {
   Work w;
   w.valid = false;
   w.b = w.g = w.s = w.lo = w.hi = w.L = w.nb = 0;
-  if (seqlens == nullptr) {
+  if (seqlens == nullptr || direct) {
     const int S = (Lmax + C - 1) / C;
     const int per_b = S * Hkv;
     const int b = bid / per_b;
     if (b >= B) return w;
     const int r = bid - b * per_b;
+    const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
     w.b = b;
     w.s = r / Hkv;
     w.g = r - w.s * Hkv;
     w.lo = w.s * C;
-    w.hi = min(w.lo + C, Lmax);
-    w.L = Lmax;
-    w.nb = S;
-    w.valid = true;
+    w.hi = max(w.lo, min(w.lo + C, L));
+    w.L = L;
+    w.nb = chunks_of(L, C);
+    w.valid = w.s < w.nb;
     return w;
   }
   const int lane = threadIdx.x & 63;
@@ -1017,7 +1022,8 @@ void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, float phi2, int mode, uint16_t *__restrict__ out,
+    float scale_log2, float phi2, int mode, bool direct,
+    uint16_t *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
   // With per-sequence lengths the grid can be as small as half the work
@@ -1025,7 +1031,7 @@ void split_mfma_kernel(
   // chunk i + gridDim.x.  (Written out twice rather than as a loop: around
   // a loop the compiler keeps lane offsets live through the tile loop and
   // spills.)
-  const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
+  const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w0, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, G, Tq, Lmax, C, S, scale_log2,
@@ -1034,7 +1040,7 @@ void split_mfma_kernel(
   // Equal lengths, or a grid that covers the upper bound: one chunk each.
   const long id1 = (long)blockIdx.x + gridDim.x;
   if (seqlens == nullptr || id1 >= (long)B * Hkv * S) return;
-  const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C);
+  const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w1, q, kc, vc, seqlens, pk, B, Hq,
@@ -1100,7 +1106,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
       sm_o[kMergeFloats > kTailFloats ? kMergeFloats : kTailFloats];
   __shared__ int sm_flag;
 
-  const Work w = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C);
+  const Work w = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, false);
   if (!w.valid) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane % LPR, rg = lane / LPR;
@@ -1381,8 +1387,8 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
     hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI>), grid,\
                        dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
                        p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk,         \
-                       p.splits, sl2, phi2, part, out, a.lse, a.o_part,      \
-                       a.lse_part, a.tickets);                               \
+                       p.splits, sl2, phi2, part, p.direct, out, a.lse,      \
+                       a.o_part, a.lse_part, a.tickets);                     \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(2)

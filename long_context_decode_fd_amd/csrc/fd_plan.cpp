@@ -178,6 +178,12 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   // two chunks, so launch max(half the bound, kGridPerCU per CU): enough for
   // the hardware to deal typical batches one chunk per workgroup, with
   // fewer empty workgroups at the end of the dispatch.
+  // When every chunk id any lengths could need fits in one round of
+  // workgroups, the matrix-core kernel maps ids straight to (b, s, g) and
+  // reads only its own sequence's length: no work list to build, and no
+  // order to keep, since all chunks run at once.
+  q.direct = varlen && q.variant == FD_VARIANT_MFMA &&
+             grid <= (long)num_cus * kBlocksPerCU;
   if (varlen && q.variant == FD_VARIANT_MFMA)
     grid = std::min(grid, std::max((grid + 1) / 2, (long)num_cus * kGridPerCU));
   q.grid = (int)grid;
