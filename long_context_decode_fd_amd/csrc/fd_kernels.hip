@@ -722,6 +722,60 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
                        : (pg * pk.page_size + off) * Hkv + w.g;
 }
 
+// Paged caches (D = 128): K of a tile goes through LDS.  With a head's rows
+// apart in memory (2 KB apart token-major), K loads in the matrix-core
+// operand layout -- each instruction reading 64 bytes of 16 rows -- stream
+// markedly slower than loads of whole rows, so the paged loop loads K as
+// whole rows (every 16 lanes one 256-byte row, 4 rows per instruction),
+// writes them to the wavefront's LDS buffer and reads the operand layout
+// back.  A contiguous cache streams either way at the same rate, and the
+// extra LDS round trip makes it slower, so it keeps the direct loads.
+template <int D, bool PAGED>
+constexpr bool kStageK = PAGED && D == 128;
+
+// K of a 32-key tile as whole rows: register i of lane l holds 16 bytes,
+// chunk l % 16, of row 4 i + l / 16.  Rows at or beyond `valid` re-read the
+// last valid row.
+template <typename Rows>
+__device__ __forceinline__ void load_k_rows(const Rows &rows, int valid,
+                                            int lane, uint4 (&kn)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = min(4 * i + (lane >> 4), valid - 1);
+    kn[i] = load_stream(
+        reinterpret_cast<const uint4 *>(rows.krow(r) + (lane & 15) * 8));
+  }
+}
+
+// The rows into the wavefront's LDS buffer (32 rows x 256 bytes), 16-byte
+// chunks XOR-swizzled by row (slot = chunk ^ (row % 16)) so that the operand
+// reads below hit distinct banks.
+__device__ __forceinline__ void store_k_lds(const uint4 (&kn)[8], int lane,
+                                            uint16_t *kbuf) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int slot = (lane & 15) ^ (r & 15);
+    *reinterpret_cast<uint4 *>(kbuf + i * 512 + ((r & 3) * 16 + slot) * 8) =
+        kn[i];
+  }
+}
+
+// The operand layout from the LDS buffer: lane (n16, q4) takes row
+// sub * 16 + n16, chunk kk * 4 + q4.
+__device__ __forceinline__ void load_k_operand(const uint16_t *kbuf, int n16,
+                                               int q4, uint4 (&kr)[2][4]) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r = sub * 16 + n16;
+      const int slot = (kk * 4 + q4) ^ n16;
+      kr[sub][kk] = *reinterpret_cast<const uint4 *>(
+          kbuf + (r >> 2) * 512 + ((r & 3) * 16 + slot) * 8);
+    }
+}
+
 // Rows of the tile starting at key k0, wavefront iteration `it`: a slab
 // offset, or two page-resident halves read from the staged page rows
 // (restaged every 32 iterations).
@@ -769,11 +823,52 @@ __device__ __forceinline__ void chunk_tiles(
     const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
     int hi_all, int hi_col, int wave, int lane, int n16, int q4,
     const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
-    floatx4 (&acc)[D / 16], float &m, float &l) {
+    floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf) {
   static_assert(NW >= 2, "the loop relies on two or more wavefronts");
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
   int t = wave;
   if (t >= ntiles) return;
+  if constexpr (kStageK<D, PAGED>) {
+    // The same loop with K staged through LDS: the rows of the next tile
+    // are in flight while this tile is staged, read back and computed.
+    int prow = 0;
+    TileRows<D, PAGED> cur =
+        tile_rows<D, NW, PAGED>(pk, w, kc, vc, slab, prs, Hkv, wave, lane,
+                                w.lo + t * kKeyTile, 0, prow);
+    uint4 kn[8];
+    load_k_rows(cur, min(kKeyTile, w.hi - (w.lo + t * kKeyTile)), lane, kn);
+    uint4 kr[2][4];
+    int it = 0;
+    for (; t + NW < ntiles; t += NW, ++it) {
+      store_k_lds(kn, lane, kbuf);
+      typename VecOf<D / 16>::type vr[8];
+      tile_load_v<D, false>(cur, kKeyTile, n16, q4, vr);
+      const int kn0 = w.lo + (t + NW) * kKeyTile;
+      TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
+          pk, w, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+      load_k_rows(nxt, min(kKeyTile, w.hi - kn0), lane, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k_operand(kbuf, n16, q4, kr);
+      tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                         qop, scale_log2, phi2, acc, m, l);
+      cur = nxt;
+    }
+    const int k0 = w.lo + t * kKeyTile;
+    const int valid = min(kKeyTile, w.hi - k0);
+    const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
+    store_k_lds(kn, lane, kbuf);
+    typename VecOf<D / 16>::type vr[8];
+    tile_load_v<D, true>(cur, valid, n16, q4, vr);
+    load_k_operand(kbuf, n16, q4, kr);
+    if (full)
+      tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+                                         qop, scale_log2, phi2, acc, m, l);
+    else
+      tile_compute<D, true, UNI, PAGED>(kr, vr, valid,
+                                        CAUSAL ? hi_col - k0 : valid, n16, q4,
+                                        qop, scale_log2, phi2, acc, m, l);
+    return;
+  }
   int prow = 0;
   TileRows<D, PAGED> cur =
       tile_rows<D, NW, PAGED>(pk, w, kc, vc, slab, prs, Hkv, wave, lane,
@@ -928,8 +1023,11 @@ __device__ __forceinline__ void chunk_pass(
   __shared__ float sm_l[NW * 16];
   __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
   __shared__ int sm_flag;
+  constexpr int kStageElems = kStageK<D, PAGED> ? 32 * D : 8;
+  __shared__ __align__(16) uint16_t sm_k[NW * kStageElems];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint16_t *kbuf = sm_k + wave * kStageElems;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int ncol = G * Tq;
 
@@ -966,7 +1064,7 @@ __device__ __forceinline__ void chunk_pass(
     chunk_tiles<D, NW, PAGED, CAUSAL, true>(w, pk, kc, vc, slab, prs, Hkv,
                                             hi_all, hi_col, wave, lane, n16,
                                             q4, qop, scale_log2, phi2, acc,
-                                            m, l);
+                                            m, l, kbuf);
     float xm = fmaxf(m, __shfl_xor(m, 16, 64));
     xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
     const bool bad = xm != FD_NEG_INF && !(xm >= -kUniRange && xm <= kUniRange);
@@ -978,7 +1076,7 @@ __device__ __forceinline__ void chunk_pass(
       chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
                                                hi_all, hi_col, wave, lane,
                                                n16, q4, qop, scale_log2, 0.f,
-                                               acc, m, l);
+                                               acc, m, l, kbuf);
     } else {
       m = xm == FD_NEG_INF ? FD_NEG_INF : phi2;
     }
@@ -986,7 +1084,7 @@ __device__ __forceinline__ void chunk_pass(
     chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
                                              hi_all, hi_col, wave, lane, n16,
                                              q4, qop, scale_log2, 0.f, acc, m,
-                                             l);
+                                             l, kbuf);
   }
 
   l += __shfl_xor(l, 16, 64);
