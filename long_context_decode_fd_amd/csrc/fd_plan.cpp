@@ -40,7 +40,7 @@ namespace {
 
 // Tunables (measured on MI355X; overridable at build time for sweeps).
 #ifndef FD_BLOCKS_PER_CU
-#define FD_BLOCKS_PER_CU 2
+#define FD_BLOCKS_PER_CU 1
 #endif
 #ifndef FD_MIN_CHUNK
 #define FD_MIN_CHUNK 256

@@ -152,20 +152,21 @@ def plan(w, varlen=None, **kw):
 
 def test_plans_for_the_five_workloads_on_256_cus(lib):
     W = wl.WORKLOADS
-    # batch 1, 64k, 8 KV heads: 8 units -> 64 chunks of 1024 keys, 512 WGs
+    # batch 1, 64k, 8 KV heads: 8 units -> 32 chunks of 2048 keys, one
+    # workgroup per CU
     p = plan(W["b1_gqa8_h64_d128_l65536"])
     assert (p["num_splits"], p["chunk"], p["grid"], p["combine"]) == \
-        (64, 1024, 512, 1)
+        (32, 2048, 256, 1)
     assert p["variant"] == fd.FD_VARIANT_MFMA
     assert p["merge"] == fd.FD_MERGE_SEPARATE and p["ticket_bytes"] == 0
-    assert p["workspace_bytes"] == 64 * 64 * 128 * 4 + 64 * 64 * 4
+    assert p["workspace_bytes"] == 64 * 32 * 128 * 4 + 64 * 32 * 4
     p = plan(W["b1_gqa8_h64_d128_l65536"], flags=fd.FD_FLAG_FUSED_MERGE)
     assert p["merge"] == fd.FD_MERGE_FUSED
     assert p["ticket_bytes"] == 256          # 8 int32 tickets, aligned
-    assert p["workspace_bytes"] == 256 + 64 * 64 * 128 * 4 + 64 * 64 * 4
-    # 4 x 32 MHA heads at 32k: 128 units -> 4 chunks of 8192
+    assert p["workspace_bytes"] == 256 + 64 * 32 * 128 * 4 + 64 * 32 * 4
+    # 4 x 32 MHA heads at 32k: 128 units -> 2 chunks of 16384
     p = plan(W["b4_mha_h32_d128_l32768_peaked"])
-    assert (p["num_splits"], p["chunk"], p["grid"]) == (4, 8192, 512)
+    assert (p["num_splits"], p["chunk"], p["grid"]) == (2, 16384, 256)
     # 64 x 8 units already fill the chip: no split, no merge, no workspace
     p = plan(W["b64_gqa4_h32_d128_l4096"])
     assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == (1, 0, 0)
@@ -303,11 +304,14 @@ def test_plan_ex_for_several_tokens_and_pages(lib):
     rows = w.B * 2 * w.Hq * p2["num_splits"]
     assert p2["lse_part_offset"] == rows * w.D * 4
     assert p2["workspace_bytes"] == rows * w.D * 4 + rows * 4
-    # paged: per-sequence lengths are implied; the even split still
-    # applies when it is finer than the var-len cap
+    # paged: per-sequence lengths are implied; the even split (here 2048
+    # keys, equal to the var-len cap) still applies when it is finer
     pp = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D, w.Lmax, "bf16", paged=True,
                        num_cus=256)
-    assert (pp["chunk"], pp["num_splits"]) == (1024, 64)
+    assert (pp["chunk"], pp["num_splits"]) == (2048, 32)
+    pp = fd.fd_plan_ex(w.B, 1, w.Hq, w.Hkv, w.D, 32768, "bf16", paged=True,
+                       num_cus=256)
+    assert (pp["chunk"], pp["num_splits"]) == (1024, 32)
     pv = fd.fd_plan_ex(16, 1, 64, 8, 128, 131072, "bf16", paged=True,
                        num_cus=256)
     assert pv["chunk"] == 2048
