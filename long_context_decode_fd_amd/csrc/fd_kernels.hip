@@ -1321,10 +1321,11 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
 //   W = r W + sum_s e^(lse_s - M'),  acc = r acc + sum_s e^(lse_s - M') o_s.
 // The wavefronts then meet in LDS the same way; out = acc / W and
 // lse = M + ln W.  Fixed order everywhere: same chunking, same bits.
-// Two shapes (launch_combine): fewer rows than CUs (batch 1: 64 rows) get
-// D / 64 workgroups of eight wavefronts per row, one column per lane and
-// eight chunks in flight per wavefront; many rows get one workgroup of four
-// wavefronts per row, D / 64 columns per lane, sixteen chunks in flight.
+// Shapes (launch_combine): fewer rows than CUs (batch 1: 64 rows) get D / 64
+// workgroups per row, one column per lane and eight chunks in flight per
+// wavefront -- four wavefronts for up to 32 chunks, eight beyond; many rows
+// get one workgroup of four wavefronts per row, D / 64 columns per lane,
+// sixteen chunks in flight.
 
 // Workgroups are dealt to MI355X's eight XCDs round robin (id % 8).  When
 // Hkv is a multiple of 8, every chunk of kv-head g ran on XCD g % 8 (the
@@ -1502,7 +1503,12 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
-  if (rows < p.num_cus)
+  if (rows < p.num_cus && p.splits <= 32)
+    hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 4, 8>), dim3(rows, D / 64),
+                       dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
+                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
+                       static_cast<OutT *>(a.out), a.lse);
+  else if (rows < p.num_cus)
     hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 8, 8>), dim3(rows, D / 64),
                        dim3(8 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
                        p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
