@@ -701,6 +701,49 @@ __device__ __forceinline__ void tile_compute(
                                                      0, 0);
 }
 
+// Order of a chunk's tiles.  When every KV slab starts at the same offset
+// modulo 32 MB (a cache padded to 128k keys of 256 bytes puts each KV head
+// exactly 32 MB after the previous one), chunks of different heads that
+// stream the same offsets in lockstep run far below the usual rate on
+// MI355X: measured, batch 1 at 64k keys took 61.5 us on such a cache
+// against 44.5 us with 16 MB between heads, and a var-len batch lost up
+// to 10% depending on which sequence sat where.  With that stride each
+// chunk walks its first nrot = ntiles - 2 tiles from a start point taken
+// from its (b, g), wrapping around: KV head g starts g / Hkv of the way in,
+// sequence b adds a fraction of one head's share (the fractional part of b
+// times the golden ratio).  The last two tiles -- the only ones that can be
+// short, or cut by a causal limit -- stay last.  Other strides keep the
+// plain order (rotating there was neutral at 16 MB and cost 2.5% at 1 MB).
+// The rule reads only the stride Lmax * D * 2 (for a paged cache, its
+// table capacity) and the order only (b, g) and the chunk, so every entry
+// point visits a chunk's keys in the same order.
+constexpr size_t kRotateStride = size_t(32) << 20;
+
+struct TileOrder {
+  int nrot, rot;
+  __device__ __forceinline__ int key0(const Work &w, int t) const {
+    int u = t;
+    if (t < nrot) {
+      u = t + rot;
+      if (u >= nrot) u -= nrot;
+    }
+    return w.lo + u * kKeyTile;
+  }
+};
+
+__device__ __forceinline__ TileOrder tile_order(const Work &w, int Hkv,
+                                                int ntiles, bool rotate) {
+  TileOrder o;
+  o.nrot = max(ntiles - 2, 0);
+  o.rot = 0;
+  if (rotate && o.nrot > 1) {
+    const float xb = (float)w.b * 0.61803398875f;
+    const float x = ((float)w.g + (xb - floorf(xb))) / (float)Hkv;
+    o.rot = min((int)(x * (float)o.nrot), o.nrot - 1);
+  }
+  return o;
+}
+
 // Paged cache: for the first key of each 16-key half of this wavefront's
 // tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
 // of its D-element row of KV head g in the pool: (page * page_size + t) *
@@ -709,10 +752,10 @@ __device__ __forceinline__ void tile_compute(
 // nothing and give 0; page indices are clamped into the pool, so no entry
 // of the table can make a load leave the K/V buffers.
 __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
-                                         int Hkv, int wave, int nw, int it0,
-                                         int lane) {
+                                         const TileOrder &ord, int Hkv,
+                                         int wave, int nw, int it0, int lane) {
   const int t = wave + (it0 + (lane >> 1)) * nw;
-  const int key = w.lo + t * kKeyTile + (lane & 1) * 16;
+  const int key = ord.key0(w, t) + (lane & 1) * 16;
   if (key >= w.hi) return 0;
   const int j = key / pk.page_size;
   int pg = pk.block_table[(size_t)w.b * pk.max_pages + j];
@@ -781,13 +824,14 @@ __device__ __forceinline__ void load_k_operand(const uint16_t *kbuf, int n16,
 // (restaged every 32 iterations).
 template <int D, int NW, bool PAGED>
 __device__ __forceinline__ TileRows<D, PAGED> tile_rows(
-    const PagedKV &pk, const Work &w, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
-    int wave, int lane, int k0, int it, int &prow) {
+    const PagedKV &pk, const Work &w, const TileOrder &ord,
+    const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    size_t slab, size_t prs, int Hkv, int wave, int lane, int k0, int it,
+    int &prow) {
   TileRows<D, PAGED> rows;
   if constexpr (PAGED) {
     const int slot = it & 31;
-    if (slot == 0) prow = page_rows(pk, w, Hkv, wave, NW, it, lane);
+    if (slot == 0) prow = page_rows(pk, w, ord, Hkv, wave, NW, it, lane);
     const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
     const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
     rows.rs = prs;
@@ -823,29 +867,31 @@ __device__ __forceinline__ void chunk_tiles(
     const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
     int hi_all, int hi_col, int wave, int lane, int n16, int q4,
     const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
-    floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf) {
+    floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf,
+    bool rotate) {
   static_assert(NW >= 2, "the loop relies on two or more wavefronts");
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
   int t = wave;
   if (t >= ntiles) return;
+  const TileOrder ord = tile_order(w, Hkv, ntiles, rotate);
   if constexpr (kStageK<D, PAGED>) {
     // The same loop with K staged through LDS: the rows of the next tile
     // are in flight while this tile is staged, read back and computed.
     int prow = 0;
-    TileRows<D, PAGED> cur =
-        tile_rows<D, NW, PAGED>(pk, w, kc, vc, slab, prs, Hkv, wave, lane,
-                                w.lo + t * kKeyTile, 0, prow);
+    const int kf0 = ord.key0(w, t);
+    TileRows<D, PAGED> cur = tile_rows<D, NW, PAGED>(
+        pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kf0, 0, prow);
     uint4 kn[8];
-    load_k_rows(cur, min(kKeyTile, w.hi - (w.lo + t * kKeyTile)), lane, kn);
+    load_k_rows(cur, min(kKeyTile, w.hi - kf0), lane, kn);
     uint4 kr[2][4];
     int it = 0;
     for (; t + NW < ntiles; t += NW, ++it) {
       store_k_lds(kn, lane, kbuf);
       typename VecOf<D / 16>::type vr[8];
       tile_load_v<D, false>(cur, kKeyTile, n16, q4, vr);
-      const int kn0 = w.lo + (t + NW) * kKeyTile;
+      const int kn0 = ord.key0(w, t + NW);
       TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
-          pk, w, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+          pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
       load_k_rows(nxt, min(kKeyTile, w.hi - kn0), lane, kn);
       __builtin_amdgcn_sched_barrier(0);
       load_k_operand(kbuf, n16, q4, kr);
@@ -853,7 +899,7 @@ __device__ __forceinline__ void chunk_tiles(
                                          qop, scale_log2, phi2, acc, m, l);
       cur = nxt;
     }
-    const int k0 = w.lo + t * kKeyTile;
+    const int k0 = ord.key0(w, t);
     const int valid = min(kKeyTile, w.hi - k0);
     const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
     store_k_lds(kn, lane, kbuf);
@@ -870,20 +916,19 @@ __device__ __forceinline__ void chunk_tiles(
     return;
   }
   int prow = 0;
-  TileRows<D, PAGED> cur =
-      tile_rows<D, NW, PAGED>(pk, w, kc, vc, slab, prs, Hkv, wave, lane,
-                              w.lo + t * kKeyTile, 0, prow);
+  const int kf0 = ord.key0(w, t);
+  TileRows<D, PAGED> cur = tile_rows<D, NW, PAGED>(
+      pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kf0, 0, prow);
   uint4 kr[2][D / 32];
-  tile_load_k<D, true>(cur, min(kKeyTile, w.hi - (w.lo + t * kKeyTile)),
-                       n16, q4, kr);
+  tile_load_k<D, true>(cur, min(kKeyTile, w.hi - kf0), n16, q4, kr);
   int it = 0;
   for (; t + NW < ntiles; t += NW, ++it) {
     typename VecOf<D / 16>::type vr[8];
     tile_load_v<D, false>(cur, kKeyTile, n16, q4, vr);
     __builtin_amdgcn_sched_barrier(0);
-    const int kn0 = w.lo + (t + NW) * kKeyTile;
+    const int kn0 = ord.key0(w, t + NW);
     TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
-        pk, w, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+        pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
     uint4 kn[2][D / 32];
     tile_load_k<D, true>(nxt, min(kKeyTile, w.hi - kn0), n16, q4, kn);
     __builtin_amdgcn_sched_barrier(0);
@@ -895,7 +940,7 @@ __device__ __forceinline__ void chunk_tiles(
       for (int kk = 0; kk < D / 32; ++kk) kr[sub][kk] = kn[sub][kk];
     cur = nxt;
   }
-  const int k0 = w.lo + t * kKeyTile;
+  const int k0 = ord.key0(w, t);
   const int valid = min(kKeyTile, w.hi - k0);
   const bool full = CAUSAL ? k0 + kKeyTile <= hi_all : valid == kKeyTile;
   typename VecOf<D / 16>::type vr[8];
@@ -1050,6 +1095,8 @@ __device__ __forceinline__ void chunk_pass(
 
   const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
   const size_t prs = pk.head_major ? (size_t)D : (size_t)Hkv * D;
+  const bool rotate =
+      (size_t)Lmax * D * sizeof(uint16_t) % kRotateStride == 0;
 
   floatx4 acc[VW];
 #pragma unroll
@@ -1064,7 +1111,7 @@ __device__ __forceinline__ void chunk_pass(
     chunk_tiles<D, NW, PAGED, CAUSAL, true>(w, pk, kc, vc, slab, prs, Hkv,
                                             hi_all, hi_col, wave, lane, n16,
                                             q4, qop, scale_log2, phi2, acc,
-                                            m, l, kbuf);
+                                            m, l, kbuf, rotate);
     float xm = fmaxf(m, __shfl_xor(m, 16, 64));
     xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
     const bool bad = xm != FD_NEG_INF && !(xm >= -kUniRange && xm <= kUniRange);
@@ -1076,7 +1123,7 @@ __device__ __forceinline__ void chunk_pass(
       chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
                                                hi_all, hi_col, wave, lane,
                                                n16, q4, qop, scale_log2, 0.f,
-                                               acc, m, l, kbuf);
+                                               acc, m, l, kbuf, rotate);
     } else {
       m = xm == FD_NEG_INF ? FD_NEG_INF : phi2;
     }
@@ -1084,7 +1131,7 @@ __device__ __forceinline__ void chunk_pass(
     chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
                                              hi_all, hi_col, wave, lane, n16,
                                              q4, qop, scale_log2, 0.f, acc, m,
-                                             l, kbuf);
+                                             l, kbuf, rotate);
   }
 
   l += __shfl_xor(l, 16, 64);
