@@ -1,7 +1,8 @@
 """GPU parity where a chunk's tiles are walked in rotated order.
 
 When every KV slab starts at the same offset modulo 32 MB (Lmax * D * 2
-bytes a multiple of 32 MB: 128k keys at D = 128), the matrix-core pass starts
+bytes a multiple of 32 MB: 128k keys at D = 128, 256k at D = 64), the
+matrix-core pass starts
 each chunk's tiles at a point taken from its (b, g) and wraps around, keeping
 the last two tiles last.  These cases put every kind of chunk on that path --
 chunks of hundreds of tiles, of a dozen, of one to three (too short to
@@ -174,3 +175,20 @@ def test_rotated_order_paged(torch, oracle_mod, hm):
         _parity(po, pl, ref_o, ref_l, f"paged hm={hm} splits={splits}")
         assert torch.equal(po.view(torch.int16), co.view(torch.int16))
         assert torch.equal(pl, cl)
+
+
+@pytest.mark.parametrize("splits", [0, 11])
+def test_rotated_order_d64(torch, oracle_mod, splits):
+    # D = 64 reaches the same stride at 256k keys (128-byte rows).
+    w = wl.Workload("rot_d64", B=2, Hq=8, Hkv=2, D=64, Lmax=2 * LMAX,
+                    dtype="bf16", seed=94)
+    sl = np.array([2 * LMAX - 7, 1000], np.int32)
+    q, k, v = _gen(w, sl)
+    ref_o, ref_l = oracle_mod.decode(q, k, v, sl, w.scale)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    sld = torch.from_numpy(sl).to("cuda")
+    for flags in (0, fd.FD_FLAG_FUSED_MERGE):
+        out, lse = fd.fd_decode_ex(qd, kd, vd, sld, w.scale,
+                                   num_splits=splits, flags=flags)
+        torch.cuda.synchronize()
+        _parity(out, lse, ref_o, ref_l, f"D=64 splits={splits} flags={flags}")
