@@ -17,7 +17,8 @@
 //     least kMinChunk keys (the per-workgroup prologue and the partial
 //     write, 2 * G * 4 bytes per key-row pair, must stay small next to the
 //     2 * C * D * elem bytes of K/V a chunk streams);
-//   * S == 1 means no partials and no merge pass at all;
+//   * S == 1 means no partials and no merge pass at all; caches of up to
+//     2 * kMinChunk keys always take it (one launch beats two there);
 //   * with per-sequence lengths the mix is unknown on the host (the library
 //     never reads device memory synchronously), so chunks are also capped
 //     at kVarlenChunk keys, so that no single long sequence sets the finish
@@ -163,6 +164,12 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     int s = (int)std::max(1L, (target + units - 1) / units);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
     chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
+    // Short caches: one launch beats two.  Up to 2 * kMinChunk keys the
+    // merge pass (a second kernel) costs more than streaming the whole
+    // sequence in one workgroup per (sequence, KV head): measured, batch 1
+    // at 512 keys took 9.8 us unsplit against 12.8 us in two chunks; from
+    // 768 keys on the split is ahead.
+    if (Lmax <= 2 * kMinChunk) chunk = full_chunk;
     // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
     // than the even split would make it were every sequence full.
     if (varlen) chunk = std::min(chunk, kVarlenChunk);

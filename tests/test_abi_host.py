@@ -182,6 +182,25 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
     assert p["variant"] == fd.FD_VARIANT_VALU and p["chunk"] % 32 == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_short_caches_take_one_launch(lib, dtype, varlen):
+    # Up to 512 keys (twice the 256-key minimum chunk) the planner keeps one
+    # chunk per sequence: no partials, no merge pass.  One key more and the
+    # usual split applies.
+    for L in (32, 300, 512):
+        p = fd.fd_plan(1, 8, 8, 128, L, dtype, varlen=varlen, num_cus=256)
+        assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == \
+            (1, 0, 0), (L, p)
+    p = fd.fd_plan(1, 8, 8, 128, 513, dtype, varlen=varlen, num_cus=256)
+    assert (p["num_splits"], p["chunk"], p["combine"]) == (3, 256, 1)
+    # a paged table of that capacity plans the same way
+    if dtype == "bf16":
+        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 512, "bf16", varlen=True,
+                          paged=True, num_cus=256)
+        assert p["num_splits"] == 1 and p["combine"] == 0
+
+
 @pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
                                  (65536, 64), (65536, 5000), (100, 100)])
 def test_forced_splits_cover_the_sequence(lib, L, S):
