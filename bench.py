@@ -222,6 +222,72 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def context_sweep(torch, fd, steps: int) -> None:
+    """Flash-Decoding against the same kernel unsplit, over context length.
+
+    [FD], section "A faster attention for decoding: Flash-Decoding", compares
+    splitting the keys/values with attention that parallelises over batch
+    and heads only, which at small batch leaves most of the GPU idle.  Here
+    the unsplit form is this library's own kernel with num_splits = 1 (one
+    workgroup per (sequence, KV head)); the split form is fd_decode's plan.
+    Batch 1 and 8, 64 query heads on 8 KV heads, D = 128, bf16, seeded
+    random inputs, KV rotated over KV_COPIES copies.  One JSON line per case.
+    """
+    D, Hq, Hkv = 128, 64, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        warm_up(torch, fn, max(3, n // 10))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for B in (1, 8):
+        for L in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072):
+            if B * L > 8 * 65536:
+                continue
+            shape = (B, Hkv, L, D)
+            ks = [torch.randn(shape, device="cuda", dtype=torch.bfloat16,
+                              generator=gen) for _ in range(KV_COPIES)]
+            vs = [torch.randn(shape, device="cuda", dtype=torch.bfloat16,
+                              generator=gen) for _ in range(KV_COPIES)]
+            q = torch.randn((B, Hq, D), device="cuda", dtype=torch.bfloat16,
+                            generator=gen)
+            out = torch.empty_like(q)
+            lse = torch.empty((B, Hq), device="cuda")
+            scale = D ** -0.5
+
+            def split(i):
+                fd.fd_decode(q, ks[i % KV_COPIES], vs[i % KV_COPIES], None,
+                             scale, out=out, lse=lse, stream=stream)
+
+            def unsplit(i):
+                fd.fd_decode_ex(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
+                                None, scale, out=out, lse=lse, num_splits=1,
+                                stream=stream)
+
+            t_split = timed(split, steps)
+            t_uns = timed(unsplit, steps)
+            nbytes = 2 * B * Hkv * L * D * 2
+            plan = fd.fd_plan(B, Hq, Hkv, D, L, "bf16")
+            print(json.dumps({
+                "sweep": "split_vs_unsplit", "B": B, "L": L, "Hq": Hq,
+                "Hkv": Hkv, "D": D, "num_splits": plan["num_splits"],
+                "split_us": round(t_split, 2), "unsplit_us": round(t_uns, 2),
+                "speedup": round(t_uns / t_split, 2),
+                "split_GBs": round(nbytes / t_split / 1e3, 1),
+                "unsplit_GBs": round(nbytes / t_uns / 1e3, 1)}), flush=True)
+            del ks, vs
+            torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +301,10 @@ def main(argv=None):
     ap.add_argument("--unified-max", type=float, default=None, metavar="PHI",
                     help="time fd_decode_unified_max with this phi instead "
                          "of fd_decode (contiguous single-token workloads)")
+    ap.add_argument("--context-sweep", action="store_true",
+                    help="instead of the benchmark line: Flash-Decoding "
+                         "against the same kernel unsplit over context "
+                         "length (batch 1 and 8), one JSON line per case")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -248,6 +318,12 @@ def main(argv=None):
     import torch
     import long_context_decode_fd_amd as fd
     from long_context_decode_fd_amd import workloads as wl
+
+    if a.context_sweep:
+        torch.cuda.set_device(0)
+        fd.load_library()
+        context_sweep(torch, fd, a.steps)
+        return 0
 
     w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
     kind = ("paged" if w.page_size else
