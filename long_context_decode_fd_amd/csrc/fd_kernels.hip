@@ -90,6 +90,8 @@ struct Work {
   int lo, hi;  // keys [lo, hi) of slab (b, g); lo == hi only when L_b == 0
   int L;       // clamped length of sequence b
   int nb;      // chunks of sequence b
+  int items;   // length of the whole work list when the scan knows it
+               // (at most 64 sequences), else INT_MAX
   bool valid;
 };
 
@@ -116,6 +118,7 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
   Work w;
   w.valid = false;
   w.b = w.g = w.s = w.lo = w.hi = w.L = w.nb = 0;
+  w.items = INT_MAX;
   if (seqlens == nullptr || direct) {
     const int S = (Lmax + C - 1) / C;
     const int per_b = S * Hkv;
@@ -150,6 +153,12 @@ __device__ Work find_work(int bid, const int32_t *__restrict__ seqlens, int B,
       if (lane >= off) incl += t;
     }
     const int total = __shfl(incl, 63, 64);
+    if (B <= 64) {
+      // the whole list: every full chunk, then one last chunk per
+      // sequence whose length is not a multiple of C (or is 0)
+      const bool has_last = b < B && (L % C != 0 || L == 0);
+      w.items = total + __popcll(__ballot(has_last)) * Hkv;
+    }
     if (bid < base + total) {
       const unsigned long long hit = __ballot(base + incl > bid);
       const int src = __ffsll((unsigned long long)hit) - 1;
@@ -1183,9 +1192,12 @@ void split_mfma_kernel(
                                         Hkv, G, Tq, Lmax, C, S, scale_log2,
                                         phi2, mode, out, lse, o_part,
                                         lse_part, tickets);
-  // Equal lengths, or a grid that covers the upper bound: one chunk each.
+  // Equal lengths, a grid that covers the upper bound, or a work list that
+  // ends before i + grid (its length is known from the scan for up to 64
+  // sequences): one chunk each, and no second look-up.
   const long id1 = (long)blockIdx.x + gridDim.x;
-  if (seqlens == nullptr || id1 >= (long)B * Hkv * S) return;
+  if (seqlens == nullptr || id1 >= (long)B * Hkv * S || id1 >= w0.items)
+    return;
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
