@@ -40,8 +40,9 @@
  * NaN included).  Pointers must be 16-byte aligned device pointers.
  *
  * Supported: D in {64, 128}; dtype FD_BF16 with 1 <= Hq/Hkv <= 16, or
- * FD_F32 with 1 <= Hq/Hkv <= 16.  bf16 scores and outputs are accumulated
- * in fp32; the bf16 output is rounded to nearest even.
+ * FD_F32 with 1 <= Hq/Hkv <= 16; Lmax <= 2^30 keys.  bf16 scores and
+ * outputs are accumulated in fp32; the bf16 output is rounded to nearest
+ * even.
  *
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
@@ -75,7 +76,8 @@ enum {
     FD_OK = 0,
     FD_ERR_INVALID_ARG = -1, /* NULL pointer, non-positive size, Hq % Hkv,
                                 non-finite scale, misaligned pointer */
-    FD_ERR_UNSUPPORTED = -2, /* D, dtype or group size outside the list */
+    FD_ERR_UNSUPPORTED = -2, /* D, dtype, group size or Lmax outside the
+                                supported range */
     FD_ERR_WORKSPACE = -3,   /* caller workspace too small / alloc failed */
     FD_ERR_HIP = -4          /* a HIP runtime call or launch failed */
 };

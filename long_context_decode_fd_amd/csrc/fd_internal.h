@@ -14,6 +14,8 @@ constexpr int kKeyTile = 32;
 // Largest query group (Hq / Hkv) one workgroup handles: the MFMA q-tile
 // has 16 columns.
 constexpr int kMaxGroup = 16;
+// Largest Lmax (keys per sequence) the library plans for.
+constexpr int kMaxKeys = 1 << 30;
 
 // Everything a launch needs, decided on the host.
 struct Plan {

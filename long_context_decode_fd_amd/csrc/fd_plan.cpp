@@ -76,6 +76,9 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
   if (dtype != FD_BF16 && dtype != FD_F32) return FD_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return FD_ERR_UNSUPPORTED;
   if (Hq / Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
+  // Keys per sequence: chunk sizes, key offsets and lo + C stay in int.
+  // (2^30 keys of one KV head at D = 128 are 256 GB, beyond any GPU's HBM.)
+  if (Lmax > kMaxKeys) return FD_ERR_UNSUPPORTED;
   // Index arithmetic below uses int for per-slab row counts and size_t for
   // element offsets; guard the products that are computed in int.
   if ((long)B * Hkv > (1L << 30) || (long)B * Hq > (1L << 30))

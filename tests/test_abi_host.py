@@ -88,6 +88,8 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(D=256), fd.FD_ERR_UNSUPPORTED),
     (dict(dtype=7), fd.FD_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(Lmax=(1 << 30) + 1), fd.FD_ERR_UNSUPPORTED),   # above 2^30 keys
+    (dict(Lmax=2**31 - 1), fd.FD_ERR_UNSUPPORTED),
     (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
     (dict(variant=3), fd.FD_ERR_INVALID_ARG),
     (dict(variant=-1), fd.FD_ERR_INVALID_ARG),
