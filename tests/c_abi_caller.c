@@ -34,6 +34,15 @@
 
 static int failures = 0;
 
+/* A HIP runtime call that must succeed in run mode. */
+#define HIP_OK(call)                                                  \
+  do {                                                                \
+    if ((call) != hipSuccess) {                                       \
+      fprintf(stderr, "%s failed at line %d\n", #call, __LINE__);     \
+      return 3;                                                       \
+    }                                                                 \
+  } while (0)
+
 static void check(const char *name, long got, long want) {
   printf("%s %ld%s\n", name, got, got == want ? "" : "  MISMATCH");
   if (got != want) ++failures;
@@ -170,10 +179,11 @@ static int run_case(const char *in_path, const char *out_path) {
     fprintf(stderr, "device allocation failed\n");
     return 3;
   }
-  hipMemcpy(dq, hq, nq * 2, hipMemcpyHostToDevice);
-  hipMemcpy(dk, hk, nkv * 2, hipMemcpyHostToDevice);
-  hipMemcpy(dv, hv, nkv * 2, hipMemcpyHostToDevice);
-  if (has_sl) hipMemcpy(dsl, hsl, (size_t)B * 4, hipMemcpyHostToDevice);
+  HIP_OK(hipMemcpy(dq, hq, nq * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dk, hk, nkv * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dv, hv, nkv * 2, hipMemcpyHostToDevice));
+  if (has_sl)
+    HIP_OK(hipMemcpy(dsl, hsl, (size_t)B * 4, hipMemcpyHostToDevice));
 
   FILE *o = fopen(out_path, "wb");
   if (!o) {
@@ -183,9 +193,9 @@ static int run_case(const char *in_path, const char *out_path) {
   int32_t status[4];
   status[0] = fd_decode(dq, dk, dv, dsl, B, Hq, Hkv, D, Lmax, scale, FD_BF16,
                         dout, dlse, st);
-  hipStreamSynchronize(st);
-  hipMemcpy(hout, dout, nq * 2, hipMemcpyDeviceToHost);
-  hipMemcpy(hlse, dlse, nlse * 4, hipMemcpyDeviceToHost);
+  HIP_OK(hipStreamSynchronize(st));
+  HIP_OK(hipMemcpy(hout, dout, nq * 2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(hlse, dlse, nlse * 4, hipMemcpyDeviceToHost));
 
   fd_plan_t plan;
   const size_t ws = fd_workspace_bytes(B, Hq, Hkv, D, Lmax, FD_BF16, has_sl,
@@ -204,12 +214,12 @@ static int run_case(const char *in_path, const char *out_path) {
   status[1] = fd_decode_ex(dq, dk, dv, dsl, B, Hq, Hkv, D, Lmax, scale,
                            FD_BF16, dout, dlse, splits, FD_VARIANT_AUTO, 0,
                            dws, ws, st);
-  hipStreamSynchronize(st);
+  HIP_OK(hipStreamSynchronize(st));
   fwrite(status, 4, 4, o);
   fwrite(hout, 2, nq, o);
   fwrite(hlse, 4, nlse, o);
-  hipMemcpy(hout, dout, nq * 2, hipMemcpyDeviceToHost);
-  hipMemcpy(hlse, dlse, nlse * 4, hipMemcpyDeviceToHost);
+  HIP_OK(hipMemcpy(hout, dout, nq * 2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(hlse, dlse, nlse * 4, hipMemcpyDeviceToHost));
   fwrite(hout, 2, nq, o);
   fwrite(hlse, 4, nlse, o);
   fclose(o);
