@@ -150,15 +150,18 @@ def test_rotated_order_multiquery(torch, oracle_mod):
     assert torch.equal(ml[:, 0].contiguous(), dl)
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("hm", [False, True], ids=["token_major",
                                                    "head_major"])
-def test_rotated_order_paged(torch, oracle_mod, hm):
-    # A block table of 128k keys' capacity takes the same order as the
-    # contiguous cache of that stride: the same bits, and the oracle's
+def test_rotated_order_paged(torch, oracle_mod, hm, D):
+    # A block table of 32 MB of keys per head (128k keys at D = 128, 256k at
+    # D = 64; K goes through LDS only at D = 128) takes the same order as
+    # the contiguous cache of that stride: the same bits, and the oracle's
     # values.
-    w = wl.Workload("rot_paged", B=2, Hq=16, Hkv=2, D=128, Lmax=LMAX,
+    lmax = LMAX * 128 // D
+    w = wl.Workload("rot_paged", B=2, Hq=16, Hkv=2, D=D, Lmax=lmax,
                     dtype="bf16", seed=93, page_size=64, head_major=hm)
-    sl = np.array([LMAX - 100, 4000], np.int32)
+    sl = np.array([lmax - 100, 4000], np.int32)
     q, k, v = _gen(w, sl)
     ref_o, ref_l = oracle_mod.decode(q, k, v, sl, w.scale)
     bt = wl.gen_block_table(w)
