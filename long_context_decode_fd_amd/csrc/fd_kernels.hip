@@ -28,9 +28,14 @@
 //   * the wavefronts of a workgroup take interleaved tiles and merge their
 //     (max, sum, accumulator) states through LDS at the end, so a chunk
 //     writes one partial per query row;
+//   * when every KV slab starts at the same offset modulo 32 MB, each
+//     chunk walks its tiles from a start point taken from (b, g) and wraps
+//     (TileOrder): slabs streamed in lockstep at such a stride run far
+//     below the usual rate on MI355X;
 //   * the same kernel, by template switches, reads the tiles from a paged
-//     pool through a block table, serves several causal new tokens per
-//     sequence (their query rows share the 16-column q-tile), or takes the
+//     pool through a block table (K staged through LDS as whole 256-byte
+//     rows at D = 128), serves several causal new tokens per sequence
+//     (their query rows share the 16-column q-tile), or takes the
 //     unified-maximum softmax of FlashDecoding++ with an exact fallback;
 //   * fp32 (and bf16 tiny groups) run a vector-ALU kernel with 16-byte
 //     loads per lane and shuffle reductions of the dot products;
