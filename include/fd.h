@@ -46,16 +46,19 @@
  *
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
- * pointer after a call returns.
+ * pointer to a caller's buffer after a call returns; the only memory it
+ * holds is its own workspace (fd_decode).
  *
  * Errors.  Every entry point returns FD_OK or a negative FD_ERR_* code;
  * argument checks run on the host before anything is launched, and nothing
  * is launched when one fails.  No C++ exception crosses the ABI.
  *
  * Synchronisation.  Calls are asynchronous on `stream`; results are valid
- * once the stream's work has completed.  The library never synchronises,
- * so it cannot validate the device-side seqlens: a value outside
- * [0, Lmax] is a caller error that the kernels clamp into that range.
+ * once the stream's work has completed.  The library does not synchronise
+ * (the one exception: when its own workspace grows, freeing the old buffer
+ * waits for the device), so it cannot validate the device-side seqlens: a
+ * value outside [0, Lmax] is a caller error that the kernels clamp into
+ * that range.
  */
 #ifndef FD_H
 #define FD_H

@@ -182,6 +182,7 @@ def _check(q, k_cache, v_cache, seqlens, out, lse, need_out=True):
                 or seqlens.shape != (B,) or not seqlens.is_contiguous()):
             raise ValueError("seqlens must be a contiguous int32 [B] "
                              "device tensor")
+    _same_device(q.device, k_cache=k_cache, v_cache=v_cache, seqlens=seqlens)
     if not need_out:
         return (B, Hq, Hkv, D, Lmax), None, None
     if out is None:
@@ -194,14 +195,30 @@ def _check(q, k_cache, v_cache, seqlens, out, lse, need_out=True):
     if (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_cuda
             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    _same_device(q.device, out=out, lse=lse)
     return (B, Hq, Hkv, D, Lmax), out, lse
 
 
-def _stream_handle(stream, device):
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _invoke(name, device, stream, *args):
+    """Call libfd's `name` on `stream` (default: the current stream of
+    `device`) with `device` made current for the call: the library plans
+    for, and keeps its own workspace on, the current device."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    elif stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, expected {device}")
+    with torch.cuda.device(device):
+        rc = getattr(load_library(), name)(*args,
+                                           ctypes.c_void_p(stream.cuda_stream))
+    if rc != FD_OK:
+        raise FdError(name, rc)
 
 
 def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
@@ -221,16 +238,15 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
         raise ValueError("scale must be finite")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
+        _same_device(q.device, workspace=workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
             workspace.element_size()
-    rc = load_library().fd_decode_ex(
+    _invoke("fd_decode_ex", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
         out.data_ptr(), lse.data_ptr(), int(num_splits), int(variant),
-        int(flags), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode_ex", rc)
+        int(flags), ws_ptr, ws_bytes)
     return out, lse
 
 
@@ -245,16 +261,15 @@ def fd_decode_unified_max(q, k_cache, v_cache, seqlens, scale, phi,
         raise ValueError("scale and phi must be finite")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
+        _same_device(q.device, workspace=workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
             workspace.element_size()
-    rc = load_library().fd_decode_unified_max(
+    _invoke("fd_decode_unified_max", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
         out.data_ptr(), lse.data_ptr(), float(phi), int(num_splits),
-        int(flags), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode_unified_max", rc)
+        int(flags), ws_ptr, ws_bytes)
     return out, lse
 
 
@@ -265,19 +280,18 @@ def fd_decode(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
     B, Hq, Hkv, D, Lmax = dims
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
-    rc = load_library().fd_decode(
+    _invoke("fd_decode", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
-        out.data_ptr(), lse.data_ptr(), _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode", rc)
+        out.data_ptr(), lse.data_ptr())
     return out, lse
 
 
-def _ws(workspace):
+def _ws(workspace, device):
     if workspace is None:
         raise ValueError("the phase calls need a caller workspace tensor")
+    _same_device(device, workspace=workspace)
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -290,15 +304,12 @@ def fd_decode_partials(q, k_cache, v_cache, seqlens, scale, workspace,
     B, Hq, Hkv, D, Lmax = dims
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
-    ws_ptr, ws_bytes = _ws(workspace)
-    rc = load_library().fd_decode_partials(
+    ws_ptr, ws_bytes = _ws(workspace, q.device)
+    _invoke("fd_decode_partials", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
-        int(num_splits), int(variant), int(flags), ws_ptr, ws_bytes,
-        _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode_partials", rc)
+        int(num_splits), int(variant), int(flags), ws_ptr, ws_bytes)
 
 
 def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
@@ -313,14 +324,14 @@ def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
     if (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_cuda
             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
-    ws_ptr, ws_bytes = _ws(workspace)
-    rc = load_library().fd_merge_partials(
+    if seqlens is not None:
+        _device_tensor("seqlens", seqlens, torch.int32, (B,))
+    _same_device(out.device, lse=lse, seqlens=seqlens)
+    ws_ptr, ws_bytes = _ws(workspace, out.device)
+    _invoke("fd_merge_partials", out.device, stream,
         None if seqlens is None else seqlens.data_ptr(), B, Hq, Hkv, D, Lmax,
         _dtype_code(dtype), int(num_splits), int(variant), int(flags),
-        ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr(),
-        _stream_handle(stream, out.device))
-    if rc != FD_OK:
-        raise FdError("fd_merge_partials", rc)
+        ws_ptr, ws_bytes, out.data_ptr(), lse.data_ptr())
 
 
 def _device_tensor(name, t, dtype, shape=None):
@@ -380,15 +391,15 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
         raise ValueError("scale must be finite")
     out, lse = _out_lse(out, lse, tuple(q.shape), tuple(q.shape[:-1]),
                         q.dtype, q.device)
-    rc = load_library().fd_decode_paged(
+    _same_device(q.device, k_pages=k_pages, v_pages=v_pages,
+                 block_table=block_table, seqlens=seqlens, out=out, lse=lse)
+    _invoke("fd_decode_paged", q.device, stream,
         q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
         FD_PAGES_HEAD_MAJOR if head_major else FD_PAGES_TOKEN_MAJOR,
         seqlens.data_ptr(), B, Tq, Hq, Hkv, D, float(scale),
         _dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
-        int(num_splits), int(flags), _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode_paged", rc)
+        int(num_splits), int(flags))
     return out, lse
 
 
@@ -416,12 +427,11 @@ def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
         raise ValueError("scale must be finite")
     out, lse = _out_lse(out, lse, (B, Tq, Hq, D), (B, Tq, Hq), q.dtype,
                         q.device)
-    rc = load_library().fd_decode_multiquery(
+    _same_device(q.device, k_cache=k_cache, v_cache=v_cache, seqlens=seqlens,
+                 out=out, lse=lse)
+    _invoke("fd_decode_multiquery", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(), B, Tq, Hq, Hkv, D,
         Lmax, float(scale), _dtype_code(q.dtype), out.data_ptr(),
-        lse.data_ptr(), int(num_splits), int(flags),
-        _stream_handle(stream, q.device))
-    if rc != FD_OK:
-        raise FdError("fd_decode_multiquery", rc)
+        lse.data_ptr(), int(num_splits), int(flags))
     return out, lse

@@ -242,6 +242,14 @@ def test_binding_marshals_nothing_but_pointers():
                          ctypes.c_size_t) or hasattr(a, "_type_"), name
 
 
+def test_binding_rejects_tensors_on_another_device():
+    torch = pytest.importorskip("torch")
+    here = torch.empty(2)
+    bnd._same_device(here.device, a=here, b=None)
+    with pytest.raises(ValueError, match="b is on meta"):
+        bnd._same_device(here.device, a=here, b=torch.empty(2, device="meta"))
+
+
 def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
                num_pages=8, layout=0, seqlens=A, B=1, Tq=1, Hq=8, Hkv=8,
                D=128, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
