@@ -47,7 +47,9 @@
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
  * pointer to a caller's buffer after a call returns; the only memory it
- * holds is its own workspace (fd_decode).
+ * holds is its own workspace (fd_decode).  Calls plan for the current HIP
+ * device (its compute-unit count) and keep that workspace on it, so the
+ * current device must be the one that holds the buffers and the stream.
  *
  * Errors.  Every entry point returns FD_OK or a negative FD_ERR_* code;
  * argument checks run on the host before anything is launched, and nothing

@@ -21,12 +21,25 @@ bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
-// Per-device compute-unit count, queried once.
+// Per-device compute-unit count, queried once.  The per-device tables
+// below grow with std::vector and are guarded by a std::mutex; both can
+// throw, and no exception may leave an extern "C" function, so each table
+// access runs in a try block that turns one into a status code.
+int device_cus_locked(int dev, int *out);
+
 int device_cus(int *out) {
-  static std::mutex mu;
-  static std::vector<int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  try {
+    return device_cus_locked(dev, out);
+  } catch (...) {
+    return FD_ERR_HIP;
+  }
+}
+
+int device_cus_locked(int dev, int *out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
   std::lock_guard<std::mutex> lk(mu);
   if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
   if (cache[dev] == 0) {
@@ -54,12 +67,24 @@ struct OwnedWorkspace {
   size_t zero_bytes = 0;
 };
 
+int owned_workspace_locked(int dev, size_t need, size_t ticket_bytes,
+                           hipStream_t stream, void **out);
+
 int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
                     void **out) {
-  static std::mutex mu;
-  static std::vector<OwnedWorkspace> ws;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  try {
+    return owned_workspace_locked(dev, need, ticket_bytes, stream, out);
+  } catch (...) {
+    return FD_ERR_WORKSPACE;
+  }
+}
+
+int owned_workspace_locked(int dev, size_t need, size_t ticket_bytes,
+                           hipStream_t stream, void **out) {
+  static std::mutex mu;
+  static std::vector<OwnedWorkspace> ws;
   std::lock_guard<std::mutex> lk(mu);
   if ((int)ws.size() <= dev) ws.resize(dev + 1);
   OwnedWorkspace &w = ws[dev];
