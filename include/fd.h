@@ -50,6 +50,9 @@
  * holds is its own workspace (fd_decode).  Calls plan for the current HIP
  * device (its compute-unit count) and keep that workspace on it, so the
  * current device must be the one that holds the buffers and the stream.
+ * out and lse must not overlap each other, an input or the workspace (the
+ * kernels read the inputs while they write the outputs); inputs may share
+ * memory, since they are only read.
  *
  * Errors.  Every entry point returns FD_OK or a negative FD_ERR_* code;
  * argument checks run on the host before anything is launched, and nothing
@@ -170,7 +173,8 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
  *               workspace_bytes 0 to use the library-owned one.  A caller
  *               workspace makes the call allocation-free and free of
  *               library state, so it can be captured in a HIP graph and
- *               replayed (it queues kernels only; no memset, no copy).  With FD_FLAG_FUSED_MERGE its first
+ *               replayed (it queues kernels only; no memset, no copy).
+ *               With FD_FLAG_FUSED_MERGE its first
  *               fd_plan_t.ticket_bytes bytes are per-group tickets that must
  *               be zero when a call starts: zero-fill a new workspace once;
  *               every call leaves its tickets zero again, but the rest of

@@ -196,6 +196,8 @@ def _check(q, k_cache, v_cache, seqlens, out, lse, need_out=True):
             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
     _same_device(q.device, out=out, lse=lse)
+    _no_overlap(dict(out=out, lse=lse), dict(q=q, k_cache=k_cache,
+                                             v_cache=v_cache, seqlens=seqlens))
     return (B, Hq, Hkv, D, Lmax), out, lse
 
 
@@ -203,6 +205,25 @@ def _same_device(device, **tensors):
     for name, t in tensors.items():
         if t is not None and t.device != device:
             raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _span(t):
+    n = t.numel() * t.element_size()
+    return t.data_ptr(), t.data_ptr() + n
+
+
+def _no_overlap(outs, ins):
+    """Outputs must not share memory with each other or with an input."""
+    outs = {k: t for k, t in outs.items() if t is not None and t.numel()}
+    ins = {k: t for k, t in ins.items() if t is not None and t.numel()}
+    names = list(outs)
+    for i, a in enumerate(names):
+        a0, a1 = _span(outs[a])
+        others = [(b, outs[b]) for b in names[i + 1:]] + list(ins.items())
+        for b, t in others:
+            b0, b1 = _span(t)
+            if a0 < b1 and b0 < a1:
+                raise ValueError(f"{a} overlaps {b}")
 
 
 def _invoke(name, device, stream, *args):
@@ -239,6 +260,7 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _same_device(q.device, workspace=workspace)
+        _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
             workspace.element_size()
     _invoke("fd_decode_ex", q.device, stream,
@@ -262,6 +284,7 @@ def fd_decode_unified_max(q, k_cache, v_cache, seqlens, scale, phi,
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _same_device(q.device, workspace=workspace)
+        _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
             workspace.element_size()
     _invoke("fd_decode_unified_max", q.device, stream,
@@ -305,6 +328,9 @@ def fd_decode_partials(q, k_cache, v_cache, seqlens, scale, workspace,
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
     ws_ptr, ws_bytes = _ws(workspace, q.device)
+    _no_overlap(dict(workspace=workspace), dict(q=q, k_cache=k_cache,
+                                                v_cache=v_cache,
+                                                seqlens=seqlens))
     _invoke("fd_decode_partials", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
@@ -328,6 +354,8 @@ def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
         _device_tensor("seqlens", seqlens, torch.int32, (B,))
     _same_device(out.device, lse=lse, seqlens=seqlens)
     ws_ptr, ws_bytes = _ws(workspace, out.device)
+    _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace,
+                                             seqlens=seqlens))
     _invoke("fd_merge_partials", out.device, stream,
         None if seqlens is None else seqlens.data_ptr(), B, Hq, Hkv, D, Lmax,
         _dtype_code(dtype), int(num_splits), int(variant), int(flags),
@@ -393,6 +421,9 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
                         q.dtype, q.device)
     _same_device(q.device, k_pages=k_pages, v_pages=v_pages,
                  block_table=block_table, seqlens=seqlens, out=out, lse=lse)
+    _no_overlap(dict(out=out, lse=lse),
+                dict(q=q, k_pages=k_pages, v_pages=v_pages,
+                     block_table=block_table, seqlens=seqlens))
     _invoke("fd_decode_paged", q.device, stream,
         q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
@@ -429,6 +460,8 @@ def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
                         q.device)
     _same_device(q.device, k_cache=k_cache, v_cache=v_cache, seqlens=seqlens,
                  out=out, lse=lse)
+    _no_overlap(dict(out=out, lse=lse), dict(q=q, k_cache=k_cache,
+                                             v_cache=v_cache, seqlens=seqlens))
     _invoke("fd_decode_multiquery", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(), B, Tq, Hq, Hkv, D,

@@ -250,6 +250,19 @@ def test_binding_rejects_tensors_on_another_device():
         bnd._same_device(here.device, a=here, b=torch.empty(2, device="meta"))
 
 
+def test_binding_rejects_outputs_that_overlap():
+    torch = pytest.importorskip("torch")
+    buf = torch.zeros(64)
+    q, out = buf[:32], buf[16:48]
+    bnd._no_overlap(dict(out=buf[32:48], lse=buf[48:]), dict(q=q, s=None))
+    with pytest.raises(ValueError, match="out overlaps q"):
+        bnd._no_overlap(dict(out=out), dict(q=q))
+    with pytest.raises(ValueError, match="out overlaps lse"):
+        bnd._no_overlap(dict(out=buf[:8], lse=buf[7:9]), {})
+    # touching ends do not overlap; empty tensors never do
+    bnd._no_overlap(dict(out=buf[8:16], lse=buf[16:16]), dict(q=buf[:8]))
+
+
 def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
                num_pages=8, layout=0, seqlens=A, B=1, Tq=1, Hq=8, Hkv=8,
                D=128, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,

@@ -3,8 +3,9 @@
 The binding only marshals arguments, but it is the layer that knows which
 device a tensor lives on: the library plans for, and keeps its own
 workspace on, the current HIP device, so the binding makes the tensors'
-device current for each call and rejects tensors, workspaces or streams on
-another device before anything is launched.
+device current for each call.  Before anything is launched it rejects
+tensors, workspaces or streams on another device, and outputs that overlap
+an input.
 """
 import numpy as np
 import pytest
@@ -53,6 +54,18 @@ def test_host_tensors_are_rejected_before_any_launch(torch, inputs):
     with pytest.raises(ValueError, match="seqlens"):
         fd.fd_merge_partials(sl.long(), W.B, W.Hq, W.Hkv, W.D, W.Lmax,
                              "bf16", dev_ws, out, lse)
+
+
+def test_outputs_that_overlap_inputs_are_rejected(torch, inputs):
+    q, k, v, sl, _, _ = inputs
+    with pytest.raises(ValueError, match="out overlaps q"):
+        fd.fd_decode(q, k, v, sl, W.scale, out=q)
+    nb = fd.fd_workspace_bytes(W.B, W.Hq, W.Hkv, W.D, W.Lmax, "bf16",
+                               varlen=True)
+    ws = torch.zeros(nb + 4 * W.B * W.Hq, dtype=torch.uint8, device="cuda")
+    lse_in_ws = ws[nb:].view(torch.float32).view(W.B, W.Hq)
+    with pytest.raises(ValueError, match="lse overlaps workspace"):
+        fd.fd_decode_ex(q, k, v, sl, W.scale, lse=lse_in_ws, workspace=ws)
 
 
 def test_explicit_stream_and_current_device(torch, inputs):
