@@ -258,8 +258,9 @@ def test_nan_in_valid_prefix_propagates(cuda):
 
 def test_owned_workspace_across_shapes(cuda, oracle_mod):
     """The library's own workspace is reused across shapes whose ticket
-    regions grow and shrink (stale partials must never be read as
-    tickets)."""
+    regions grow and shrink, and by separate-merge calls whose partials
+    land where the next fused call keeps its tickets (stale partials must
+    never be read as tickets)."""
     seq = [("b1_gqa8", SMALL["b1_gqa8"]),
            ("b64_gqa4_split", SMALL["b64_gqa4"]),
            ("b1_gqa8", SMALL["b1_gqa8"]),
@@ -268,12 +269,13 @@ def test_owned_workspace_across_shapes(cuda, oracle_mod):
     for name, w in seq:
         q, k, v, sl_dev, seqlens, host = inputs(name, w)
         ref_out, ref_lse = reference(oracle_mod, w, host, seqlens)
-        for _ in range(2):
+        for flags in (fd.FD_FLAG_FUSED_MERGE, fd.FD_FLAG_FUSED_MERGE, 0,
+                      fd.FD_FLAG_FUSED_MERGE):
             out, lse = fd.fd_decode_ex(q, k, v, sl_dev, w.scale,
-                                       num_splits=5,
-                                       flags=fd.FD_FLAG_FUSED_MERGE)
+                                       num_splits=5, flags=flags)
             cuda.cuda.synchronize()
-            assert_parity(w, out, lse, ref_out, ref_lse, f"reuse {name}")
+            assert_parity(w, out, lse, ref_out, ref_lse,
+                          f"reuse {name} flags {flags}")
 
 
 @pytest.mark.parametrize("name,S", [("b1_gqa8_h64_d128_l65536", 64),
