@@ -122,7 +122,7 @@ enum {
 };
 
 /* What the planner decided for one problem shape (filled by fd_plan). */
-typedef struct fd_plan {
+typedef struct fd_plan_info {
     int num_splits;      /* chunks per sequence of length Lmax (S) */
     int chunk;           /* keys per chunk (C), a multiple of 32 */
     int variant;         /* FD_VARIANT_MFMA or FD_VARIANT_VALU */
