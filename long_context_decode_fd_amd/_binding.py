@@ -96,6 +96,14 @@ def load_library(path: str | None = None):
         raise RuntimeError(
             f"{p} not found: build it with "
             "`python -m long_context_decode_fd_amd.build` (needs hipcc)")
+    # Streams and memory pass between torch and the library, so both must
+    # use one HIP runtime.  torch ships its own: load it first, so that the
+    # library's HIP dependency resolves to it.  Loading the library first
+    # would put the system runtime under torch instead.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
