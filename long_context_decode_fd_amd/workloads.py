@@ -34,6 +34,9 @@ pattern and are handled as ``numpy.uint16`` arrays throughout.
 from __future__ import annotations
 
 import math
+import os
+from collections import deque
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -275,15 +278,61 @@ def gen_slab(w: Workload, b: int, g: int, seqlens=None):
     return k, v
 
 
-def gen_all(w: Workload):
-    """q, k, v, seqlens as host arrays (only for workloads that fit easily)."""
-    seqlens = gen_seqlens(w)
+def gen_threads() -> int:
+    """Host threads for slab generation: the cores this process may use,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def iter_slabs(w: Workload, seqlens=None, threads: int | None = None):
+    """Yields (b, g, L, k_rows, v_rows) for every slab in b-major order,
+    KV head fastest: the rows gen_slab_rows gives, drawn on a thread pool
+    (every slab has its own generator stream, so the values do not depend
+    on the thread count).  L is the length clamped to [0, Lmax].  At most
+    2 * threads slabs are held at once."""
+    jobs = [(b, g, min(max(seqlen_of(w, seqlens, b), 0), w.Lmax))
+            for b in range(w.B) for g in range(w.Hkv)]
+    n = threads or gen_threads()
+    if n <= 1:
+        for b, g, L in jobs:
+            yield (b, g, L) + gen_slab_rows(w, b, g, L)
+        return
+    with ThreadPoolExecutor(n) as ex:
+        pending = deque()
+        it = iter(jobs)
+        for job in it:
+            pending.append((job, ex.submit(gen_slab_rows, w, *job)))
+            if len(pending) >= 2 * n:
+                break
+        while pending:
+            (b, g, L), fut = pending.popleft()
+            job = next(it, None)
+            if job is not None:
+                pending.append((job, ex.submit(gen_slab_rows, w, *job)))
+            yield (b, g, L) + fut.result()
+
+
+def _poison(a: np.ndarray) -> None:
+    a.view(np.uint8)[:] = 0xFF          # all-ones bit patterns are NaN
+
+
+def gen_all(w: Workload, seqlens=None, threads: int | None = None):
+    """q, k, v, seqlens as host arrays (only for workloads that fit easily);
+    rows at or beyond a sequence's length hold NaN."""
+    if seqlens is None:
+        seqlens = gen_seqlens(w)
     q = gen_q(w)
     k = np.empty((w.B, w.Hkv, w.Lmax, w.D), dtype=w.np_dtype)
     v = np.empty_like(k)
-    for b in range(w.B):
-        for g in range(w.Hkv):
-            fill_slab(w, b, g, seqlen_of(w, seqlens, b), k[b, g], v[b, g])
+    for b, g, L, kr, vr in iter_slabs(w, seqlens, threads):
+        k[b, g, :L], v[b, g, :L] = kr[:L], vr[:L]
+        if L < w.Lmax:
+            _poison(k[b, g, L:])
+            _poison(v[b, g, L:])
     return q, k, v, seqlens
 
 
@@ -320,18 +369,15 @@ def device_inputs(w: Workload, seqlens=None, keep_host: bool = False,
     host = None
     if keep_host:
         host = (q_h, np.empty(shape, w.np_dtype), np.empty(shape, w.np_dtype))
-    for b in range(w.B):
-        L = seqlen_of(w, seqlens, b)
-        for g in range(w.Hkv):
-            kr, vr = gen_slab_rows(w, b, g, L)
-            if L:
-                k[b, g, :L].copy_(to_device(kr, device))
-                v[b, g, :L].copy_(to_device(vr, device))
-            if keep_host:
-                host[1][b, g, :L], host[2][b, g, :L] = kr, vr
-                if L < w.Lmax:
-                    host[1][b, g, L:].view(np.uint8)[:] = 0xFF
-                    host[2][b, g, L:].view(np.uint8)[:] = 0xFF
+    for b, g, L, kr, vr in iter_slabs(w, seqlens):
+        if L:
+            k[b, g, :L].copy_(to_device(kr, device))
+            v[b, g, :L].copy_(to_device(vr, device))
+        if keep_host:
+            host[1][b, g, :L], host[2][b, g, :L] = kr, vr
+            if L < w.Lmax:
+                _poison(host[1][b, g, L:])
+                _poison(host[2][b, g, L:])
     sl_dev = None
     if seqlens is not None:
         sl_dev = torch.from_numpy(np.asarray(seqlens, np.int32)).to(device)
@@ -346,9 +392,19 @@ def device_paged_inputs(w: Workload, seqlens=None, device: str = "cuda"):
     the device (rows past a length and spare pages hold NaN bits), then
     released.
     """
-    import torch
     seqlens = paged_seqlens(w, seqlens)
     q, k, v, sl_dev, _, _ = device_inputs(w, seqlens=seqlens, device=device)
+    kp, vp, bt_dev, bt = pages_from_contiguous(w, k, v, device)
+    del k, v
+    return q, kp, vp, bt_dev, sl_dev, seqlens, bt
+
+
+def pages_from_contiguous(w: Workload, k, v, device: str = "cuda"):
+    """Page pools holding the rows of the contiguous device cache k, v
+    [B, Hkv, Lmax, D] (whose rows past each length must already be NaN):
+    (k_pages, v_pages, block_table_dev, block_table_host).  Page j of
+    sequence b is pool page block_table[b, j]; spare pages are NaN."""
+    import torch
     bt = gen_block_table(w)
     P, mp = w.page_size, w.max_pages
     iv = torch.int16 if w.dtype == "bf16" else torch.int32
@@ -370,9 +426,8 @@ def device_paged_inputs(w: Workload, seqlens=None, device: str = "cuda"):
         pool.view(iv).index_copy_(0, idx, pages.reshape(
             (w.B * mp,) + shape[1:]).view(iv))
         pools.append(pool)
-    del k, v
     bt_dev = torch.from_numpy(bt).to(device)
-    return q, pools[0], pools[1], bt_dev, sl_dev, seqlens, bt
+    return pools[0], pools[1], bt_dev, bt
 
 
 def algorithmic_bytes(w: Workload, seqlens=None) -> int:

@@ -19,34 +19,64 @@ def out_to_host(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def sample_rows(w: wl.Workload, seqlens, n: int, seed: int = 0):
-    """(b, h) rows to check one by one: first, last, the shortest and the
-    longest sequence, and n random others."""
-    rng = np.random.default_rng(seed)
-    rows = {(0, 0), (w.B - 1, w.Hq - 1)}
+def upload_full(w: wl.Workload, oracle_mod=None, seqlens=None,
+                device: str = "cuda"):
+    """Device inputs of workload w, built slab by slab as
+    wl.device_inputs builds them, and, with oracle_mod, the oracle's
+    out/lse for EVERY row: each batch entry's slabs are kept on the host
+    just long enough for the fp64 oracle to attend all its query rows
+    (all host threads), so no padded host copy of the cache is made.
+
+    Returns (q, k, v, seqlens_dev, seqlens_host, ref) with ref =
+    (out [B, Hq, D] or [B, Tq, Hq, D], lse [B, Hq] or [B, Tq, Hq]),
+    float64, or None without oracle_mod."""
+    import torch
+    if seqlens is None:
+        seqlens = wl.gen_seqlens(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q_h = wl.gen_q(w)
+    q = to_dev(q_h, device)
+    shape = (w.B, w.Hkv, w.Lmax, w.D)
+    k = torch.empty(shape, dtype=tdt, device=device)
+    v = torch.empty(shape, dtype=tdt, device=device)
     if seqlens is not None:
-        rows.add((int(np.argmin(seqlens)), 0))
-        rows.add((int(np.argmax(seqlens)), w.Hq // 2))
-    target = min(len(rows) + n, w.B * w.Hq)
-    while len(rows) < target:
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq))))
-    return sorted(rows)
+        iv = torch.int16 if w.dtype == "bf16" else torch.int32
+        k.view(iv).fill_(-1)            # NaN past every length
+        v.view(iv).fill_(-1)
+    ref = None
+    if oracle_mod is not None:
+        ref = (np.empty(q_h.shape, np.float64),
+               np.empty(q_h.shape[:-1], np.float64))
+    slab = {}
 
+    def attend(b):
+        L = slab["L"]
+        sl1 = np.array([L], np.int32)
+        if w.Tq > 1:
+            o, l = oracle_mod.decode_multiquery(q_h[b:b + 1], slab["k"],
+                                                slab["v"], sl1, w.scale)
+        else:
+            o, l = oracle_mod.decode(q_h[b:b + 1], slab["k"], slab["v"],
+                                     sl1, w.scale)
+        ref[0][b], ref[1][b] = o[0], l[0]
 
-def oracle_rows(oracle_mod, w: wl.Workload, seqlens, rows):
-    """Exact out/lse for the given (b, h) rows, regenerating only the
-    slabs they read."""
-    q = wl.gen_q(w)
-    res = {}
-    by_slab = {}
-    for b, h in rows:
-        by_slab.setdefault((b, h // w.G), []).append(h)
-    for (b, g), hs in by_slab.items():
-        L = wl.seqlen_of(w, seqlens, b)
-        kr, vr = wl.gen_slab_rows(w, b, g, L)
-        if L == 0:
-            kr = np.zeros((1, w.D), w.np_dtype)
-            vr = np.zeros((1, w.D), w.np_dtype)
-        for h in hs:
-            res[(b, h)] = oracle_mod.attend_row(q[b, h], kr, vr, L, w.scale)
-    return res
+    for b, g, L, kr, vr in wl.iter_slabs(w, seqlens):
+        if L:
+            k[b, g, :L].copy_(to_dev(kr, device))
+            v[b, g, :L].copy_(to_dev(vr, device))
+        if ref is None:
+            continue
+        if slab.get("b") != b:
+            if "b" in slab:
+                attend(slab["b"])
+            n = max(L, 1)
+            slab = {"b": b, "L": L,
+                    "k": np.zeros((1, w.Hkv, n, w.D), w.np_dtype),
+                    "v": np.zeros((1, w.Hkv, n, w.D), w.np_dtype)}
+        slab["k"][0, g, :L], slab["v"][0, g, :L] = kr, vr
+    if ref is not None and "b" in slab:
+        attend(slab["b"])
+    sl_dev = None
+    if seqlens is not None:
+        sl_dev = torch.from_numpy(np.asarray(seqlens, np.int32)).to(device)
+    return q, k, v, sl_dev, seqlens, ref

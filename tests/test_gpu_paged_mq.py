@@ -7,14 +7,15 @@ decode_multiquery.  Sizes span several 32-key tiles, several chunks and a
 ragged tail; page sizes 16 .. 256; lengths include 0, 1, a page boundary,
 lengths below Tq, and lengths beyond the table's capacity (clamped).  At
 the 64k shape the paged call must reproduce the contiguous call bit for bit
-(same plan, same rows), and sampled rows are checked against the oracle.
+(same plan, same rows), and every row is checked against the oracle; so
+are the two multi-token workloads at full size.
 """
 import numpy as np
 import pytest
 
 import long_context_decode_fd_amd as fd
 from long_context_decode_fd_amd import workloads as wl
-from gpu_util import out_to_host, sample_rows, to_dev
+from gpu_util import out_to_host, to_dev, upload_full
 from parity import check_lse, check_out
 
 pytestmark = pytest.mark.gpu
@@ -151,31 +152,22 @@ def test_paged_equals_contiguous_bitwise(torch, hm):
                                   "paged_hm_p64_b1_gqa8_h64_d128_l65536"])
 def test_paged_full_size_64k(torch, oracle_mod, name):
     """The 64k batch-1 shape from 64-token pages, in the benchmark's launch
-    configuration: bit-identical to the contiguous call, sampled rows
-    against the oracle."""
+    configuration: bit-identical to the contiguous call, every row against
+    the oracle."""
     w = wl.EXTRA_WORKLOADS[name]
-    _note(f"{w.name}: generating")
-    q, kp, vp, btd, sld, seqlens, bt = wl.device_paged_inputs(w)
+    _note(f"{w.name}: generating inputs and the oracle's rows")
+    seqlens = wl.paged_seqlens(w)
+    q, k, v, sld, seqlens, ref = upload_full(w.with_(page_size=0),
+                                             oracle_mod, seqlens=seqlens)
+    kp, vp, btd, _ = wl.pages_from_contiguous(w, k, v)
     out, lse = fd.fd_decode_paged(q, kp, vp, btd, sld, w.scale,
                                   head_major=w.head_major)
-    torch.cuda.synchronize()
-    del kp, vp
-    _, k, v, _, _, _ = wl.device_inputs(w.with_(page_size=0),
-                                        seqlens=seqlens)
     co, cl = fd.fd_decode(q, k, v, sld, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), co.view(torch.int16))
     assert torch.equal(lse, cl)
-    rows = sample_rows(w, seqlens, n=6, seed=7)
-    qh = wl.gen_q(w)
-    o_h, l_h = out_to_host(out), lse.cpu().numpy()
-    for b, h in rows:
-        kr, vr = wl.gen_slab_rows(w, b, h // w.G, int(seqlens[b]))
-        ro, rl = oracle_mod.attend_row(qh[b, h], kr, vr, int(seqlens[b]),
-                                       w.scale)
-        _assert_parity(out[b, h], lse[b, h:h + 1], ro, np.array([rl]),
-                       f"{w.name} row {(b, h)}")
-    assert o_h.shape == (1, 64, 128) and l_h.shape == (1, 64)
+    assert out.shape == (1, 64, 128) and lse.shape == (1, 64)
+    _assert_parity(out, lse, ref[0], ref[1], f"{w.name} every row")
 
 
 PAGED_MQ_SHAPES = [
@@ -216,28 +208,20 @@ def test_paged_multiquery_matches_oracle(torch, oracle_mod, shape, splits,
 def test_paged_multiquery_full_size_equals_contiguous(torch, oracle_mod):
     """Two new tokens over 64-token head-major pages at batch-1 64k: bit
     for bit the contiguous multi-token call on the same rows (same plan),
-    sampled rows against the oracle."""
+    every row against the oracle."""
     w = wl.EXTRA_WORKLOADS["paged_hm_p64_mq2_b1_gqa8_h64_d128_l65536"]
-    _note(f"{w.name}: generating")
-    q, kp, vp, btd, sld, seqlens, _ = wl.device_paged_inputs(w)
+    _note(f"{w.name}: generating inputs and the oracle's rows")
+    seqlens = wl.paged_seqlens(w)
+    q, k, v, sld, seqlens, ref = upload_full(w.with_(page_size=0),
+                                             oracle_mod, seqlens=seqlens)
+    kp, vp, btd, _ = wl.pages_from_contiguous(w, k, v)
     out, lse = fd.fd_decode_paged(q, kp, vp, btd, sld, w.scale,
                                   head_major=True)
-    torch.cuda.synchronize()
-    del kp, vp
-    _, k, v, _, _, _ = wl.device_inputs(w.with_(page_size=0),
-                                        seqlens=seqlens)
     co, cl = fd.fd_decode_multiquery(q, k, v, sld, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), co.view(torch.int16))
     assert torch.equal(lse, cl)
-    qh = wl.gen_q(w)
-    for b, t, h in [(0, 0, 0), (0, 1, 63), (0, 0, 17), (0, 1, 40)]:
-        L = int(seqlens[b])
-        kr, vr = wl.gen_slab_rows(w, b, h // w.G, L)
-        ro, rl = oracle_mod.attend_row(qh[b, t, h], kr, vr,
-                                       L - (w.Tq - 1 - t), w.scale)
-        _assert_parity(out[b, t, h], lse[b, t, h:h + 1], ro, np.array([rl]),
-                       f"{w.name} row {(b, t, h)}")
+    _assert_parity(out, lse, ref[0], ref[1], f"{w.name} every row")
 
 
 # ---------------------------------------------------------------------------
@@ -316,11 +300,11 @@ def test_multiquery_one_token_is_decode_bitwise(torch):
                                   "mq4_b64_gqa4_h32_d128_l4096"])
 def test_multiquery_full_size(torch, oracle_mod, name):
     """The two multi-token workloads at full size, as the benchmark runs
-    them: sampled (b, token, head) rows against the oracle, and every row
-    inside its V column range."""
+    them: every (b, token, head) row against the oracle, bitwise
+    repeatable, and every row inside its V column range."""
     w = wl.EXTRA_WORKLOADS[name]
-    _note(f"{name}: generating")
-    q, k, v, sl, seqlens, _ = wl.device_inputs(w)
+    _note(f"{name}: generating inputs and the oracle's rows")
+    q, k, v, sl, seqlens, ref = upload_full(w, oracle_mod)
     out, lse = fd.fd_decode_multiquery(q, k, v, sl, w.scale)
     out2, lse2 = fd.fd_decode_multiquery(q, k, v, sl, w.scale)
     torch.cuda.synchronize()
@@ -333,16 +317,5 @@ def test_multiquery_full_size(torch, oracle_mod, name):
     slack = 1e-2 + 2 ** -7 * torch.maximum(vmax.abs(), vmin.abs())
     assert bool((of <= vmax[:, None] + slack[:, None]).all())
     assert bool((of >= vmin[:, None] - slack[:, None]).all())
-    qh = wl.gen_q(w)
-    rng = np.random.default_rng(w.seed)
-    picks = {(0, 0, 0), (w.B - 1, w.Tq - 1, w.Hq - 1), (0, w.Tq - 1, 5)}
-    while len(picks) < 10:
-        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Tq)),
-                   int(rng.integers(w.Hq))))
-    for b, t, h in sorted(picks):
-        L = wl.seqlen_of(w, seqlens, b)
-        Lt = max(0, L - (w.Tq - 1 - t))
-        kr, vr = wl.gen_slab_rows(w, b, h // w.G, L)
-        ro, rl = oracle_mod.attend_row(qh[b, t, h], kr, vr, Lt, w.scale)
-        _assert_parity(out[b, t, h], lse[b, t, h:h + 1], ro, np.array([rl]),
-                       f"{name} row {(b, t, h)}")
+    _assert_parity(out, lse, ref[0], ref[1], f"{name} every row")
+

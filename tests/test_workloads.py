@@ -135,3 +135,22 @@ def test_multi_token_queries_extend_the_q_stream():
     base = wl.WORKLOADS["b64_gqa4_h32_d128_l4096"]
     assert wl.algorithmic_bytes(w) - wl.algorithmic_bytes(base) == \
         3 * (2 * 64 * 32 * 128 * 2 + 4 * 64 * 32)
+
+
+def test_threaded_generation_matches_one_slab_at_a_time():
+    w = wl.WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=3, Hq=8, Hkv=4, Lmax=300, varlen=(20, 300))
+    seqlens = np.array([300, 0, 77], np.int32)
+    q, k, v, _ = wl.gen_all(w, seqlens=seqlens, threads=4)
+    slabs = list(wl.iter_slabs(w, seqlens, threads=3))
+    assert [(b, g) for b, g, *_ in slabs] == [(b, g) for b in range(3)
+                                              for g in range(4)]
+    for b, g, L, kr, vr in slabs:
+        assert L == int(seqlens[b])
+        k1, v1 = wl.gen_slab(w, b, g, seqlens)
+        np.testing.assert_array_equal(k[b, g], k1)
+        np.testing.assert_array_equal(v[b, g], v1)
+        np.testing.assert_array_equal(kr, k1[:L])
+        np.testing.assert_array_equal(vr, v1[:L])
+    k_serial = wl.gen_all(w, seqlens=seqlens, threads=1)[1]
+    np.testing.assert_array_equal(k, k_serial)
