@@ -47,7 +47,7 @@
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
  * pointer to a caller's buffer after a call returns; the only memory it
- * holds is its own workspace (fd_decode).  Calls plan for the current HIP
+ * holds is its own workspace (calls given no workspace use it).  Calls plan for the current HIP
  * device (its compute-unit count) and keep that workspace on it, so the
  * current device must be the one that holds the buffers and the stream.
  * out and lse must not overlap each other, an input or the workspace (the
@@ -64,6 +64,14 @@
  * waits for the device), so it cannot validate the device-side seqlens: a
  * value outside [0, Lmax] is a caller error that the kernels clamp into
  * that range.
+ *
+ * Graph capture.  A call with a caller workspace (or whose plan needs no
+ * workspace) queues kernels only and may be captured in a HIP graph.  A
+ * call that would use the library-owned workspace returns FD_ERR_CAPTURE
+ * while `stream` is capturing: a later call may free and replace that
+ * buffer, which a graph must not hold.
+ *
+ * Symbols.  libfd.so exports exactly the functions declared here.
  */
 #ifndef FD_H
 #define FD_H
@@ -73,6 +81,12 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+/* Marks the exported entry points (the library is built with every other
+   symbol hidden). */
+#ifndef FD_API
+#define FD_API __attribute__((visibility("default")))
 #endif
 
 typedef enum fd_dtype {
@@ -87,16 +101,19 @@ enum {
     FD_ERR_UNSUPPORTED = -2, /* D, dtype, group size or Lmax outside the
                                 supported range */
     FD_ERR_WORKSPACE = -3,   /* caller workspace too small / alloc failed */
-    FD_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+    FD_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+    FD_ERR_CAPTURE = -5      /* the library-owned workspace was needed while
+                                `stream` is capturing a graph */
 };
 
 /* Flags of fd_decode_ex / fd_plan. */
 enum {
     /* Merge the chunks inside the per-chunk launch: the last workgroup of
        each (b, KV head) group, found with a ticket counter, merges it.
-       Publishing partials across MI355X's eight L2s then takes an
-       agent-scope release (an L2 write-back) per workgroup, which costs
-       more than the second launch it saves; kept for callers that must
+       The partials then cross MI355X's eight L2 caches as write-through
+       stores, and one workgroup per group merges them at the end of the
+       launch; measured slower than the separate merge kernel at batch 1,
+       so the planner never picks it by itself.  For callers that must
        have a single launch. */
     FD_FLAG_FUSED_MERGE = 1,
     /* Always leave per-chunk partials, even when one chunk per sequence
@@ -151,16 +168,18 @@ typedef struct fd_plan_info {
 /*
  * fd_decode -- out, lse = attention(q, k_cache, v_cache) as defined above.
  * Uses a workspace owned by the library: allocated on first use per
- * device and grown when a larger problem needs it (that call allocates,
- * so keep it out of graph capture).  Calls on different streams of one
- * device must not overlap, since they share that workspace.  Results do
- * not depend on the order in which workgroups finish: for a given plan the
- * output is bitwise reproducible.
+ * device and grown when a larger problem needs it (that call allocates
+ * and synchronises; the others queue kernels only).  Calls on different
+ * streams of one device must not overlap, since they share that
+ * workspace.  Under stream capture: FD_ERR_CAPTURE whenever the plan needs
+ * a workspace (see "Graph capture").  Results do not depend on the order
+ * in which workgroups finish: for a given plan the output is bitwise
+ * reproducible.
  */
-int fd_decode(const void *q, const void *k_cache, const void *v_cache,
-              const int32_t *seqlens, int B, int Hq, int Hkv, int D,
-              int Lmax, float scale, fd_dtype_t dtype, void *out, float *lse,
-              void *stream);
+FD_API int fd_decode(const void *q, const void *k_cache,
+                     const void *v_cache, const int32_t *seqlens, int B,
+                     int Hq, int Hkv, int D, int Lmax, float scale,
+                     fd_dtype_t dtype, void *out, float *lse, void *stream);
 
 /*
  * fd_decode_ex -- as fd_decode, with the caller's choices:
@@ -181,11 +200,13 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
  *               the buffer holds partials, so zero-fill again before reusing
  *               it for a fused call with a larger B * Hkv.
  */
-int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
-                 const int32_t *seqlens, int B, int Hq, int Hkv, int D,
-                 int Lmax, float scale, fd_dtype_t dtype, void *out,
-                 float *lse, int num_splits, int variant, int flags,
-                 void *workspace, size_t workspace_bytes, void *stream);
+FD_API int fd_decode_ex(const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *seqlens, int B,
+                        int Hq, int Hkv, int D, int Lmax, float scale,
+                        fd_dtype_t dtype, void *out, float *lse,
+                        int num_splits, int variant, int flags,
+                        void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /*
  * fd_decode_partials / fd_merge_partials -- the two phases of a split decode
@@ -199,18 +220,18 @@ int fd_decode_ex(const void *q, const void *k_cache, const void *v_cache,
  * and flags as the fd_decode_partials call that filled the workspace, and
  * run after it (same stream, or ordered by the caller).
  */
-int fd_decode_partials(const void *q, const void *k_cache,
-                       const void *v_cache, const int32_t *seqlens, int B,
-                       int Hq, int Hkv, int D, int Lmax, float scale,
-                       fd_dtype_t dtype, int num_splits, int variant,
-                       int flags, void *workspace, size_t workspace_bytes,
-                       void *stream);
+FD_API int fd_decode_partials(const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *seqlens,
+                              int B, int Hq, int Hkv, int D, int Lmax,
+                              float scale, fd_dtype_t dtype, int num_splits,
+                              int variant, int flags, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
-int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
-                      int Lmax, fd_dtype_t dtype, int num_splits, int variant,
-                      int flags, const void *workspace,
-                      size_t workspace_bytes, void *out, float *lse,
-                      void *stream);
+FD_API int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv,
+                             int D, int Lmax, fd_dtype_t dtype,
+                             int num_splits, int variant, int flags,
+                             const void *workspace, size_t workspace_bytes,
+                             void *out, float *lse, void *stream);
 
 /*
  * fd_plan -- the decision fd_decode_ex would take, without launching.
@@ -218,9 +239,9 @@ int fd_merge_partials(const int32_t *seqlens, int B, int Hq, int Hkv, int D,
  * a mix of lengths).  num_cus: compute units to plan for; 0 queries the
  * current HIP device.  Returns FD_OK or an FD_ERR_* code (plan untouched).
  */
-int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
-            int varlen, int num_splits, int variant, int flags, int num_cus,
-            fd_plan_t *plan);
+FD_API int fd_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
+                   int varlen, int num_splits, int variant, int flags,
+                   int num_cus, fd_plan_t *plan);
 
 /* Page-pool layouts of fd_decode_paged. */
 enum {
@@ -256,15 +277,19 @@ enum {
  * outside the pools).
  * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Tq * Hq/Hkv <= 16.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
- * tokens; FD_FLAG_FUSED_MERGE allowed).  Workspace: the library-owned one,
- * as for fd_decode.
+ * tokens; FD_FLAG_FUSED_MERGE allowed).  workspace, workspace_bytes: as
+ * for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D,
+ * max_pages * page_size, dtype, 1, 1, num_splits, FD_VARIANT_AUTO, flags,
+ * 0, &plan).workspace_bytes; NULL and 0 use the library-owned one.
  */
-int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
-                    const int32_t *block_table, int max_pages, int page_size,
-                    int num_pages, int layout, const int32_t *seqlens, int B,
-                    int Tq, int Hq, int Hkv, int D, float scale,
-                    fd_dtype_t dtype, void *out, float *lse, int num_splits,
-                    int flags, void *stream);
+FD_API int fd_decode_paged(const void *q, const void *k_pages,
+                           const void *v_pages, const int32_t *block_table,
+                           int max_pages, int page_size, int num_pages,
+                           int layout, const int32_t *seqlens, int B, int Tq,
+                           int Hq, int Hkv, int D, float scale,
+                           fd_dtype_t dtype, void *out, float *lse,
+                           int num_splits, int flags, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * fd_decode_multiquery -- Tq new query tokens per sequence at once (the
@@ -281,13 +306,17 @@ int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
  * for the tile and weighted by exactly 0: their V rows must be finite.
  * bf16 only, 1 <= Tq * Hq/Hkv <= 16 (all query rows of a KV head share
  * one 16-column matrix-core tile).  num_splits, flags and the workspace
- * as for fd_decode_paged.
+ * as for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, dtype,
+ * seqlens != NULL, 0, num_splits, FD_VARIANT_AUTO, flags, 0,
+ * &plan).workspace_bytes.
  */
-int fd_decode_multiquery(const void *q, const void *k_cache,
-                         const void *v_cache, const int32_t *seqlens, int B,
-                         int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
-                         fd_dtype_t dtype, void *out, float *lse,
-                         int num_splits, int flags, void *stream);
+FD_API int fd_decode_multiquery(const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *seqlens,
+                                int B, int Tq, int Hq, int Hkv, int D,
+                                int Lmax, float scale, fd_dtype_t dtype,
+                                void *out, float *lse, int num_splits,
+                                int flags, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * fd_decode_unified_max -- fd_decode_ex computed with FlashDecoding++'s
@@ -308,12 +337,13 @@ int fd_decode_multiquery(const void *q, const void *k_cache,
  * num_splits, flags (FD_FLAG_FUSED_MERGE), workspace: as for
  * fd_decode_ex; plan with FD_FLAG_UNIFIED_MAX for the workspace size.
  */
-int fd_decode_unified_max(const void *q, const void *k_cache,
-                          const void *v_cache, const int32_t *seqlens, int B,
-                          int Hq, int Hkv, int D, int Lmax, float scale,
-                          fd_dtype_t dtype, void *out, float *lse, float phi,
-                          int num_splits, int flags, void *workspace,
-                          size_t workspace_bytes, void *stream);
+FD_API int fd_decode_unified_max(const void *q, const void *k_cache,
+                                 const void *v_cache, const int32_t *seqlens,
+                                 int B, int Hq, int Hkv, int D, int Lmax,
+                                 float scale, fd_dtype_t dtype, void *out,
+                                 float *lse, float phi, int num_splits,
+                                 int flags, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * fd_plan_ex -- fd_plan for the calls above: Tq query tokens per sequence
@@ -322,24 +352,24 @@ int fd_decode_unified_max(const void *q, const void *k_cache,
  * partial layouts gain the token index: o_part [B][Tq][Hq][S][D], lse_part
  * [B][Tq][Hq][S].
  */
-int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
-               fd_dtype_t dtype, int varlen, int paged, int num_splits,
-               int variant, int flags, int num_cus, fd_plan_t *plan);
+FD_API int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
+                      fd_dtype_t dtype, int varlen, int paged, int num_splits,
+                      int variant, int flags, int num_cus, fd_plan_t *plan);
 
 /*
  * fd_workspace_bytes -- bytes of device workspace fd_decode_ex needs for
  * these arguments on the current device (0 when no merge pass is needed).
  * Returns 0 as well for invalid arguments; fd_plan reports why.
  */
-size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
-                          fd_dtype_t dtype, int varlen, int num_splits,
-                          int variant, int flags);
+FD_API size_t fd_workspace_bytes(int B, int Hq, int Hkv, int D, int Lmax,
+                                 fd_dtype_t dtype, int varlen, int num_splits,
+                                 int variant, int flags);
 
 /* Static English text for a status code. */
-const char *fd_status_string(int status);
+FD_API const char *fd_status_string(int status);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
-int fd_version(void);
+FD_API int fd_version(void);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,8 @@ seeded synthetic workloads used by the tests and the benchmark.
     from long_context_decode_fd_amd import fd_decode
     out, lse = fd_decode(q, k_cache, v_cache, seqlens, scale)
 """
-from ._binding import (FD_BF16, FD_ERR_HIP, FD_ERR_INVALID_ARG,  # noqa: F401
+from ._binding import (FD_BF16, FD_ERR_CAPTURE, FD_ERR_HIP,  # noqa: F401
+                       FD_ERR_INVALID_ARG,
                        FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32,
                        FD_FLAG_FUSED_MERGE, FD_FLAG_PARTIALS,
                        FD_FLAG_UNIFIED_MAX, FD_MERGE_FUSED,

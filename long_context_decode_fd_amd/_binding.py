@@ -22,6 +22,7 @@ FD_ERR_INVALID_ARG = -1
 FD_ERR_UNSUPPORTED = -2
 FD_ERR_WORKSPACE = -3
 FD_ERR_HIP = -4
+FD_ERR_CAPTURE = -5
 FD_VARIANT_AUTO = 0
 FD_VARIANT_MFMA = 1
 FD_VARIANT_VALU = 2
@@ -60,10 +61,10 @@ SIGNATURES = {
                                 _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
     "fd_decode_paged": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                               _i32p, _ci, _ci, _ci, _ci, _ci, _cf, _ci, _vp,
-                              _vp, _ci, _ci, _vp]),
+                              _vp, _ci, _ci, _vp, _sz, _vp]),
     "fd_decode_multiquery": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                                    _ci, _ci, _cf, _ci, _vp, _vp, _ci, _ci,
-                                   _vp]),
+                                   _vp, _sz, _vp]),
     "fd_decode_unified_max": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci,
                                     _ci, _ci, _cf, _ci, _vp, _vp, _cf, _ci,
                                     _ci, _vp, _sz, _vp]),
@@ -250,6 +251,16 @@ def _invoke(name, device, stream, *args):
         raise FdError(name, rc)
 
 
+def _opt_ws(workspace, device, out, lse):
+    """(pointer, bytes) of an optional caller workspace tensor, checked to
+    be on `device` and apart from the outputs; (None, 0) for none."""
+    if workspace is None:
+        return None, 0
+    _same_device(device, workspace=workspace)
+    _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace))
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
                  num_splits=0, variant=FD_VARIANT_AUTO, flags=0,
                  workspace=None, stream=None):
@@ -265,12 +276,7 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
     B, Hq, Hkv, D, Lmax = dims
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        _same_device(q.device, workspace=workspace)
-        _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace))
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
-            workspace.element_size()
+    ws_ptr, ws_bytes = _opt_ws(workspace, q.device, out, lse)
     _invoke("fd_decode_ex", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
@@ -289,12 +295,7 @@ def fd_decode_unified_max(q, k_cache, v_cache, seqlens, scale, phi,
     B, Hq, Hkv, D, Lmax = dims
     if not math.isfinite(float(scale)) or not math.isfinite(float(phi)):
         raise ValueError("scale and phi must be finite")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        _same_device(q.device, workspace=workspace)
-        _no_overlap(dict(out=out, lse=lse), dict(workspace=workspace))
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * \
-            workspace.element_size()
+    ws_ptr, ws_bytes = _opt_ws(workspace, q.device, out, lse)
     _invoke("fd_decode_unified_max", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(),
@@ -393,14 +394,16 @@ def _out_lse(out, lse, shape, lse_shape, dtype, device):
 
 def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
                     out=None, lse=None, num_splits=0, flags=0,
-                    head_major=False, stream=None):
+                    head_major=False, workspace=None, stream=None):
     """Decode attention over a paged KV cache -- see fd.h.
 
     q [B,Hq,D] bf16, or [B,Tq,Hq,D] for Tq causal new tokens;
     k_pages/v_pages [num_pages,page_size,Hkv,D] bf16 (token-major) or
     [num_pages,Hkv,page_size,D] (head_major); block_table int32
     [B,max_pages]; seqlens int32 [B] (required); all on the GPU.  Returns
-    (out, lse) shaped like q and q without its last axis.
+    (out, lse) shaped like q and q without its last axis.  workspace: a
+    uint8 device tensor of fd_plan_ex(..., paged=True)'s workspace_bytes
+    (zero-filled for the fused merge), or None for the library's.
     """
     import torch
     if q.dim() not in (3, 4) or k_pages.dim() != 4:
@@ -432,22 +435,27 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
     _no_overlap(dict(out=out, lse=lse),
                 dict(q=q, k_pages=k_pages, v_pages=v_pages,
                      block_table=block_table, seqlens=seqlens))
+    ws_ptr, ws_bytes = _opt_ws(workspace, q.device, out, lse)
     _invoke("fd_decode_paged", q.device, stream,
         q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], page_size, num_pages,
         FD_PAGES_HEAD_MAJOR if head_major else FD_PAGES_TOKEN_MAJOR,
         seqlens.data_ptr(), B, Tq, Hq, Hkv, D, float(scale),
         _dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
-        int(num_splits), int(flags))
+        int(num_splits), int(flags), ws_ptr, ws_bytes)
     return out, lse
 
 
 def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
-                         lse=None, num_splits=0, flags=0, stream=None):
+                         lse=None, num_splits=0, flags=0, workspace=None,
+                         stream=None):
     """Tq causal query tokens per sequence -- see fd.h.
 
     q [B,Tq,Hq,D] bf16; k_cache/v_cache [B,Hkv,Lmax,D]; seqlens int32 [B]
     on the GPU or None.  Returns (out [B,Tq,Hq,D], lse [B,Tq,Hq]).
+    workspace: a uint8 device tensor of fd_plan_ex(B, Tq, ...)'s
+    workspace_bytes (zero-filled for the fused merge), or None for the
+    library's.
     """
     import torch
     if q.dim() != 4 or k_cache.dim() != 4:
@@ -470,9 +478,10 @@ def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
                  out=out, lse=lse)
     _no_overlap(dict(out=out, lse=lse), dict(q=q, k_cache=k_cache,
                                              v_cache=v_cache, seqlens=seqlens))
+    ws_ptr, ws_bytes = _opt_ws(workspace, q.device, out, lse)
     _invoke("fd_decode_multiquery", q.device, stream,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         None if seqlens is None else seqlens.data_ptr(), B, Tq, Hq, Hkv, D,
         Lmax, float(scale), _dtype_code(q.dtype), out.data_ptr(),
-        lse.data_ptr(), int(num_splits), int(flags))
+        lse.data_ptr(), int(num_splits), int(flags), ws_ptr, ws_bytes)
     return out, lse

@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfd.so")
 SOURCES = ["fd_api.hip", "fd_kernels.hip", "fd_plan.cpp"]
+# Exports of libfd.so: exactly the fd_* entry points of include/fd.h.
+VERSION_SCRIPT = os.path.join(CSRC, "libfd.version")
 # The benchmark's streaming-read helper (not part of the decode path).
 PROBE_LIB = os.path.join(PKG, "libfdprobe.so")
 PROBE_SOURCES = ["fd_probe.hip"]
@@ -36,6 +38,9 @@ def build(out: str = LIB, defines=(), verbose: bool = False,
            # no packed-fp32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument"]
+    if sources == SOURCES:
+        cmd += ["-fvisibility=hidden",
+                f"-Wl,--version-script={VERSION_SCRIPT}"]
     cmd += [f"-D{d}" for d in defines]
     cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", out + ".tmp"]

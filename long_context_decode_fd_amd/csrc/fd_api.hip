@@ -6,6 +6,7 @@
 // compute-unit count, and the kernels are queued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <mutex>
@@ -15,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 20000;  // 2.0.0
 
 bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -54,63 +55,77 @@ int device_cus_locked(int dev, int *out) {
   return FD_OK;
 }
 
-// Library-owned workspace, one per device, grown on demand.  Growing frees
-// the old buffer; hipFree waits for the device, so work still queued on
-// the old buffer completes first.  The fused merge needs its leading ticket
-// bytes to be zero: calls leave their own tickets zero, and zero_bytes
-// tracks how much of the head is known to be zero (a call's partials start
-// right after its tickets, so a call with fewer groups shrinks it).  When a
-// call needs more, the head is cleared on the caller's stream first.
+// Library-owned workspace, one per device, grown on demand.  Layout:
+// [ticket region][partials].  The ticket region, reserved in every layout
+// and zeroed once when the buffer is allocated, holds the fused merge's
+// per-group tickets; fused calls leave their tickets zero again and no
+// other call writes there, so steady-state calls queue kernels only.  The
+// partials of every plan start right after it.  Growing frees the old
+// buffer (hipFree waits for the device, so work still queued on it
+// completes first); a larger buffer is queued for zeroing on the caller's
+// stream before that call's kernels.  The buffer may be freed and replaced
+// by any later call, so a call that needs it is refused under stream
+// capture: a graph must not hold its address.
 struct OwnedWorkspace {
   void *ptr = nullptr;
   size_t bytes = 0;
-  size_t zero_bytes = 0;
+  size_t ticket_cap = 0;  // bytes of the ticket region (256-aligned)
 };
 
-int owned_workspace_locked(int dev, size_t need, size_t ticket_bytes,
-                           hipStream_t stream, void **out);
+// Smallest ticket region: room for 16384 (b, KV head) groups.
+constexpr size_t kMinTicketBytes = 16384 * sizeof(int);
 
-int owned_workspace(size_t need, size_t ticket_bytes, hipStream_t stream,
-                    void **out) {
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int owned_workspace_locked(int dev, size_t ticket_bytes, size_t part_bytes,
+                           hipStream_t stream, void **tickets, void **parts);
+
+int owned_workspace(size_t ticket_bytes, size_t part_bytes,
+                    hipStream_t stream, void **tickets, void **parts) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return FD_ERR_HIP;
+  if (cs != hipStreamCaptureStatusNone) return FD_ERR_CAPTURE;
   try {
-    return owned_workspace_locked(dev, need, ticket_bytes, stream, out);
+    return owned_workspace_locked(dev, ticket_bytes, part_bytes, stream,
+                                  tickets, parts);
   } catch (...) {
     return FD_ERR_WORKSPACE;
   }
 }
 
-int owned_workspace_locked(int dev, size_t need, size_t ticket_bytes,
-                           hipStream_t stream, void **out) {
+int owned_workspace_locked(int dev, size_t ticket_bytes, size_t part_bytes,
+                           hipStream_t stream, void **tickets, void **parts) {
   static std::mutex mu;
   static std::vector<OwnedWorkspace> ws;
   std::lock_guard<std::mutex> lk(mu);
   if ((int)ws.size() <= dev) ws.resize(dev + 1);
   OwnedWorkspace &w = ws[dev];
-  if (w.bytes < need) {
+  if (w.ticket_cap < ticket_bytes || w.bytes - w.ticket_cap < part_bytes) {
+    const size_t tcap = round_up(
+        std::max({w.ticket_cap, ticket_bytes, kMinTicketBytes}), 256);
+    // Round the partials up so that slowly growing problems do not
+    // reallocate often.
+    size_t pcap = std::max(w.bytes - w.ticket_cap, part_bytes);
+    pcap = round_up(pcap + pcap / 4, (size_t)1 << 20);
     if (w.ptr) {
       if (hipFree(w.ptr) != hipSuccess) return FD_ERR_HIP;
       w.ptr = nullptr;
-      w.bytes = 0;
+      w.bytes = w.ticket_cap = 0;
     }
-    // Round up so that slowly growing problems do not reallocate often.
-    size_t sz = need + need / 4;
-    sz = (sz + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
-    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
-      w.ptr = nullptr;
-      return FD_ERR_WORKSPACE;
-    }
-    w.bytes = sz;
-    w.zero_bytes = 0;
-  }
-  if (ticket_bytes > w.zero_bytes) {
-    if (hipMemsetAsync(w.ptr, 0, ticket_bytes, stream) != hipSuccess)
+    void *p = nullptr;
+    if (hipMalloc(&p, tcap + pcap) != hipSuccess) return FD_ERR_WORKSPACE;
+    if (hipMemsetAsync(p, 0, tcap, stream) != hipSuccess) {
+      (void)hipFree(p);
       return FD_ERR_HIP;
+    }
+    w.ptr = p;
+    w.bytes = tcap + pcap;
+    w.ticket_cap = tcap;
   }
-  // This call's partials overwrite everything after its tickets.
-  w.zero_bytes = ticket_bytes;
-  *out = w.ptr;
+  *tickets = w.ptr;
+  *parts = static_cast<char *>(w.ptr) + w.ticket_cap;
   return FD_OK;
 }
 
@@ -121,6 +136,7 @@ int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int Hkv,
                 int *cap) {
   if (!pk.block_table || !seqlens) return FD_ERR_INVALID_ARG;
   if (!aligned(pk.block_table, 4)) return FD_ERR_INVALID_ARG;
+  if (Hkv <= 0) return FD_ERR_INVALID_ARG;
   if (pk.max_pages <= 0 || pk.page_size <= 0 || pk.num_pages <= 0)
     return FD_ERR_INVALID_ARG;
   if (pk.head_major != FD_PAGES_TOKEN_MAJOR &&
@@ -128,9 +144,10 @@ int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int Hkv,
     return FD_ERR_INVALID_ARG;
   // A 16-key half tile must lie inside one page.
   if (pk.page_size % 16 != 0) return FD_ERR_UNSUPPORTED;
-  // Token counts and D-element pool rows are computed in int.
-  if ((long)pk.max_pages * pk.page_size > INT_MAX ||
-      (long)pk.num_pages * pk.page_size * (Hkv > 0 ? Hkv : 1) > INT_MAX)
+  // Token counts and D-element pool rows are computed in int: checked by
+  // division, so that no product can overflow.
+  if (pk.max_pages > INT_MAX / pk.page_size ||
+      pk.num_pages > INT_MAX / pk.page_size / Hkv)
     return FD_ERR_UNSUPPORTED;
   *cap = pk.max_pages * pk.page_size;
   return FD_OK;
@@ -201,20 +218,23 @@ int run(const void *q, const void *k_cache, const void *v_cache,
   a.stream = stream;
   a.phases = phases;
   if (p.combine) {
-    void *ws = workspace;
     const fd::WorkspaceLayout lay = fd::workspace_layout(p);
-    if (ws) {
+    char *tickets = static_cast<char *>(workspace);
+    char *parts = tickets + lay.o_part_off;
+    if (workspace) {
       if (workspace_bytes < p.ws_bytes) return FD_ERR_WORKSPACE;
     } else {
-      rc = owned_workspace(p.ws_bytes, lay.ticket_bytes,
-                           static_cast<hipStream_t>(stream), &ws);
+      void *t = nullptr, *pp = nullptr;
+      rc = owned_workspace(lay.ticket_bytes, lay.total - lay.o_part_off,
+                           static_cast<hipStream_t>(stream), &t, &pp);
       if (rc != FD_OK) return rc;
+      tickets = static_cast<char *>(t);
+      parts = static_cast<char *>(pp);
     }
-    a.tickets = lay.ticket_bytes ? static_cast<int *>(ws) : nullptr;
-    a.o_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                         lay.o_part_off);
-    a.lse_part = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                           lay.lse_part_off);
+    a.tickets = lay.ticket_bytes ? reinterpret_cast<int *>(tickets) : nullptr;
+    a.o_part = reinterpret_cast<float *>(parts);
+    a.lse_part = reinterpret_cast<float *>(parts + (lay.lse_part_off -
+                                                    lay.o_part_off));
   }
   return fd::launch_decode(p, a) == 0 ? FD_OK : FD_ERR_HIP;
 }
@@ -272,7 +292,8 @@ int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int num_pages, int layout, const int32_t *seqlens, int B,
                     int Tq, int Hq, int Hkv, int D, float scale,
                     fd_dtype_t dtype, void *out, float *lse, int num_splits,
-                    int flags, void *stream) {
+                    int flags, void *workspace, size_t workspace_bytes,
+                    void *stream) {
   if (Tq <= 0 || (flags & FD_FLAG_UNIFIED_MAX)) return FD_ERR_INVALID_ARG;
   const fd::PagedKV pk{block_table, max_pages, page_size, num_pages, layout};
   int cap = 0;
@@ -282,22 +303,24 @@ int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
   ex.paged = true;
   ex.Tq = Tq;
   return run(q, k_pages, v_pages, seqlens, B, Hq, Hkv, D, cap, scale, dtype,
-             out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
-             fd::kPhaseChunks | fd::kPhaseMerge, ex, pk);
+             out, lse, num_splits, FD_VARIANT_AUTO, flags, workspace,
+             workspace_bytes, stream, fd::kPhaseChunks | fd::kPhaseMerge, ex,
+             pk);
 }
 
 int fd_decode_multiquery(const void *q, const void *k_cache,
                          const void *v_cache, const int32_t *seqlens, int B,
                          int Tq, int Hq, int Hkv, int D, int Lmax, float scale,
                          fd_dtype_t dtype, void *out, float *lse,
-                         int num_splits, int flags, void *stream) {
+                         int num_splits, int flags, void *workspace,
+                         size_t workspace_bytes, void *stream) {
   if (Tq <= 0 || (flags & FD_FLAG_UNIFIED_MAX)) return FD_ERR_INVALID_ARG;
   if (dtype != FD_BF16) return FD_ERR_UNSUPPORTED;  // also for Tq == 1
   fd::Extra ex;
   ex.Tq = Tq;
   return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
-             out, lse, num_splits, FD_VARIANT_AUTO, flags, nullptr, 0, stream,
-             fd::kPhaseChunks | fd::kPhaseMerge, ex);
+             out, lse, num_splits, FD_VARIANT_AUTO, flags, workspace,
+             workspace_bytes, stream, fd::kPhaseChunks | fd::kPhaseMerge, ex);
 }
 
 int fd_decode_unified_max(const void *q, const void *k_cache,
@@ -381,6 +404,9 @@ const char *fd_status_string(int status) {
       return "workspace too small or could not be allocated";
     case FD_ERR_HIP:
       return "HIP runtime error";
+    case FD_ERR_CAPTURE:
+      return "the library-owned workspace cannot be used under stream "
+             "capture; pass a caller workspace";
     default:
       return "unknown status";
   }

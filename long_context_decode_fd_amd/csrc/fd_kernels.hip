@@ -318,20 +318,30 @@ __device__ void merge_and_store(const float *sm_m, const float *sm_l,
 // group's counter.  The one that takes ticket nb - 1 knows that all nb
 // partials of the group are written; it merges them into out/lse exactly
 // as the separate merge pass would and puts the counter back to zero for
-// the next call.  Ordering across the eight XCDs (separate L2 caches): an
-// agent-scope release fence after the workgroup barrier and before the
-// ticket, and an agent-scope acquire fence in the last workgroup before it
-// reads the other workgroups' partials.  No workgroup ever waits for
-// another, so there is no co-residency requirement.
+// the next call.  No workgroup ever waits for another, so there is no
+// co-residency requirement.
+//
+// Ordering across MI355X's eight XCDs, whose L2 caches are not coherent
+// with each other:
+//   writers  every partial is an agent-scope atomic store, which gfx950
+//            writes through its XCD's L2 to the device coherence point;
+//            each thread then waits for all of its memory operations to
+//            complete (s_waitcnt 0) before the workgroup barrier, and only
+//            then does one thread take the ticket (an agent-scope atomic).
+//            This is the part of an agent-scope release that concerns
+//            atomic stores; the other part, an L2 write-back for plain
+//            stores, is left out on purpose: there are none to publish,
+//            and it would write back the XCD's whole L2 once per
+//            workgroup (measured: far slower than a second launch).
+//   reader   the last workgroup issues an agent-scope acquire fence after
+//            its ticket came back (one L1/L2 invalidate per group, not per
+//            workgroup) and reads the partials with agent-scope atomic
+//            loads.
 //
 // The merge spreads the group's G x D outputs over the workgroup as
 // (row, 4 columns) items; when there are fewer items than threads, each
 // item's chunks are split over `slices` threads whose states meet in LDS.
 constexpr int kTailBatch = 16;
-
-// s_waitcnt with vmcnt(0) and the other counters left alone (gfx9 layout:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-constexpr unsigned kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -477,12 +487,10 @@ __device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
                                     OutT *__restrict__ out,
                                     float *__restrict__ lse, float *scratch,
                                     int *sm_flag) {
-  // Each thread waits until its device-coherent partial stores have
-  // completed; after the barrier all of the workgroup's partials are
-  // visible device-wide, so the relaxed ticket cannot overtake them.  (An
-  // agent-scope release fence would also write back this XCD's whole L2,
-  // once per workgroup: far too slow here.)
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Writer side: every memory operation of this thread, the agent-scope
+  // partial stores included, has completed before the barrier, so the
+  // relaxed ticket below cannot overtake any partial of the workgroup.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     int *t = tickets + (size_t)w.b * Hkv + w.g;
@@ -495,8 +503,9 @@ __device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
   }
   __syncthreads();
   if (!*sm_flag) return;
-  // The last workgroup reads the partials with device-coherent loads,
-  // issued only after its ticket came back.
+  // Reader side: acquire at agent scope after the ticket, then read the
+  // partials with agent-scope atomic loads.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   group_merge<D, OutT>(w, G, Tq, Hq, S, o_part, lse_part, out, lse, scratch);
 }
 

@@ -44,13 +44,28 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in bnd.SIGNATURES
 
 
+def test_library_exports_nothing_else(lib):
+    """The dynamic symbol table holds the header's functions and nothing of
+    the library's internals (planner, launch code, C++ helpers)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    res = subprocess.run([nm, "-D", "--defined-only", bnd.LIB_PATH],
+                         check=True, capture_output=True, text=True)
+    exported = sorted(line.split()[-1] for line in res.stdout.splitlines()
+                      if line.strip())
+    assert exported == declared_functions()
+
+
 def test_status_strings_and_version(lib):
     for code in (fd.FD_OK, fd.FD_ERR_INVALID_ARG, fd.FD_ERR_UNSUPPORTED,
-                 fd.FD_ERR_WORKSPACE, fd.FD_ERR_HIP):
+                 fd.FD_ERR_WORKSPACE, fd.FD_ERR_HIP, fd.FD_ERR_CAPTURE):
         s = fd.fd_status_string(code)
         assert s and s != "unknown status"
     assert fd.fd_status_string(12345) == "unknown status"
-    assert fd.fd_version() == 10000
+    assert fd.fd_version() == 20000
 
 
 # Fake, never dereferenced device addresses: every call below must be
@@ -266,10 +281,11 @@ def test_binding_rejects_outputs_that_overlap():
 def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
                num_pages=8, layout=0, seqlens=A, B=1, Tq=1, Hq=8, Hkv=8,
                D=128, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
-               flags=0):
+               flags=0, ws=None, ws_bytes=0):
     return lib.fd_decode_paged(q, k, v, bt, max_pages, page_size, num_pages,
                                layout, seqlens, B, Tq, Hq, Hkv, D, scale,
-                               dtype, out, lse, num_splits, flags, None)
+                               dtype, out, lse, num_splits, flags, ws,
+                               ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -284,6 +300,15 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(max_pages=1 << 26, page_size=64), fd.FD_ERR_UNSUPPORTED),
     (dict(num_pages=1 << 26, page_size=64), fd.FD_ERR_UNSUPPORTED),
     (dict(num_pages=1 << 22, page_size=64, Hkv=8), fd.FD_ERR_UNSUPPORTED),
+    # products that would overflow a signed 64-bit long are refused too
+    (dict(num_pages=(1 << 31) - 1, page_size=(1 << 30) + 16 * 4,
+          Hkv=1 << 29, Hq=1 << 29), fd.FD_ERR_UNSUPPORTED),
+    (dict(max_pages=(1 << 31) - 1, page_size=(1 << 31) - 16),
+     fd.FD_ERR_UNSUPPORTED),
+    (dict(Hkv=0), fd.FD_ERR_INVALID_ARG),
+    (dict(Hkv=-8), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=256), fd.FD_ERR_INVALID_ARG),
+    (dict(ws=A + 16, ws_bytes=1 << 20), fd.FD_ERR_INVALID_ARG),  # alignment
     (dict(layout=2), fd.FD_ERR_INVALID_ARG),
     (dict(layout=-1), fd.FD_ERR_INVALID_ARG),
     (dict(layout=1, page_size=8), fd.FD_ERR_UNSUPPORTED),
@@ -308,10 +333,10 @@ def test_paged_arguments_rejected_on_host(lib, kw, code):
 
 def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
             D=128, Lmax=64, scale=0.1, dtype=0, out=A, lse=A, num_splits=0,
-            flags=0):
+            flags=0, ws=None, ws_bytes=0):
     return lib.fd_decode_multiquery(q, k, v, seqlens, B, Tq, Hq, Hkv, D, Lmax,
                                     scale, dtype, out, lse, num_splits, flags,
-                                    None)
+                                    ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
