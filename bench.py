@@ -19,7 +19,11 @@ once, q, out, lse) / step time, in GB/s; the roofline object compares the
 dominant kernel with MI355X's 8 TB/s HBM peak (and, as frac_of_stream_ceiling,
 with stream_read_ceiling: a plain streaming read of the same number of bytes,
 measured in the same run); cpu_baseline times the fp64 CPU oracle on the
-host's cores over the same workload.
+host's cores over the same workload.  `configs` reports the five decode
+workloads (tiny fp32 multi-head, batch-1 64k, batch-4 multi-head 32k with
+peaked rows, batch-64 4k, variable-length batch of 16), each timed the
+same way in the same run: µs/step, GB/s and fraction of 8 TB/s for the
+whole step and for the per-chunk pass alone, and the plan.
 
 --workload picks another workload of long_context_decode_fd_amd.workloads,
 including the paged-cache (fd_decode_paged) and multi-token
@@ -222,6 +226,137 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def timed_us(torch, fn, steps: int, warmup: int, stream) -> float:
+    """Average µs of fn(i) over `steps` calls between two HIP events on
+    `stream`, after warm_up(warmup) and a device synchronisation."""
+    warm_up(torch, fn, warmup)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+GRAPH_STEPS = 20    # decode calls per captured graph
+
+
+def graph_us(torch, call, steps: int, warmup: int) -> float:
+    """Device time per call: GRAPH_STEPS calls call(i) captured in one HIP
+    graph (the calls must queue kernels only), the graph replayed until
+    steps calls have run, between two HIP events; no host work between
+    the kernels, so short steps are not limited by the Python caller."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(GRAPH_STEPS):
+            call(i)
+    torch.cuda.synchronize()
+    reps = max(1, steps // GRAPH_STEPS)
+    stream = torch.cuda.current_stream()
+    warm_up(torch, lambda i: g.replay(), max(1, warmup // GRAPH_STEPS))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * GRAPH_STEPS) * 1e3
+
+
+def config_table(torch, fd, wl, steps: int, warmup: int, stream) -> dict:
+    """The five decode workloads, each timed the same way in this run.
+
+    Per workload: the whole fd_decode step (planner's plan, KV rotated over
+    KV_COPIES copies when one copy is under 1 GB, so that the 256 MB
+    Infinity Cache cannot serve a repeat; larger caches exceed it alone),
+    algorithmic bytes / step time against 8 TB/s, and for split plans the
+    per-chunk pass alone (fd_decode_partials, same plan) with its bytes
+    (K, V, q) / time.  A single-pass plan (no merge) is its own per-chunk
+    pass.  us_per_step_graph is the same step replayed from a HIP graph
+    (fd_decode_ex with a caller workspace: the same plan and kernels),
+    which takes the Python caller out of the measurement.  The tiny fp32
+    workload is latency-bound: its fraction of peak is not a bandwidth
+    figure."""
+    table = {}
+    for name in wl.WORKLOAD_ORDER:
+        w = wl.WORKLOADS[name]
+        log(f"[bench] config {name}: generating inputs")
+        q, k, v, sl, seqlens, _ = wl.device_inputs(w)
+        kv_bytes = 2 * k.numel() * k.element_size()
+        copies = KV_COPIES if kv_bytes < (1 << 30) else 1
+        ks = [k] + [k.clone() for _ in range(copies - 1)]
+        vs = [v] + [v.clone() for _ in range(copies - 1)]
+        out = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        plan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                          varlen=sl is not None)
+        step_us = timed_us(torch, lambda i: fd.fd_decode(
+            q, ks[i % copies], vs[i % copies], sl, w.scale, out=out,
+            lse=lse, stream=stream), steps, warmup, stream)
+        ws = torch.empty(max(plan["workspace_bytes"], 256),
+                         dtype=torch.uint8, device="cuda")
+        step_graph_us = graph_us(torch, lambda i: fd.fd_decode_ex(
+            q, ks[i % copies], vs[i % copies], sl, w.scale, out=out,
+            lse=lse, workspace=ws), steps, warmup)
+        del ws
+        nbytes = wl.algorithmic_bytes(w, seqlens)
+        io_bytes = w.B * w.Hq * w.D * w.elem_bytes + 4 * w.B * w.Hq
+        row = {
+            "us_per_step": step_us,
+            "us_per_step_graph": step_graph_us,
+            "GBs": nbytes / step_us / 1e3,
+            "frac_of_peak": nbytes / step_us / 1e3 / PEAK_HBM_GBS,
+            "algorithmic_bytes": nbytes,
+            "kv_copies_rotated": copies,
+            "plan": {"num_splits": plan["num_splits"],
+                     "chunk": plan["chunk"], "grid": plan["grid"],
+                     "variant": "mfma" if plan["variant"] ==
+                     fd.FD_VARIANT_MFMA else "valu",
+                     "merge_pass": bool(plan["combine"])},
+        }
+        if plan["combine"]:
+            pplan = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                               varlen=sl is not None,
+                               flags=fd.FD_FLAG_PARTIALS)
+            ws = torch.zeros(pplan["workspace_bytes"], dtype=torch.uint8,
+                             device="cuda")
+            kern_us = timed_us(torch, lambda i: fd.fd_decode_partials(
+                q, ks[i % copies], vs[i % copies], sl, w.scale, ws,
+                stream=stream), steps, warmup, stream)
+            kern_graph_us = graph_us(torch, lambda i: fd.fd_decode_partials(
+                q, ks[i % copies], vs[i % copies], sl, w.scale, ws),
+                steps, warmup)
+            kbytes = nbytes - io_bytes
+            row["per_chunk_pass"] = {
+                "us": kern_us, "us_graph": kern_graph_us,
+                "GBs": kbytes / kern_us / 1e3,
+                "frac_of_peak": kbytes / kern_us / 1e3 / PEAK_HBM_GBS,
+                "bytes": kbytes}
+            del ws
+        else:
+            row["per_chunk_pass"] = {
+                "us": step_us, "us_graph": step_graph_us, "GBs": row["GBs"],
+                "frac_of_peak": row["frac_of_peak"], "bytes": nbytes,
+                "note": "single-pass plan: the step is the per-chunk pass"}
+        if w.dtype == "f32":
+            row["note"] = ("latency-bound (4 MB per step): report the µs; "
+                           "the fraction of peak is not a bandwidth figure")
+        log(f"[bench] config {name}: {step_us:.2f} us/step "
+            f"({step_graph_us:.2f} from a graph), "
+            f"{row['frac_of_peak'] * 100:.1f}% of 8 TB/s, per-chunk pass "
+            f"{row['per_chunk_pass']['us']:.2f} us")
+        table[name] = row
+        del q, k, v, ks, vs, out, lse
+        torch.cuda.empty_cache()
+    return table
+
+
 def context_sweep(torch, fd, steps: int) -> None:
     """Flash-Decoding against the same kernel unsplit, over context length.
 
@@ -305,6 +440,9 @@ def main(argv=None):
                     help="instead of the benchmark line: Flash-Decoding "
                          "against the same kernel unsplit over context "
                          "length (batch 1 and 8), one JSON line per case")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table of the five decode "
+                         "workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -508,6 +646,11 @@ def main(argv=None):
         "stream_read_ceiling": ceiling,
     }
     roof["frac_of_stream_ceiling"] = roof["achieved"] / ceiling["GBs"]
+    if not a.no_configs and a.workload is None and a.unified_max is None:
+        del ks, vs, k, v
+        torch.cuda.empty_cache()
+        res["configs"] = config_table(torch, fd, wl, a.steps, a.warmup,
+                                      stream)
     if not a.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
