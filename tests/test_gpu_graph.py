@@ -107,7 +107,7 @@ def test_captured_paged_decode_with_caller_workspace(torch, flags):
     torch.cuda.synchronize()
     _replays_match_eager(
         torch, g, q, (out_g, lse_g),
-        lambda: fd.fd_decode_paged(q, kp, vp, bt, sl, w.scale,
+        lambda: fd.fd_decode_paged(q, kp, vp, bt, sl, w.scale, flags=flags,
                                    head_major=True), 3, f"paged {flags}")
     if plan["ticket_bytes"]:
         assert int(ws[:plan["ticket_bytes"]].count_nonzero()) == 0
