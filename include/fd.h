@@ -102,8 +102,10 @@ enum {
                                 supported range */
     FD_ERR_WORKSPACE = -3,   /* caller workspace too small / alloc failed */
     FD_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
-    FD_ERR_CAPTURE = -5      /* the library-owned workspace was needed while
+    FD_ERR_CAPTURE = -5,     /* the library-owned workspace was needed while
                                 `stream` is capturing a graph */
+    FD_ERR_TOO_LARGE = -6    /* fd_decode_noalloc: the plan's partials do
+                                not fit FD_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Flags of fd_decode_ex / fd_plan. */
@@ -207,6 +209,39 @@ FD_API int fd_decode_ex(const void *q, const void *k_cache,
                         int num_splits, int variant, int flags,
                         void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/* Size of fd_decode_noalloc's fixed scratch array, per device. */
+#define FD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fd_decode_noalloc -- fd_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no hipMalloc, hipFree or allocating
+ * library routine and takes no workspace: the chunk partials live in a
+ * fixed device array inside the library, FD_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * on each device, held until the process ends.  A plan whose partials
+ * need more (fd_plan(...).workspace_bytes > FD_NOALLOC_SCRATCH_BYTES)
+ * returns FD_ERR_TOO_LARGE before anything is launched; a single-pass
+ * plan needs none.  The first call on a device looks up that device's
+ * copy of the array (no allocation, no work queued).
+ *   num_splits, variant  as for fd_decode_ex
+ *   flags                0 or FD_FLAG_PARTIALS; FD_FLAG_FUSED_MERGE is
+ *                        FD_ERR_UNSUPPORTED (its tickets would have to be
+ *                        zeroed by every call), FD_FLAG_UNIFIED_MAX
+ *                        FD_ERR_INVALID_ARG
+ * Every call on one device shares that device's array, which keeps the
+ * last call's partials; nothing in it needs to start at zero.  Calls that
+ * overlap on one device (different streams without ordering between them)
+ * race on it and give undefined results: serialise them.  Queues kernels
+ * only, so it can be captured in a HIP graph; a replay uses the array as
+ * any other call on that device does.
+ */
+FD_API int fd_decode_noalloc(const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *seqlens,
+                             int B, int Hq, int Hkv, int D, int Lmax,
+                             float scale, fd_dtype_t dtype, void *out,
+                             float *lse, int num_splits, int variant,
+                             int flags, void *stream);
 
 /*
  * fd_decode_partials / fd_merge_partials -- the two phases of a split decode

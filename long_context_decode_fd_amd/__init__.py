@@ -8,7 +8,7 @@ seeded synthetic workloads used by the tests and the benchmark.
     out, lse = fd_decode(q, k_cache, v_cache, seqlens, scale)
 """
 from ._binding import (FD_BF16, FD_ERR_CAPTURE, FD_ERR_HIP,  # noqa: F401
-                       FD_ERR_INVALID_ARG,
+                       FD_ERR_INVALID_ARG, FD_ERR_TOO_LARGE,
                        FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32,
                        FD_FLAG_FUSED_MERGE, FD_FLAG_PARTIALS,
                        FD_FLAG_UNIFIED_MAX, FD_MERGE_FUSED,
@@ -16,7 +16,8 @@ from ._binding import (FD_BF16, FD_ERR_CAPTURE, FD_ERR_HIP,  # noqa: F401
                        FD_MERGE_SEPARATE, FD_OK, FD_PAGES_HEAD_MAJOR,
                        FD_PAGES_TOKEN_MAJOR,
                        FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
-                       LIB_PATH, FdError, fd_decode, fd_decode_ex,
+                       LIB_PATH, NOALLOC_SCRATCH_BYTES, FdError, fd_decode,
+                       fd_decode_ex, fd_decode_noalloc,
                        fd_decode_multiquery, fd_decode_paged,
                        fd_decode_unified_max,
                        fd_decode_partials, fd_merge_partials, fd_plan,

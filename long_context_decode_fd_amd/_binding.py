@@ -23,6 +23,8 @@ FD_ERR_UNSUPPORTED = -2
 FD_ERR_WORKSPACE = -3
 FD_ERR_HIP = -4
 FD_ERR_CAPTURE = -5
+FD_ERR_TOO_LARGE = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 FD_VARIANT_AUTO = 0
 FD_VARIANT_MFMA = 1
 FD_VARIANT_VALU = 2
@@ -54,6 +56,9 @@ SIGNATURES = {
     "fd_decode_ex": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci, _ci,
                            _cf, _ci, _vp, _vp, _ci, _ci, _ci, _vp, _sz,
                            _vp]),
+    "fd_decode_noalloc": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
+                                _ci, _cf, _ci, _vp, _vp, _ci, _ci, _ci,
+                                _vp]),
     "fd_decode_partials": (_ci, [_vp, _vp, _vp, _i32p, _ci, _ci, _ci, _ci,
                                  _ci, _cf, _ci, _ci, _ci, _ci, _vp, _sz,
                                  _vp]),
@@ -317,6 +322,25 @@ def fd_decode(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
         None if seqlens is None else seqlens.data_ptr(),
         B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
         out.data_ptr(), lse.data_ptr())
+    return out, lse
+
+
+def fd_decode_noalloc(q, k_cache, v_cache, seqlens, scale, out=None,
+                      lse=None, num_splits=0, variant=FD_VARIANT_AUTO,
+                      flags=0, stream=None):
+    """fd_decode_ex with the partials in the library's fixed per-device
+    scratch array: allocates nothing (see fd.h for the size limit and the
+    rule that calls overlapping on one device race)."""
+    dims, out, lse = _check(q, k_cache, v_cache, seqlens, out, lse)
+    B, Hq, Hkv, D, Lmax = dims
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    _invoke("fd_decode_noalloc", q.device, stream,
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if seqlens is None else seqlens.data_ptr(),
+        B, Hq, Hkv, D, Lmax, float(scale), _dtype_code(q.dtype),
+        out.data_ptr(), lse.data_ptr(), int(num_splits), int(variant),
+        int(flags))
     return out, lse
 
 

@@ -130,6 +130,44 @@ int owned_workspace_locked(int dev, size_t ticket_bytes, size_t part_bytes,
 }
 
 
+// Fixed scratch of fd_decode_noalloc: partials of callers that cannot
+// allocate.  Each device holds its own copy of this array for the life of
+// the process.  On the host, `scratch` only names the array; its device
+// address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static_assert(kScratchBytes == FD_NOALLOC_SCRATCH_BYTES,
+              "fd.h states the scratch size");
+
+int scratch_address_locked(int dev, void **out);
+
+int scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_HIP;
+  try {
+    return scratch_address_locked(dev, out);
+  } catch (...) {
+    return FD_ERR_HIP;
+  }
+}
+
+int scratch_address_locked(int dev, void **out) {
+  static std::mutex mu;
+  static std::vector<void *> addr;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess ||
+        p == nullptr)
+      return FD_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return FD_OK;
+}
+
 // Checks of the paged-cache arguments; returns the block table's capacity
 // in tokens (max_pages * page_size) through *cap.
 int check_paged(const fd::PagedKV &pk, const int32_t *seqlens, int Hkv,
@@ -163,7 +201,7 @@ int run(const void *q, const void *k_cache, const void *v_cache,
         int variant, int flags, void *workspace, size_t workspace_bytes,
         void *stream, int phases, fd::Extra ex = fd::Extra(),
         fd::PagedKV pk = fd::PagedKV{nullptr, 0, 0, 0, 0},
-        float unified_max = 0.f) {
+        float unified_max = 0.f, bool use_scratch = false) {
   const bool chunks = phases & fd::kPhaseChunks;
   const bool merge = phases & fd::kPhaseMerge;
   if (chunks) {
@@ -221,7 +259,14 @@ int run(const void *q, const void *k_cache, const void *v_cache,
     const fd::WorkspaceLayout lay = fd::workspace_layout(p);
     char *tickets = static_cast<char *>(workspace);
     char *parts = tickets + lay.o_part_off;
-    if (workspace) {
+    if (use_scratch) {
+      if (p.ws_bytes > kScratchBytes) return FD_ERR_TOO_LARGE;
+      void *sp = nullptr;
+      rc = scratch_address(&sp);
+      if (rc != FD_OK) return rc;
+      tickets = static_cast<char *>(sp);
+      parts = tickets + lay.o_part_off;
+    } else if (workspace) {
       if (workspace_bytes < p.ws_bytes) return FD_ERR_WORKSPACE;
     } else {
       void *t = nullptr, *pp = nullptr;
@@ -261,6 +306,20 @@ int fd_decode(const void *q, const void *k_cache, const void *v_cache,
   return fd_decode_ex(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax,
                       scale, dtype, out, lse, 0, FD_VARIANT_AUTO, 0, nullptr,
                       0, stream);
+}
+
+int fd_decode_noalloc(const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *seqlens, int B,
+                      int Hq, int Hkv, int D, int Lmax, float scale,
+                      fd_dtype_t dtype, void *out, float *lse, int num_splits,
+                      int variant, int flags, void *stream) {
+  if (flags & (FD_FLAG_UNIFIED_MAX | FD_FLAG_FUSED_MERGE))
+    return (flags & FD_FLAG_UNIFIED_MAX) ? FD_ERR_INVALID_ARG
+                                         : FD_ERR_UNSUPPORTED;
+  return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,
+             out, lse, num_splits, variant, flags, nullptr, 0, stream,
+             fd::kPhaseChunks | fd::kPhaseMerge, fd::Extra(),
+             fd::PagedKV{nullptr, 0, 0, 0, 0}, 0.f, true);
 }
 
 int fd_decode_partials(const void *q, const void *k_cache,
@@ -407,6 +466,9 @@ const char *fd_status_string(int status) {
     case FD_ERR_CAPTURE:
       return "the library-owned workspace cannot be used under stream "
              "capture; pass a caller workspace";
+    case FD_ERR_TOO_LARGE:
+      return "the plan's partials exceed fd_decode_noalloc's fixed 64 MiB "
+             "scratch array";
     default:
       return "unknown status";
   }

@@ -35,7 +35,7 @@ def test_header_declares_the_documented_entry_points():
                             "fd_version", "fd_decode_partials",
                             "fd_merge_partials", "fd_decode_paged",
                             "fd_decode_multiquery", "fd_plan_ex",
-                            "fd_decode_unified_max"])
+                            "fd_decode_unified_max", "fd_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -61,7 +61,8 @@ def test_library_exports_nothing_else(lib):
 
 def test_status_strings_and_version(lib):
     for code in (fd.FD_OK, fd.FD_ERR_INVALID_ARG, fd.FD_ERR_UNSUPPORTED,
-                 fd.FD_ERR_WORKSPACE, fd.FD_ERR_HIP, fd.FD_ERR_CAPTURE):
+                 fd.FD_ERR_WORKSPACE, fd.FD_ERR_HIP, fd.FD_ERR_CAPTURE,
+                 fd.FD_ERR_TOO_LARGE):
         s = fd.fd_status_string(code)
         assert s and s != "unknown status"
     assert fd.fd_status_string(12345) == "unknown status"
@@ -430,3 +431,4 @@ def test_unified_max_plans_like_the_exact_pass(lib):
     with pytest.raises(fd.FdError):
         fd.fd_plan_ex(1, 1, 8, 8, 128, 4096, "bf16", paged=True,
                       flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
+
