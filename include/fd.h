@@ -158,14 +158,29 @@ typedef struct fd_plan_info {
     size_t ticket_bytes;    /* leading bytes of the workspace that hold the
                                per-group tickets of the fused merge
                                (0 unless FD_FLAG_FUSED_MERGE) */
-    size_t o_part_offset;   /* byte offset of the partial outputs:
-                               float32 [B][Hq][num_splits][D], each chunk's
-                               own softmax-normalised output */
-    size_t lse_part_offset; /* byte offset of the partial log-sum-exps:
-                               float32 [B][Hq][num_splits], natural log;
-                               chunk s of sequence b exists iff
+    size_t o_part_offset;   /* byte offset of the partial outputs, each
+                               chunk's own softmax-normalised output,
+                               float32, laid out as partial_layout says */
+    size_t lse_part_offset; /* byte offset of the partial log-sum-exps,
+                               float32, natural log, same layout without
+                               the D axis; chunk s of sequence b exists iff
                                s < max(1, ceil(seqlens[b] / chunk)) */
+    int partial_layout;     /* FD_PARTIALS_ROW_MAJOR or _CHUNK_MAJOR */
 } fd_plan_t;
+
+/* Layouts of the chunk partials (fd_plan_t.partial_layout), with S =
+   num_splits, G = Hq / Hkv, Tq query tokens per sequence (1 for decode):
+     FD_PARTIALS_ROW_MAJOR    o_part [B][Tq][Hq][S][D], lse_part
+                              [B][Tq][Hq][S]: a query row's chunks together
+                              (plans whose chunks all run in one round of
+                              workgroups);
+     FD_PARTIALS_CHUNK_MAJOR  o_part [B][Hkv][S][Tq][G][D], lse_part
+                              [B][Hkv][S][Tq][G]: one chunk's rows together
+                              (plans that run in several rounds). */
+enum {
+    FD_PARTIALS_ROW_MAJOR = 0,
+    FD_PARTIALS_CHUNK_MAJOR = 1
+};
 
 /*
  * fd_decode -- out, lse = attention(q, k_cache, v_cache) as defined above.
@@ -384,8 +399,7 @@ FD_API int fd_decode_unified_max(const void *q, const void *k_cache,
  * fd_plan_ex -- fd_plan for the calls above: Tq query tokens per sequence
  * (1 for fd_decode), paged nonzero for a paged cache
  * (then Lmax = max_pages * page_size and seqlens are implied).  The
- * partial layouts gain the token index: o_part [B][Tq][Hq][S][D], lse_part
- * [B][Tq][Hq][S].
+ * partial layouts carry the token index as fd_plan_t.partial_layout shows.
  */
 FD_API int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
                       fd_dtype_t dtype, int varlen, int paged, int num_splits,

@@ -14,7 +14,8 @@ from ._binding import (FD_BF16, FD_ERR_CAPTURE, FD_ERR_HIP,  # noqa: F401
                        FD_FLAG_UNIFIED_MAX, FD_MERGE_FUSED,
                        FD_MERGE_NONE,
                        FD_MERGE_SEPARATE, FD_OK, FD_PAGES_HEAD_MAJOR,
-                       FD_PAGES_TOKEN_MAJOR,
+                       FD_PAGES_TOKEN_MAJOR, FD_PARTIALS_CHUNK_MAJOR,
+                       FD_PARTIALS_ROW_MAJOR,
                        FD_VARIANT_AUTO, FD_VARIANT_MFMA, FD_VARIANT_VALU,
                        LIB_PATH, NOALLOC_SCRATCH_BYTES, FdError, fd_decode,
                        fd_decode_ex, fd_decode_noalloc,

@@ -36,6 +36,8 @@ FD_MERGE_FUSED = 1
 FD_MERGE_SEPARATE = 2
 FD_PAGES_TOKEN_MAJOR = 0
 FD_PAGES_HEAD_MAJOR = 1
+FD_PARTIALS_ROW_MAJOR = 0
+FD_PARTIALS_CHUNK_MAJOR = 1
 
 # Every function the C header declares, with its ctypes signature.
 _vp, _i32p = ctypes.c_void_p, ctypes.c_void_p
@@ -47,7 +49,7 @@ class FdPlanStruct(ctypes.Structure):
                 ("waves_per_block", _ci), ("grid", _ci), ("combine", _ci),
                 ("merge", _ci), ("num_cus", _ci), ("workspace_bytes", _sz),
                 ("ticket_bytes", _sz), ("o_part_offset", _sz),
-                ("lse_part_offset", _sz)]
+                ("lse_part_offset", _sz), ("partial_layout", _ci)]
 
 
 SIGNATURES = {

@@ -429,6 +429,8 @@ int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
   plan->ticket_bytes = lay.ticket_bytes;
   plan->o_part_offset = p.combine ? lay.o_part_off : 0;
   plan->lse_part_offset = p.combine ? lay.lse_part_off : 0;
+  plan->partial_layout =
+      p.chunk_major ? FD_PARTIALS_CHUNK_MAJOR : FD_PARTIALS_ROW_MAJOR;
   return FD_OK;
 }
 

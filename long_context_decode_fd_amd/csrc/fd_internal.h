@@ -34,6 +34,8 @@ struct Plan {
   bool direct;      // with seqlens: chunk ids map straight to (b, s, g)
   bool combine;     // chunks leave partials to be merged (splits > 1)
   bool fused;       // merged by the last workgroup of each group
+  bool chunk_major; // partial layout: chunk-major (several rounds of
+                    // workgroups) or row-major (one round)
   size_t ws_bytes;  // tickets + partial outputs + partial lse
 };
 

@@ -237,6 +237,44 @@ __device__ __forceinline__ size_t row_of(const Work &w, int G, int Hq, int Tq,
   return ((size_t)w.b * Tq + t) * Hq + (size_t)w.g * G + h;
 }
 
+// Where the chunk partials live (the plan picks the layout).  Partial i is
+// lse_part[i] and o_part[i * D ..].
+//   row-major    (one round of workgroups): the S partials of a query row
+//                r = (b, t, head) are consecutive, i = r * S + s;
+//   chunk-major  (several rounds): the G * Tq rows of one chunk of (b, g)
+//                are consecutive, i = ((b * Hkv + g) * S + s) * G * Tq + c
+//                with c = t * G + h the q-tile column, so a chunk stores
+//                one contiguous block of G * Tq * D floats.
+// Either way the partials of one query row are base + s * stride.
+struct PartLayout {
+  int G, Tq, Hq, Hkv, S;
+  bool chunk_major;
+  struct Row {
+    size_t base;
+    int stride;
+  };
+  // q-tile column c of the group (b, g)
+  __device__ __forceinline__ Row row(int b, int g, int c) const {
+    if (chunk_major)
+      return {((size_t)b * Hkv + g) * S * (size_t)(G * Tq) + c, G * Tq};
+    const int t = c / G, h = c - t * G;
+    return {(((size_t)b * Tq + t) * Hq + (size_t)g * G + h) * S, 1};
+  }
+  // query row r = (b * Tq + t) * Hq + head of the outputs
+  __device__ __forceinline__ Row row_of_out(size_t r) const {
+    const int b = (int)(r / ((size_t)Tq * Hq));
+    const int th = (int)(r - (size_t)b * Tq * Hq);
+    const int t = th / Hq, hq = th - t * Hq;
+    const int g = hq / G;
+    return row(b, g, t * G + (hq - g * G));
+  }
+  // partial of chunk w.s, column c
+  __device__ __forceinline__ size_t at(const Work &w, int c) const {
+    const Row r = row(w.b, w.g, c);
+    return r.base + (size_t)w.s * r.stride;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Element helpers.
 
@@ -267,11 +305,12 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 template <int D, typename OutT>
 __device__ void merge_and_store(const float *sm_m, const float *sm_l,
                                 const float *sm_o, int nslot, int rows,
-                                int G, int Tq, const Work &w, int Hq, int S,
+                                const PartLayout &pl, const Work &w,
                                 int mode, OutT *__restrict__ out,
                                 float *__restrict__ lse,
                                 float *__restrict__ o_part,
                                 float *__restrict__ lse_part) {
+  const int G = pl.G, Tq = pl.Tq, Hq = pl.Hq;
   for (int idx = threadIdx.x; idx < G * Tq * D; idx += blockDim.x) {
     const int h = idx / D, d = idx - h * D;
     float M = FD_NEG_INF;
@@ -295,13 +334,13 @@ __device__ void merge_and_store(const float *sm_m, const float *sm_l,
       store_out<OutT>(out + hq * D + d, o);
       if (d == 0) lse[hq] = ls;
     } else if (mode == kModePartial) {
-      const size_t row = hq * S + w.s;
+      const size_t row = pl.at(w, h);
       o_part[row * D + d] = o;
       if (d == 0) lse_part[row] = ls;
     } else {
       // Read by another workgroup of this launch, possibly on another XCD:
       // device-coherent stores (written through the local L2).
-      const size_t row = hq * S + w.s;
+      const size_t row = pl.at(w, h);
       __hip_atomic_store(o_part + row * D + d, o, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0)
@@ -356,15 +395,17 @@ struct TailState {
 // column it / (D/4), output columns 4 (it % (D/4)) ..) into a TailState,
 // kTailBatch chunks per step with all of a step's loads issued first.
 template <int D>
-__device__ TailState merge_item(const Work &w, int G, int Tq, int Hq, int S,
-                                int it, int s_first, int s_step,
+__device__ TailState merge_item(const Work &w, const PartLayout &pl, int it,
+                                int s_first, int s_step,
                                 const float *__restrict__ o_part,
                                 const float *__restrict__ lse_part) {
   constexpr int V4 = D / 4;
   const int h = it / V4, d4 = it - h * V4;
-  const size_t row = row_of(w, G, Hq, Tq, h);
-  const float *lp = lse_part + row * S;
-  const float *op = o_part + row * S * D + d4 * 4;
+  const PartLayout::Row pr = pl.row(w.b, w.g, h);
+  const float *lp = lse_part + pr.base;
+  const float *op = o_part + pr.base * D + d4 * 4;
+  const int ls_step = pr.stride;
+  const size_t o_step = (size_t)pr.stride * D;
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   for (int s0 = s_first; s0 < w.nb; s0 += s_step * kTailBatch) {
     float ls[kTailBatch];
@@ -373,8 +414,9 @@ __device__ TailState merge_item(const Work &w, int G, int Tq, int Hq, int S,
     for (int j = 0; j < kTailBatch; ++j) {
       const int s = s0 + j * s_step;
       const int sc = s < w.nb ? s : s0;
-      ls[j] = s < w.nb ? load_coherent(lp + sc) : FD_NEG_INF;
-      const float *o4 = op + (size_t)sc * D;
+      ls[j] = s < w.nb ? load_coherent(lp + (size_t)sc * ls_step)
+                       : FD_NEG_INF;
+      const float *o4 = op + (size_t)sc * o_step;
       ov[j] = make_float4(load_coherent(o4), load_coherent(o4 + 1),
                           load_coherent(o4 + 2), load_coherent(o4 + 3));
     }
@@ -428,12 +470,13 @@ __device__ void store_item(const Work &w, int G, int Tq, int Hq, int it,
 // Merges the nb chunk partials of group (w.b, w.g) into out/lse with the
 // whole workgroup (the fused path's last workgroup).
 template <int D, typename OutT>
-__device__ void group_merge(const Work &w, int G, int Tq, int Hq, int S,
+__device__ void group_merge(const Work &w, const PartLayout &pl,
                             const float *__restrict__ o_part,
                             const float *__restrict__ lse_part,
                             OutT *__restrict__ out, float *__restrict__ lse,
                             float *scratch) {
   constexpr int V4 = D / 4;
+  const int G = pl.G, Tq = pl.Tq, Hq = pl.Hq;
   const int T = blockDim.x, tid = threadIdx.x;
   const int items = G * Tq * V4;
   // More items than threads: each thread merges whole items on its own.
@@ -441,7 +484,7 @@ __device__ void group_merge(const Work &w, int G, int Tq, int Hq, int S,
   const int slices = max(1, T / items);
   if (slices == 1) {
     for (int it = tid; it < items; it += T) {
-      const TailState st = merge_item<D>(w, G, Tq, Hq, S, it, 0, 1, o_part,
+      const TailState st = merge_item<D>(w, pl, it, 0, 1, o_part,
                                          lse_part);
       store_item<D, OutT>(w, G, Tq, Hq, it, st.M, st.W, st.acc, out, lse);
     }
@@ -451,8 +494,8 @@ __device__ void group_merge(const Work &w, int G, int Tq, int Hq, int S,
   float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   if (tid < items * slices)
-    st = merge_item<D>(w, G, Tq, Hq, S, tid % items, tid / items, slices,
-                       o_part, lse_part);
+    st = merge_item<D>(w, pl, tid % items, tid / items, slices, o_part,
+                       lse_part);
   sM[tid] = st.M;
   sW[tid] = st.W;
   sA[tid] = st.acc;
@@ -479,8 +522,7 @@ __device__ void group_merge(const Work &w, int G, int Tq, int Hq, int S,
 }
 
 template <int D, typename OutT>
-__device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
-                                    int Hkv, int S,
+__device__ void merge_group_if_last(const Work &w, const PartLayout &pl,
                                     const float *__restrict__ o_part,
                                     const float *__restrict__ lse_part,
                                     int *__restrict__ tickets,
@@ -493,7 +535,7 @@ __device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int *t = tickets + (size_t)w.b * Hkv + w.g;
+    int *t = tickets + (size_t)w.b * pl.Hkv + w.g;
     const int prev = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == w.nb - 1;
@@ -506,7 +548,7 @@ __device__ void merge_group_if_last(const Work &w, int G, int Tq, int Hq,
   // Reader side: acquire at agent scope after the ticket, then read the
   // partials with agent-scope atomic loads.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  group_merge<D, OutT>(w, G, Tq, Hq, S, o_part, lse_part, out, lse, scratch);
+  group_merge<D, OutT>(w, pl, o_part, lse_part, out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -997,7 +1039,7 @@ template <int D, int NW>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
     int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
-    const Work &w, int G, int Tq, int Hq, int S, int mode,
+    const Work &w, const PartLayout &pl, int mode,
     uint16_t *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part) {
   constexpr int VW = D / 16;
@@ -1034,7 +1076,9 @@ __device__ __forceinline__ void wave_merge_store(
   const float inv = M == FD_NEG_INF ? 0.f : 1.f / W;
 #pragma unroll
   for (int sl = 0; sl < NW; ++sl) wt[sl] *= inv;
-  const size_t row = row_of(w, G, Hq, Tq, n16);
+  // out/lse row (direct) or partial index (partial mode) of this column
+  const size_t row = mode == kModeDirect ? row_of(w, pl.G, pl.Hq, pl.Tq, n16)
+                                         : pl.at(w, n16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -1057,7 +1101,7 @@ __device__ __forceinline__ void wave_merge_store(
         bits.y = (uint32_t)to_bf16_bits(o.z) | ((uint32_t)to_bf16_bits(o.w) << 16);
         *reinterpret_cast<uint2 *>(out + row * D + d0) = bits;
       } else {
-        *reinterpret_cast<float4 *>(o_part + (row * S + w.s) * D + d0) = o;
+        *reinterpret_cast<float4 *>(o_part + row * D + d0) = o;
       }
     }
   }
@@ -1066,7 +1110,7 @@ __device__ __forceinline__ void wave_merge_store(
     if (mode == kModeDirect)
       lse[row] = ls;
     else
-      lse_part[row * S + w.s] = ls;
+      lse_part[row] = ls;
   }
 }
 
@@ -1082,12 +1126,14 @@ __device__ __forceinline__ void chunk_pass(
     const Work &w, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, float phi2, int mode, uint16_t *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ o_part,
-    float *__restrict__ lse_part, int *__restrict__ tickets) {
+    float scale_log2, float phi2, int mode, bool chunk_major,
+    uint16_t *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part,
+    int *__restrict__ tickets) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   static_assert(16 * (D + 1) >= 6 * 64, "LDS reused by the fused merge");
+  const PartLayout pl{G, Tq, Hq, Hkv, S, chunk_major};
   __shared__ float sm_m[NW * 16];
   __shared__ float sm_l[NW * 16];
   __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
@@ -1162,8 +1208,7 @@ __device__ __forceinline__ void chunk_pass(
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
     wave_merge_store<D, NW>(sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l,
-                            acc, w, G, Tq, Hq, S, mode, out, lse, o_part,
-                            lse_part);
+                            acc, w, pl, mode, out, lse, o_part, lse_part);
     return;
   }
   if (n16 < ncol) {
@@ -1178,11 +1223,11 @@ __device__ __forceinline__ void chunk_pass(
       for (int j = 0; j < 4; ++j) o[(q4 * 4 + j) * VW + e] = acc[e][j];
   }
   __syncthreads();
-  merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, G, Tq, w, Hq, S,
-                               mode, out, lse, o_part, lse_part);
+  merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out,
+                               lse, o_part, lse_part);
   if (mode == kModeFused)
-    merge_group_if_last<D, uint16_t>(w, G, Tq, Hq, Hkv, S, o_part, lse_part,
-                                     tickets, out, lse, sm_o, &sm_flag);
+    merge_group_if_last<D, uint16_t>(w, pl, o_part, lse_part, tickets, out,
+                                     lse, sm_o, &sm_flag);
 }
 
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
@@ -1191,7 +1236,7 @@ void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, float phi2, int mode, bool direct,
+    float scale_log2, float phi2, int mode, bool direct, bool chunk_major,
     uint16_t *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
@@ -1204,8 +1249,8 @@ void split_mfma_kernel(
   if (!w0.valid) return;
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w0, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, G, Tq, Lmax, C, S, scale_log2,
-                                        phi2, mode, out, lse, o_part,
-                                        lse_part, tickets);
+                                        phi2, mode, chunk_major, out, lse,
+                                        o_part, lse_part, tickets);
   // Equal lengths, a grid that covers the upper bound, or a work list that
   // ends before i + grid (its length is known from the scan for up to 64
   // sequences): one chunk each, and no second look-up.
@@ -1217,8 +1262,8 @@ void split_mfma_kernel(
   __syncthreads();  // the second chunk reuses the LDS
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w1, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, G, Tq, Lmax, C, S, scale_log2,
-                                        phi2, mode, out, lse, o_part,
-                                        lse_part, tickets);
+                                        phi2, mode, chunk_major, out, lse,
+                                        o_part, lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------
@@ -1261,7 +1306,7 @@ template <typename T, int D, int NW, int GT>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ seqlens, int B, int Hq, int Hkv, int G,
-    int Lmax, int C, int S, float scale_log2, int mode,
+    int Lmax, int C, int S, float scale_log2, int mode, bool chunk_major,
     T *__restrict__ out, float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
   constexpr int EPL = Elem<T>::kPerLane;
@@ -1378,11 +1423,12 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     }
   }
   __syncthreads();
-  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, G, 1, w, Hq, S, mode,
-                        out, lse, o_part, lse_part);
+  const PartLayout pl{G, 1, Hq, Hkv, S, chunk_major};
+  merge_and_store<D, T>(sm_m, sm_l, sm_o, NSLOT, GT, pl, w, mode, out, lse,
+                        o_part, lse_part);
   if (mode == kModeFused)
-    merge_group_if_last<D, T>(w, G, 1, Hq, Hkv, S, o_part, lse_part, tickets,
-                              out, lse, sm_o, &sm_flag);
+    merge_group_if_last<D, T>(w, pl, o_part, lse_part, tickets, out, lse,
+                              sm_o, &sm_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -1417,21 +1463,22 @@ __device__ __forceinline__ int merge_row(int id, int G, int Hkv) {
 template <int D, typename OutT, int CPL, int MW, int MB>
 __global__ __launch_bounds__(MW * 64) void combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
-    const int32_t *__restrict__ seqlens, int rows_per_b, int G, int Hkv,
-    int Lmax, int C, int S, OutT *__restrict__ out,
-    float *__restrict__ lse) {
+    const int32_t *__restrict__ seqlens, PartLayout pl, int Lmax, int C,
+    OutT *__restrict__ out, float *__restrict__ lse) {
   constexpr int COLS = 64 * CPL;  // output columns of this workgroup
   static_assert(D % COLS == 0, "column blocks tile the head dimension");
   __shared__ float sm_M[MW], sm_W[MW];
   __shared__ float sm_acc[MW][COLS];
-  const int row = merge_row(blockIdx.x, G, Hkv);
+  const int row = merge_row(blockIdx.x, pl.G, pl.Hkv);
   const int c0 = blockIdx.y * COLS;
-  const int b = row / rows_per_b;
+  const int b = row / (pl.Tq * pl.Hq);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int L = seqlens ? clamp_len(seqlens[b], Lmax) : Lmax;
-  const int nb = min(S, chunks_of(L, C));
-  const float *lp = lse_part + (size_t)row * S;
-  const float *op = o_part + (size_t)row * S * D + c0 + lane * CPL;
+  const int nb = min(pl.S, chunks_of(L, C));
+  const PartLayout::Row pr = pl.row_of_out(row);
+  const float *lp = lse_part + pr.base;
+  const float *op = o_part + pr.base * D + c0 + lane * CPL;
+  const size_t o_step = (size_t)pr.stride * D;
 
   float M = FD_NEG_INF, W = 0.f, acc[CPL];
 #pragma unroll
@@ -1442,9 +1489,9 @@ __global__ __launch_bounds__(MW * 64) void combine_kernel(
     for (int j = 0; j < MB; ++j) {
       const int s = s0 + j * MW;
       const int sc = s < nb ? s : s0;
-      ls[j] = s < nb ? lp[sc] : FD_NEG_INF;
+      ls[j] = s < nb ? lp[(size_t)sc * pr.stride] : FD_NEG_INF;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) ov[j][i] = op[(size_t)sc * D + i];
+      for (int i = 0; i < CPL; ++i) ov[j][i] = op[(size_t)sc * o_step + i];
     }
     float mb = ls[0];
 #pragma unroll
@@ -1514,8 +1561,8 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
   case GTV:                                                                  \
     hipLaunchKernelGGL((split_valu_kernel<T, D, NW, GTV>), grid, block, 0,   \
                        st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G, p.Lmax, \
-                       p.chunk, p.splits, sl2, part, out, a.lse, a.o_part,    \
-                       a.lse_part, a.tickets);                               \
+                       p.chunk, p.splits, sl2, part, p.chunk_major, out,     \
+                       a.lse, a.o_part, a.lse_part, a.tickets);              \
     break;
   switch (gt) {
     FD_VALU_CASE(1)
@@ -1526,16 +1573,17 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
         if (gt == 8) {
           hipLaunchKernelGGL((split_valu_kernel<T, D, NW, 8>), grid, block, 0,
                              st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G,
-                             p.Lmax, p.chunk, p.splits, sl2, part, out, a.lse,
-                             a.o_part, a.lse_part, a.tickets);
+                             p.Lmax, p.chunk, p.splits, sl2, part,
+                             p.chunk_major, out, a.lse, a.o_part, a.lse_part,
+                             a.tickets);
           break;
         }
         if (gt == 16) {
           hipLaunchKernelGGL((split_valu_kernel<T, D, 2, 16>), grid,
                              dim3(2 * 64), 0, st, q, k, v, a.seqlens, p.B,
                              p.Hq, p.Hkv, p.G, p.Lmax, p.chunk, p.splits, sl2,
-                             part, out, a.lse, a.o_part, a.lse_part,
-                             a.tickets);
+                             part, p.chunk_major, out, a.lse, a.o_part,
+                             a.lse_part, a.tickets);
           break;
         }
       }
@@ -1560,8 +1608,8 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
     hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI>), grid,\
                        dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
                        p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk,         \
-                       p.splits, sl2, phi2, part, p.direct, out, a.lse,      \
-                       a.o_part, a.lse_part, a.tickets);                     \
+                       p.splits, sl2, phi2, part, p.direct, p.chunk_major,   \
+                       out, a.lse, a.o_part, a.lse_part, a.tickets);         \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(2)
@@ -1577,21 +1625,22 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
+  const PartLayout pl{p.G, p.Tq, p.Hq, p.Hkv, p.splits, p.chunk_major};
   if (rows < p.num_cus && p.splits <= 32)
     hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 4, 8>), dim3(rows, D / 64),
                        dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
-                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
-                       static_cast<OutT *>(a.out), a.lse);
+                       pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
+                       a.lse);
   else if (rows < p.num_cus)
     hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 8, 8>), dim3(rows, D / 64),
                        dim3(8 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
-                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
-                       static_cast<OutT *>(a.out), a.lse);
+                       pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
+                       a.lse);
   else
     hipLaunchKernelGGL((combine_kernel<D, OutT, D / 64, 4, 16>), dim3(rows),
                        dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
-                       p.Tq * p.Hq, p.G, p.Hkv, p.Lmax, p.chunk, p.splits,
-                       static_cast<OutT *>(a.out), a.lse);
+                       pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
+                       a.lse);
 }
 
 }  // namespace

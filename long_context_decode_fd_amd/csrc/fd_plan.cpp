@@ -52,8 +52,17 @@ namespace {
 #ifndef FD_MFMA_WAVES
 #define FD_MFMA_WAVES 4
 #endif
+#ifndef FD_MIN_CHUNK_VALU
+#define FD_MIN_CHUNK_VALU 64
+#endif
+// Partial layout: -1 by the rounds of workgroups (the rule below), 0 always
+// row-major, 1 always chunk-major (for measuring one against the other).
+#ifndef FD_PARTIAL_LAYOUT
+#define FD_PARTIAL_LAYOUT -1
+#endif
 constexpr int kBlocksPerCU = FD_BLOCKS_PER_CU;
 constexpr int kMinChunk = FD_MIN_CHUNK;
+constexpr int kMinChunkValu = FD_MIN_CHUNK_VALU;
 constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
 constexpr int kGridPerCU = 8;
 constexpr int kMfmaWaves = FD_MFMA_WAVES;
@@ -165,14 +174,22 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     const long units = (long)B * Hkv;
     const long target = (long)num_cus * kBlocksPerCU;
     int s = (int)std::max(1L, (target + units - 1) / units);
+    // The vector-ALU kernel works through a chunk 16 keys per wavefront
+    // step with a chain of cross-lane reductions per key group, so its
+    // chunks are best kept short: measured on MI355X (steps replayed from
+    // a graph), the tiny fp32 decode (8 heads, 1024 keys, D = 64) took
+    // 8.2 us in 256-key chunks, 7.0 in 128 and 6.2 in 64, and longer fp32
+    // caches gained alike; the matrix-core kernel keeps 256.
+    const int min_chunk =
+        q.variant == FD_VARIANT_VALU ? kMinChunkValu : kMinChunk;
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
-    chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
-    // Short caches: one launch beats two.  Up to 2 * kMinChunk keys the
+    chunk = std::max(chunk, std::min(min_chunk, full_chunk));
+    // Short caches: one launch beats two.  Up to 2 * min_chunk keys the
     // merge pass (a second kernel) costs more than streaming the whole
     // sequence in one workgroup per (sequence, KV head): measured, batch 1
     // at 512 keys took 9.8 us unsplit against 12.8 us in two chunks; from
     // 768 keys on the split is ahead.
-    if (Lmax <= 2 * kMinChunk) chunk = full_chunk;
+    if (Lmax <= 2 * min_chunk) chunk = full_chunk;
     // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
     // than the even split would make it were every sequence full.
     if (varlen) chunk = std::min(chunk, kVarlenChunk);
@@ -197,6 +214,16 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (varlen && q.variant == FD_VARIANT_MFMA)
     grid = std::min(grid, std::max((grid + 1) / 2, (long)num_cus * kGridPerCU));
   q.grid = (int)grid;
+  // Partial layout.  When the workgroups run in several rounds, chunks that
+  // finish store their partials while the others still stream K/V, and on
+  // MI355X those stores slow the read stream far beyond their bytes; one
+  // contiguous block per chunk (chunk-major) costs less there than G rows
+  // S partials apart.  When every chunk runs in the same round, the stores
+  // come together at the end, and the merge's contiguous reads of each
+  // row's partials (row-major) are the cheaper side.
+  q.chunk_major = q.combine && (FD_PARTIAL_LAYOUT >= 0
+                                    ? FD_PARTIAL_LAYOUT == 1
+                                    : grid > (long)num_cus * kBlocksPerCU);
   q.ws_bytes = workspace_layout(q).total;
   *p = q;
   return FD_OK;

@@ -195,23 +195,29 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
     # (the work list's upper bound 16 * 8 * 64, halved: two chunks per
     # workgroup)
     assert (p["chunk"], p["num_splits"], p["grid"]) == (2048, 64, 16 * 8 * 32)
-    # fp32 runs on the vector ALU
+    # fp32 runs on the vector ALU, in 64-key chunks: the tiny decode (8
+    # units) splits 1024 keys 16 ways (measured fastest of 1..32 splits
+    # but for 32, which was level)
     p = plan(W["tiny_mha_f32_b1_h8_d64_l1024"])
-    assert p["variant"] == fd.FD_VARIANT_VALU and p["chunk"] % 32 == 0
+    assert p["variant"] == fd.FD_VARIANT_VALU
+    assert (p["chunk"], p["num_splits"], p["grid"]) == (64, 16, 128)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("varlen", [False, True])
 def test_short_caches_take_one_launch(lib, dtype, varlen):
-    # Up to 512 keys (twice the 256-key minimum chunk) the planner keeps one
-    # chunk per sequence: no partials, no merge pass.  One key more and the
-    # usual split applies.
-    for L in (32, 300, 512):
+    # Up to twice the minimum chunk (256 keys for the matrix-core kernel,
+    # 64 for the fp32 vector-ALU kernel) the planner keeps one chunk per
+    # sequence: no partials, no merge pass.  One key more and the usual
+    # split applies.
+    mc = 256 if dtype == "bf16" else 64
+    for L in (32, mc + 44, 2 * mc):
         p = fd.fd_plan(1, 8, 8, 128, L, dtype, varlen=varlen, num_cus=256)
         assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == \
             (1, 0, 0), (L, p)
-    p = fd.fd_plan(1, 8, 8, 128, 513, dtype, varlen=varlen, num_cus=256)
-    assert (p["num_splits"], p["chunk"], p["combine"]) == (3, 256, 1)
+    p = fd.fd_plan(1, 8, 8, 128, 2 * mc + 1, dtype, varlen=varlen,
+                   num_cus=256)
+    assert (p["num_splits"], p["chunk"], p["combine"]) == (3, mc, 1)
     # a paged table of that capacity plans the same way
     if dtype == "bf16":
         p = fd.fd_plan_ex(1, 1, 8, 8, 128, 512, "bf16", varlen=True,
@@ -432,3 +438,25 @@ def test_unified_max_plans_like_the_exact_pass(lib):
         fd.fd_plan_ex(1, 1, 8, 8, 128, 4096, "bf16", paged=True,
                       flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
 
+
+@pytest.mark.parametrize("name,layout", [
+    ("b1_gqa8_h64_d128_l65536", fd.FD_PARTIALS_ROW_MAJOR),
+    ("b4_mha_h32_d128_l32768_peaked", fd.FD_PARTIALS_ROW_MAJOR),
+    ("varlen_b16_gqa8_h64_d128_lmax131072", fd.FD_PARTIALS_CHUNK_MAJOR),
+])
+def test_partial_layout_follows_the_rounds_of_workgroups(lib, name, layout):
+    """Plans whose chunks run in several rounds of workgroups keep each
+    chunk's partial rows together; one-round plans keep each query row's
+    chunks together.  Same workspace size either way."""
+    w = wl.WORKLOADS[name]
+    p = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
+                   varlen=w.varlen is not None, num_cus=256)
+    assert p["partial_layout"] == layout
+    assert (p["grid"] > 256) == (layout == fd.FD_PARTIALS_CHUNK_MAJOR)
+    rows = w.B * w.Hq * p["num_splits"]
+    assert p["lse_part_offset"] - p["o_part_offset"] >= rows * w.D * 4
+    # one chunk per sequence: no partials, and the layout field says row
+    one = fd.fd_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype, num_splits=1,
+                     num_cus=256)
+    assert not one["combine"] and \
+        one["partial_layout"] == fd.FD_PARTIALS_ROW_MAJOR

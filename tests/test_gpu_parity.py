@@ -315,6 +315,7 @@ def test_fused_merge_never_reads_stale_partials(cuda, name, S):
 
 
 @pytest.mark.parametrize("name,num_splits", [("b1_gqa8", 7), ("b1_gqa8", 1),
+                                             ("b64_gqa4", 7),
                                              ("varlen_gqa8", 0),
                                              ("b4_mha_peaked", 3),
                                              ("tiny_mha_f32", 4),
@@ -350,10 +351,23 @@ def test_phase_calls_and_chunk_partials(cuda, oracle_mod, name, num_splits):
 
     o_off, l_off = plan["o_part_offset"], plan["lse_part_offset"]
     wsh = ws.cpu().numpy()
-    o_part = wsh[o_off:o_off + w.B * w.Hq * S * w.D * 4].view(
-        np.float32).reshape(w.B, w.Hq, S, w.D)
-    l_part = wsh[l_off:l_off + w.B * w.Hq * S * 4].view(
-        np.float32).reshape(w.B, w.Hq, S)
+    n = w.B * w.Hq * S
+    o_flat = wsh[o_off:o_off + n * w.D * 4].view(np.float32)
+    l_flat = wsh[l_off:l_off + n * 4].view(np.float32)
+    if plan["partial_layout"] == fd.FD_PARTIALS_CHUNK_MAJOR:
+        # [B][Hkv][S][G] rows -> [B][Hq][S]
+        o_part = o_flat.reshape(w.B, w.Hkv, S, w.G, w.D).transpose(
+            0, 1, 3, 2, 4).reshape(w.B, w.Hq, S, w.D)
+        l_part = l_flat.reshape(w.B, w.Hkv, S, w.G).transpose(
+            0, 1, 3, 2).reshape(w.B, w.Hq, S)
+    else:
+        assert plan["partial_layout"] == fd.FD_PARTIALS_ROW_MAJOR
+        o_part = o_flat.reshape(w.B, w.Hq, S, w.D)
+        l_part = l_flat.reshape(w.B, w.Hq, S)
+    # several rounds of workgroups: chunk-major; one round: row-major
+    rounds = plan["grid"] > plan["num_cus"]
+    assert plan["partial_layout"] == (fd.FD_PARTIALS_CHUNK_MAJOR if rounds
+                                      else fd.FD_PARTIALS_ROW_MAJOR)
     qh, kh, vh = host
     for b in range(w.B):
         L = wl.seqlen_of(w, seqlens, b)
