@@ -223,37 +223,62 @@ def _same_device(device, **tensors):
             raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _span(t):
-    n = t.numel() * t.element_size()
-    return t.data_ptr(), t.data_ptr() + n
+def _spans(tensors):
+    """(name, first byte, end) of the non-empty tensors of a name -> tensor
+    mapping."""
+    res = []
+    for k, t in tensors.items():
+        if t is not None:
+            n = t.nbytes
+            if n:
+                p = t.data_ptr()
+                res.append((k, p, p + n))
+    return res
 
 
 def _no_overlap(outs, ins):
     """Outputs must not share memory with each other or with an input."""
-    outs = {k: t for k, t in outs.items() if t is not None and t.numel()}
-    ins = {k: t for k, t in ins.items() if t is not None and t.numel()}
-    names = list(outs)
-    for i, a in enumerate(names):
-        a0, a1 = _span(outs[a])
-        others = [(b, outs[b]) for b in names[i + 1:]] + list(ins.items())
-        for b, t in others:
-            b0, b1 = _span(t)
+    o = _spans(outs)
+    others = o + _spans(ins)
+    for i, (a, a0, a1) in enumerate(o):
+        for b, b0, b1 in others[i + 1:]:
             if a0 < b1 and b0 < a1:
                 raise ValueError(f"{a} overlaps {b}")
 
 
+_raw_stream = None
+
+
+def _current_stream_ptr(device):
+    """hipStream_t of `device`'s current stream, as an int: torch's raw
+    getter where it has one (no Stream object is built), else the public
+    API."""
+    global _raw_stream
+    import torch
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
 def _invoke(name, device, stream, *args):
     """Call libfd's `name` on `stream` (default: the current stream of
-    `device`) with `device` made current for the call: the library plans
-    for, and keeps its own workspace on, the current device."""
+    `device`) with `device` current for the call: the library plans for,
+    and keeps its own workspace on, the current device."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        sp = _current_stream_ptr(device)
     elif stream.device != device:
         raise ValueError(f"stream is on {stream.device}, expected {device}")
-    with torch.cuda.device(device):
-        rc = getattr(load_library(), name)(*args,
-                                           ctypes.c_void_p(stream.cuda_stream))
+    else:
+        sp = stream.cuda_stream
+    fn = getattr(load_library(), name)
+    if torch.cuda.current_device() == device.index:
+        rc = fn(*args, sp)
+    else:
+        with torch.cuda.device(device):
+            rc = fn(*args, sp)
     if rc != FD_OK:
         raise FdError(name, rc)
 

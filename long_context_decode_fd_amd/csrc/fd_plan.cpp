@@ -14,11 +14,13 @@
 //     from HBM exactly once;
 //   * aim for kBlocksPerCU workgroups per CU; split each sequence into
 //     S = ceil(target / U) chunks, each a multiple of the 32-key tile and at
-//     least kMinChunk keys (the per-workgroup prologue and the partial
-//     write, 2 * G * 4 bytes per key-row pair, must stay small next to the
-//     2 * C * D * elem bytes of K/V a chunk streams);
-//   * S == 1 means no partials and no merge pass at all; caches of up to
-//     2 * kMinChunk keys always take it (one launch beats two there);
+//     least kMinChunk keys.  Short chunks pay: at batch 1 a workgroup's
+//     time is mostly the latency of its tile chain, so 64-key chunks over
+//     all CUs beat 256-key chunks over a quarter of them (1024 keys: 7.8
+//     against 10.3 us);
+//   * S == 1 means no partials and no merge pass at all; it is taken when a
+//     split would not take more than kSplitGain keys off each workgroup's
+//     share, about what the merge pass costs;
 //   * with per-sequence lengths the mix is unknown on the host (the library
 //     never reads device memory synchronously), so chunks are also capped
 //     at kVarlenChunk keys, so that no single long sequence sets the finish
@@ -44,16 +46,16 @@ namespace {
 #define FD_BLOCKS_PER_CU 1
 #endif
 #ifndef FD_MIN_CHUNK
-#define FD_MIN_CHUNK 256
+#define FD_MIN_CHUNK 64
+#endif
+#ifndef FD_SPLIT_GAIN
+#define FD_SPLIT_GAIN 256
 #endif
 #ifndef FD_VARLEN_CHUNK
 #define FD_VARLEN_CHUNK 2048
 #endif
 #ifndef FD_MFMA_WAVES
 #define FD_MFMA_WAVES 4
-#endif
-#ifndef FD_MIN_CHUNK_VALU
-#define FD_MIN_CHUNK_VALU 64
 #endif
 // Partial layout: -1 by the rounds of workgroups (the rule below), 0 always
 // row-major, 1 always chunk-major (for measuring one against the other).
@@ -62,7 +64,7 @@ namespace {
 #endif
 constexpr int kBlocksPerCU = FD_BLOCKS_PER_CU;
 constexpr int kMinChunk = FD_MIN_CHUNK;
-constexpr int kMinChunkValu = FD_MIN_CHUNK_VALU;
+constexpr int kSplitGain = FD_SPLIT_GAIN;
 constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
 constexpr int kGridPerCU = 8;
 constexpr int kMfmaWaves = FD_MFMA_WAVES;
@@ -174,22 +176,16 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     const long units = (long)B * Hkv;
     const long target = (long)num_cus * kBlocksPerCU;
     int s = (int)std::max(1L, (target + units - 1) / units);
-    // The vector-ALU kernel works through a chunk 16 keys per wavefront
-    // step with a chain of cross-lane reductions per key group, so its
-    // chunks are best kept short: measured on MI355X (steps replayed from
-    // a graph), the tiny fp32 decode (8 heads, 1024 keys, D = 64) took
-    // 8.2 us in 256-key chunks, 7.0 in 128 and 6.2 in 64, and longer fp32
-    // caches gained alike; the matrix-core kernel keeps 256.
-    const int min_chunk =
-        q.variant == FD_VARIANT_VALU ? kMinChunkValu : kMinChunk;
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
-    chunk = std::max(chunk, std::min(min_chunk, full_chunk));
-    // Short caches: one launch beats two.  Up to 2 * min_chunk keys the
-    // merge pass (a second kernel) costs more than streaming the whole
-    // sequence in one workgroup per (sequence, KV head): measured, batch 1
-    // at 512 keys took 9.8 us unsplit against 12.8 us in two chunks; from
-    // 768 keys on the split is ahead.
-    if (Lmax <= 2 * min_chunk) chunk = full_chunk;
+    chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
+    // Short caches: one launch beats two.  The merge pass (a second kernel)
+    // costs about as much as a workgroup streaming kSplitGain more keys, so
+    // a split must take more than that off each workgroup's share.
+    // Measured on MI355X (device time of steps replayed from a graph):
+    // batch 1, 64 query / 8 KV heads, 256 keys: 6.4 us unsplit, 7.0 in
+    // 8 chunks; 512 keys: 10.1 unsplit, 7.4 in 16 chunks; 16 sequences
+    // at 512 keys: 12.4 unsplit, 13.3 in two chunks.
+    if (Lmax - chunk <= kSplitGain) chunk = full_chunk;
     // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
     // than the even split would make it were every sequence full.
     if (varlen) chunk = std::min(chunk, kVarlenChunk);

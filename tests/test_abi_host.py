@@ -206,23 +206,33 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("varlen", [False, True])
 def test_short_caches_take_one_launch(lib, dtype, varlen):
-    # Up to twice the minimum chunk (256 keys for the matrix-core kernel,
-    # 64 for the fp32 vector-ALU kernel) the planner keeps one chunk per
-    # sequence: no partials, no merge pass.  One key more and the usual
-    # split applies.
-    mc = 256 if dtype == "bf16" else 64
-    for L in (32, mc + 44, 2 * mc):
+    # The planner splits only when a split takes more than 256 keys off
+    # each workgroup's share (chunks of at least 64 keys): with 8 units
+    # (batch 1, 8 KV heads) up to 320 keys stay in one chunk per sequence,
+    # with no partials and no merge pass; one key more and the sequence is
+    # cut into 64-key chunks.
+    for L in (32, 300, 320):
         p = fd.fd_plan(1, 8, 8, 128, L, dtype, varlen=varlen, num_cus=256)
         assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == \
             (1, 0, 0), (L, p)
-    p = fd.fd_plan(1, 8, 8, 128, 2 * mc + 1, dtype, varlen=varlen,
-                   num_cus=256)
-    assert (p["num_splits"], p["chunk"], p["combine"]) == (3, mc, 1)
+    p = fd.fd_plan(1, 8, 8, 128, 321, dtype, varlen=varlen, num_cus=256)
+    assert (p["num_splits"], p["chunk"], p["combine"]) == (6, 64, 1)
     # a paged table of that capacity plans the same way
     if dtype == "bf16":
-        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 512, "bf16", varlen=True,
+        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 320, "bf16", varlen=True,
                           paged=True, num_cus=256)
         assert p["num_splits"] == 1 and p["combine"] == 0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,S", [
+    # measured fastest or within 7% of it (device time, MI355X)
+    (1, 64, 8, 1024, 16), (1, 64, 8, 4096, 32), (1, 64, 8, 65536, 32),
+    (2, 64, 8, 2048, 16), (4, 64, 8, 512, 8), (8, 32, 8, 512, 4),
+    (16, 32, 8, 512, 1), (16, 32, 8, 768, 2), (4, 32, 32, 512, 1),
+    (4, 32, 32, 32768, 2), (64, 32, 8, 4096, 1)])
+def test_split_counts_follow_the_measured_rule(lib, B, Hq, Hkv, L, S):
+    p = fd.fd_plan(B, Hq, Hkv, 128, L, "bf16", num_cus=256)
+    assert p["num_splits"] == S, p
 
 
 @pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
