@@ -364,26 +364,17 @@ def context_sweep(torch, fd, steps: int) -> None:
     splitting the keys/values with attention that parallelises over batch
     and heads only, which at small batch leaves most of the GPU idle.  Here
     the unsplit form is this library's own kernel with num_splits = 1 (one
-    workgroup per (sequence, KV head)); the split form is fd_decode's plan.
-    Batch 1 and 8, 64 query heads on 8 KV heads, D = 128, bf16, seeded
-    random inputs, KV rotated over KV_COPIES copies.  One JSON line per case.
+    workgroup per (sequence, KV head)); the split form is the planner's
+    plan.  Batch 1 and 8, 64 query heads on 8 KV heads, D = 128, bf16,
+    seeded random inputs, KV rotated over KV_COPIES copies.  Each form is
+    timed from a HIP graph (device time per step: at short contexts an
+    eager Python call costs more host time than the step takes on the GPU)
+    and eagerly through fd_decode / fd_decode_ex.  One JSON line per case.
     """
     D, Hq, Hkv = 128, 64, 8
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
     stream = torch.cuda.current_stream()
-
-    def timed(fn, n):
-        warm_up(torch, fn, max(3, n // 10))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
-
     for B in (1, 8):
         for L in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072):
             if B * L > 8 * 65536:
@@ -398,27 +389,95 @@ def context_sweep(torch, fd, steps: int) -> None:
             out = torch.empty_like(q)
             lse = torch.empty((B, Hq), device="cuda")
             scale = D ** -0.5
-
-            def split(i):
-                fd.fd_decode(q, ks[i % KV_COPIES], vs[i % KV_COPIES], None,
-                             scale, out=out, lse=lse, stream=stream)
-
-            def unsplit(i):
-                fd.fd_decode_ex(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
-                                None, scale, out=out, lse=lse, num_splits=1,
-                                stream=stream)
-
-            t_split = timed(split, steps)
-            t_uns = timed(unsplit, steps)
-            nbytes = 2 * B * Hkv * L * D * 2
             plan = fd.fd_plan(B, Hq, Hkv, D, L, "bf16")
-            print(json.dumps({
-                "sweep": "split_vs_unsplit", "B": B, "L": L, "Hq": Hq,
-                "Hkv": Hkv, "D": D, "num_splits": plan["num_splits"],
-                "split_us": round(t_split, 2), "unsplit_us": round(t_uns, 2),
-                "speedup": round(t_uns / t_split, 2),
-                "split_GBs": round(nbytes / t_split / 1e3, 1),
-                "unsplit_GBs": round(nbytes / t_uns / 1e3, 1)}), flush=True)
+            ws = torch.empty(max(plan["workspace_bytes"], 256),
+                             dtype=torch.uint8, device="cuda")
+            res = {"sweep": "split_vs_unsplit", "B": B, "L": L, "Hq": Hq,
+                   "Hkv": Hkv, "D": D, "num_splits": plan["num_splits"],
+                   "chunk": plan["chunk"]}
+            for tag, S in (("split", 0), ("unsplit", 1)):
+                def call(i, S=S):
+                    fd.fd_decode_ex(q, ks[i % KV_COPIES], vs[i % KV_COPIES],
+                                    None, scale, out=out, lse=lse,
+                                    num_splits=S, workspace=ws)
+                res[f"{tag}_us"] = round(graph_us(torch, call, steps,
+                                                  steps), 2)
+                res[f"{tag}_us_eager"] = round(
+                    timed_us(torch, call, steps, steps, stream), 2)
+            nbytes = 2 * B * Hkv * L * D * 2
+            res["speedup"] = round(res["unsplit_us"] / res["split_us"], 2)
+            res["split_GBs"] = round(nbytes / res["split_us"] / 1e3, 1)
+            res["unsplit_GBs"] = round(nbytes / res["unsplit_us"] / 1e3, 1)
+            print(json.dumps(res), flush=True)
+            del ks, vs, ws
+            torch.cuda.empty_cache()
+
+
+SPLIT_SWEEP_SHAPES = [  # (B, Hq, Hkv, D, dtype)
+    (1, 64, 8, 128, "bf16"), (2, 64, 8, 128, "bf16"), (4, 64, 8, 128, "bf16"),
+    (8, 32, 8, 128, "bf16"), (16, 32, 8, 128, "bf16"),
+    (1, 32, 32, 128, "bf16"), (4, 32, 32, 128, "bf16"),
+    (1, 8, 8, 64, "f32"), (4, 8, 8, 64, "f32")]
+SPLIT_SWEEP_LENGTHS = (256, 384, 512, 768, 1024, 1536, 2048, 4096, 8192,
+                       16384, 32768)
+
+
+def split_sweep(torch, fd, steps: int) -> None:
+    """The planner's split count against every split count from 1 to 128,
+    over batch, head layout and context length: device time per step from
+    a HIP graph (fd_decode_ex with forced num_splits and a caller
+    workspace), KV rotated over up to 8 copies so that the working set of
+    short caches exceeds the 256 MB Infinity Cache.  One JSON line per
+    shape: the planner's choice, every split count's time, the fastest."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    for B, Hq, Hkv, D, dtype in SPLIT_SWEEP_SHAPES:
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        for L in SPLIT_SWEEP_LENGTHS:
+            if dtype == "f32" and L > 4096:
+                continue
+            shape = (B, Hkv, L, D)
+            kvb = 2 * B * Hkv * L * D * (2 if dtype == "bf16" else 4)
+            copies = max(1, min(8, (1 << 30) // kvb))
+            ks = [torch.randn(shape, device="cuda", dtype=tdt,
+                              generator=gen) for _ in range(copies)]
+            vs = [torch.randn(shape, device="cuda", dtype=tdt,
+                              generator=gen) for _ in range(copies)]
+            q = torch.randn((B, Hq, D), device="cuda", dtype=tdt,
+                            generator=gen)
+            out = torch.empty_like(q)
+            lse = torch.empty((B, Hq), device="cuda")
+            scale = D ** -0.5
+            auto = fd.fd_plan(B, Hq, Hkv, D, L, dtype)
+            res = {"sweep": "split_count", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "D": D, "dtype": dtype, "L": L,
+                   "planner": [auto["num_splits"], auto["chunk"]]}
+            n = steps if kvb < (32 << 20) else max(40, steps // 4)
+            for S in (1, 2, 4, 8, 16, 32, 64, 128):
+                if S > L // 32 or B * Hkv * S > 8192:
+                    continue
+                p = fd.fd_plan(B, Hq, Hkv, D, L, dtype, num_splits=S)
+                ws = torch.empty(max(p["workspace_bytes"], 256),
+                                 dtype=torch.uint8, device="cuda")
+
+                def call(i, S=S, ws=ws):
+                    fd.fd_decode_ex(q, ks[i % copies], vs[i % copies], None,
+                                    scale, out=out, lse=lse, num_splits=S,
+                                    workspace=ws)
+                res[f"S{p['num_splits']}"] = round(
+                    graph_us(torch, call, n, n // 2), 2)
+            if f"S{auto['num_splits']}" not in res:
+                ws = torch.empty(max(auto["workspace_bytes"], 256),
+                                 dtype=torch.uint8, device="cuda")
+                res[f"S{auto['num_splits']}"] = round(graph_us(
+                    torch, lambda i: fd.fd_decode_ex(
+                        q, ks[i % copies], vs[i % copies], None, scale,
+                        out=out, lse=lse, workspace=ws), n, n // 2), 2)
+            times = {k: v for k, v in res.items() if k[0] == "S"}
+            res["fastest"] = min(times, key=times.get)
+            res["planner_over_fastest"] = round(
+                times[f"S{auto['num_splits']}"] / times[res["fastest"]], 3)
+            print(json.dumps(res), flush=True)
             del ks, vs
             torch.cuda.empty_cache()
 
@@ -443,6 +502,10 @@ def main(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload table of the five decode "
                          "workloads")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="instead of the benchmark line: the planner's split "
+                         "count against split counts 1..128 over batch, "
+                         "heads and context length, one JSON line per shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -457,10 +520,13 @@ def main(argv=None):
     import long_context_decode_fd_amd as fd
     from long_context_decode_fd_amd import workloads as wl
 
-    if a.context_sweep:
+    if a.context_sweep or a.split_sweep:
         torch.cuda.set_device(0)
         fd.load_library()
-        context_sweep(torch, fd, a.steps)
+        if a.context_sweep:
+            context_sweep(torch, fd, a.steps)
+        if a.split_sweep:
+            split_sweep(torch, fd, a.steps)
         return 0
 
     w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
