@@ -27,8 +27,9 @@ whole step and for the per-chunk pass alone, and the plan.
 
 --workload picks another workload of long_context_decode_fd_amd.workloads,
 including the paged-cache (fd_decode_paged) and multi-token
-(fd_decode_multiquery) ones; for those the roofline object covers the whole
-step, since their per-chunk pass has no separate phase call.
+(fd_decode_multiquery) ones; for those, as for --unified-max and
+--fused-merge, the roofline object covers the whole step, since their
+per-chunk pass has no separate phase call.
 """
 from __future__ import annotations
 
@@ -502,6 +503,10 @@ def main(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload table of the five decode "
                          "workloads")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="time fd_decode_ex with FD_FLAG_FUSED_MERGE (the "
+                         "single-launch merge) instead of fd_decode "
+                         "(contiguous single-token workloads)")
     ap.add_argument("--split-sweep", action="store_true",
                     help="instead of the benchmark line: the planner's split "
                          "count against split counts 1..128 over batch, "
@@ -532,7 +537,8 @@ def main(argv=None):
     w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
     kind = ("paged" if w.page_size else
             "multiquery" if w.Tq > 1 else
-            "unified_max" if a.unified_max is not None else "decode")
+            "unified_max" if a.unified_max is not None else
+            "fused" if a.fused_merge else "decode")
     torch.cuda.set_device(0)
     fd.load_library()
     log(f"[bench] workload {w.name} ({kind}): generating inputs")
@@ -546,7 +552,12 @@ def main(argv=None):
         plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D, w.Lmax, w.dtype,
                              varlen=sl is not None,
                              flags=fd.FD_FLAG_UNIFIED_MAX
-                             if kind == "unified_max" else 0)
+                             if kind == "unified_max" else
+                             fd.FD_FLAG_FUSED_MERGE if kind == "fused" else 0)
+    # the fused merge's tickets start at zero and every call leaves them so
+    fused_ws = (torch.zeros(max(plan["workspace_bytes"], 256),
+                            dtype=torch.uint8, device="cuda")
+                if kind == "fused" else None)
     ks = [k] + [k.clone() for _ in range(KV_COPIES - 1)]
     vs = [v] + [v.clone() for _ in range(KV_COPIES - 1)]
     out = torch.empty_like(q)
@@ -562,12 +573,36 @@ def main(argv=None):
         elif kind == "unified_max":
             fd.fd_decode_unified_max(q, kk, vv, sl, w.scale, a.unified_max,
                                      out=out, lse=lse, stream=stream)
+        elif kind == "fused":
+            fd.fd_decode_ex(q, kk, vv, sl, w.scale, out=out, lse=lse,
+                            flags=fd.FD_FLAG_FUSED_MERGE, workspace=fused_ws,
+                            stream=stream)
         else:
             fd.fd_decode(q, kk, vv, sl, w.scale, out=out, lse=lse,
                          stream=stream)
 
     def step(i):
         call(ks[i % KV_COPIES], vs[i % KV_COPIES])
+
+    # The same step with a caller workspace (the same plan and kernels),
+    # for replay from a HIP graph: device time without the Python caller.
+    gws = torch.zeros(max(plan["workspace_bytes"], 256), dtype=torch.uint8,
+                      device="cuda") if kind != "fused" else fused_ws
+
+    def call_ws(kk, vv):
+        if kind == "paged":
+            fd.fd_decode_paged(q, kk, vv, bt, sl, w.scale, out=out, lse=lse,
+                               head_major=w.head_major, workspace=gws)
+        elif kind == "multiquery":
+            fd.fd_decode_multiquery(q, kk, vv, sl, w.scale, out=out, lse=lse,
+                                    workspace=gws)
+        elif kind == "unified_max":
+            fd.fd_decode_unified_max(q, kk, vv, sl, w.scale, a.unified_max,
+                                     out=out, lse=lse, workspace=gws)
+        else:
+            fd.fd_decode_ex(q, kk, vv, sl, w.scale, out=out, lse=lse,
+                            flags=fd.FD_FLAG_FUSED_MERGE if kind == "fused"
+                            else 0, workspace=gws)
 
     log(f"[bench] plan {plan}")
     warmup_run = warm_up(torch, step, a.warmup)
@@ -602,6 +637,12 @@ def main(argv=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_hot = e0.elapsed_time(e1) / a.steps
+
+    step_graph_us = graph_us(torch, lambda i: call_ws(ks[i % KV_COPIES],
+                                                       vs[i % KV_COPIES]),
+                             a.steps, a.warmup)
+    log(f"[bench] the same steps replayed from a graph: "
+        f"{step_graph_us:.2f} us/step")
 
     kern_avg_ms = None
     if kind == "decode":
@@ -645,7 +686,8 @@ def main(argv=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     split_kernel = (f"split_mfma_kernel<{w.D}, {plan['waves_per_block']}, "
                     f"{'paged' if kind == 'paged' else 'contiguous'}"
-                    f"{', unified max' if kind == 'unified_max' else ''}>"
+                    f"{', unified max' if kind == 'unified_max' else ''}"
+                    f"{', fused merge' if kind == 'fused' else ''}>"
                     if plan["variant"] == fd.FD_VARIANT_MFMA else
                     f"split_valu_kernel<{w.dtype}, {w.D}>")
     if kern_avg_ms is not None:
@@ -686,10 +728,12 @@ def main(argv=None):
         "steps": a.steps, "warmup": a.warmup,
         "warmup_steps_run": warmup_run, "ms_per_step": ms,
         "us_per_step": ms * 1e3, "frac_of_peak": gbs / PEAK_HBM_GBS,
+        "us_per_step_graph": step_graph_us,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype,
         "data": f"synthetic (seeded N(0,1) {w.dtype} q/K/V)",
         "config": {"workload": w.name, "call": "fd_decode" if kind == "decode"
+                   else "fd_decode_ex (FD_FLAG_FUSED_MERGE)" if kind == "fused"
                    else f"fd_decode_{kind}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "seq_len": w.Lmax, "Tq": w.Tq,
                    "page_size": w.page_size, "unified_max_phi": a.unified_max,
@@ -712,7 +756,8 @@ def main(argv=None):
         "stream_read_ceiling": ceiling,
     }
     roof["frac_of_stream_ceiling"] = roof["achieved"] / ceiling["GBs"]
-    if not a.no_configs and a.workload is None and a.unified_max is None:
+    if (not a.no_configs and a.workload is None and a.unified_max is None
+            and not a.fused_merge):
         del ks, vs, k, v
         torch.cuda.empty_cache()
         res["configs"] = config_table(torch, fd, wl, a.steps, a.warmup,

@@ -235,6 +235,16 @@ def test_split_counts_follow_the_measured_rule(lib, B, Hq, Hkv, L, S):
     assert p["num_splits"] == S, p
 
 
+@pytest.mark.parametrize("B,L,S", [(1, 1024, 16), (1, 4096, 64),
+                                   (4, 1024, 16), (4, 4096, 32),
+                                   (1, 256, 1)])
+def test_fp32_plans_for_four_workgroups_per_cu(lib, B, L, S):
+    # the vector-ALU kernel: four resident workgroups per CU, 64-key chunks
+    p = fd.fd_plan(B, 8, 8, 64, L, "f32", num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_VALU
+    assert p["num_splits"] == S, p
+
+
 @pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
                                  (65536, 64), (65536, 5000), (100, 100)])
 def test_forced_splits_cover_the_sequence(lib, L, S):
