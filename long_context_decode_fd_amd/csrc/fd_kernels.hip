@@ -394,7 +394,10 @@ struct TailState {
 // Folds chunks s = s_first, s_first + s_step, ... of item `it` (q-tile
 // column it / (D/4), output columns 4 (it % (D/4)) ..) into a TailState,
 // kTailBatch chunks per step with all of a step's loads issued first.
-template <int D>
+// COHERENT: the partials were written by other workgroups of the same
+// launch (the fused merge) and are read with agent-scope loads; otherwise
+// (a later kernel) with plain 16-byte loads.
+template <int D, bool COHERENT>
 __device__ TailState merge_item(const Work &w, const PartLayout &pl, int it,
                                 int s_first, int s_step,
                                 const float *__restrict__ o_part,
@@ -414,11 +417,16 @@ __device__ TailState merge_item(const Work &w, const PartLayout &pl, int it,
     for (int j = 0; j < kTailBatch; ++j) {
       const int s = s0 + j * s_step;
       const int sc = s < w.nb ? s : s0;
-      ls[j] = s < w.nb ? load_coherent(lp + (size_t)sc * ls_step)
-                       : FD_NEG_INF;
+      const float *l1 = lp + (size_t)sc * ls_step;
       const float *o4 = op + (size_t)sc * o_step;
-      ov[j] = make_float4(load_coherent(o4), load_coherent(o4 + 1),
-                          load_coherent(o4 + 2), load_coherent(o4 + 3));
+      if constexpr (COHERENT) {
+        ls[j] = s < w.nb ? load_coherent(l1) : FD_NEG_INF;
+        ov[j] = make_float4(load_coherent(o4), load_coherent(o4 + 1),
+                            load_coherent(o4 + 2), load_coherent(o4 + 3));
+      } else {
+        ls[j] = s < w.nb ? *l1 : FD_NEG_INF;
+        ov[j] = *reinterpret_cast<const float4 *>(o4);
+      }
     }
     float mb = ls[0];
 #pragma unroll
@@ -469,7 +477,7 @@ __device__ void store_item(const Work &w, int G, int Tq, int Hq, int it,
 
 // Merges the nb chunk partials of group (w.b, w.g) into out/lse with the
 // whole workgroup (the fused path's last workgroup).
-template <int D, typename OutT>
+template <int D, typename OutT, bool COHERENT>
 __device__ void group_merge(const Work &w, const PartLayout &pl,
                             const float *__restrict__ o_part,
                             const float *__restrict__ lse_part,
@@ -484,8 +492,8 @@ __device__ void group_merge(const Work &w, const PartLayout &pl,
   const int slices = max(1, T / items);
   if (slices == 1) {
     for (int it = tid; it < items; it += T) {
-      const TailState st = merge_item<D>(w, pl, it, 0, 1, o_part,
-                                         lse_part);
+      const TailState st = merge_item<D, COHERENT>(w, pl, it, 0, 1, o_part,
+                                                   lse_part);
       store_item<D, OutT>(w, G, Tq, Hq, it, st.M, st.W, st.acc, out, lse);
     }
     return;
@@ -494,8 +502,8 @@ __device__ void group_merge(const Work &w, const PartLayout &pl,
   float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   if (tid < items * slices)
-    st = merge_item<D>(w, pl, tid % items, tid / items, slices, o_part,
-                       lse_part);
+    st = merge_item<D, COHERENT>(w, pl, tid % items, tid / items, slices,
+                                 o_part, lse_part);
   sM[tid] = st.M;
   sW[tid] = st.W;
   sA[tid] = st.acc;
@@ -548,7 +556,7 @@ __device__ void merge_group_if_last(const Work &w, const PartLayout &pl,
   // Reader side: acquire at agent scope after the ticket, then read the
   // partials with agent-scope atomic loads.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  group_merge<D, OutT>(w, pl, o_part, lse_part, out, lse, scratch);
+  group_merge<D, OutT, true>(w, pl, o_part, lse_part, out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1539,8 +1547,37 @@ __global__ __launch_bounds__(MW * 64) void combine_kernel(
   }
 }
 
+// Merge pass for chunk-major partials: one workgroup of 1024 threads per
+// (sequence, KV head) group.  Each chunk's G * Tq rows are one contiguous
+// block, so the workgroup reads it whole (a wavefront's load instruction
+// covers 1 KB of it) where the row-wise pass above reads each row's piece
+// of every block separately; the group's chunks are split over as many
+// thread slices as the threads allow, which meet in LDS (group_merge).
+// Group b * Hkv + g runs on the XCD that wrote it when Hkv % 8 == 0, as in
+// merge_row.
+template <int D, typename OutT>
+__global__ __launch_bounds__(1024) void group_combine_kernel(
+    const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    const int32_t *__restrict__ seqlens, PartLayout pl, int Lmax, int C,
+    OutT *__restrict__ out, float *__restrict__ lse) {
+  __shared__ __align__(16) float sm[6 * 1024];
+  Work w{};
+  w.b = blockIdx.x / pl.Hkv;
+  w.g = blockIdx.x - w.b * pl.Hkv;
+  const int L = seqlens ? clamp_len(seqlens[w.b], Lmax) : Lmax;
+  w.nb = min(pl.S, chunks_of(L, C));
+  group_merge<D, OutT, false>(w, pl, o_part, lse_part, out, lse, sm);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side dispatch.
+
+// Chunk-major partials merged group-wise (1) or row-wise (0); a switch
+// for measuring one against the other.
+#ifndef FD_GROUP_MERGE
+#define FD_GROUP_MERGE 1
+#endif
+constexpr bool kGroupMerge = FD_GROUP_MERGE != 0;
 
 int mode_of(const Plan &p) {
   return !p.combine ? kModeDirect : (p.fused ? kModeFused : kModePartial);
@@ -1626,7 +1663,12 @@ template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
   const PartLayout pl{p.G, p.Tq, p.Hq, p.Hkv, p.splits, p.chunk_major};
-  if (rows < p.num_cus && p.splits <= 32)
+  if (p.chunk_major && kGroupMerge)
+    hipLaunchKernelGGL((group_combine_kernel<D, OutT>), dim3(p.B * p.Hkv),
+                       dim3(1024), 0, st, a.o_part, a.lse_part, a.seqlens,
+                       pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
+                       a.lse);
+  else if (rows < p.num_cus && p.splits <= 32)
     hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 4, 8>), dim3(rows, D / 64),
                        dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
                        pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
