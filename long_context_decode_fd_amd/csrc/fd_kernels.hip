@@ -475,23 +475,24 @@ __device__ void store_item(const Work &w, int G, int Tq, int Hq, int it,
   if (d4 == 0) lse[row] = ls;
 }
 
-// Merges the nb chunk partials of group (w.b, w.g) into out/lse with the
-// whole workgroup (the fused path's last workgroup).
+// Merges the nb chunk partials of group (w.b, w.g) into out/lse: items
+// [it0, it1) of the group's G * Tq * D / 4 (row, 4 columns) items, with
+// the whole workgroup (the fused path's last workgroup takes all items;
+// the merge pass splits a group's items over several workgroups).
 template <int D, typename OutT, bool COHERENT>
-__device__ void group_merge(const Work &w, const PartLayout &pl,
-                            const float *__restrict__ o_part,
+__device__ void group_merge(const Work &w, const PartLayout &pl, int it0,
+                            int it1, const float *__restrict__ o_part,
                             const float *__restrict__ lse_part,
                             OutT *__restrict__ out, float *__restrict__ lse,
                             float *scratch) {
-  constexpr int V4 = D / 4;
   const int G = pl.G, Tq = pl.Tq, Hq = pl.Hq;
   const int T = blockDim.x, tid = threadIdx.x;
-  const int items = G * Tq * V4;
+  const int items = it1 - it0;
   // More items than threads: each thread merges whole items on its own.
   // Otherwise each item's chunks are split over `slices` threads.
   const int slices = max(1, T / items);
   if (slices == 1) {
-    for (int it = tid; it < items; it += T) {
+    for (int it = it0 + tid; it < it1; it += T) {
       const TailState st = merge_item<D, COHERENT>(w, pl, it, 0, 1, o_part,
                                                    lse_part);
       store_item<D, OutT>(w, G, Tq, Hq, it, st.M, st.W, st.acc, out, lse);
@@ -502,21 +503,20 @@ __device__ void group_merge(const Work &w, const PartLayout &pl,
   float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   if (tid < items * slices)
-    st = merge_item<D, COHERENT>(w, pl, tid % items, tid / items, slices,
-                                 o_part, lse_part);
+    st = merge_item<D, COHERENT>(w, pl, it0 + tid % items, tid / items,
+                                 slices, o_part, lse_part);
   sM[tid] = st.M;
   sW[tid] = st.W;
   sA[tid] = st.acc;
   __syncthreads();
   if (tid < items) {
-    const int it = tid;
     float Mt = FD_NEG_INF;
-    for (int sl = 0; sl < slices; ++sl) Mt = fmaxf(Mt, sM[sl * items + it]);
+    for (int sl = 0; sl < slices; ++sl) Mt = fmaxf(Mt, sM[sl * items + tid]);
     float Wt = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     if (Mt != FD_NEG_INF) {
       for (int sl = 0; sl < slices; ++sl) {
-        const int k = sl * items + it;
+        const int k = sl * items + tid;
         const float r = exp2_f((sM[k] - Mt) * kLog2e);
         Wt += r * sW[k];
         a.x += r * sA[k].x;
@@ -525,7 +525,7 @@ __device__ void group_merge(const Work &w, const PartLayout &pl,
         a.w += r * sA[k].w;
       }
     }
-    store_item<D, OutT>(w, G, Tq, Hq, it, Mt, Wt, a, out, lse);
+    store_item<D, OutT>(w, G, Tq, Hq, it0 + tid, Mt, Wt, a, out, lse);
   }
 }
 
@@ -556,7 +556,8 @@ __device__ void merge_group_if_last(const Work &w, const PartLayout &pl,
   // Reader side: acquire at agent scope after the ticket, then read the
   // partials with agent-scope atomic loads.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  group_merge<D, OutT, true>(w, pl, o_part, lse_part, out, lse, scratch);
+  group_merge<D, OutT, true>(w, pl, 0, pl.G * pl.Tq * (D / 4), o_part,
+                             lse_part, out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1547,26 +1548,41 @@ __global__ __launch_bounds__(MW * 64) void combine_kernel(
   }
 }
 
-// Merge pass for chunk-major partials: one workgroup of 1024 threads per
-// (sequence, KV head) group.  Each chunk's G * Tq rows are one contiguous
-// block, so the workgroup reads it whole (a wavefront's load instruction
-// covers 1 KB of it) where the row-wise pass above reads each row's piece
-// of every block separately; the group's chunks are split over as many
-// thread slices as the threads allow, which meet in LDS (group_merge).
-// Group b * Hkv + g runs on the XCD that wrote it when Hkv % 8 == 0, as in
+// Merge pass for chunk-major partials: per (sequence, KV head) group,
+// gridDim.y workgroups of kGroupMergeThreads threads, each taking an equal
+// share of the group's (row, 4 columns) items.  Each chunk's G * Tq rows
+// are one contiguous block, so a workgroup reads its share of every block
+// (a wavefront's load covers one row's 256-byte piece at D = 128) where
+// the row-wise pass reads each row's piece of every block separately; the
+// group's chunks are split over as many thread slices as the threads
+// allow, which meet in LDS (group_merge).  Spreading a group over several
+// workgroups spreads a long sequence's partials over several CUs, whose
+// loads then all fit in flight at once.  Group b * Hkv + g runs on the
+// XCD that wrote it when B * Hkv and Hkv are multiples of 8, as in
 // merge_row.
+constexpr int kGroupMergeThreads = 256;
+// Items per merge workgroup: one per thread of a quarter of it, so that
+// each thread folds a quarter of the group's chunks.
+constexpr int kGroupMergeItems = kGroupMergeThreads / 4;
+
 template <int D, typename OutT>
-__global__ __launch_bounds__(1024) void group_combine_kernel(
+__global__ __launch_bounds__(kGroupMergeThreads) void group_combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
     const int32_t *__restrict__ seqlens, PartLayout pl, int Lmax, int C,
     OutT *__restrict__ out, float *__restrict__ lse) {
-  __shared__ __align__(16) float sm[6 * 1024];
+  __shared__ __align__(16) float sm[6 * kGroupMergeThreads];
   Work w{};
   w.b = blockIdx.x / pl.Hkv;
   w.g = blockIdx.x - w.b * pl.Hkv;
   const int L = seqlens ? clamp_len(seqlens[w.b], Lmax) : Lmax;
   w.nb = min(pl.S, chunks_of(L, C));
-  group_merge<D, OutT, false>(w, pl, o_part, lse_part, out, lse, sm);
+  const int items = pl.G * pl.Tq * (D / 4);
+  const int share = (items + gridDim.y - 1) / gridDim.y;
+  const int it0 = blockIdx.y * share;
+  const int it1 = min(items, it0 + share);
+  if (it0 >= it1) return;
+  group_merge<D, OutT, false>(w, pl, it0, it1, o_part, lse_part, out, lse,
+                              sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1663,11 +1679,14 @@ template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
   const PartLayout pl{p.G, p.Tq, p.Hq, p.Hkv, p.splits, p.chunk_major};
-  if (p.chunk_major && kGroupMerge)
-    hipLaunchKernelGGL((group_combine_kernel<D, OutT>), dim3(p.B * p.Hkv),
-                       dim3(1024), 0, st, a.o_part, a.lse_part, a.seqlens,
-                       pl, p.Lmax, p.chunk, static_cast<OutT *>(a.out),
-                       a.lse);
+  if (p.chunk_major && kGroupMerge) {
+    const int items = p.G * p.Tq * (D / 4);
+    const int split = (items + kGroupMergeItems - 1) / kGroupMergeItems;
+    hipLaunchKernelGGL((group_combine_kernel<D, OutT>),
+                       dim3(p.B * p.Hkv, split), dim3(kGroupMergeThreads), 0,
+                       st, a.o_part, a.lse_part, a.seqlens, pl, p.Lmax,
+                       p.chunk, static_cast<OutT *>(a.out), a.lse);
+  }
   else if (rows < p.num_cus && p.splits <= 32)
     hipLaunchKernelGGL((combine_kernel<D, OutT, 1, 4, 8>), dim3(rows, D / 64),
                        dim3(4 * 64), 0, st, a.o_part, a.lse_part, a.seqlens,
