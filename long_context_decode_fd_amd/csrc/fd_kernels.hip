@@ -1552,8 +1552,8 @@ __global__ __launch_bounds__(MW * 64) void combine_kernel(
 // gridDim.y workgroups of kGroupMergeThreads threads, each taking an equal
 // share of the group's (row, 4 columns) items.  Each chunk's G * Tq rows
 // are one contiguous block, so a workgroup reads its share of every block
-// (a wavefront's load covers one row's 256-byte piece at D = 128) where
-// the row-wise pass reads each row's piece of every block separately; the
+// (a wavefront's load covers 1 KB of it, two rows' outputs at D = 128)
+// where the row-wise pass reads each row's piece of every block; the
 // group's chunks are split over as many thread slices as the threads
 // allow, which meet in LDS (group_merge).  Spreading a group over several
 // workgroups spreads a long sequence's partials over several CUs, whose
