@@ -487,6 +487,60 @@ def split_sweep(torch, fd, steps: int) -> None:
             torch.cuda.empty_cache()
 
 
+def fused_sweep(torch, fd, steps: int) -> None:
+    """The single-launch merge (FD_FLAG_FUSED_MERGE) against the separate
+    merge pass over the split-sweep shapes and 256-32768 keys: device time
+    per step from a HIP graph (fd_decode_ex with a caller workspace whose
+    tickets start at zero; the faster of two measurements), the separate
+    merge at the planner's split count, the fused one at that count, half
+    and a quarter of it.  One JSON line per shape."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    F = fd.FD_FLAG_FUSED_MERGE
+    for B, Hq, Hkv, D, dtype in SPLIT_SWEEP_SHAPES:
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        for L in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+            if dtype == "f32" and L > 4096:
+                continue
+            shape = (B, Hkv, L, D)
+            kvb = 2 * B * Hkv * L * D * (2 if dtype == "bf16" else 4)
+            copies = max(1, min(8, (1 << 30) // kvb))
+            ks = [torch.randn(shape, device="cuda", dtype=tdt,
+                              generator=gen) for _ in range(copies)]
+            vs = [torch.randn(shape, device="cuda", dtype=tdt,
+                              generator=gen) for _ in range(copies)]
+            q = torch.randn((B, Hq, D), device="cuda", dtype=tdt,
+                            generator=gen)
+            out = torch.empty_like(q)
+            lse = torch.empty((B, Hq), device="cuda")
+            scale = D ** -0.5
+            S0 = fd.fd_plan(B, Hq, Hkv, D, L, dtype)["num_splits"]
+            n = steps if kvb < (32 << 20) else max(40, steps // 4)
+
+            def timed(S, flags):
+                p = fd.fd_plan(B, Hq, Hkv, D, L, dtype, num_splits=S,
+                               flags=flags)
+                ws = torch.zeros(max(p["workspace_bytes"], 256),
+                                 dtype=torch.uint8, device="cuda")
+
+                def call(i):
+                    fd.fd_decode_ex(q, ks[i % copies], vs[i % copies], None,
+                                    scale, out=out, lse=lse, num_splits=S,
+                                    flags=flags, workspace=ws)
+                return round(min(graph_us(torch, call, n, n // 2)
+                                 for _ in range(2)), 2)
+            res = {"sweep": "fused_merge", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "D": D, "dtype": dtype, "L": L, "planner_splits": S0,
+                   "separate": timed(S0, 0)}
+            if S0 > 1:
+                for S in sorted({S0, max(2, S0 // 2), max(2, S0 // 4)},
+                                reverse=True):
+                    res[f"fused_S{S}"] = timed(S, F)
+            print(json.dumps(res), flush=True)
+            del ks, vs
+            torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -515,6 +569,10 @@ def main(argv=None):
                     help="instead of the benchmark line: the planner's split "
                          "count against split counts 1..128 over batch, "
                          "heads and context length, one JSON line per shape")
+    ap.add_argument("--fused-sweep", action="store_true",
+                    help="instead of the benchmark line: the single-launch "
+                         "merge against the separate merge pass over the "
+                         "same shapes, one JSON line per shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter "
                          "runs: HBM bytes per counter unit)")
@@ -529,13 +587,15 @@ def main(argv=None):
     import long_context_decode_fd_amd as fd
     from long_context_decode_fd_amd import workloads as wl
 
-    if a.context_sweep or a.split_sweep:
+    if a.context_sweep or a.split_sweep or a.fused_sweep:
         torch.cuda.set_device(0)
         fd.load_library()
         if a.context_sweep:
             context_sweep(torch, fd, a.steps)
         if a.split_sweep:
             split_sweep(torch, fd, a.steps)
+        if a.fused_sweep:
+            fused_sweep(torch, fd, a.steps)
         return 0
 
     w = wl.ALL_WORKLOADS[a.workload or wl.BENCH_WORKLOAD]
