@@ -14,13 +14,18 @@
 //     from HBM exactly once;
 //   * aim for kBlocksPerCU workgroups per CU; split each sequence into
 //     S = ceil(target / U) chunks, each a multiple of the 32-key tile and at
-//     least kMinChunk keys.  Short chunks pay: at batch 1 a workgroup's
-//     time is mostly the latency of its tile chain, so 64-key chunks over
-//     all CUs beat 256-key chunks over a quarter of them (1024 keys: 7.8
-//     against 10.3 us);
+//     least kMinChunk keys -- or a single tile on the matrix cores, when
+//     one-tile chunks of every sequence still fit one round of workgroups
+//     and leave a row at most kMaxTileChunks partials.  Short chunks pay: at
+//     batch 1 a workgroup's time is mostly the latency of its tile chain,
+//     so 64-key chunks over all CUs beat 256-key chunks over a quarter of
+//     them (1024 keys: 7.8 against 10.3 us), and 32-key ones beat 64-key
+//     ones (7.5 against 7.9 us);
 //   * S == 1 means no partials and no merge pass at all; it is taken when a
-//     split would not take more than kSplitGain keys off each workgroup's
-//     share, about what the merge pass costs;
+//     split would not take more than kSplitGain keys of 256 bytes (one
+//     D = 128 bf16 row) off each workgroup's share, about what the merge
+//     pass costs; the matrix-core pass counts it in bytes, so rows of
+//     D = 64 give twice the keys;
 //   * with per-sequence lengths the mix is unknown on the host (the library
 //     never reads device memory synchronously), so chunks are also capped
 //     at kVarlenChunk keys, so that no single long sequence sets the finish
@@ -67,6 +72,10 @@ constexpr int kMinChunk = FD_MIN_CHUNK;
 constexpr int kSplitGain = FD_SPLIT_GAIN;
 constexpr int kVarlenChunk = FD_VARLEN_CHUNK;
 constexpr int kGridPerCU = 8;
+// One-tile chunks at most this many per sequence (the merge of more
+// partials per row outweighs the shorter chunks: measured at batch 1, 2
+// KV heads, 2048 keys, 64 one-tile chunks took 9.1 us against 8.5 in 32).
+constexpr int kMaxTileChunks = 32;
 constexpr int kMfmaWaves = FD_MFMA_WAVES;
 static_assert(kMfmaWaves == 2 || kMfmaWaves == 4 || kMfmaWaves == 8,
               "the matrix-core kernel is built for 2, 4 or 8 wavefronts");
@@ -184,15 +193,30 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     const long target = (long)num_cus * blocks_per_cu;
     int s = (int)std::max(1L, (target + units - 1) / units);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
-    chunk = std::max(chunk, std::min(kMinChunk, full_chunk));
+    // Matrix cores, short caches: one-tile chunks when they all run in one
+    // round and a row merges at most kMaxTileChunks partials.  Measured
+    // (device time of steps replayed from a graph), 64 query / 8 KV heads,
+    // D = 128, batch 1: 384 keys 7.44 -> 6.91 us, 640 keys 7.93 -> 7.33,
+    // 1024 keys 7.86 -> 7.54; batch 2 at 512 keys 7.94 -> 7.44; with 8 KV
+    // heads at 1280 keys (40 tiles, 320 workgroups) they were slower.
+    const int tiles = ceil_div(Lmax, kKeyTile);
+    const bool tile_chunks = q.variant == FD_VARIANT_MFMA &&
+                             tiles <= kMaxTileChunks &&
+                             units * tiles <= target;
+    chunk = std::max(chunk,
+                     std::min(tile_chunks ? kKeyTile : kMinChunk, full_chunk));
     // Short caches: one launch beats two.  The merge pass (a second kernel)
     // costs about as much as a workgroup streaming kSplitGain more keys, so
     // a split must take more than that off each workgroup's share.
     // Measured on MI355X (device time of steps replayed from a graph):
     // batch 1, 64 query / 8 KV heads, 256 keys: 6.4 us unsplit, 7.0 in
     // 8 chunks; 512 keys: 10.1 unsplit, 7.4 in 16 chunks; 16 sequences
-    // at 512 keys: 12.4 unsplit, 13.3 in two chunks.
-    if (Lmax - chunk <= kSplitGain) chunk = full_chunk;
+    // at 512 keys: 12.4 unsplit, 13.3 in two chunks.  D = 64 rows are half
+    // as long: 384 keys, 5.8 unsplit against 6.9 in six chunks.
+    const int gain = q.variant == FD_VARIANT_MFMA
+                         ? kSplitGain * 128 / D  // 256-byte bf16 rows
+                         : kSplitGain;
+    if (Lmax - chunk <= gain) chunk = full_chunk;
     // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
     // than the even split would make it were every sequence full.
     if (varlen) chunk = std::min(chunk, kVarlenChunk);

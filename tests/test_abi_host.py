@@ -206,27 +206,46 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("varlen", [False, True])
 def test_short_caches_take_one_launch(lib, dtype, varlen):
-    # The planner splits only when a split takes more than 256 keys off
-    # each workgroup's share (chunks of at least 64 keys): with 8 units
-    # (batch 1, 8 KV heads) up to 320 keys stay in one chunk per sequence,
-    # with no partials and no merge pass; one key more and the sequence is
-    # cut into 64-key chunks.
-    for L in (32, 300, 320):
+    # The planner splits only when a split takes more than 256 keys of
+    # D = 128 off each workgroup's share.  With 8 units (batch 1, 8 KV
+    # heads) the matrix cores (bf16) take one-tile chunks of 32 keys, so up
+    # to 288 keys stay in one chunk per sequence, with no partials and no
+    # merge pass, and one key more is cut into 32-key chunks; the vector ALU
+    # (fp32) keeps chunks of at least 64 keys, so its bound is 320 keys.
+    one = 288 if dtype == "bf16" else 320
+    for L in (32, 250, one):
         p = fd.fd_plan(1, 8, 8, 128, L, dtype, varlen=varlen, num_cus=256)
         assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == \
             (1, 0, 0), (L, p)
-    p = fd.fd_plan(1, 8, 8, 128, 321, dtype, varlen=varlen, num_cus=256)
-    assert (p["num_splits"], p["chunk"], p["combine"]) == (6, 64, 1)
+    p = fd.fd_plan(1, 8, 8, 128, one + 1, dtype, varlen=varlen, num_cus=256)
+    assert (p["num_splits"], p["chunk"], p["combine"]) == \
+        ((10, 32, 1) if dtype == "bf16" else (6, 64, 1))
     # a paged table of that capacity plans the same way
     if dtype == "bf16":
-        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 320, "bf16", varlen=True,
+        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 288, "bf16", varlen=True,
                           paged=True, num_cus=256)
         assert p["num_splits"] == 1 and p["combine"] == 0
+        p = fd.fd_plan_ex(1, 1, 8, 8, 128, 289, "bf16", varlen=True,
+                          paged=True, num_cus=256)
+        assert (p["num_splits"], p["chunk"]) == (10, 32)
+
+
+def test_head_dim_64_counts_the_split_gain_in_bytes(lib):
+    # D = 64 rows are half as long: up to 512 keys (minus a chunk) stay in
+    # one launch (measured, batch 1, 64 query / 8 KV heads, 384 keys: 5.8
+    # us unsplit against 6.9 in six chunks); beyond, one-tile chunks.
+    for L in (384, 544):
+        p = fd.fd_plan(1, 64, 8, 64, L, "bf16", num_cus=256)
+        assert p["num_splits"] == 1, (L, p)
+    p = fd.fd_plan(1, 64, 8, 64, 640, "bf16", num_cus=256)
+    assert (p["num_splits"], p["chunk"]) == (20, 32)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,S", [
     # measured fastest or within 7% of it (device time, MI355X)
-    (1, 64, 8, 1024, 16), (1, 64, 8, 4096, 32), (1, 64, 8, 65536, 32),
+    (1, 64, 8, 1024, 32), (1, 64, 8, 4096, 32), (1, 64, 8, 65536, 32),
+    (1, 64, 8, 512, 16), (2, 64, 8, 512, 16), (1, 64, 8, 1280, 20),
+    (2, 64, 8, 640, 10), (1, 16, 2, 2048, 32),
     (2, 64, 8, 2048, 16), (4, 64, 8, 512, 8), (8, 32, 8, 512, 4),
     (16, 32, 8, 512, 1), (16, 32, 8, 768, 2), (4, 32, 32, 512, 1),
     (4, 32, 32, 32768, 2), (64, 32, 8, 4096, 1)])
