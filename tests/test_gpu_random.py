@@ -5,8 +5,9 @@ layout, split count, merge mode, dtype) from a fixed seed, so a failure
 names a case that can be rerun alone.  Sizes stay small enough for the
 oracle (at most a few hundred thousand key rows per case) while spanning
 several tiles, chunks and ragged tails; some cases draw 60-80 short
-sequences, whose work lists go past one round of workgroups.  The rule is the suite's: |out - ref|
-<= 1e-2 or faithful bf16 rounding, |lse - ref| <= 1e-3.
+sequences, whose work lists go past one round of workgroups, and the long
+cases caches of up to 24k keys.  The rule is the suite's (tests/parity.py):
+|out - ref| <= max(1e-2, half a bf16 ulp of ref), |lse - ref| <= 1e-3.
 """
 import numpy as np
 import pytest
@@ -59,6 +60,27 @@ def draw_case(i):
                 seed=2000 + i)
 
 
+N_LONG_CASES = 24
+
+
+def draw_long_case(i):
+    """A case of draw_case(i) with longer caches (up to 24k keys, up to 8
+    sequences, often all full): plans of 2048-key var-len chunks, direct
+    and listed chunk ids, and split counts up to 100."""
+    c = draw_case(i)
+    rng = np.random.default_rng(50000 + i)
+    c["B"] = int(rng.integers(1, 9))
+    c["Lmax"] = int(rng.integers(1, 24000))
+    c["seqlens"] = rng.integers(0, c["Lmax"] + 3,
+                                size=c["B"]).astype(np.int32)
+    if rng.random() < 0.4:
+        c["seqlens"][:] = c["Lmax"]
+    if c["kind"] in ("paged", "paged_mq"):
+        c["seqlens"] = np.minimum(c["seqlens"], c["Lmax"])
+    c["splits"] = int(rng.choice([0, 0, 0, 3, 40, 100]))
+    return c
+
+
 @pytest.fixture(scope="module")
 def torch():
     t = pytest.importorskip("torch")
@@ -81,7 +103,15 @@ def _host(w, seqlens):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(torch, oracle_mod, i):
-    c = draw_case(i)
+    _run_case(torch, oracle_mod, i, draw_case(i))
+
+
+@pytest.mark.parametrize("i", range(N_LONG_CASES))
+def test_random_long_case(torch, oracle_mod, i):
+    _run_case(torch, oracle_mod, i, draw_long_case(i))
+
+
+def _run_case(torch, oracle_mod, i, c):
     print(f"[random {i}] {dict((k, v) for k, v in c.items() if k != 'seqlens')}"
           f" seqlens={c['seqlens'].tolist()}", flush=True)
     kind = c["kind"]
