@@ -200,11 +200,19 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     // 1024 keys 7.86 -> 7.54; batch 2 at 512 keys 7.94 -> 7.44; with 8 KV
     // heads at 1280 keys (40 tiles, 320 workgroups) they were slower.
     const int tiles = ceil_div(Lmax, kKeyTile);
-    const bool tile_chunks = q.variant == FD_VARIANT_MFMA &&
-                             tiles <= kMaxTileChunks &&
-                             units * tiles <= target;
-    chunk = std::max(chunk,
-                     std::min(tile_chunks ? kKeyTile : kMinChunk, full_chunk));
+    const bool mfma = q.variant == FD_VARIANT_MFMA;
+    // The vector-ALU kernel does G dot products per key, so its chunks pay
+    // for themselves sooner as G grows: from G = 4 on, one-tile chunks at
+    // any length that still fits one round (measured, fp32, one sequence:
+    // 4 query heads on each of 4 KV heads, D = 128, 2048 keys 12.6 -> 10.6
+    // us; 16 on one, D = 64, 1024 keys 23.6 -> 18.4).
+    const bool tile_chunks =
+        (tiles <= kMaxTileChunks || (!mfma && q.G >= 4)) &&
+        units * tiles <= target;
+    const int chunk64 = std::max(chunk, std::min(kMinChunk, full_chunk));
+    chunk = mfma && tile_chunks
+                ? std::max(chunk, std::min(kKeyTile, full_chunk))
+                : chunk64;
     // Short caches: one launch beats two.  The merge pass (a second kernel)
     // costs about as much as a workgroup streaming kSplitGain more keys, so
     // a split must take more than that off each workgroup's share.
@@ -213,10 +221,22 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     // 8 chunks; 512 keys: 10.1 unsplit, 7.4 in 16 chunks; 16 sequences
     // at 512 keys: 12.4 unsplit, 13.3 in two chunks.  D = 64 rows are half
     // as long: 384 keys, 5.8 unsplit against 6.9 in six chunks.
-    const int gain = q.variant == FD_VARIANT_MFMA
-                         ? kSplitGain * 128 / D  // 256-byte bf16 rows
-                         : kSplitGain;
-    if (Lmax - chunk <= gain) chunk = full_chunk;
+    // Counted in bytes of 256-byte rows (one D = 128 bf16 row), and on the
+    // vector ALU per query row of the group, whose work per key is G dot
+    // products (measured, fp32, 256 keys: 16 query heads on one KV head,
+    // D = 64, 53 us unsplit against 17 in 8 chunks; 8 heads, D = 128,
+    // 2 sequences, 11.2 against 7.1).
+    const int elem = dtype == FD_BF16 ? 2 : 4;
+    const int gain =
+        kSplitGain * 256 / (D * elem) / (mfma ? 1 : q.G);
+    if (Lmax - chunk <= gain) {
+      chunk = full_chunk;
+    } else if (!mfma && tile_chunks) {
+      // fp32: decided on 64-key chunks, split into one-tile ones
+      // (measured, 8 heads, D = 64, one sequence, 1024 keys: 7.0 -> 6.8 us;
+      // four sequences, 512 keys: 7.6 -> 7.4)
+      chunk = std::max(round_up(ceil_div(Lmax, s), kKeyTile), kKeyTile);
+    }
     // Unknown lengths: no chunk longer than kVarlenChunk, and no longer
     // than the even split would make it were every sequence full.
     if (varlen) chunk = std::min(chunk, kVarlenChunk);

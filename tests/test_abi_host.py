@@ -195,31 +195,32 @@ def test_plans_for_the_five_workloads_on_256_cus(lib):
     # (the work list's upper bound 16 * 8 * 64, halved: two chunks per
     # workgroup)
     assert (p["chunk"], p["num_splits"], p["grid"]) == (2048, 64, 16 * 8 * 32)
-    # fp32 runs on the vector ALU, in 64-key chunks: the tiny decode (8
-    # units) splits 1024 keys 16 ways (measured fastest of 1..32 splits
-    # but for 32, which was level)
+    # fp32 runs on the vector ALU: the tiny decode (8 units) splits 1024
+    # keys into 32 one-tile chunks (measured 6.8 us against 7.0 in 16
+    # chunks of 64 keys)
     p = plan(W["tiny_mha_f32_b1_h8_d64_l1024"])
     assert p["variant"] == fd.FD_VARIANT_VALU
-    assert (p["chunk"], p["num_splits"], p["grid"]) == (64, 16, 128)
+    assert (p["chunk"], p["num_splits"], p["grid"]) == (32, 32, 256)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("varlen", [False, True])
 def test_short_caches_take_one_launch(lib, dtype, varlen):
-    # The planner splits only when a split takes more than 256 keys of
-    # D = 128 off each workgroup's share.  With 8 units (batch 1, 8 KV
-    # heads) the matrix cores (bf16) take one-tile chunks of 32 keys, so up
-    # to 288 keys stay in one chunk per sequence, with no partials and no
-    # merge pass, and one key more is cut into 32-key chunks; the vector ALU
-    # (fp32) keeps chunks of at least 64 keys, so its bound is 320 keys.
-    one = 288 if dtype == "bf16" else 320
-    for L in (32, 250, one):
+    # The planner splits only when a split takes more than 64 KB of K (256
+    # bf16 rows of D = 128, 128 fp32 ones) off each workgroup's share.
+    # With 8 units (batch 1, 8 KV heads) the matrix cores (bf16) take
+    # one-tile chunks of 32 keys, so up to 288 keys stay in one chunk per
+    # sequence, with no partials and no merge pass, and one key more is cut
+    # into 32-key chunks; the vector ALU (fp32) decides on 64-key chunks,
+    # so its bound is 192 keys, and then cuts one-tile chunks too.
+    one = 288 if dtype == "bf16" else 192
+    for L in (32, 150, one):
         p = fd.fd_plan(1, 8, 8, 128, L, dtype, varlen=varlen, num_cus=256)
         assert (p["num_splits"], p["combine"], p["workspace_bytes"]) == \
             (1, 0, 0), (L, p)
     p = fd.fd_plan(1, 8, 8, 128, one + 1, dtype, varlen=varlen, num_cus=256)
     assert (p["num_splits"], p["chunk"], p["combine"]) == \
-        ((10, 32, 1) if dtype == "bf16" else (6, 64, 1))
+        ((10, 32, 1) if dtype == "bf16" else (7, 32, 1))
     # a paged table of that capacity plans the same way
     if dtype == "bf16":
         p = fd.fd_plan_ex(1, 1, 8, 8, 128, 288, "bf16", varlen=True,
@@ -254,14 +255,32 @@ def test_split_counts_follow_the_measured_rule(lib, B, Hq, Hkv, L, S):
     assert p["num_splits"] == S, p
 
 
-@pytest.mark.parametrize("B,L,S", [(1, 1024, 16), (1, 4096, 64),
-                                   (4, 1024, 16), (4, 4096, 32),
-                                   (1, 256, 1)])
+@pytest.mark.parametrize("B,L,S", [(1, 1024, 32), (1, 4096, 64),
+                                   (4, 1024, 32), (4, 4096, 32),
+                                   (1, 256, 1), (1, 320, 1), (1, 2048, 32)])
 def test_fp32_plans_for_four_workgroups_per_cu(lib, B, L, S):
-    # the vector-ALU kernel: four resident workgroups per CU, 64-key chunks
+    # the vector-ALU kernel: four resident workgroups per CU; one-tile
+    # chunks up to 32 per sequence, 64-key ones beyond (measured fastest or
+    # within 5% of it, 8 heads, D = 64)
     p = fd.fd_plan(B, 8, 8, 64, L, "f32", num_cus=256)
     assert p["variant"] == fd.FD_VARIANT_VALU
     assert p["num_splits"] == S, p
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,L,S", [(16, 1, 64, 256, 8),
+                                          (16, 1, 64, 2048, 64),
+                                          (16, 4, 128, 2048, 64),
+                                          (8, 8, 128, 256, 8)])
+def test_fp32_groups_split_sooner(lib, Hq, Hkv, D, L, S):
+    # G dot products per key on the vector ALU: the split gain shrinks with
+    # G and, from G = 4 on, one-tile chunks pay at any length that fits one
+    # round (measured: 16 heads on one KV head, D = 64, 256 keys 53 us
+    # unsplit against 17 in 8 chunks; 4 on each of 4, D = 128, 2048 keys
+    # 12.6 in 32 chunks against 10.6 in 64)
+    B = 2 if Hq == 8 else 1
+    p = fd.fd_plan(B, Hq, Hkv, D, L, "f32", num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_VALU
+    assert (p["num_splits"], p["chunk"]) == (S, 32), p
 
 
 @pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
