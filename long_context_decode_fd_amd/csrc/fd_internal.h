@@ -36,6 +36,9 @@ struct Plan {
   bool fused;       // merged by the last workgroup of each group
   bool chunk_major; // partial layout: chunk-major (several rounds of
                     // workgroups) or row-major (one round)
+  int kv_rep;       // vector-ALU groups of more than 8 query heads run as
+                    // kv_rep half-groups on the same K/V slab: Hkv and G
+                    // above are the virtual ones (Hkv * kv_rep, G / kv_rep)
   size_t ws_bytes;  // tickets + partial outputs + partial lse
 };
 

@@ -1315,9 +1315,10 @@ template <typename T, int D, int NW, int GT>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ seqlens, int B, int Hq, int Hkv, int G,
-    int Lmax, int C, int S, float scale_log2, int mode, bool chunk_major,
-    T *__restrict__ out, float *__restrict__ lse, float *__restrict__ o_part,
-    float *__restrict__ lse_part, int *__restrict__ tickets) {
+    int kv_rep, int Lmax, int C, int S, float scale_log2, int mode,
+    bool chunk_major, T *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part,
+    int *__restrict__ tickets) {
   constexpr int EPL = Elem<T>::kPerLane;
   constexpr int LPR = D / EPL;
   constexpr int RPW = 64 / LPR;
@@ -1351,7 +1352,10 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
       for (int e = 0; e < EPL; ++e) qf[gi][e] = 0.f;
     }
   }
-  const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
+  // Hkv and G may be virtual: kv_rep groups of G query heads share each
+  // KV slab (query head w.g * G + gi either way).
+  const size_t slab =
+      ((size_t)w.b * Hkv + w.g) / kv_rep * (size_t)Lmax * D;
   const T *kslab = kc + slab + col * EPL;
   const T *vslab = vc + slab + col * EPL;
 
@@ -1613,9 +1617,10 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
 #define FD_VALU_CASE(GTV)                                                    \
   case GTV:                                                                  \
     hipLaunchKernelGGL((split_valu_kernel<T, D, NW, GTV>), grid, block, 0,   \
-                       st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G, p.Lmax, \
-                       p.chunk, p.splits, sl2, part, p.chunk_major, out,     \
-                       a.lse, a.o_part, a.lse_part, a.tickets);              \
+                       st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G,        \
+                       p.kv_rep, p.Lmax, p.chunk, p.splits, sl2, part,       \
+                       p.chunk_major, out, a.lse, a.o_part, a.lse_part,      \
+                       a.tickets);                                           \
     break;
   switch (gt) {
     FD_VALU_CASE(1)
@@ -1626,7 +1631,7 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
         if (gt == 8) {
           hipLaunchKernelGGL((split_valu_kernel<T, D, NW, 8>), grid, block, 0,
                              st, q, k, v, a.seqlens, p.B, p.Hq, p.Hkv, p.G,
-                             p.Lmax, p.chunk, p.splits, sl2, part,
+                             p.kv_rep, p.Lmax, p.chunk, p.splits, sl2, part,
                              p.chunk_major, out, a.lse, a.o_part, a.lse_part,
                              a.tickets);
           break;
@@ -1634,9 +1639,9 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
         if (gt == 16) {
           hipLaunchKernelGGL((split_valu_kernel<T, D, 2, 16>), grid,
                              dim3(2 * 64), 0, st, q, k, v, a.seqlens, p.B,
-                             p.Hq, p.Hkv, p.G, p.Lmax, p.chunk, p.splits, sl2,
-                             part, p.chunk_major, out, a.lse, a.o_part,
-                             a.lse_part, a.tickets);
+                             p.Hq, p.Hkv, p.G, p.kv_rep, p.Lmax, p.chunk,
+                             p.splits, sl2, part, p.chunk_major, out, a.lse,
+                             a.o_part, a.lse_part, a.tickets);
           break;
         }
       }

@@ -80,11 +80,15 @@ constexpr int kMfmaWaves = FD_MFMA_WAVES;
 static_assert(kMfmaWaves == 2 || kMfmaWaves == 4 || kMfmaWaves == 8,
               "the matrix-core kernel is built for 2, 4 or 8 wavefronts");
 constexpr int kValuWaves = 4;
-// The vector-ALU kernel is latency-bound per workgroup and light on
-// registers, so it is planned for four resident workgroups per CU:
-// measured (fp32, D = 64, 8 query heads), batch 4 at 1024 keys took 9.2 us
-// in 8 chunks and 8.3 in 32; batch 1 at 4096 keys 8.9 in 32 and 8.7 in 64.
-constexpr int kValuBlocksPerCU = 4;
+// The vector-ALU kernel is latency-bound per workgroup, so it is planned
+// for two workgroups per CU, twice the matrix-core pass (short caches also
+// take one-tile chunks, below).  Measured (fp32, device time of steps
+// replayed from a graph) against four per CU: 16k keys, 32 query / 8 KV
+// heads, D = 128: 31.1 us against 32.6; 64 / 8 heads 48.4 against 54.0;
+// 64k keys 94.9 against 102.1; one sequence of 8 query heads on one KV
+// head at 16k keys 23.7 against 27.7 (256 chunks against 512); at 8192 keys
+// and below within 1-3% either way.
+constexpr int kValuBlocksPerCU = 2;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int round_up(long a, long b) { return (int)(((a + b - 1) / b) * b); }
@@ -175,6 +179,17 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   // registers; beyond 4 rows the matrix-core kernel is the one to use.
   if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)
     return FD_ERR_UNSUPPORTED;
+  // The vector-ALU kernel computes G dot products per key, each finished by
+  // a butterfly across the lanes of a row; past 8 query heads (16 rows in
+  // registers, two wavefronts) it ran at 0.27 TB/s.  Even groups of 10-16
+  // heads run as two half-groups instead, each its own virtual KV head on
+  // the same slab: K/V are read twice, at the rate of the 8-row kernel.
+  q.kv_rep = 1;
+  if (q.variant == FD_VARIANT_VALU && q.G > 8 && q.G % 2 == 0) {
+    q.kv_rep = 2;
+    q.Hkv *= 2;
+    q.G /= 2;
+  }
   if (q.variant == FD_VARIANT_MFMA)
     q.waves = kMfmaWaves;
   else
@@ -189,7 +204,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     int s = std::min(requested_splits, max_splits);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
   } else {
-    const long units = (long)B * Hkv;
+    const long units = (long)B * q.Hkv;
     const long target = (long)num_cus * blocks_per_cu;
     int s = (int)std::max(1L, (target + units - 1) / units);
     chunk = round_up(ceil_div(Lmax, s), kKeyTile);
@@ -202,12 +217,13 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     const int tiles = ceil_div(Lmax, kKeyTile);
     const bool mfma = q.variant == FD_VARIANT_MFMA;
     // The vector-ALU kernel does G dot products per key, so its chunks pay
-    // for themselves sooner as G grows: from G = 4 on, one-tile chunks at
-    // any length that still fits one round (measured, fp32, one sequence:
-    // 4 query heads on each of 4 KV heads, D = 128, 2048 keys 12.6 -> 10.6
-    // us; 16 on one, D = 64, 1024 keys 23.6 -> 18.4).
+    // for themselves sooner as G grows: from G = 4 on, one-tile chunks up to
+    // twice as many per sequence (measured, fp32, one sequence, 4 query
+    // heads on each of 4 KV heads, D = 128, 2048 keys: 12.6 -> 10.6 us; at
+    // 16k keys 128-key chunks were fastest).
     const bool tile_chunks =
-        (tiles <= kMaxTileChunks || (!mfma && q.G >= 4)) &&
+        (tiles <= kMaxTileChunks ||
+         (!mfma && q.G >= 4 && tiles <= 2 * kMaxTileChunks)) &&
         units * tiles <= target;
     const int chunk64 = std::max(chunk, std::min(kMinChunk, full_chunk));
     chunk = mfma && tile_chunks
@@ -245,7 +261,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.splits = ceil_div(Lmax, chunk);
   q.combine = q.splits > 1 || (flags & FD_FLAG_PARTIALS);
   q.fused = q.combine && (flags & FD_FLAG_FUSED_MERGE);
-  long grid = (long)B * Hkv * q.splits;
+  long grid = (long)B * q.Hkv * q.splits;
   if (grid > 0x7FFFFFFFL) return FD_ERR_UNSUPPORTED;
   // Per-sequence lengths: the chunk count is only an upper bound (every
   // sequence at Lmax), and each workgroup of the matrix-core kernel can take

@@ -49,10 +49,11 @@ int main() {
               }
               ++plans;
               const long long C = p.chunk, Sp = p.splits;
-              const long long bound = (long long)B * h[1] * Sp;
+              const long long bound = (long long)B * h[1] * p.kv_rep * Sp;
               bool ok = C >= fd::kKeyTile && C % fd::kKeyTile == 0 && Sp >= 1 &&
                         Sp * C >= L && (Sp - 1) * C < L && p.grid >= 1 &&
-                        p.grid <= bound && p.G == h[0] / h[1] &&
+                        p.grid <= bound && p.G * p.kv_rep == h[0] / h[1] && p.Hkv == h[1] * p.kv_rep &&
+                        (p.kv_rep == 1 || p.variant == FD_VARIANT_VALU) &&
                         p.combine == (Sp > 1 || (flags & FD_FLAG_PARTIALS)) &&
                         p.ws_bytes == fd::workspace_layout(p).total &&
                         (p.combine || p.ws_bytes == 0);

@@ -256,12 +256,13 @@ def test_split_counts_follow_the_measured_rule(lib, B, Hq, Hkv, L, S):
 
 
 @pytest.mark.parametrize("B,L,S", [(1, 1024, 32), (1, 4096, 64),
-                                   (4, 1024, 32), (4, 4096, 32),
-                                   (1, 256, 1), (1, 320, 1), (1, 2048, 32)])
-def test_fp32_plans_for_four_workgroups_per_cu(lib, B, L, S):
-    # the vector-ALU kernel: four resident workgroups per CU; one-tile
-    # chunks up to 32 per sequence, 64-key ones beyond (measured fastest or
-    # within 5% of it, 8 heads, D = 64)
+                                   (4, 1024, 16), (4, 4096, 16),
+                                   (1, 256, 1), (1, 320, 1), (1, 2048, 32),
+                                   (1, 16384, 64)])
+def test_fp32_plans_for_two_workgroups_per_cu(lib, B, L, S):
+    # the vector-ALU kernel: two workgroups per CU; one-tile chunks up to 32
+    # per sequence, 64-key ones beyond (measured fastest or within 5% of
+    # it, 8 heads, D = 64)
     p = fd.fd_plan(B, 8, 8, 64, L, "f32", num_cus=256)
     assert p["variant"] == fd.FD_VARIANT_VALU
     assert p["num_splits"] == S, p
@@ -281,6 +282,28 @@ def test_fp32_groups_split_sooner(lib, Hq, Hkv, D, L, S):
     p = fd.fd_plan(B, Hq, Hkv, D, L, "f32", num_cus=256)
     assert p["variant"] == fd.FD_VARIANT_VALU
     assert (p["num_splits"], p["chunk"]) == (S, 32), p
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,L,S,C", [(8, 1, 128, 16384, 256, 64),
+                                            (8, 1, 128, 65536, 512, 128),
+                                            (16, 4, 128, 16384, 128, 128),
+                                            (16, 1, 64, 65536, 256, 256)])
+def test_fp32_long_caches_keep_chunks_of_64_keys_or_more(lib, Hq, Hkv, D, L,
+                                                         S, C):
+    # measured fastest (fp32, one sequence): past 64 tiles the split count
+    # follows two workgroups per CU and chunks stay at 64 keys or more
+    p = fd.fd_plan(1, Hq, Hkv, D, L, "f32", num_cus=256)
+    assert (p["num_splits"], p["chunk"]) == (S, C), p
+
+
+def test_fp32_groups_past_8_heads_run_as_half_groups(lib):
+    # 16 query heads on one KV head: two virtual groups of 8 on the same
+    # slab, so the plan counts two units (grid = 2 * S)
+    p = fd.fd_plan(1, 16, 1, 64, 65536, "f32", num_cus=256)
+    assert p["grid"] == 2 * p["num_splits"]
+    # odd groups past 8 keep one 16-row group
+    p = fd.fd_plan(1, 9, 1, 64, 65536, "f32", num_cus=256)
+    assert p["grid"] == p["num_splits"]
 
 
 @pytest.mark.parametrize("L,S", [(1, 1), (31, 1), (33, 2), (1000, 7),
