@@ -136,7 +136,8 @@ enum {
 /* Kernel variant chosen for the per-chunk pass. */
 enum {
     FD_VARIANT_AUTO = 0,
-    FD_VARIANT_MFMA = 1, /* bf16 matrix-core pass, q group padded to 16 */
+    FD_VARIANT_MFMA = 1, /* matrix-core pass, q group padded to 16 (bf16;
+                            fp32 for plain single-token decode) */
     FD_VARIANT_VALU = 2  /* vector-ALU pass (fp32, or bf16 small groups) */
 };
 
@@ -202,7 +203,10 @@ FD_API int fd_decode(const void *q, const void *k_cache,
  * fd_decode_ex -- as fd_decode, with the caller's choices:
  *   num_splits  0 = planner's choice, else chunks per Lmax-long sequence
  *               (clamped to [1, ceil(Lmax / 32)]); 1 disables the merge.
- *   variant     FD_VARIANT_AUTO / _MFMA / _VALU (MFMA needs bf16).
+ *   variant     FD_VARIANT_AUTO / _MFMA / _VALU.  AUTO: the matrix cores
+ *               for bf16 and for fp32 groups of more than 4 query heads,
+ *               the vector ALU for smaller fp32 groups.  VALU takes bf16
+ *               groups of at most 4 heads only.
  *   flags       0 or FD_FLAG_FUSED_MERGE.
  *   workspace   device buffer of at least fd_workspace_bytes(...) bytes
  *               for the same arguments, 256-byte aligned, or NULL with

@@ -37,8 +37,11 @@
 //     rows at D = 128), serves several causal new tokens per sequence
 //     (their query rows share the 16-column q-tile), or takes the
 //     unified-maximum softmax of FlashDecoding++ with an exact fallback;
-//   * fp32 (and bf16 tiny groups) run a vector-ALU kernel with 16-byte
-//     loads per lane and shuffle reductions of the dot products;
+//   * fp32 groups of more than 4 query heads run a matrix-core kernel on
+//     v_mfma_f32_16x16x4_f32 (16-key halves, the next half in flight);
+//     smaller fp32 groups (and bf16 tiny groups, on request) a vector-ALU
+//     kernel with 16-byte loads per lane and shuffle reductions of the dot
+//     products;
 //   * a second, small kernel merges the chunk partials of every query row
 //     (or, opt-in, the last workgroup of each group merges them).
 #include <hip/hip_runtime.h>
@@ -1044,12 +1047,13 @@ constexpr float kUniRange = 64.f;
 // 2^(m - M) / W, adds the weighted accumulators in wavefront order and
 // stores its lane's contiguous run of output columns, (q4 * 4 + j) * VW + e,
 // with vector stores.  A column that saw no key gets out 0 and lse -inf.
-template <int D, int NW>
+// OutT: uint16_t (bf16 bits, rounded to nearest even) or float.
+template <int D, int NW, typename OutT = uint16_t>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
     int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
     const Work &w, const PartLayout &pl, int mode,
-    uint16_t *__restrict__ out, float *__restrict__ lse,
+    OutT *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part) {
   constexpr int VW = D / 16;
   constexpr int V4 = VW / 4;  // float4 per (lane, j)
@@ -1105,10 +1109,16 @@ __device__ __forceinline__ void wave_merge_store(
       }
       const int d0 = (q4 * 4 + j) * VW + 4 * e4;
       if (mode == kModeDirect) {
-        uint2 bits;
-        bits.x = (uint32_t)to_bf16_bits(o.x) | ((uint32_t)to_bf16_bits(o.y) << 16);
-        bits.y = (uint32_t)to_bf16_bits(o.z) | ((uint32_t)to_bf16_bits(o.w) << 16);
-        *reinterpret_cast<uint2 *>(out + row * D + d0) = bits;
+        if constexpr (sizeof(OutT) == 2) {
+          uint2 bits;
+          bits.x = (uint32_t)to_bf16_bits(o.x) |
+                   ((uint32_t)to_bf16_bits(o.y) << 16);
+          bits.y = (uint32_t)to_bf16_bits(o.z) |
+                   ((uint32_t)to_bf16_bits(o.w) << 16);
+          *reinterpret_cast<uint2 *>(out + row * D + d0) = bits;
+        } else {
+          *reinterpret_cast<float4 *>(out + row * D + d0) = o;
+        }
       } else {
         *reinterpret_cast<float4 *>(o_part + row * D + d0) = o;
       }
@@ -1273,6 +1283,238 @@ void split_mfma_kernel(
                                         Hkv, G, Tq, Lmax, C, S, scale_log2,
                                         phi2, mode, chunk_major, out, lse,
                                         o_part, lse_part, tickets);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel for fp32 caches (one new token per sequence, contiguous
+// cache).
+//
+// v_mfma_f32_16x16x4_f32 takes one fp32 value of each operand per lane.  For
+// the scores S^T = K Q^T lane (n16, q4) loads 16 bytes of key row n16 per
+// register j, elements d = 16 j + 4 q4 + e (e = 0..3), and the q-tile holds
+// the same d of query column n16, so one register serves four MFMAs: the
+// dot product only runs over d in another order.  The scores then sit in
+// the bf16 kernel's layout (lane (n16, q4), element r: key 4 q4 + r of the
+// 16-key half, column n16) and the softmax is the same.  For O^T += V^T P^T
+// the four keys 4 q4 + r (r fixed) form one MFMA's k-slice: its B operand
+// is the lane's own p of element r, its A operand V[key][n16 * VW + e], so
+// the accumulators also match the bf16 kernel's (element j of block e:
+// column n16, d = (4 q4 + j) * VW + e) and the end-of-chunk merge is
+// shared.  P stays fp32 (no hi/lo split).  A wavefront works through its
+// tiles in 16-key halves (one MFMA k-slice of scores each) and keeps the
+// next half's K and V in flight while the current half computes: 16 KB of
+// K/V per half at D = 128, two halves of registers, where a whole second
+// 32-key tile would not fit.
+__device__ __forceinline__ floatx4 load_stream_f4(const float *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+}
+
+template <int D>
+struct F32Half {
+  floatx4 k[D / 16];     // K row n16, d = 16 j + 4 q4 + e
+  floatx4 v[4][D / 64];  // V row 4 q4 + r, d = n16 * (D / 16) + 4 h + e
+};
+
+// The 16 keys from k0 (rows at or beyond `valid` re-read the last valid
+// one).
+template <int D, bool TAIL>
+__device__ __forceinline__ void f32_half_load(const float *__restrict__ k,
+                                              const float *__restrict__ v,
+                                              int k0, int valid, int n16,
+                                              int q4, F32Half<D> &h) {
+  constexpr int VW = D / 16;
+  const int rk = TAIL ? min(n16, valid - 1) : n16;
+  const float *pk = k + (size_t)(k0 + rk) * D + q4 * 4;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) h.k[j] = load_stream_f4(pk + 16 * j);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rv = TAIL ? min(q4 * 4 + r, valid - 1) : q4 * 4 + r;
+    const float *pv = v + (size_t)(k0 + rv) * D + n16 * VW;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) h.v[r][c] = load_stream_f4(pv + 4 * c);
+  }
+}
+
+template <int D, bool TAIL>
+__device__ __forceinline__ void f32_half_compute(
+    F32Half<D> &h, int valid, int q4, const floatx4 (&qf)[D / 16],
+    float scale_log2, floatx4 (&acc)[D / 16], float &m, float &l) {
+  constexpr int VW = D / 16;
+  floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sc = __builtin_amdgcn_mfma_f32_16x16x4f32(h.k[j][e], qf[j][e], sc, 0, 0,
+                                                0);
+  float s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x = sc[r] * scale_log2;
+    if (TAIL && q4 * 4 + r >= valid) x = FD_NEG_INF;
+    s[r] = x;
+  }
+  float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m, mt);
+  const float mref = mn == FD_NEG_INF ? 0.f : mn;
+  const float alpha = exp2_f(m - mref);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = exp2_f(s[r] - mref);
+  m = mn;
+  l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+  for (int e = 0; e < VW; ++e) acc[e] *= alpha;
+  if (TAIL) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (q4 * 4 + r >= valid)
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c)
+          h.v[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < VW; ++e)
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(h.v[r][e >> 2][e & 3],
+                                                    p[r], acc[e], 0, 0, 0);
+}
+
+// One chunk of the fp32 matrix-core pass: wavefront `wave` takes tiles
+// wave, wave + NW, ... in the chunk's tile order; every tile but the
+// chunk's last is full.
+template <int D, int NW>
+__device__ __forceinline__ void f32_chunk_pass(
+    const Work &w, const float *__restrict__ q, const float *__restrict__ kc,
+    const float *__restrict__ vc, int Hq, int Hkv, int G, int Lmax, int S,
+    float scale_log2, int mode, bool chunk_major, float *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ o_part,
+    float *__restrict__ lse_part, int *__restrict__ tickets) {
+  constexpr int VW = D / 16;
+  const PartLayout pl{G, 1, Hq, Hkv, S, chunk_major};
+  __shared__ float sm_m[NW * 16];
+  __shared__ float sm_l[NW * 16];
+  __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
+  __shared__ int sm_flag;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, q4 = lane >> 4;
+
+  floatx4 qf[D / 16];
+  {
+    const bool live = n16 < G;
+    const float *qr = q + row_of(w, G, Hq, 1, live ? n16 : 0) * D + q4 * 4;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      qf[j] = live ? *reinterpret_cast<const floatx4 *>(qr + 16 * j)
+                   : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
+  const float *k = kc + slab, *v = vc + slab;
+  const bool rotate = (size_t)Lmax * D * sizeof(float) % kRotateStride == 0;
+
+  floatx4 acc[VW];
+#pragma unroll
+  for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = FD_NEG_INF, l = 0.f;
+
+  // The wavefront's tiles wave, wave + NW, ... as a list of 16-key halves;
+  // only the chunk's last tile can be short, so only the last half of the
+  // list can be partial (a last tile of at most 16 keys gives one half).
+  const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
+  if (wave < ntiles) {
+    const TileOrder ord = tile_order(w, Hkv, ntiles, rotate);
+    const int nt = (ntiles - wave + NW - 1) / NW;
+    const int last0 = ord.key0(w, wave + (nt - 1) * NW);
+    const int nh = 2 * nt - (w.hi - last0 <= 16 ? 1 : 0);
+    auto key_of = [&](int i) {
+      return ord.key0(w, wave + (i >> 1) * NW) + (i & 1) * 16;
+    };
+    // two register sets taken in turn (a copy between them would wait for
+    // the loads in flight)
+    F32Half<D> h0, h1;
+    int ka = key_of(0);
+    f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h0);
+    int i = 0;
+    for (; i + 2 < nh; i += 2) {
+      ka = key_of(i + 1);
+      f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h1);
+      __builtin_amdgcn_sched_barrier(0);
+      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
+      ka = key_of(i + 2);
+      f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h0);
+      __builtin_amdgcn_sched_barrier(0);
+      f32_half_compute<D, false>(h1, 16, q4, qf, scale_log2, acc, m, l);
+    }
+    const int valid = min(16, w.hi - key_of(nh - 1));
+    if (i + 2 == nh) {
+      ka = key_of(i + 1);
+      f32_half_load<D, true>(k, v, ka, valid, n16, q4, h1);
+      __builtin_amdgcn_sched_barrier(0);
+      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
+      if (valid == 16)
+        f32_half_compute<D, false>(h1, 16, q4, qf, scale_log2, acc, m, l);
+      else
+        f32_half_compute<D, true>(h1, valid, q4, qf, scale_log2, acc, m, l);
+    } else if (valid == 16) {
+      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
+    } else {
+      f32_half_compute<D, true>(h0, valid, q4, qf, scale_log2, acc, m, l);
+    }
+  }
+
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (mode != kModeFused) {
+    wave_merge_store<D, NW, float>(sm_m, sm_l, sm_o, wave, lane, n16, q4, G,
+                                   m, l, acc, w, pl, mode, out, lse, o_part,
+                                   lse_part);
+    return;
+  }
+  if (n16 < G) {
+    if (q4 == 0) {
+      sm_m[wave * 16 + n16] = m;
+      sm_l[wave * 16 + n16] = l;
+    }
+    float *o = sm_o + (wave * 16 + n16) * (D + 1);
+#pragma unroll
+    for (int e = 0; e < VW; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[(q4 * 4 + j) * VW + e] = acc[e][j];
+  }
+  __syncthreads();
+  merge_and_store<D, float>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out, lse,
+                            o_part, lse_part);
+  merge_group_if_last<D, float>(w, pl, o_part, lse_part, tickets, out, lse,
+                                sm_o, &sm_flag);
+}
+
+// Launched exactly like split_mfma_kernel (the same plan, grid and work
+// list; a workgroup may take a second chunk).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
+void split_mfma_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ kc,
+    const float *__restrict__ vc, const int32_t *__restrict__ seqlens,
+    int B, int Hq, int Hkv, int G, int Lmax, int C, int S, float scale_log2,
+    int mode, bool direct, bool chunk_major, float *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ o_part,
+    float *__restrict__ lse_part, int *__restrict__ tickets) {
+  const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
+  if (!w0.valid) return;
+  f32_chunk_pass<D, NW>(w0, q, kc, vc, Hq, Hkv, G, Lmax, S, scale_log2, mode,
+                        chunk_major, out, lse, o_part, lse_part, tickets);
+  const long id1 = (long)blockIdx.x + gridDim.x;
+  if (seqlens == nullptr || id1 >= (long)B * Hkv * S || id1 >= w0.items)
+    return;
+  const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
+  if (!w1.valid) return;
+  __syncthreads();  // the second chunk reuses the LDS
+  f32_chunk_pass<D, NW>(w1, q, kc, vc, Hq, Hkv, G, Lmax, S, scale_log2, mode,
+                        chunk_major, out, lse, o_part, lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------
@@ -1680,6 +1922,20 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   return hipSuccess;
 }
 
+template <int D>
+hipError_t launch_mfma_f32(const Plan &p, const LaunchArgs &a, float sl2,
+                           hipStream_t st) {
+  if (p.waves != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4>), dim3(p.grid),
+                     dim3(4 * 64), 0, st, static_cast<const float *>(a.q),
+                     static_cast<const float *>(a.k),
+                     static_cast<const float *>(a.v), a.seqlens, p.B, p.Hq,
+                     p.Hkv, p.G, p.Lmax, p.chunk, p.splits, sl2, mode_of(p),
+                     p.direct, p.chunk_major, static_cast<float *>(a.out),
+                     a.lse, a.o_part, a.lse_part, a.tickets);
+  return hipSuccess;
+}
+
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
@@ -1717,6 +1973,12 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   hipError_t e = hipSuccess;
   if (!(a.phases & kPhaseChunks)) {
     // merge only
+  } else if (p.variant == FD_VARIANT_MFMA && p.dtype == FD_F32) {
+    // the planner allows fp32 on the matrix cores for contiguous
+    // single-token decode only
+    e = p.paged || p.Tq != 1 || p.unified ? hipErrorInvalidValue
+        : p.D == 128 ? launch_mfma_f32<128>(p, a, sl2, st)
+                     : launch_mfma_f32<64>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA && p.unified) {
     // the planner allows the unified maximum for contiguous single-token
     // decode only

@@ -168,13 +168,19 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.unified = unified;
   q.num_cus = num_cus;
 
-  // Kernel variant: matrix cores need bf16; fp32 runs on the vector ALU.
-  if (requested_variant == FD_VARIANT_MFMA && dtype != FD_BF16)
-    return FD_ERR_UNSUPPORTED;
+  // Kernel variant: bf16 on the matrix cores; fp32 on the matrix cores for
+  // groups of more than 4 query heads, else on the vector ALU, whose cost
+  // per key grows with G while the fp32 MFMA pass pays for 16 columns at
+  // any G.  Measured (fp32, one sequence of 8 KV heads, D = 128, device time
+  // of steps replayed from a graph), vector ALU against matrix cores:
+  // 16k keys G = 1 26.1 / 30.1 us, G = 2 29.5 / 29.8, G = 4 30.5 / 30.1,
+  // G = 8 47.8 / 29.7, G = 16 82.0 / 30.0; 64k keys G = 8 149.5 / 93.5;
+  // four sequences at G = 4, 16k keys, 90.5 / 95.0.
   if (requested_variant != FD_VARIANT_AUTO)
     q.variant = requested_variant;
   else
-    q.variant = dtype == FD_BF16 ? FD_VARIANT_MFMA : FD_VARIANT_VALU;
+    q.variant = dtype == FD_BF16 || q.G > 4 ? FD_VARIANT_MFMA
+                                            : FD_VARIANT_VALU;
   // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
   // registers; beyond 4 rows the matrix-core kernel is the one to use.
   if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)

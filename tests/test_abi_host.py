@@ -279,7 +279,8 @@ def test_fp32_groups_split_sooner(lib, Hq, Hkv, D, L, S):
     # unsplit against 17 in 8 chunks; 4 on each of 4, D = 128, 2048 keys
     # 12.6 in 32 chunks against 10.6 in 64)
     B = 2 if Hq == 8 else 1
-    p = fd.fd_plan(B, Hq, Hkv, D, L, "f32", num_cus=256)
+    p = fd.fd_plan(B, Hq, Hkv, D, L, "f32", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
     assert p["variant"] == fd.FD_VARIANT_VALU
     assert (p["num_splits"], p["chunk"]) == (S, 32), p
 
@@ -292,17 +293,19 @@ def test_fp32_long_caches_keep_chunks_of_64_keys_or_more(lib, Hq, Hkv, D, L,
                                                          S, C):
     # measured fastest (fp32, one sequence): past 64 tiles the split count
     # follows two workgroups per CU and chunks stay at 64 keys or more
-    p = fd.fd_plan(1, Hq, Hkv, D, L, "f32", num_cus=256)
+    p = fd.fd_plan(1, Hq, Hkv, D, L, "f32", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
     assert (p["num_splits"], p["chunk"]) == (S, C), p
 
 
 def test_fp32_groups_past_8_heads_run_as_half_groups(lib):
     # 16 query heads on one KV head: two virtual groups of 8 on the same
     # slab, so the plan counts two units (grid = 2 * S)
-    p = fd.fd_plan(1, 16, 1, 64, 65536, "f32", num_cus=256)
+    valu = fd.FD_VARIANT_VALU
+    p = fd.fd_plan(1, 16, 1, 64, 65536, "f32", variant=valu, num_cus=256)
     assert p["grid"] == 2 * p["num_splits"]
     # odd groups past 8 keep one 16-row group
-    p = fd.fd_plan(1, 9, 1, 64, 65536, "f32", num_cus=256)
+    p = fd.fd_plan(1, 9, 1, 64, 65536, "f32", variant=valu, num_cus=256)
     assert p["grid"] == p["num_splits"]
 
 
@@ -317,9 +320,15 @@ def test_forced_splits_cover_the_sequence(lib, L, S):
 
 
 def test_plan_rejections(lib):
+    with pytest.raises(fd.FdError):        # fp32: plain decode only
+        fd.fd_plan_ex(1, 1, 8, 8, 128, 64, "f32", paged=True,
+                      variant=fd.FD_VARIANT_MFMA, num_cus=256)
+    with pytest.raises(fd.FdError):
+        fd.fd_plan_ex(1, 2, 8, 8, 128, 64, "f32",
+                      variant=fd.FD_VARIANT_MFMA, num_cus=256)
     with pytest.raises(fd.FdError):
         fd.fd_plan(1, 8, 8, 128, 64, "f32", variant=fd.FD_VARIANT_MFMA,
-                   num_cus=256)
+                   flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
     with pytest.raises(fd.FdError):        # bf16 vector path: G <= 4
         fd.fd_plan(1, 64, 8, 128, 64, "bf16", variant=fd.FD_VARIANT_VALU,
                    num_cus=256)
@@ -541,3 +550,33 @@ def test_partial_layout_follows_the_rounds_of_workgroups(lib, name, layout):
                      num_cus=256)
     assert not one["combine"] and \
         one["partial_layout"] == fd.FD_PARTIALS_ROW_MAJOR
+
+
+@pytest.mark.parametrize("G", [1, 5, 8, 16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_matrix_core_plans(lib, G, D):
+    # fp32 on the matrix cores: the whole group in one q-tile (no half
+    # groups), four wavefronts, the matrix-core split rule
+    p = fd.fd_plan(2, 2 * G, 2, D, 4096, "f32", variant=fd.FD_VARIANT_MFMA,
+                   num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
+    assert p["waves_per_block"] == 4
+    assert p["grid"] == 2 * 2 * p["num_splits"]
+    if D == 64:
+        # rows of 256 bytes, as bf16 at D = 128: the same chunks
+        pb = fd.fd_plan(2, 2 * G, 2, 128, 4096, "bf16", num_cus=256)
+        assert (p["num_splits"], p["chunk"]) == (pb["num_splits"],
+                                                 pb["chunk"])
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 9, 16])
+def test_fp32_groups_past_4_heads_take_the_matrix_cores(lib, G):
+    # fp32: the vector ALU's work per key grows with G, the matrix cores'
+    # does not (measured at 16k keys, 8 KV heads, D = 128: G = 4 level,
+    # G = 8 47.8 against 29.7 us, G = 16 82.0 against 30.0)
+    p = fd.fd_plan(1, 8 * G, 8, 128, 16384, "f32", num_cus=256)
+    assert p["variant"] == (fd.FD_VARIANT_MFMA if G > 4
+                            else fd.FD_VARIANT_VALU)
+    if G > 4:
+        # the bf16 matrix-core rule, counted in bytes: 512-byte rows
+        assert p["waves_per_block"] == 4 and p["grid"] == 8 * 32

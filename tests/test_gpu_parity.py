@@ -40,6 +40,10 @@ SMALL = {
         D=128, B=2, Hq=16, Hkv=4, Lmax=450),
     "f32_gqa16_d64": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
         B=1, Hq=16, Hkv=1, Lmax=300),
+    "f32_gqa5_d64": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
+        B=3, Hq=10, Hkv=2, Lmax=700),
+    "f32_varlen_gqa8_d128": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=5, Hq=16, Hkv=2, Lmax=2100, varlen=(1, 2100), dtype="f32"),
 }
 
 
@@ -80,7 +84,7 @@ def assert_parity(w, out, lse, ref_out, ref_lse, what=""):
 
 def variants_for(w):
     if w.dtype == "f32":
-        return [fd.FD_VARIANT_AUTO]
+        return [fd.FD_VARIANT_MFMA, fd.FD_VARIANT_VALU]
     if w.G <= 4:
         return [fd.FD_VARIANT_MFMA, fd.FD_VARIANT_VALU]
     return [fd.FD_VARIANT_MFMA]

@@ -148,8 +148,15 @@ def _run_case(torch, oracle_mod, i, c):
                                             flags=c["flags"])
         ref_o, ref_l = oracle_mod.decode(q, k, v, sl, w.scale)
     else:
+        # fp32 cases take the planner's kernel, the matrix cores or the
+        # vector ALU in turn
+        variant = ((fd.FD_VARIANT_AUTO, fd.FD_VARIANT_MFMA,
+                    fd.FD_VARIANT_VALU)[(i // 6) % 3]
+                   if w.dtype == "f32" else fd.FD_VARIANT_AUTO)
+        print(f"[random {i}] variant {variant}", flush=True)
         out, lse = fd.fd_decode_ex(qd, to_dev(k), to_dev(v), sld, w.scale,
-                                   num_splits=c["splits"], flags=c["flags"])
+                                   num_splits=c["splits"], variant=variant,
+                                   flags=c["flags"])
         ref_o, ref_l = oracle_mod.decode(q, k, v, sl, w.scale)
     torch.cuda.synchronize()
     ok_o, rep_o = check_out(out_to_host(out), ref_o, w.dtype)
