@@ -418,7 +418,7 @@ SPLIT_SWEEP_SHAPES = [  # (B, Hq, Hkv, D, dtype)
     (1, 64, 8, 128, "bf16"), (2, 64, 8, 128, "bf16"), (4, 64, 8, 128, "bf16"),
     (8, 32, 8, 128, "bf16"), (16, 32, 8, 128, "bf16"),
     (1, 32, 32, 128, "bf16"), (4, 32, 32, 128, "bf16"),
-    (1, 8, 8, 64, "f32"), (4, 8, 8, 64, "f32")]
+    (1, 8, 8, 64, "f32"), (4, 8, 8, 64, "f32"), (1, 64, 8, 128, "f32")]
 SPLIT_SWEEP_LENGTHS = (256, 384, 512, 768, 1024, 1536, 2048, 4096, 8192,
                        16384, 32768)
 

@@ -144,6 +144,9 @@ EXTRA_WORKLOADS = {
         WORKLOADS["b64_gqa4_h32_d128_l4096"].with_(
             name="mq4_b64_gqa4_h32_d128_l4096", Tq=4,
             note="four causal new tokens, batch 64 at 4k"),
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="f32_b1_gqa8_h64_d128_l65536", dtype="f32",
+            note="the batch-1 64k shape with an fp32 cache"),
     ]
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}

@@ -41,10 +41,11 @@ def _compare_all_rows(name, label, out, lse, ref, dtype):
     assert ok_l, rep_l
 
 
-@pytest.mark.parametrize("name", wl.WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", wl.WORKLOAD_ORDER +
+                         ["f32_b1_gqa8_h64_d128_l65536"])
 def test_full_size_workload(cuda, oracle_mod, name):
     torch = cuda
-    w = wl.WORKLOADS[name]
+    w = wl.ALL_WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs and the oracle's rows",
           flush=True)
     q, k, v, sl, seqlens, ref = upload_full(w, oracle_mod)
