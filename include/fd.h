@@ -136,8 +136,8 @@ enum {
 /* Kernel variant chosen for the per-chunk pass. */
 enum {
     FD_VARIANT_AUTO = 0,
-    FD_VARIANT_MFMA = 1, /* matrix-core pass, q group padded to 16 (bf16;
-                            fp32 for plain single-token decode) */
+    FD_VARIANT_MFMA = 1, /* matrix-core pass, q group padded to 16 (bf16
+                            or fp32; paged and several tokens: always) */
     FD_VARIANT_VALU = 2  /* vector-ALU pass (fp32, or bf16 small groups) */
 };
 
@@ -329,7 +329,7 @@ enum {
  * page_size * Hkv at most INT_MAX.  A table entry outside [0, num_pages)
  * is a caller error that the kernel clamps into that range (never a read
  * outside the pools).
- * bf16 only (FD_ERR_UNSUPPORTED for FD_F32), 1 <= Tq * Hq/Hkv <= 16.
+ * FD_BF16 or FD_F32 (both on the matrix cores), 1 <= Tq * Hq/Hkv <= 16.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
  * tokens; FD_FLAG_FUSED_MERGE allowed).  workspace, workspace_bytes: as
  * for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D,
@@ -358,8 +358,9 @@ FD_API int fd_decode_paged(const void *q, const void *k_pages,
  * sees no key gets out = 0, lse = -inf.  Tq = 1 is fd_decode.
  * The keys a token must not see (j in [L - Tq + 1, L)) are still loaded
  * for the tile and weighted by exactly 0: their V rows must be finite.
- * bf16 only, 1 <= Tq * Hq/Hkv <= 16 (all query rows of a KV head share
- * one 16-column matrix-core tile).  num_splits, flags and the workspace
+ * FD_BF16 or FD_F32, 1 <= Tq * Hq/Hkv <= 16 (all query rows of a KV head
+ * share one 16-column matrix-core tile; with Tq = 1 fp32 may run on the
+ * vector ALU, as in fd_decode).  num_splits, flags and the workspace
  * as for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, dtype,
  * seqlens != NULL, 0, num_splits, FD_VARIANT_AUTO, flags, 0,
  * &plan).workspace_bytes.

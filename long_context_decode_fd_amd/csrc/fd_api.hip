@@ -374,7 +374,6 @@ int fd_decode_multiquery(const void *q, const void *k_cache,
                          int num_splits, int flags, void *workspace,
                          size_t workspace_bytes, void *stream) {
   if (Tq <= 0 || (flags & FD_FLAG_UNIFIED_MAX)) return FD_ERR_INVALID_ARG;
-  if (dtype != FD_BF16) return FD_ERR_UNSUPPORTED;  // also for Tq == 1
   fd::Extra ex;
   ex.Tq = Tq;
   return run(q, k_cache, v_cache, seqlens, B, Hq, Hkv, D, Lmax, scale, dtype,

@@ -1315,30 +1315,34 @@ struct F32Half {
   floatx4 v[4][D / 64];  // V row 4 q4 + r, d = n16 * (D / 16) + 4 h + e
 };
 
-// The 16 keys from k0 (rows at or beyond `valid` re-read the last valid
-// one).
-template <int D, bool TAIL>
-__device__ __forceinline__ void f32_half_load(const float *__restrict__ k,
-                                              const float *__restrict__ v,
-                                              int k0, int valid, int n16,
+// The 16 keys of a half: key r at kb + r * rs (K) and vb + r * rs (V),
+// rows at or beyond `valid` re-reading the last valid one.  rs = D for a
+// contiguous slab; in a page pool the half lies inside one page, rows
+// Hkv * D (token-major) or D (head-major) apart.
+template <int D>
+__device__ __forceinline__ void f32_half_load(const float *__restrict__ kb,
+                                              const float *__restrict__ vb,
+                                              size_t rs, int valid, int n16,
                                               int q4, F32Half<D> &h) {
   constexpr int VW = D / 16;
-  const int rk = TAIL ? min(n16, valid - 1) : n16;
-  const float *pk = k + (size_t)(k0 + rk) * D + q4 * 4;
+  const float *pk = kb + (size_t)min(n16, valid - 1) * rs + q4 * 4;
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) h.k[j] = load_stream_f4(pk + 16 * j);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int rv = TAIL ? min(q4 * 4 + r, valid - 1) : q4 * 4 + r;
-    const float *pv = v + (size_t)(k0 + rv) * D + n16 * VW;
+    const float *pv =
+        vb + (size_t)min(q4 * 4 + r, valid - 1) * rs + n16 * VW;
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) h.v[r][c] = load_stream_f4(pv + 4 * c);
   }
 }
 
-template <int D, bool TAIL>
+// MASK: keys at or beyond `lim` (this lane's column; the half's own valid
+// count, or a causal limit) score -inf, and V rows at or beyond `valid`
+// are zeroed.
+template <int D, bool MASK>
 __device__ __forceinline__ void f32_half_compute(
-    F32Half<D> &h, int valid, int q4, const floatx4 (&qf)[D / 16],
+    F32Half<D> &h, int valid, int lim, int q4, const floatx4 (&qf)[D / 16],
     float scale_log2, floatx4 (&acc)[D / 16], float &m, float &l) {
   constexpr int VW = D / 16;
   floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1352,7 +1356,7 @@ __device__ __forceinline__ void f32_half_compute(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float x = sc[r] * scale_log2;
-    if (TAIL && q4 * 4 + r >= valid) x = FD_NEG_INF;
+    if (MASK && q4 * 4 + r >= lim) x = FD_NEG_INF;
     s[r] = x;
   }
   float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -1368,7 +1372,7 @@ __device__ __forceinline__ void f32_half_compute(
   l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
   for (int e = 0; e < VW; ++e) acc[e] *= alpha;
-  if (TAIL) {
+  if (MASK) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (q4 * 4 + r >= valid)
@@ -1385,35 +1389,47 @@ __device__ __forceinline__ void f32_half_compute(
 }
 
 // One chunk of the fp32 matrix-core pass: wavefront `wave` takes tiles
-// wave, wave + NW, ... in the chunk's tile order; every tile but the
-// chunk's last is full.
-template <int D, int NW>
+// wave, wave + NW, ... in the chunk's tile order, as a list of 16-key
+// halves.  Only the chunk's last tile can be short, so only the last half of
+// the list can be partial (a last tile of at most 16 keys gives one half);
+// the causal limits of several new tokens (at most 15 keys apart) cut only
+// into the chunk's last two tiles, each some wavefront's last, so only a
+// wavefront's last two halves can need masks.  PAGED: the halves' pool
+// rows are staged 64 at a time (page_rows, one table entry per lane).
+template <int D, int NW, bool PAGED, bool CAUSAL>
 __device__ __forceinline__ void f32_chunk_pass(
     const Work &w, const float *__restrict__ q, const float *__restrict__ kc,
-    const float *__restrict__ vc, int Hq, int Hkv, int G, int Lmax, int S,
-    float scale_log2, int mode, bool chunk_major, float *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ o_part,
-    float *__restrict__ lse_part, int *__restrict__ tickets) {
+    const float *__restrict__ vc, const PagedKV &pk, int Hq, int Hkv, int G,
+    int Tq, int Lmax, int S, float scale_log2, int mode, bool chunk_major,
+    float *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part,
+    int *__restrict__ tickets) {
   constexpr int VW = D / 16;
-  const PartLayout pl{G, 1, Hq, Hkv, S, chunk_major};
+  const PartLayout pl{G, Tq, Hq, Hkv, S, chunk_major};
   __shared__ float sm_m[NW * 16];
   __shared__ float sm_l[NW * 16];
   __shared__ __align__(16) float sm_o[NW * 16 * (D + 1)];
   __shared__ int sm_flag;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, q4 = lane >> 4;
+  const int ncol = G * Tq;
 
   floatx4 qf[D / 16];
   {
-    const bool live = n16 < G;
-    const float *qr = q + row_of(w, G, Hq, 1, live ? n16 : 0) * D + q4 * 4;
+    const bool live = n16 < ncol;
+    const float *qr = q + row_of(w, G, Hq, Tq, live ? n16 : 0) * D + q4 * 4;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
       qf[j] = live ? *reinterpret_cast<const floatx4 *>(qr + 16 * j)
                    : floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  // Causal limit of this lane's column (token t = c / G of the Tq newest)
+  // and the smallest over the columns.
+  const int hi_col = min(w.hi, w.L - (Tq - 1 - n16 / G));
+  const int hi_all = min(w.hi, w.L - (Tq - 1));
   const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
-  const float *k = kc + slab, *v = vc + slab;
+  const size_t rs = !PAGED ? (size_t)D
+                           : (pk.head_major ? (size_t)D : (size_t)Hkv * D);
   const bool rotate = (size_t)Lmax * D * sizeof(float) % kRotateStride == 0;
 
   floatx4 acc[VW];
@@ -1421,60 +1437,104 @@ __device__ __forceinline__ void f32_chunk_pass(
   for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = FD_NEG_INF, l = 0.f;
 
-  // The wavefront's tiles wave, wave + NW, ... as a list of 16-key halves;
-  // only the chunk's last tile can be short, so only the last half of the
-  // list can be partial (a last tile of at most 16 keys gives one half).
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
   if (wave < ntiles) {
     const TileOrder ord = tile_order(w, Hkv, ntiles, rotate);
     const int nt = (ntiles - wave + NW - 1) / NW;
     const int last0 = ord.key0(w, wave + (nt - 1) * NW);
     const int nh = 2 * nt - (w.hi - last0 <= 16 ? 1 : 0);
+    int prow = 0;
     auto key_of = [&](int i) {
       return ord.key0(w, wave + (i >> 1) * NW) + (i & 1) * 16;
+    };
+    auto load = [&](int i, F32Half<D> &h) {
+      const int k0 = key_of(i);
+      const float *kb, *vb;
+      if constexpr (PAGED) {
+        if ((i & 63) == 0)
+          prow = page_rows(pk, w, ord, Hkv, wave, NW, i >> 1, lane);
+        const int r0 = __builtin_amdgcn_readlane(prow, i & 63);
+        kb = kc + (size_t)r0 * D;
+        vb = vc + (size_t)r0 * D;
+      } else {
+        kb = kc + slab + (size_t)k0 * D;
+        vb = vc + slab + (size_t)k0 * D;
+      }
+      f32_half_load<D>(kb, vb, rs, min(16, w.hi - k0), n16, q4, h);
+    };
+    // masks only where the half is short or a causal limit cuts into it
+    auto compute = [&](int i, F32Half<D> &h) {
+      const int k0 = key_of(i);
+      const int valid = min(16, w.hi - k0);
+      if (CAUSAL ? k0 + 16 <= hi_all : valid == 16)
+        f32_half_compute<D, false>(h, 16, 16, q4, qf, scale_log2, acc, m, l);
+      else
+        f32_half_compute<D, true>(h, valid, CAUSAL ? hi_col - k0 : valid, q4,
+                                  qf, scale_log2, acc, m, l);
+    };
+    auto compute_full = [&](F32Half<D> &h) {
+      f32_half_compute<D, false>(h, 16, 16, q4, qf, scale_log2, acc, m, l);
     };
     // two register sets taken in turn (a copy between them would wait for
     // the loads in flight)
     F32Half<D> h0, h1;
-    int ka = key_of(0);
-    f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h0);
+    load(0, h0);
     int i = 0;
-    for (; i + 2 < nh; i += 2) {
-      ka = key_of(i + 1);
-      f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h1);
-      __builtin_amdgcn_sched_barrier(0);
-      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
-      ka = key_of(i + 2);
-      f32_half_load<D, true>(k, v, ka, min(16, w.hi - ka), n16, q4, h0);
-      __builtin_amdgcn_sched_barrier(0);
-      f32_half_compute<D, false>(h1, 16, q4, qf, scale_log2, acc, m, l);
-    }
-    const int valid = min(16, w.hi - key_of(nh - 1));
-    if (i + 2 == nh) {
-      ka = key_of(i + 1);
-      f32_half_load<D, true>(k, v, ka, valid, n16, q4, h1);
-      __builtin_amdgcn_sched_barrier(0);
-      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
-      if (valid == 16)
-        f32_half_compute<D, false>(h1, 16, q4, qf, scale_log2, acc, m, l);
-      else
-        f32_half_compute<D, true>(h1, valid, q4, qf, scale_log2, acc, m, l);
-    } else if (valid == 16) {
-      f32_half_compute<D, false>(h0, 16, q4, qf, scale_log2, acc, m, l);
+    if constexpr (!CAUSAL) {
+      for (; i + 2 < nh; i += 2) {
+        load(i + 1, h1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h0);
+        load(i + 2, h0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h1);
+      }
+      if (i + 2 == nh) {
+        load(i + 1, h1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h0);
+        compute(i + 1, h1);
+      } else {
+        compute(i, h0);
+      }
     } else {
-      f32_half_compute<D, true>(h0, valid, q4, qf, scale_log2, acc, m, l);
+      // halves before the last three are never cut
+      for (; i + 3 < nh; i += 2) {
+        load(i + 1, h1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h0);
+        load(i + 2, h0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h1);
+      }
+      if (i + 3 == nh) {
+        load(i + 1, h1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_full(h0);
+        load(i + 2, h0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 1, h1);
+        compute(i + 2, h0);
+      } else if (i + 2 == nh) {
+        load(i + 1, h1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, h0);
+        compute(i + 1, h1);
+      } else {
+        compute(i, h0);
+      }
     }
   }
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
-    wave_merge_store<D, NW, float>(sm_m, sm_l, sm_o, wave, lane, n16, q4, G,
-                                   m, l, acc, w, pl, mode, out, lse, o_part,
-                                   lse_part);
+    wave_merge_store<D, NW, float>(sm_m, sm_l, sm_o, wave, lane, n16, q4,
+                                   ncol, m, l, acc, w, pl, mode, out, lse,
+                                   o_part, lse_part);
     return;
   }
-  if (n16 < G) {
+  if (n16 < ncol) {
     if (q4 == 0) {
       sm_m[wave * 16 + n16] = m;
       sm_l[wave * 16 + n16] = l;
@@ -1494,27 +1554,30 @@ __device__ __forceinline__ void f32_chunk_pass(
 
 // Launched exactly like split_mfma_kernel (the same plan, grid and work
 // list; a workgroup may take a second chunk).
-template <int D, int NW>
+template <int D, int NW, bool PAGED, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
 void split_mfma_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc,
     const float *__restrict__ vc, const int32_t *__restrict__ seqlens,
-    int B, int Hq, int Hkv, int G, int Lmax, int C, int S, float scale_log2,
-    int mode, bool direct, bool chunk_major, float *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ o_part,
-    float *__restrict__ lse_part, int *__restrict__ tickets) {
+    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C,
+    int S, float scale_log2, int mode, bool direct, bool chunk_major,
+    float *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part,
+    int *__restrict__ tickets) {
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
-  f32_chunk_pass<D, NW>(w0, q, kc, vc, Hq, Hkv, G, Lmax, S, scale_log2, mode,
-                        chunk_major, out, lse, o_part, lse_part, tickets);
+  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w0, q, kc, vc, pk, Hq, Hkv, G, Tq,
+                                       Lmax, S, scale_log2, mode, chunk_major,
+                                       out, lse, o_part, lse_part, tickets);
   const long id1 = (long)blockIdx.x + gridDim.x;
   if (seqlens == nullptr || id1 >= (long)B * Hkv * S || id1 >= w0.items)
     return;
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
-  f32_chunk_pass<D, NW>(w1, q, kc, vc, Hq, Hkv, G, Lmax, S, scale_log2, mode,
-                        chunk_major, out, lse, o_part, lse_part, tickets);
+  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w1, q, kc, vc, pk, Hq, Hkv, G, Tq,
+                                       Lmax, S, scale_log2, mode, chunk_major,
+                                       out, lse, o_part, lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------
@@ -1922,18 +1985,30 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   return hipSuccess;
 }
 
-template <int D>
+template <int D, bool PAGED, bool CAUSAL>
 hipError_t launch_mfma_f32(const Plan &p, const LaunchArgs &a, float sl2,
                            hipStream_t st) {
   if (p.waves != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4>), dim3(p.grid),
-                     dim3(4 * 64), 0, st, static_cast<const float *>(a.q),
+  hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4, PAGED, CAUSAL>),
+                     dim3(p.grid), dim3(4 * 64), 0, st,
+                     static_cast<const float *>(a.q),
                      static_cast<const float *>(a.k),
-                     static_cast<const float *>(a.v), a.seqlens, p.B, p.Hq,
-                     p.Hkv, p.G, p.Lmax, p.chunk, p.splits, sl2, mode_of(p),
-                     p.direct, p.chunk_major, static_cast<float *>(a.out),
-                     a.lse, a.o_part, a.lse_part, a.tickets);
+                     static_cast<const float *>(a.v), a.seqlens, a.paged,
+                     p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk, p.splits,
+                     sl2, mode_of(p), p.direct, p.chunk_major,
+                     static_cast<float *>(a.out), a.lse, a.o_part,
+                     a.lse_part, a.tickets);
   return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_mfma_f32_any(const Plan &p, const LaunchArgs &a, float sl2,
+                               hipStream_t st) {
+  const bool causal = p.Tq > 1;
+  return p.paged ? (causal ? launch_mfma_f32<D, true, true>(p, a, sl2, st)
+                           : launch_mfma_f32<D, true, false>(p, a, sl2, st))
+                 : (causal ? launch_mfma_f32<D, false, true>(p, a, sl2, st)
+                           : launch_mfma_f32<D, false, false>(p, a, sl2, st));
 }
 
 template <int D, typename OutT>
@@ -1974,11 +2049,10 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   if (!(a.phases & kPhaseChunks)) {
     // merge only
   } else if (p.variant == FD_VARIANT_MFMA && p.dtype == FD_F32) {
-    // the planner allows fp32 on the matrix cores for contiguous
-    // single-token decode only
-    e = p.paged || p.Tq != 1 || p.unified ? hipErrorInvalidValue
-        : p.D == 128 ? launch_mfma_f32<128>(p, a, sl2, st)
-                     : launch_mfma_f32<64>(p, a, sl2, st);
+    // the planner keeps the unified maximum to bf16
+    e = p.unified ? hipErrorInvalidValue
+        : p.D == 128 ? launch_mfma_f32_any<128>(p, a, sl2, st)
+                     : launch_mfma_f32_any<64>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA && p.unified) {
     // the planner allows the unified maximum for contiguous single-token
     // decode only

@@ -132,12 +132,12 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   int rc = validate_shape(B, Hq, Hkv, D, Lmax, dtype);
   if (rc != FD_OK) return rc;
   if (extra.Tq < 1) return FD_ERR_INVALID_ARG;
-  // Several new tokens or a paged cache: the matrix-core kernel only, with
-  // all G * Tq query rows of a KV head in its 16-column q-tile.
+  // Several new tokens or a paged cache: the matrix-core kernels only (bf16
+  // or fp32), with all G * Tq query rows of a KV head in the 16-column
+  // q-tile.
   const bool general = extra.Tq > 1 || extra.paged;
   if (general) {
-    if (dtype != FD_BF16 || requested_variant == FD_VARIANT_VALU)
-      return FD_ERR_UNSUPPORTED;
+    if (requested_variant == FD_VARIANT_VALU) return FD_ERR_UNSUPPORTED;
     if ((long)(Hq / Hkv) * extra.Tq > kMaxGroup) return FD_ERR_UNSUPPORTED;
     if ((long)B * Hq * extra.Tq > (1L << 30)) return FD_ERR_UNSUPPORTED;
   }
@@ -179,8 +179,8 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_variant != FD_VARIANT_AUTO)
     q.variant = requested_variant;
   else
-    q.variant = dtype == FD_BF16 || q.G > 4 ? FD_VARIANT_MFMA
-                                            : FD_VARIANT_VALU;
+    q.variant = dtype == FD_BF16 || q.G > 4 || general ? FD_VARIANT_MFMA
+                                                       : FD_VARIANT_VALU;
   // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
   // registers; beyond 4 rows the matrix-core kernel is the one to use.
   if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)

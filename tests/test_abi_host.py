@@ -320,12 +320,12 @@ def test_forced_splits_cover_the_sequence(lib, L, S):
 
 
 def test_plan_rejections(lib):
-    with pytest.raises(fd.FdError):        # fp32: plain decode only
+    with pytest.raises(fd.FdError):  # paged / several tokens: matrix cores
         fd.fd_plan_ex(1, 1, 8, 8, 128, 64, "f32", paged=True,
-                      variant=fd.FD_VARIANT_MFMA, num_cus=256)
+                      variant=fd.FD_VARIANT_VALU, num_cus=256)
     with pytest.raises(fd.FdError):
         fd.fd_plan_ex(1, 2, 8, 8, 128, 64, "f32",
-                      variant=fd.FD_VARIANT_MFMA, num_cus=256)
+                      variant=fd.FD_VARIANT_VALU, num_cus=256)
     with pytest.raises(fd.FdError):
         fd.fd_plan(1, 8, 8, 128, 64, "f32", variant=fd.FD_VARIANT_MFMA,
                    flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
@@ -412,7 +412,8 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
     (dict(Tq=3, Hq=48, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 6 x 3 = 18 rows
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),
-    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),        # bf16 only
+    (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),        # bf16 or fp32 only
+    (dict(dtype=1, Tq=3, Hq=48, Hkv=8), fd.FD_ERR_UNSUPPORTED),
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
     (dict(q=None), fd.FD_ERR_INVALID_ARG),
@@ -442,8 +443,9 @@ def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 17 columns
     (dict(Tq=5, Hq=32, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 4 x 5 = 20
     (dict(Tq=2, Hq=64, Hkv=4), fd.FD_ERR_UNSUPPORTED),   # G alone is 16
-    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),
-    (dict(Tq=1, dtype=1), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(Tq=1, dtype=-1), fd.FD_ERR_UNSUPPORTED),
+    (dict(Tq=5, Hq=32, Hkv=8, dtype=1), fd.FD_ERR_UNSUPPORTED),
     (dict(B=1 << 20, Tq=16, Hq=128, Hkv=128), fd.FD_ERR_UNSUPPORTED),
     (dict(q=None), fd.FD_ERR_INVALID_ARG),
     (dict(seqlens=A + 1), fd.FD_ERR_INVALID_ARG),
@@ -479,8 +481,10 @@ def test_plan_ex_for_several_tokens_and_pages(lib):
     pv = fd.fd_plan_ex(16, 1, 64, 8, 128, 131072, "bf16", paged=True,
                        num_cus=256)
     assert pv["chunk"] == 2048
-    for kw in (dict(Tq=3, Hq=64, Hkv=8), dict(Tq=2, dtype="f32"),
-               dict(Tq=1, dtype="f32", paged=True),
+    for kw in (dict(Tq=3, Hq=64, Hkv=8), dict(Tq=3, Hq=64, Hkv=8, dtype="f32"),
+               dict(Tq=2, dtype="f32", variant=fd.FD_VARIANT_VALU),
+               dict(Tq=1, dtype="f32", paged=True,
+                    variant=fd.FD_VARIANT_VALU),
                dict(Tq=2, variant=fd.FD_VARIANT_VALU), dict(Tq=0)):
         args = dict(B=1, Tq=1, Hq=8, Hkv=8, D=128, Lmax=4096, dtype="bf16",
                     num_cus=256)
@@ -580,3 +584,18 @@ def test_fp32_groups_past_4_heads_take_the_matrix_cores(lib, G):
     if G > 4:
         # the bf16 matrix-core rule, counted in bytes: 512-byte rows
         assert p["waves_per_block"] == 4 and p["grid"] == 8 * 32
+
+
+@pytest.mark.parametrize("Tq,paged", [(2, False), (1, True), (4, True)])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_fp32_paged_and_several_tokens_take_the_matrix_cores(lib, Tq, paged,
+                                                             G):
+    # the vector-ALU kernel serves neither, so fp32 takes the matrix cores
+    # at any group size, like bf16
+    p = fd.fd_plan_ex(2, Tq, 4 * G, 4, 128, 4096, "f32", paged=paged,
+                      num_cus=256)
+    pb = fd.fd_plan_ex(2, Tq, 4 * G, 4, 64, 4096, "bf16", paged=paged,
+                       num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
+    # 512-byte rows count as bf16 rows of D = 256: at most the bf16 chunks
+    assert p["chunk"] <= pb["chunk"] or p["num_splits"] >= pb["num_splits"]

@@ -34,8 +34,13 @@ def _note(msg):
     print(f"[paged/mq] {msg}", flush=True)
 
 
-def _assert_parity(out, lse, ref_o, ref_l, tag):
-    ok_o, rep_o = check_out(out_to_host(out), ref_o, "bf16")
+def _bits(torch, t):
+    """The raw bits of a bf16 or fp32 tensor, for bitwise comparisons."""
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def _assert_parity(out, lse, ref_o, ref_l, tag, dtype="bf16"):
+    ok_o, rep_o = check_out(out_to_host(out), ref_o, dtype)
     ok_l, rep_l = check_lse(lse.cpu().numpy(), ref_l)
     _note(f"{tag}: out {rep_o} lse {rep_l}")
     assert ok_o, (tag, rep_o)
@@ -93,14 +98,16 @@ PAGED_SHAPES = [
                               f"_P{s[5]}" for s in PAGED_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (5, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm,
+                              dtype):
     B, Hq, Hkv, D, L, P, sls = shape
     w = wl.Workload("paged_case", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=L,
-                    dtype="bf16", seed=40 + P, page_size=P, head_major=hm)
+                    dtype=dtype, seed=40 + P, page_size=P, head_major=hm)
     seqlens = np.array(sls, np.int32)
     (q, kp, vp, bt, sl), (qd, kd, vd, btd, sld) = paged_case(torch, w,
                                                              seqlens)
-    _note(f"{shape} hm={hm} splits={splits} flags={flags} "
+    _note(f"{shape} {dtype} hm={hm} splits={splits} flags={flags} "
           f"pages={w.num_pages}")
     out, lse = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale,
                                   num_splits=splits, flags=flags,
@@ -108,13 +115,14 @@ def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mod.decode_paged(q, kp, vp, bt, sl, w.scale,
                                            head_major=hm)
-    _assert_parity(out, lse, ref_o, ref_l, f"paged {shape} hm={hm}")
+    _assert_parity(out, lse, ref_o, ref_l, f"paged {shape} hm={hm}", dtype)
 
 
 @pytest.mark.parametrize("hm", [False, True])
-def test_paged_table_entries_past_the_length_are_not_read(torch, hm):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_paged_table_entries_past_the_length_are_not_read(torch, hm, dtype):
     w = wl.Workload("paged_tail", B=3, Hq=16, Hkv=2, D=128, Lmax=1024,
-                    dtype="bf16", seed=47, page_size=64, head_major=hm)
+                    dtype=dtype, seed=47, page_size=64, head_major=hm)
     seqlens = np.array([1024, 300, 0], np.int32)
     _, (qd, kd, vd, btd, sld) = paged_case(torch, w, seqlens)
     _, (_, _, _, btd2, _) = paged_case(torch, w, seqlens,
@@ -124,15 +132,17 @@ def test_paged_table_entries_past_the_length_are_not_read(torch, hm):
     o2, l2 = fd.fd_decode_paged(qd, kd, vd, btd2, sld, w.scale,
                                 head_major=hm)
     torch.cuda.synchronize()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(_bits(torch, o1), _bits(torch, o2))
     assert torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("hm", [False, True])
-def test_paged_equals_contiguous_bitwise(torch, hm):
-    # Same lengths, so the same plan; the pool holds the same rows.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_paged_equals_contiguous_bitwise(torch, hm, dtype):
+    # Same lengths, so the same plan; the pool holds the same rows (G = 8:
+    # fp32 runs on the matrix cores either way).
     w = wl.Workload("paged_vs_contig", B=4, Hq=32, Hkv=4, D=128, Lmax=3072,
-                    dtype="bf16", seed=48, page_size=32, head_major=hm)
+                    dtype=dtype, seed=48, page_size=32, head_major=hm)
     seqlens = np.array([3072, 2048, 777, 5], np.int32)
     (q, k_unused, _, _, _), (qd, kd, vd, btd, sld) = paged_case(
         torch, w, seqlens)
@@ -144,7 +154,7 @@ def test_paged_equals_contiguous_bitwise(torch, hm):
         co, cl = fd.fd_decode_ex(qd, kc, vc, sld, w.scale,
                                  num_splits=splits)
         torch.cuda.synchronize()
-        assert torch.equal(po.view(torch.int16), co.view(torch.int16))
+        assert torch.equal(_bits(torch, po), _bits(torch, co))
         assert torch.equal(pl, cl)
 
 
@@ -186,23 +196,26 @@ PAGED_MQ_SHAPES = [
                               f"_L{s[5]}_P{s[6]}" for s in PAGED_MQ_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (7, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_paged_multiquery_matches_oracle(torch, oracle_mod, shape, splits,
-                                         flags, hm):
+                                         flags, hm, dtype):
     B, Tq, Hq, Hkv, D, L, P, sls = shape
     w = wl.Workload("paged_mq_case", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=L,
-                    dtype="bf16", seed=80 + Tq, page_size=P, head_major=hm,
+                    dtype=dtype, seed=80 + Tq, page_size=P, head_major=hm,
                     Tq=Tq)
     seqlens = np.array(sls, np.int32)
     (q, kp, vp, bt, sl), (qd, kd, vd, btd, sld) = paged_case(torch, w,
                                                              seqlens)
-    _note(f"paged mq {shape} hm={hm} splits={splits} flags={flags}")
+    _note(f"paged mq {shape} {dtype} hm={hm} splits={splits} "
+          f"flags={flags}")
     out, lse = fd.fd_decode_paged(qd, kd, vd, btd, sld, w.scale,
                                   num_splits=splits, flags=flags,
                                   head_major=hm)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mod.decode_paged(q, kp, vp, bt, sl, w.scale,
                                            head_major=hm)
-    _assert_parity(out, lse, ref_o, ref_l, f"paged mq {shape} hm={hm}")
+    _assert_parity(out, lse, ref_o, ref_l, f"paged mq {shape} hm={hm}",
+                   dtype)
 
 
 def test_paged_multiquery_full_size_equals_contiguous(torch, oracle_mod):
@@ -243,10 +256,12 @@ MQ_SHAPES = [
                               f"_L{s[5]}" for s in MQ_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (9, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-def test_multiquery_matches_oracle(torch, oracle_mod, shape, splits, flags):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_multiquery_matches_oracle(torch, oracle_mod, shape, splits, flags,
+                                   dtype):
     B, Tq, Hq, Hkv, D, L, sls = shape
     w = wl.Workload("mq_case", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=L,
-                    dtype="bf16", seed=60 + Tq, Tq=Tq)
+                    dtype=dtype, seed=60 + Tq, Tq=Tq)
     seqlens = None if sls is None else np.array(sls, np.int32)
     if seqlens is None:
         q, k, v, _ = wl.gen_all(w)
@@ -255,20 +270,25 @@ def test_multiquery_matches_oracle(torch, oracle_mod, shape, splits, flags):
     q = q.reshape(B, Tq, Hq, D)          # Tq = 1 is drawn as [B, Hq, D]
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     sld = None if seqlens is None else torch.from_numpy(seqlens).to("cuda")
-    _note(f"{shape} splits={splits} flags={flags}")
+    _note(f"{shape} {dtype} splits={splits} flags={flags}")
     out, lse = fd.fd_decode_multiquery(qd, kd, vd, sld, w.scale,
                                        num_splits=splits, flags=flags)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mod.decode_multiquery(q, k, v, seqlens, w.scale)
-    _assert_parity(out, lse, ref_o, ref_l, f"mq {shape}")
+    _assert_parity(out, lse, ref_o, ref_l, f"mq {shape}", dtype)
 
 
-def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod,
+                                                       dtype):
     # 32-key chunks: the last Tq - 1 keys straddle a chunk edge for some
-    # lengths and sit inside one for others.
+    # lengths and sit inside one for others (and, in the fp32 kernel's
+    # 16-key halves, a half edge).
     w = wl.Workload("mq_edges", B=8, Hq=8, Hkv=2, D=128, Lmax=256,
-                    dtype="bf16", seed=70, Tq=4)
-    seqlens = np.array([256, 255, 226, 225, 224, 33, 32, 4], np.int32)
+                    dtype=dtype, seed=70, Tq=4)
+    seqlens = np.array([256, 255, 226, 225, 224, 33, 32, 4] if dtype ==
+                       "bf16" else [256, 242, 241, 209, 18, 17, 16, 2],
+                       np.int32)
     q, k, v, _ = _gen_with(w, seqlens)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     sld = torch.from_numpy(seqlens).to("cuda")
@@ -277,12 +297,14 @@ def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod):
         out, lse = fd.fd_decode_multiquery(qd, kd, vd, sld, w.scale,
                                            num_splits=splits)
         torch.cuda.synchronize()
-        _assert_parity(out, lse, ref_o, ref_l, f"mq edges splits={splits}")
+        _assert_parity(out, lse, ref_o, ref_l, f"mq edges splits={splits}",
+                       dtype)
 
 
-def test_multiquery_one_token_is_decode_bitwise(torch):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_multiquery_one_token_is_decode_bitwise(torch, dtype):
     w = wl.Workload("mq1", B=3, Hq=32, Hkv=4, D=128, Lmax=2000,
-                    dtype="bf16", seed=71)
+                    dtype=dtype, seed=71)
     seqlens = np.array([2000, 1000, 31], np.int32)
     q, k, v, _ = _gen_with(w, seqlens)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
@@ -291,8 +313,7 @@ def test_multiquery_one_token_is_decode_bitwise(torch):
                                      w.scale)
     do, dl = fd.fd_decode(qd, kd, vd, sld, w.scale)
     torch.cuda.synchronize()
-    assert torch.equal(mo[:, 0].contiguous().view(torch.int16),
-                       do.view(torch.int16))
+    assert torch.equal(_bits(torch, mo[:, 0].contiguous()), _bits(torch, do))
     assert torch.equal(ml[:, 0].contiguous(), dl)
 
 

@@ -54,6 +54,8 @@ def draw_case(i):
     page = int(rng.choice([16, 32, 48, 64, 128]))
     head_major = bool(rng.random() < 0.5)
     phi = float(rng.choice([0.0, 3.0, -50.0]))
+    if kind in ("paged", "multiquery", "paged_mq") and (i // 6) % 3 == 2:
+        dtype = "f32"        # without a draw: the other fields stay as they were
     return dict(kind=kind, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=Lmax,
                 dtype=dtype, seqlens=seqlens, Tq=Tq, splits=splits,
                 flags=flags, page=page, head_major=head_major, phi=phi,

@@ -85,11 +85,16 @@ PINS = [
     (pins.test_split_batch_twin_matches_batch, ()),
     (pins.test_torch_fp64_attention_agrees, ()),
     (pins.test_mpmath_brute_force_50_digits, ()),
-    (pins.test_paged_equals_contiguous_after_scatter, (32, False)),
-    (pins.test_paged_equals_contiguous_after_scatter, (64, False)),
-    (pins.test_paged_equals_contiguous_after_scatter, (32, True)),
-    (pins.test_paged_multiquery_equals_contiguous_after_scatter, (False,)),
-    (pins.test_multiquery_single_token_is_decode, ()),
+    (pins.test_paged_equals_contiguous_after_scatter, (32, False, "bf16")),
+    (pins.test_paged_equals_contiguous_after_scatter, (64, False, "bf16")),
+    (pins.test_paged_equals_contiguous_after_scatter, (32, True, "bf16")),
+    (pins.test_paged_equals_contiguous_after_scatter, (16, False, "f32")),
+    (pins.test_paged_multiquery_equals_contiguous_after_scatter,
+     (False, "bf16")),
+    (pins.test_paged_multiquery_equals_contiguous_after_scatter,
+     (False, "f32")),
+    (pins.test_multiquery_single_token_is_decode, ("bf16",)),
+    (pins.test_multiquery_single_token_is_decode, ("f32",)),
     (pins.test_multiquery_identical_keys_closed_form, ()),
     (pins.test_multiquery_query_never_sees_later_tokens, ()),
 ]

@@ -404,18 +404,26 @@ def scatter_to_pages(k, v, seqlens, page_size, rng, extra_pages=3,
     return kp, vp, bt
 
 
-@pytest.mark.parametrize("page_size,head_major", [(32, False), (64, False),
-                                                  (16, False), (32, True),
-                                                  (48, True)])
+def rand_elem(rng, shape, dtype):
+    """bf16 bit patterns or fp32 values, N(0, 1)."""
+    if dtype == "bf16":
+        return rand_bf16(rng, shape)
+    return rng.standard_normal(shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("page_size,head_major,dtype", [
+    (32, False, "bf16"), (64, False, "bf16"), (16, False, "bf16"),
+    (32, True, "bf16"), (48, True, "bf16"), (16, False, "f32"),
+    (32, True, "f32")])
 def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size,
-                                               head_major):
+                                               head_major, dtype):
     # Same rows, same order: a shuffled page pool must give the contiguous
     # result bit for bit, with NaN in every byte the pages do not own.
     rng = np.random.default_rng(30 + page_size)
     B, Hq, Hkv, D, L = 3, 8, 2, 16, 150
-    q = rand_bf16(rng, (B, Hq, D))
-    k = rand_bf16(rng, (B, Hkv, L, D))
-    v = rand_bf16(rng, (B, Hkv, L, D))
+    q = rand_elem(rng, (B, Hq, D), dtype)
+    k = rand_elem(rng, (B, Hkv, L, D), dtype)
+    v = rand_elem(rng, (B, Hkv, L, D), dtype)
     seq = np.array([150, 1, 97], np.int32)
     kp, vp, bt = scatter_to_pages(k, v, seq, page_size, rng,
                                   head_major=head_major)
@@ -432,16 +440,18 @@ def test_paged_equals_contiguous_after_scatter(oracle_mod, page_size,
     assert not np.array_equal(np.nan_to_num(o3), o1)
 
 
-@pytest.mark.parametrize("head_major", [False, True])
+@pytest.mark.parametrize("head_major,dtype", [(False, "bf16"),
+                                              (True, "bf16"),
+                                              (False, "f32")])
 def test_paged_multiquery_equals_contiguous_after_scatter(oracle_mod,
-                                                        head_major):
+                                                        head_major, dtype):
     # Several new tokens over a shuffled page pool: the contiguous
     # multi-token oracle's result bit for bit, token by token.
     rng = np.random.default_rng(34)
     B, Tq, Hq, Hkv, D, L, P = 3, 3, 4, 2, 16, 130, 32
-    q = rand_bf16(rng, (B, Tq, Hq, D))
-    k = rand_bf16(rng, (B, Hkv, L, D))
-    v = rand_bf16(rng, (B, Hkv, L, D))
+    q = rand_elem(rng, (B, Tq, Hq, D), dtype)
+    k = rand_elem(rng, (B, Hkv, L, D), dtype)
+    v = rand_elem(rng, (B, Hkv, L, D), dtype)
     seq = np.array([130, 2, 65], np.int32)
     kp, vp, bt = scatter_to_pages(k, v, seq, P, rng, head_major=head_major)
     o1, l1 = oracle_mod.decode_multiquery(q, k, v, seq, 0.3)
@@ -452,12 +462,13 @@ def test_paged_multiquery_equals_contiguous_after_scatter(oracle_mod,
     assert np.isinf(l1[1, 0]).all()          # length 2 < Tq: token 0 sees none
 
 
-def test_multiquery_single_token_is_decode(oracle_mod):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_multiquery_single_token_is_decode(oracle_mod, dtype):
     rng = np.random.default_rng(31)
     B, Hq, Hkv, D, L = 2, 6, 3, 8, 40
-    q = rand_bf16(rng, (B, Hq, D))
-    k = rand_bf16(rng, (B, Hkv, L, D))
-    v = rand_bf16(rng, (B, Hkv, L, D))
+    q = rand_elem(rng, (B, Hq, D), dtype)
+    k = rand_elem(rng, (B, Hkv, L, D), dtype)
+    v = rand_elem(rng, (B, Hkv, L, D), dtype)
     seq = np.array([40, 17], np.int32)
     o1, l1 = oracle_mod.decode(q, k, v, seq, 0.5)
     o2, l2 = oracle_mod.decode_multiquery(q[:, None].copy(), k, v, seq, 0.5)
