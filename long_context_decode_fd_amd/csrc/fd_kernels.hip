@@ -1047,8 +1047,12 @@ constexpr float kUniRange = 64.f;
 // 2^(m - M) / W, adds the weighted accumulators in wavefront order and
 // stores its lane's contiguous run of output columns, (q4 * 4 + j) * VW + e,
 // with vector stores.  A column that saw no key gets out 0 and lse -inf.
-// OutT: uint16_t (bf16 bits, rounded to nearest even) or float.
-template <int D, int NW, typename OutT = uint16_t>
+// OutT: uint16_t (bf16 bits, rounded to nearest even) or float.  ROWS64:
+// accumulator block e holds, for lane row i = 4 q4 + j, column
+// d = 64 (e / 4) + 4 i + e % 4 (the fp32 kernel's V layout) instead of
+// d = i VW + e; either way a lane's four blocks 4 e4 .. 4 e4 + 3 of one j
+// are four consecutive columns.
+template <int D, int NW, typename OutT = uint16_t, bool ROWS64 = false>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
     int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
@@ -1107,7 +1111,8 @@ __device__ __forceinline__ void wave_merge_store(
         o.z += p.z * wt[sl];
         o.w += p.w * wt[sl];
       }
-      const int d0 = (q4 * 4 + j) * VW + 4 * e4;
+      const int d0 = ROWS64 ? 64 * e4 + 4 * (q4 * 4 + j)
+                            : (q4 * 4 + j) * VW + 4 * e4;
       if (mode == kModeDirect) {
         if constexpr (sizeof(OutT) == 2) {
           uint2 bits;
@@ -1286,8 +1291,8 @@ void split_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel for fp32 caches (one new token per sequence, contiguous
-// cache).
+// Matrix-core kernel for fp32 caches (contiguous or paged, one or several
+// new tokens).
 //
 // v_mfma_f32_16x16x4_f32 takes one fp32 value of each operand per lane.  For
 // the scores S^T = K Q^T lane (n16, q4) loads 16 bytes of key row n16 per
@@ -1297,10 +1302,13 @@ void split_mfma_kernel(
 // the bf16 kernel's layout (lane (n16, q4), element r: key 4 q4 + r of the
 // 16-key half, column n16) and the softmax is the same.  For O^T += V^T P^T
 // the four keys 4 q4 + r (r fixed) form one MFMA's k-slice: its B operand
-// is the lane's own p of element r, its A operand V[key][n16 * VW + e], so
-// the accumulators also match the bf16 kernel's (element j of block e:
-// column n16, d = (4 q4 + j) * VW + e) and the end-of-chunk merge is
-// shared.  P stays fp32 (no hi/lo split).  A wavefront works through its
+// is the lane's own p of element r, its A operand V[key][d] with
+// d = 64 (e / 4) + 4 n16 + e % 4: each V load instruction reads whole
+// 256-byte row pieces (16 lanes x 16 bytes), which at D = 128 streamed ~9%
+// faster than 32 contiguous bytes per lane.  Element j of accumulator block
+// e is then column n16, d = 64 (e / 4) + 4 (4 q4 + j) + e % 4, and the
+// bf16 kernel's end-of-chunk merge is shared with that column order
+// (wave_merge_store's ROWS64).  P stays fp32 (no hi/lo split).  A wavefront works through its
 // tiles in 16-key halves (one MFMA k-slice of scores each) and keeps the
 // next half's K and V in flight while the current half computes: 16 KB of
 // K/V per half at D = 128, two halves of registers, where a whole second
@@ -1312,7 +1320,7 @@ __device__ __forceinline__ floatx4 load_stream_f4(const float *p) {
 template <int D>
 struct F32Half {
   floatx4 k[D / 16];     // K row n16, d = 16 j + 4 q4 + e
-  floatx4 v[4][D / 64];  // V row 4 q4 + r, d = n16 * (D / 16) + 4 h + e
+  floatx4 v[4][D / 64];  // V row 4 q4 + r, d = 64 c + 4 n16 + e
 };
 
 // The 16 keys of a half: key r at kb + r * rs (K) and vb + r * rs (V),
@@ -1324,16 +1332,14 @@ __device__ __forceinline__ void f32_half_load(const float *__restrict__ kb,
                                               const float *__restrict__ vb,
                                               size_t rs, int valid, int n16,
                                               int q4, F32Half<D> &h) {
-  constexpr int VW = D / 16;
   const float *pk = kb + (size_t)min(n16, valid - 1) * rs + q4 * 4;
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) h.k[j] = load_stream_f4(pk + 16 * j);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float *pv =
-        vb + (size_t)min(q4 * 4 + r, valid - 1) * rs + n16 * VW;
+    const float *pv = vb + (size_t)min(q4 * 4 + r, valid - 1) * rs + n16 * 4;
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) h.v[r][c] = load_stream_f4(pv + 4 * c);
+    for (int c = 0; c < D / 64; ++c) h.v[r][c] = load_stream_f4(pv + 64 * c);
   }
 }
 
@@ -1529,9 +1535,9 @@ __device__ __forceinline__ void f32_chunk_pass(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
-    wave_merge_store<D, NW, float>(sm_m, sm_l, sm_o, wave, lane, n16, q4,
-                                   ncol, m, l, acc, w, pl, mode, out, lse,
-                                   o_part, lse_part);
+    wave_merge_store<D, NW, float, true>(sm_m, sm_l, sm_o, wave, lane, n16,
+                                         q4, ncol, m, l, acc, w, pl, mode,
+                                         out, lse, o_part, lse_part);
     return;
   }
   if (n16 < ncol) {
@@ -1543,7 +1549,8 @@ __device__ __forceinline__ void f32_chunk_pass(
 #pragma unroll
     for (int e = 0; e < VW; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[(q4 * 4 + j) * VW + e] = acc[e][j];
+      for (int j = 0; j < 4; ++j)
+        o[64 * (e >> 2) + 4 * (q4 * 4 + j) + (e & 3)] = acc[e][j];
   }
   __syncthreads();
   merge_and_store<D, float>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out, lse,
