@@ -204,9 +204,10 @@ FD_API int fd_decode(const void *q, const void *k_cache,
  *   num_splits  0 = planner's choice, else chunks per Lmax-long sequence
  *               (clamped to [1, ceil(Lmax / 32)]); 1 disables the merge.
  *   variant     FD_VARIANT_AUTO / _MFMA / _VALU.  AUTO: the matrix cores
- *               for bf16 and for fp32 groups of more than 4 query heads,
- *               the vector ALU for smaller fp32 groups.  VALU takes bf16
- *               groups of at most 4 heads only.
+ *               for bf16, and for fp32 from groups of 3 query heads (at
+ *               D = 64 also smaller groups from Lmax = 4096); the vector
+ *               ALU for the other fp32 shapes.  VALU takes bf16 groups of
+ *               at most 4 heads only.
  *   flags       0 or FD_FLAG_FUSED_MERGE.
  *   workspace   device buffer of at least fd_workspace_bytes(...) bytes
  *               for the same arguments, 256-byte aligned, or NULL with

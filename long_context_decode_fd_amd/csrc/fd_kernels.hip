@@ -37,11 +37,11 @@
 //     rows at D = 128), serves several causal new tokens per sequence
 //     (their query rows share the 16-column q-tile), or takes the
 //     unified-maximum softmax of FlashDecoding++ with an exact fallback;
-//   * fp32 groups of more than 4 query heads run a matrix-core kernel on
-//     v_mfma_f32_16x16x4_f32 (16-key halves, the next half in flight);
-//     smaller fp32 groups (and bf16 tiny groups, on request) a vector-ALU
-//     kernel with 16-byte loads per lane and shuffle reductions of the dot
-//     products;
+//   * fp32 runs a matrix-core kernel on v_mfma_f32_16x16x4_f32 (16-key
+//     halves, the next half in flight) from groups of 3 query heads, and
+//     for every paged or several-token call; the smallest fp32 groups (and
+//     bf16 tiny groups, on request) a vector-ALU kernel with 16-byte loads
+//     per lane and shuffle reductions of the dot products;
 //   * a second, small kernel merges the chunk partials of every query row
 //     (or, opt-in, the last workgroup of each group merges them).
 #include <hip/hip_runtime.h>

@@ -168,19 +168,24 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.unified = unified;
   q.num_cus = num_cus;
 
-  // Kernel variant: bf16 on the matrix cores; fp32 on the matrix cores for
-  // groups of more than 4 query heads, else on the vector ALU, whose cost
-  // per key grows with G while the fp32 MFMA pass pays for 16 columns at
-  // any G.  Measured (fp32, one sequence of 8 KV heads, D = 128, device time
-  // of steps replayed from a graph), vector ALU against matrix cores:
-  // 16k keys G = 1 26.1 / 30.1 us, G = 2 29.5 / 29.8, G = 4 30.5 / 30.1,
-  // G = 8 47.8 / 29.7, G = 16 82.0 / 30.0; 64k keys G = 8 149.5 / 93.5;
-  // four sequences at G = 4, 16k keys, 90.5 / 95.0.
+  // Kernel variant: bf16 on the matrix cores.  fp32 on the matrix cores too
+  // from groups of 3 query heads (and, at D = 64, for smaller groups from
+  // 4096 keys on); below that on the vector ALU, whose cost per key grows
+  // with G while the fp32 MFMA pass pays for 16 columns at any G.  Measured
+  // (fp32, device time of steps replayed from a graph, vector ALU against
+  // matrix cores at each one's planned split count), one sequence on 8 KV
+  // heads: D = 128, 16k keys, G = 1 26.0 / 28.6 us, G = 2 26.7 / 28.6,
+  // G = 3 30.5 / 28.7, G = 4 30.5 / 28.7, G = 8 47.8 / 29.4; 64k keys G = 2
+  // 83.5 / 85.8, G = 4 91.7 / 85.8; D = 64, G = 1: 1024 keys 6.6 / 7.2,
+  // 4096 keys 8.8 / 8.7, 16k keys 15.9 / 15.6; G = 3 at 1024 keys 8.1 / 7.4.
+  // Paged caches and several tokens run on the matrix cores only.
   if (requested_variant != FD_VARIANT_AUTO)
     q.variant = requested_variant;
   else
-    q.variant = dtype == FD_BF16 || q.G > 4 || general ? FD_VARIANT_MFMA
-                                                       : FD_VARIANT_VALU;
+    q.variant = dtype == FD_BF16 || general || q.G >= 3 ||
+                        (D == 64 && Lmax >= 4096)
+                    ? FD_VARIANT_MFMA
+                    : FD_VARIANT_VALU;
   // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
   // registers; beyond 4 rows the matrix-core kernel is the one to use.
   if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)

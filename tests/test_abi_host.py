@@ -263,7 +263,8 @@ def test_fp32_plans_for_two_workgroups_per_cu(lib, B, L, S):
     # the vector-ALU kernel: two workgroups per CU; one-tile chunks up to 32
     # per sequence, 64-key ones beyond (measured fastest or within 5% of
     # it, 8 heads, D = 64)
-    p = fd.fd_plan(B, 8, 8, 64, L, "f32", num_cus=256)
+    p = fd.fd_plan(B, 8, 8, 64, L, "f32", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
     assert p["variant"] == fd.FD_VARIANT_VALU
     assert p["num_splits"] == S, p
 
@@ -574,16 +575,21 @@ def test_fp32_matrix_core_plans(lib, G, D):
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 9, 16])
-def test_fp32_groups_past_4_heads_take_the_matrix_cores(lib, G):
-    # fp32: the vector ALU's work per key grows with G, the matrix cores'
-    # does not (measured at 16k keys, 8 KV heads, D = 128: G = 4 level,
-    # G = 8 47.8 against 29.7 us, G = 16 82.0 against 30.0)
-    p = fd.fd_plan(1, 8 * G, 8, 128, 16384, "f32", num_cus=256)
-    assert p["variant"] == (fd.FD_VARIANT_MFMA if G > 4
+@pytest.mark.parametrize("D,L", [(128, 1024), (128, 16384), (64, 1024),
+                                 (64, 2048), (64, 4096), (64, 65536)])
+def test_fp32_variant_follows_the_measured_rule(lib, G, D, L):
+    # fp32 on the matrix cores from G = 3, and at D = 64 from 4096 keys at
+    # any G; the vector ALU otherwise (measured, one sequence on 8 KV heads:
+    # D = 128, 16k keys, G = 2 26.7 against 28.6 us, G = 3 30.5 against
+    # 28.7; D = 64, G = 1, 1024 keys 6.6 against 7.2, 4096 keys 8.8 against
+    # 8.7)
+    p = fd.fd_plan(1, 8 * G, 8, D, L, "f32", num_cus=256)
+    mfma = G >= 3 or (D == 64 and L >= 4096)
+    assert p["variant"] == (fd.FD_VARIANT_MFMA if mfma
                             else fd.FD_VARIANT_VALU)
-    if G > 4:
-        # the bf16 matrix-core rule, counted in bytes: 512-byte rows
-        assert p["waves_per_block"] == 4 and p["grid"] == 8 * 32
+    if mfma:
+        # the matrix-core rule: one workgroup per CU
+        assert p["waves_per_block"] == 4 and p["grid"] <= 256
 
 
 @pytest.mark.parametrize("Tq,paged", [(2, False), (1, True), (4, True)])
