@@ -72,6 +72,10 @@ def test_two_calls_in_a_row_second_smaller(torch, oracle_mod):
     # and once more with forced splits, fp32 and the vector-ALU kernel
     tiny = wl.WORKLOADS["tiny_mha_f32_b1_h8_d64_l1024"]
     _check_case(torch, oracle_mod, tiny, None, 3, "third, fp32")
+    # fp32 on the matrix cores
+    f32 = wl.ALL_WORKLOADS["f32_b1_gqa8_h64_d128_l65536"].with_(Lmax=2000)
+    p4 = _check_case(torch, oracle_mod, f32, None, 0, "fourth, fp32 MFMA")
+    assert p4["variant"] == fd.FD_VARIANT_MFMA
 
 
 def test_single_pass_plan_uses_no_scratch(torch, oracle_mod):
