@@ -30,7 +30,9 @@ def torch():
 
 
 def _same(torch, a, b):
-    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    """Bitwise equality of two bf16 or fp32 tensors."""
+    it = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(it), b.view(it))
 
 
 @pytest.mark.parametrize("flags", [0, fd.FD_FLAG_FUSED_MERGE])
@@ -88,12 +90,13 @@ def _replays_match_eager(torch, g, q, outs_g, eager, reps, tag):
 
 
 @pytest.mark.parametrize("flags", [0, fd.FD_FLAG_FUSED_MERGE])
-def test_captured_paged_decode_with_caller_workspace(torch, flags):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_captured_paged_decode_with_caller_workspace(torch, flags, dtype):
     w = wl.EXTRA_WORKLOADS["paged_hm_p64_b1_gqa8_h64_d128_l65536"].with_(
-        Lmax=4096)
+        Lmax=4096, dtype=dtype)
     q, kp, vp, bt, sl, _, _ = wl.device_paged_inputs(w)
     plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D,
-                         w.max_pages * w.page_size, "bf16", paged=True,
+                         w.max_pages * w.page_size, dtype, paged=True,
                          flags=flags)
     assert plan["combine"]
     ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8,
@@ -108,15 +111,18 @@ def test_captured_paged_decode_with_caller_workspace(torch, flags):
     _replays_match_eager(
         torch, g, q, (out_g, lse_g),
         lambda: fd.fd_decode_paged(q, kp, vp, bt, sl, w.scale, flags=flags,
-                                   head_major=True), 3, f"paged {flags}")
+                                   head_major=True), 3,
+        f"paged {dtype} {flags}")
     if plan["ticket_bytes"]:
         assert int(ws[:plan["ticket_bytes"]].count_nonzero()) == 0
 
 
-def test_captured_multiquery_decode_with_caller_workspace(torch):
-    w = wl.EXTRA_WORKLOADS["mq2_b1_gqa8_h64_d128_l65536"].with_(Lmax=4096)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_captured_multiquery_decode_with_caller_workspace(torch, dtype):
+    w = wl.EXTRA_WORKLOADS["mq2_b1_gqa8_h64_d128_l65536"].with_(Lmax=4096,
+                                                                 dtype=dtype)
     q, k, v, sl, _, _ = dev_inputs(w)
-    plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D, w.Lmax, "bf16")
+    plan = fd.fd_plan_ex(w.B, w.Tq, w.Hq, w.Hkv, w.D, w.Lmax, dtype)
     assert plan["combine"]
     ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8,
                      device="cuda")
@@ -129,7 +135,8 @@ def test_captured_multiquery_decode_with_caller_workspace(torch):
     torch.cuda.synchronize()
     _replays_match_eager(
         torch, g, q, (out_g, lse_g),
-        lambda: fd.fd_decode_multiquery(q, k, v, sl, w.scale), 3, "mq")
+        lambda: fd.fd_decode_multiquery(q, k, v, sl, w.scale), 3,
+        f"mq {dtype}")
 
 
 def test_owned_workspace_is_refused_under_capture(torch):
