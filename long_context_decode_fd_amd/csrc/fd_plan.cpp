@@ -9,6 +9,10 @@
 // unsplit kernel by problem size.  This planner makes that choice for the
 // compute-unit count of the device at hand (256 on MI355X):
 //
+//   * kernel: the matrix cores for bf16, and for fp32 from groups of 3
+//     query heads (at D = 64 also smaller groups from 4096 keys) and for
+//     every paged or several-token call; the vector ALU for the other fp32
+//     shapes (planned for two workgroups per CU, below);
 //   * work units U = B * Hkv: one workgroup streams one KV-head slab range
 //     and serves all Hq / Hkv query heads of that group, so K/V are read
 //     from HBM exactly once;
