@@ -54,6 +54,11 @@ int main() {
                         Sp * C >= L && (Sp - 1) * C < L && p.grid >= 1 &&
                         p.grid <= bound && p.G * p.kv_rep == h[0] / h[1] && p.Hkv == h[1] * p.kv_rep &&
                         (p.kv_rep == 1 || p.variant == FD_VARIANT_VALU) &&
+                        // paged caches and several tokens: matrix cores only;
+                        // the unified maximum: bf16 only
+                        ((!ex.paged && ex.Tq == 1) ||
+                         p.variant == FD_VARIANT_MFMA) &&
+                        (!(flags & FD_FLAG_UNIFIED_MAX) || dt == FD_BF16) &&
                         p.combine == (Sp > 1 || (flags & FD_FLAG_PARTIALS)) &&
                         p.ws_bytes == fd::workspace_layout(p).total &&
                         (p.combine || p.ws_bytes == 0);
