@@ -39,10 +39,12 @@
  * Rows j >= seqlens[b] of a slab are never read (they may hold anything,
  * NaN included).  Pointers must be 16-byte aligned device pointers.
  *
- * Supported: D in {64, 128}; dtype FD_BF16 with 1 <= Hq/Hkv <= 16, or
- * FD_F32 with 1 <= Hq/Hkv <= 16; Lmax <= 2^30 keys.  bf16 scores and
- * outputs are accumulated in fp32; the bf16 output is rounded to nearest
- * even.
+ * Supported: D in {64, 128}; dtype FD_BF16 or FD_F32; 1 <= Hq/Hkv <= 128;
+ * Lmax <= 2^30 keys.  A KV head serves up to 16 query rows per workgroup
+ * (the matrix cores' q-tile); a larger group runs as the fewest equal
+ * groups that fit, each reading the KV head's rows again (so K/V bytes are
+ * read that many times).  bf16 scores and outputs are accumulated in fp32;
+ * the bf16 output is rounded to nearest even.
  *
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
@@ -330,7 +332,8 @@ enum {
  * page_size * Hkv at most INT_MAX.  A table entry outside [0, num_pages)
  * is a caller error that the kernel clamps into that range (never a read
  * outside the pools).
- * FD_BF16 or FD_F32 (both on the matrix cores), 1 <= Tq * Hq/Hkv <= 16.
+ * FD_BF16 or FD_F32 (both on the matrix cores), 1 <= Tq <= 16; groups of
+ * more than 16 query rows (Tq * Hq/Hkv) are split as for fd_decode.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
  * tokens; FD_FLAG_FUSED_MERGE allowed).  workspace, workspace_bytes: as
  * for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D,
@@ -359,9 +362,10 @@ FD_API int fd_decode_paged(const void *q, const void *k_pages,
  * sees no key gets out = 0, lse = -inf.  Tq = 1 is fd_decode.
  * The keys a token must not see (j in [L - Tq + 1, L)) are still loaded
  * for the tile and weighted by exactly 0: their V rows must be finite.
- * FD_BF16 or FD_F32, 1 <= Tq * Hq/Hkv <= 16 (all query rows of a KV head
- * share one 16-column matrix-core tile; with Tq = 1 fp32 may run on the
- * vector ALU, as in fd_decode).  num_splits, flags and the workspace
+ * FD_BF16 or FD_F32, 1 <= Tq <= 16.  The Tq * Hq/Hkv query rows of a KV
+ * head share one 16-column matrix-core tile, or, when there are more, the
+ * fewest equal groups of them that fit (each reading the KV head's rows);
+ * with Tq = 1 fp32 may run on the vector ALU, as in fd_decode.  num_splits, flags and the workspace
  * as for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, dtype,
  * seqlens != NULL, 0, num_splits, FD_VARIANT_AUTO, flags, 0,
  * &plan).workspace_bytes.

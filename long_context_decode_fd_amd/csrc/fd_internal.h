@@ -12,8 +12,10 @@ namespace fd {
 // Keys per MFMA tile step of one wavefront, and the granularity of chunks.
 constexpr int kKeyTile = 32;
 // Largest query group (Hq / Hkv) one workgroup handles: the MFMA q-tile
-// has 16 columns.
+// has 16 columns.  Larger groups run as several virtual KV heads.
 constexpr int kMaxGroup = 16;
+// Largest Hq / Hkv the library takes.
+constexpr int kMaxHeadsPerKv = 128;
 // Largest Lmax (keys per sequence) the library plans for.
 constexpr int kMaxKeys = 1 << 30;
 
@@ -36,9 +38,10 @@ struct Plan {
   bool fused;       // merged by the last workgroup of each group
   bool chunk_major; // partial layout: chunk-major (several rounds of
                     // workgroups) or row-major (one round)
-  int kv_rep;       // vector-ALU groups of more than 8 query heads run as
-                    // kv_rep half-groups on the same K/V slab: Hkv and G
-                    // above are the virtual ones (Hkv * kv_rep, G / kv_rep)
+  int kv_rep;       // a group runs as kv_rep virtual KV heads on the same
+                    // K/V slab (matrix cores: G * Tq > 16 query rows;
+                    // vector ALU: half-groups past 8 heads): Hkv and G above
+                    // are the virtual ones (Hkv * kv_rep, G / kv_rep)
   size_t ws_bytes;  // tickets + partial outputs + partial lse
 };
 

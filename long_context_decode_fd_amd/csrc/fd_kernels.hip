@@ -824,13 +824,13 @@ __device__ __forceinline__ TileOrder tile_order(const Work &w, int Hkv,
 
 // Paged cache: for the first key of each 16-key half of this wavefront's
 // tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
-// of its D-element row of KV head g in the pool: (page * page_size + t) *
-// Hkv + g token-major, (page * Hkv + g) * page_size + t head-major, with t
-// the key's place in its page.  Halves at or beyond the chunk end read
+// of its D-element row of KV head g (of the pool's Hkv) in the pool:
+// (page * page_size + t) * Hkv + g token-major, (page * Hkv + g) *
+// page_size + t head-major, with t the key's place in its page.  Halves at or beyond the chunk end read
 // nothing and give 0; page indices are clamped into the pool, so no entry
 // of the table can make a load leave the K/V buffers.
 __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
-                                         const TileOrder &ord, int Hkv,
+                                         const TileOrder &ord, int Hkv, int g,
                                          int wave, int nw, int it0, int lane) {
   const int t = wave + (it0 + (lane >> 1)) * nw;
   const int key = ord.key0(w, t) + (lane & 1) * 16;
@@ -839,8 +839,8 @@ __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
   int pg = pk.block_table[(size_t)w.b * pk.max_pages + j];
   pg = min(max(pg, 0), pk.num_pages - 1);
   const int off = key - j * pk.page_size;
-  return pk.head_major ? (pg * Hkv + w.g) * pk.page_size + off
-                       : (pg * pk.page_size + off) * Hkv + w.g;
+  return pk.head_major ? (pg * Hkv + g) * pk.page_size + off
+                       : (pg * pk.page_size + off) * Hkv + g;
 }
 
 // Paged caches (D = 128): K of a tile goes through LDS.  With a head's rows
@@ -904,12 +904,13 @@ template <int D, int NW, bool PAGED>
 __device__ __forceinline__ TileRows<D, PAGED> tile_rows(
     const PagedKV &pk, const Work &w, const TileOrder &ord,
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
-    size_t slab, size_t prs, int Hkv, int wave, int lane, int k0, int it,
-    int &prow) {
+    size_t slab, size_t prs, int hkv_kv, int g_kv, int wave, int lane,
+    int k0, int it, int &prow) {
   TileRows<D, PAGED> rows;
   if constexpr (PAGED) {
     const int slot = it & 31;
-    if (slot == 0) prow = page_rows(pk, w, ord, Hkv, wave, NW, it, lane);
+    if (slot == 0)
+      prow = page_rows(pk, w, ord, hkv_kv, g_kv, wave, NW, it, lane);
     const int r0 = __builtin_amdgcn_readlane(prow, 2 * slot);
     const int r1 = __builtin_amdgcn_readlane(prow, 2 * slot + 1);
     rows.rs = prs;
@@ -943,9 +944,9 @@ template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
 __device__ __forceinline__ void chunk_tiles(
     const Work &w, const PagedKV &pk, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
-    int hi_all, int hi_col, int wave, int lane, int n16, int q4,
-    const bf16x8 (&qop)[D / 32], float scale_log2, float phi2,
-    floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf,
+    int hkv_kv, int g_kv, int hi_all, int hi_col, int wave, int lane,
+    int n16, int q4, const bf16x8 (&qop)[D / 32], float scale_log2,
+    float phi2, floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf,
     bool rotate) {
   static_assert(NW >= 2, "the loop relies on two or more wavefronts");
   const int ntiles = (w.hi - w.lo + kKeyTile - 1) / kKeyTile;
@@ -958,7 +959,8 @@ __device__ __forceinline__ void chunk_tiles(
     int prow = 0;
     const int kf0 = ord.key0(w, t);
     TileRows<D, PAGED> cur = tile_rows<D, NW, PAGED>(
-        pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kf0, 0, prow);
+        pk, w, ord, kc, vc, slab, prs, hkv_kv, g_kv, wave, lane, kf0, 0,
+        prow);
     uint4 kn[8];
     load_k_rows(cur, min(kKeyTile, w.hi - kf0), lane, kn);
     uint4 kr[2][4];
@@ -969,7 +971,8 @@ __device__ __forceinline__ void chunk_tiles(
       tile_load_v<D, false>(cur, kKeyTile, n16, q4, vr);
       const int kn0 = ord.key0(w, t + NW);
       TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
-          pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+          pk, w, ord, kc, vc, slab, prs, hkv_kv, g_kv, wave, lane, kn0,
+          it + 1, prow);
       load_k_rows(nxt, min(kKeyTile, w.hi - kn0), lane, kn);
       __builtin_amdgcn_sched_barrier(0);
       load_k_operand(kbuf, n16, q4, kr);
@@ -996,7 +999,8 @@ __device__ __forceinline__ void chunk_tiles(
   int prow = 0;
   const int kf0 = ord.key0(w, t);
   TileRows<D, PAGED> cur = tile_rows<D, NW, PAGED>(
-      pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kf0, 0, prow);
+      pk, w, ord, kc, vc, slab, prs, hkv_kv, g_kv, wave, lane, kf0, 0,
+      prow);
   uint4 kr[2][D / 32];
   tile_load_k<D, true>(cur, min(kKeyTile, w.hi - kf0), n16, q4, kr);
   int it = 0;
@@ -1006,7 +1010,8 @@ __device__ __forceinline__ void chunk_tiles(
     __builtin_amdgcn_sched_barrier(0);
     const int kn0 = ord.key0(w, t + NW);
     TileRows<D, PAGED> nxt = tile_rows<D, NW, PAGED>(
-        pk, w, ord, kc, vc, slab, prs, Hkv, wave, lane, kn0, it + 1, prow);
+        pk, w, ord, kc, vc, slab, prs, hkv_kv, g_kv, wave, lane, kn0,
+        it + 1, prow);
     uint4 kn[2][D / 32];
     tile_load_k<D, true>(nxt, min(kKeyTile, w.hi - kn0), n16, q4, kn);
     __builtin_amdgcn_sched_barrier(0);
@@ -1149,8 +1154,8 @@ template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
 __device__ __forceinline__ void chunk_pass(
     const Work &w, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
-    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, float phi2, int mode, bool chunk_major,
+    PagedKV pk, int B, int Hq, int Hkv, int kv_rep, int G, int Tq, int Lmax,
+    int C, int S, float scale_log2, float phi2, int mode, bool chunk_major,
     uint16_t *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part,
     int *__restrict__ tickets) {
@@ -1187,8 +1192,12 @@ __device__ __forceinline__ void chunk_pass(
   const int hi_col = min(w.hi, w.L - (Tq - 1 - n16 / G));
   const int hi_all = min(w.hi, w.L - (Tq - 1));
 
-  const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
-  const size_t prs = pk.head_major ? (size_t)D : (size_t)Hkv * D;
+  // Groups of more than 16 query rows run as kv_rep virtual KV heads of
+  // G rows each (Hkv counts them): virtual head w.g reads the cache of KV
+  // head w.g / kv_rep, one of Hkv / kv_rep.
+  const int hkv_kv = Hkv / kv_rep, g_kv = w.g / kv_rep;
+  const size_t slab = ((size_t)w.b * hkv_kv + g_kv) * (size_t)Lmax * D;
+  const size_t prs = pk.head_major ? (size_t)D : (size_t)hkv_kv * D;
   const bool rotate =
       (size_t)Lmax * D * sizeof(uint16_t) % kRotateStride == 0;
 
@@ -1202,10 +1211,9 @@ __device__ __forceinline__ void chunk_pass(
     // column's largest x = score - phi2 leaves [-kUniRange, kUniRange] the
     // fixed reference risks overflow or lost precision, and the whole
     // workgroup recomputes the chunk with the running maximum.
-    chunk_tiles<D, NW, PAGED, CAUSAL, true>(w, pk, kc, vc, slab, prs, Hkv,
-                                            hi_all, hi_col, wave, lane, n16,
-                                            q4, qop, scale_log2, phi2, acc,
-                                            m, l, kbuf, rotate);
+    chunk_tiles<D, NW, PAGED, CAUSAL, true>(
+        w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
+        lane, n16, q4, qop, scale_log2, phi2, acc, m, l, kbuf, rotate);
     float xm = fmaxf(m, __shfl_xor(m, 16, 64));
     xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
     const bool bad = xm != FD_NEG_INF && !(xm >= -kUniRange && xm <= kUniRange);
@@ -1214,18 +1222,16 @@ __device__ __forceinline__ void chunk_pass(
       for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
       m = FD_NEG_INF;
       l = 0.f;
-      chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
-                                               hi_all, hi_col, wave, lane,
-                                               n16, q4, qop, scale_log2, 0.f,
-                                               acc, m, l, kbuf, rotate);
+      chunk_tiles<D, NW, PAGED, CAUSAL, false>(
+          w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
+          lane, n16, q4, qop, scale_log2, 0.f, acc, m, l, kbuf, rotate);
     } else {
       m = xm == FD_NEG_INF ? FD_NEG_INF : phi2;
     }
   } else {
-    chunk_tiles<D, NW, PAGED, CAUSAL, false>(w, pk, kc, vc, slab, prs, Hkv,
-                                             hi_all, hi_col, wave, lane, n16,
-                                             q4, qop, scale_log2, 0.f, acc, m,
-                                             l, kbuf, rotate);
+    chunk_tiles<D, NW, PAGED, CAUSAL, false>(
+        w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
+        lane, n16, q4, qop, scale_log2, 0.f, acc, m, l, kbuf, rotate);
   }
 
   l += __shfl_xor(l, 16, 64);
@@ -1259,8 +1265,9 @@ __global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
 void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
-    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C, int S,
-    float scale_log2, float phi2, int mode, bool direct, bool chunk_major,
+    PagedKV pk, int B, int Hq, int Hkv, int kv_rep, int G, int Tq, int Lmax,
+    int C, int S, float scale_log2, float phi2, int mode, bool direct,
+    bool chunk_major,
     uint16_t *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
@@ -1272,9 +1279,9 @@ void split_mfma_kernel(
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w0, q, kc, vc, seqlens, pk, B, Hq,
-                                        Hkv, G, Tq, Lmax, C, S, scale_log2,
-                                        phi2, mode, chunk_major, out, lse,
-                                        o_part, lse_part, tickets);
+                                        Hkv, kv_rep, G, Tq, Lmax, C, S,
+                                        scale_log2, phi2, mode, chunk_major,
+                                        out, lse, o_part, lse_part, tickets);
   // Equal lengths, a grid that covers the upper bound, or a work list that
   // ends before i + grid (its length is known from the scan for up to 64
   // sequences): one chunk each, and no second look-up.
@@ -1285,9 +1292,9 @@ void split_mfma_kernel(
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
   chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w1, q, kc, vc, seqlens, pk, B, Hq,
-                                        Hkv, G, Tq, Lmax, C, S, scale_log2,
-                                        phi2, mode, chunk_major, out, lse,
-                                        o_part, lse_part, tickets);
+                                        Hkv, kv_rep, G, Tq, Lmax, C, S,
+                                        scale_log2, phi2, mode, chunk_major,
+                                        out, lse, o_part, lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------
@@ -1405,8 +1412,9 @@ __device__ __forceinline__ void f32_half_compute(
 template <int D, int NW, bool PAGED, bool CAUSAL>
 __device__ __forceinline__ void f32_chunk_pass(
     const Work &w, const float *__restrict__ q, const float *__restrict__ kc,
-    const float *__restrict__ vc, const PagedKV &pk, int Hq, int Hkv, int G,
-    int Tq, int Lmax, int S, float scale_log2, int mode, bool chunk_major,
+    const float *__restrict__ vc, const PagedKV &pk, int Hq, int Hkv,
+    int kv_rep, int G, int Tq, int Lmax, int S, float scale_log2, int mode,
+    bool chunk_major,
     float *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part,
     int *__restrict__ tickets) {
@@ -1433,9 +1441,11 @@ __device__ __forceinline__ void f32_chunk_pass(
   // and the smallest over the columns.
   const int hi_col = min(w.hi, w.L - (Tq - 1 - n16 / G));
   const int hi_all = min(w.hi, w.L - (Tq - 1));
-  const size_t slab = ((size_t)w.b * Hkv + w.g) * (size_t)Lmax * D;
+  // virtual KV heads as in the bf16 pass
+  const int hkv_kv = Hkv / kv_rep, g_kv = w.g / kv_rep;
+  const size_t slab = ((size_t)w.b * hkv_kv + g_kv) * (size_t)Lmax * D;
   const size_t rs = !PAGED ? (size_t)D
-                           : (pk.head_major ? (size_t)D : (size_t)Hkv * D);
+                           : (pk.head_major ? (size_t)D : (size_t)hkv_kv * D);
   const bool rotate = (size_t)Lmax * D * sizeof(float) % kRotateStride == 0;
 
   floatx4 acc[VW];
@@ -1458,7 +1468,7 @@ __device__ __forceinline__ void f32_chunk_pass(
       const float *kb, *vb;
       if constexpr (PAGED) {
         if ((i & 63) == 0)
-          prow = page_rows(pk, w, ord, Hkv, wave, NW, i >> 1, lane);
+          prow = page_rows(pk, w, ord, hkv_kv, g_kv, wave, NW, i >> 1, lane);
         const int r0 = __builtin_amdgcn_readlane(prow, i & 63);
         kb = kc + (size_t)r0 * D;
         vb = vc + (size_t)r0 * D;
@@ -1566,25 +1576,27 @@ __global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
 void split_mfma_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc,
     const float *__restrict__ vc, const int32_t *__restrict__ seqlens,
-    PagedKV pk, int B, int Hq, int Hkv, int G, int Tq, int Lmax, int C,
-    int S, float scale_log2, int mode, bool direct, bool chunk_major,
+    PagedKV pk, int B, int Hq, int Hkv, int kv_rep, int G, int Tq, int Lmax,
+    int C, int S, float scale_log2, int mode, bool direct, bool chunk_major,
     float *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part,
     int *__restrict__ tickets) {
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
-  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w0, q, kc, vc, pk, Hq, Hkv, G, Tq,
-                                       Lmax, S, scale_log2, mode, chunk_major,
-                                       out, lse, o_part, lse_part, tickets);
+  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w0, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
+                                       Tq, Lmax, S, scale_log2, mode,
+                                       chunk_major, out, lse, o_part,
+                                       lse_part, tickets);
   const long id1 = (long)blockIdx.x + gridDim.x;
   if (seqlens == nullptr || id1 >= (long)B * Hkv * S || id1 >= w0.items)
     return;
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
-  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w1, q, kc, vc, pk, Hq, Hkv, G, Tq,
-                                       Lmax, S, scale_log2, mode, chunk_major,
-                                       out, lse, o_part, lse_part, tickets);
+  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w1, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
+                                       Tq, Lmax, S, scale_log2, mode,
+                                       chunk_major, out, lse, o_part,
+                                       lse_part, tickets);
 }
 
 // ---------------------------------------------------------------------------
@@ -1977,8 +1989,9 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   case NWV:                                                                  \
     hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI>), grid,\
                        dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
-                       p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk,         \
-                       p.splits, sl2, phi2, part, p.direct, p.chunk_major,   \
+                       p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax,        \
+                       p.chunk, p.splits, sl2, phi2, part, p.direct,         \
+                       p.chunk_major,                                        \
                        out, a.lse, a.o_part, a.lse_part, a.tickets);         \
     break;
   switch (p.waves) {
@@ -2001,7 +2014,8 @@ hipError_t launch_mfma_f32(const Plan &p, const LaunchArgs &a, float sl2,
                      static_cast<const float *>(a.q),
                      static_cast<const float *>(a.k),
                      static_cast<const float *>(a.v), a.seqlens, a.paged,
-                     p.B, p.Hq, p.Hkv, p.G, p.Tq, p.Lmax, p.chunk, p.splits,
+                     p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax, p.chunk,
+                     p.splits,
                      sl2, mode_of(p), p.direct, p.chunk_major,
                      static_cast<float *>(a.out), a.lse, a.o_part,
                      a.lse_part, a.tickets);

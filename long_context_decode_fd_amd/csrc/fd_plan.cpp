@@ -108,7 +108,7 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
   if (Hq % Hkv != 0) return FD_ERR_INVALID_ARG;
   if (dtype != FD_BF16 && dtype != FD_F32) return FD_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return FD_ERR_UNSUPPORTED;
-  if (Hq / Hkv > kMaxGroup) return FD_ERR_UNSUPPORTED;
+  if (Hq / Hkv > kMaxHeadsPerKv) return FD_ERR_UNSUPPORTED;
   // Keys per sequence: chunk sizes, key offsets and lo + C stay in int.
   // (2^30 keys of one KV head at D = 128 are 256 GB, beyond any GPU's HBM.)
   if (Lmax > kMaxKeys) return FD_ERR_UNSUPPORTED;
@@ -137,12 +137,12 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (rc != FD_OK) return rc;
   if (extra.Tq < 1) return FD_ERR_INVALID_ARG;
   // Several new tokens or a paged cache: the matrix-core kernels only (bf16
-  // or fp32), with all G * Tq query rows of a KV head in the 16-column
-  // q-tile.
+  // or fp32), whose 16-column q-tile holds the G * Tq query rows of a KV
+  // head (or of a virtual one, below).
   const bool general = extra.Tq > 1 || extra.paged;
   if (general) {
     if (requested_variant == FD_VARIANT_VALU) return FD_ERR_UNSUPPORTED;
-    if ((long)(Hq / Hkv) * extra.Tq > kMaxGroup) return FD_ERR_UNSUPPORTED;
+    if (extra.Tq > kMaxGroup) return FD_ERR_UNSUPPORTED;
     if ((long)B * Hq * extra.Tq > (1L << 30)) return FD_ERR_UNSUPPORTED;
   }
   if (num_cus <= 0) return FD_ERR_INVALID_ARG;
@@ -191,8 +191,11 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
                     ? FD_VARIANT_MFMA
                     : FD_VARIANT_VALU;
   // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
-  // registers; beyond 4 rows the matrix-core kernel is the one to use.
+  // registers; beyond 4 rows the matrix-core kernel is the one to use.  The
+  // fp32 one serves up to 16.
   if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)
+    return FD_ERR_UNSUPPORTED;
+  if (q.variant == FD_VARIANT_VALU && q.G > kMaxGroup)
     return FD_ERR_UNSUPPORTED;
   // The vector-ALU kernel computes G dot products per key, each finished by
   // a butterfly across the lanes of a row; past 8 query heads (16 rows in
@@ -204,6 +207,17 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     q.kv_rep = 2;
     q.Hkv *= 2;
     q.G /= 2;
+  }
+  // Matrix cores: more than 16 query rows per KV head (G * Tq) run as the
+  // fewest equal virtual groups that fit the q-tile, each a virtual KV head
+  // reading the same slab, so K/V are read kv_rep times (multi-query models
+  // with many query heads per KV head; several tokens of a large group).
+  if (q.variant == FD_VARIANT_MFMA && (long)q.G * q.Tq > kMaxGroup) {
+    int r = (q.G * q.Tq + kMaxGroup - 1) / kMaxGroup;
+    while (q.G % r != 0 || (q.G / r) * q.Tq > kMaxGroup) ++r;
+    q.kv_rep = r;
+    q.Hkv *= r;
+    q.G /= r;
   }
   if (q.variant == FD_VARIANT_MFMA)
     q.waves = kMfmaWaves;

@@ -12,7 +12,8 @@
 
 int main() {
   const int Bs[] = {1, 2, 7, 64, 130, 4096, 1 << 20};
-  const int Hs[][2] = {{8, 8}, {64, 8}, {32, 32}, {16, 1}, {6, 2}, {256, 16}};
+  const int Hs[][2] = {{8, 8},  {64, 8}, {32, 32}, {16, 1},
+                       {6, 2},  {256, 16}, {64, 2}, {128, 1}, {129, 1}};
   const int Ds[] = {64, 128, 96};
   const int Ls[] = {1, 31, 32, 33, 512, 513, 2048, 65536, 131072, 1 << 24,
                     (1 << 30) + 1, INT_MAX};
@@ -53,7 +54,12 @@ int main() {
               bool ok = C >= fd::kKeyTile && C % fd::kKeyTile == 0 && Sp >= 1 &&
                         Sp * C >= L && (Sp - 1) * C < L && p.grid >= 1 &&
                         p.grid <= bound && p.G * p.kv_rep == h[0] / h[1] && p.Hkv == h[1] * p.kv_rep &&
-                        (p.kv_rep == 1 || p.variant == FD_VARIANT_VALU) &&
+                        // virtual KV heads: vector-ALU half-groups, or
+                        // matrix-core groups of more than 16 query rows
+                        (p.kv_rep == 1 || p.variant == FD_VARIANT_VALU ||
+                         (long)(h[0] / h[1]) * ex.Tq > fd::kMaxGroup) &&
+                        (p.variant != FD_VARIANT_MFMA ||
+                         (long)p.G * p.Tq <= fd::kMaxGroup) &&
                         // paged caches and several tokens: matrix cores only;
                         // the unified maximum: bf16 only
                         ((!ex.paged && ex.Tq == 1) ||

@@ -103,7 +103,7 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
     (dict(D=256), fd.FD_ERR_UNSUPPORTED),
     (dict(dtype=7), fd.FD_ERR_UNSUPPORTED),
-    (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=258, Hkv=2), fd.FD_ERR_UNSUPPORTED),    # 129 heads per KV head
     (dict(Lmax=(1 << 30) + 1), fd.FD_ERR_UNSUPPORTED),   # above 2^30 keys
     (dict(Lmax=2**31 - 1), fd.FD_ERR_UNSUPPORTED),
     (dict(num_splits=-1), fd.FD_ERR_INVALID_ARG),
@@ -411,12 +411,12 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(layout=-1), fd.FD_ERR_INVALID_ARG),
     (dict(layout=1, page_size=8), fd.FD_ERR_UNSUPPORTED),
     (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
-    (dict(Tq=3, Hq=48, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 6 x 3 = 18 rows
+    (dict(Tq=3, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # 129 per KV head
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),
     (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),        # bf16 or fp32 only
-    (dict(dtype=1, Tq=3, Hq=48, Hkv=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=1, Tq=3, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
-    (dict(Hq=64, Hkv=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(Hq=258, Hkv=2), fd.FD_ERR_UNSUPPORTED),    # 129 heads per KV head
     (dict(q=None), fd.FD_ERR_INVALID_ARG),
     (dict(k=A + 8), fd.FD_ERR_INVALID_ARG),
     (dict(lse=None), fd.FD_ERR_INVALID_ARG),
@@ -442,11 +442,11 @@ def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
     (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
     (dict(Tq=-3), fd.FD_ERR_INVALID_ARG),
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 17 columns
-    (dict(Tq=5, Hq=32, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 4 x 5 = 20
-    (dict(Tq=2, Hq=64, Hkv=4), fd.FD_ERR_UNSUPPORTED),   # G alone is 16
+    (dict(Tq=17, Hq=16, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # no split fits
+    (dict(Tq=2, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # 129 per KV head
     (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),
     (dict(Tq=1, dtype=-1), fd.FD_ERR_UNSUPPORTED),
-    (dict(Tq=5, Hq=32, Hkv=8, dtype=1), fd.FD_ERR_UNSUPPORTED),
+    (dict(Tq=17, Hq=32, Hkv=8, dtype=1), fd.FD_ERR_UNSUPPORTED),
     (dict(B=1 << 20, Tq=16, Hq=128, Hkv=128), fd.FD_ERR_UNSUPPORTED),
     (dict(q=None), fd.FD_ERR_INVALID_ARG),
     (dict(seqlens=A + 1), fd.FD_ERR_INVALID_ARG),
@@ -482,7 +482,8 @@ def test_plan_ex_for_several_tokens_and_pages(lib):
     pv = fd.fd_plan_ex(16, 1, 64, 8, 128, 131072, "bf16", paged=True,
                        num_cus=256)
     assert pv["chunk"] == 2048
-    for kw in (dict(Tq=3, Hq=64, Hkv=8), dict(Tq=3, Hq=64, Hkv=8, dtype="f32"),
+    for kw in (dict(Tq=17, Hq=64, Hkv=8), dict(Tq=17, Hq=64, Hkv=8, dtype="f32"),
+               dict(Tq=2, Hq=1032, Hkv=8),
                dict(Tq=2, dtype="f32", variant=fd.FD_VARIANT_VALU),
                dict(Tq=1, dtype="f32", paged=True,
                     variant=fd.FD_VARIANT_VALU),
@@ -605,3 +606,33 @@ def test_fp32_paged_and_several_tokens_take_the_matrix_cores(lib, Tq, paged,
     assert p["variant"] == fd.FD_VARIANT_MFMA
     # 512-byte rows count as bf16 rows of D = 256: at most the bf16 chunks
     assert p["chunk"] <= pb["chunk"] or p["num_splits"] >= pb["num_splits"]
+
+
+@pytest.mark.parametrize("G,Tq,rep", [(17, 1, 17), (24, 1, 2), (32, 1, 2),
+                                      (48, 1, 3), (64, 1, 4), (128, 1, 8),
+                                      (8, 3, 2), (8, 4, 2), (6, 3, 2),
+                                      (16, 2, 2), (4, 16, 4), (64, 2, 8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_groups_run_as_virtual_kv_heads(lib, G, Tq, rep, dtype):
+    # more than 16 query rows per KV head (G * Tq): the fewest equal
+    # virtual groups that fit the 16-column q-tile, each its own workgroup
+    # on the same K/V slab, so the grid counts rep virtual heads per head
+    Hkv, B = 2, 3
+    p = fd.fd_plan_ex(B, Tq, G * Hkv, Hkv, 128, 4096, dtype,
+                      num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
+    assert p["grid"] == B * Hkv * rep * p["num_splits"]
+    assert (G // rep) * Tq <= 16 and G % rep == 0
+    # the partials still hold one row per real query head and token
+    if p["combine"]:
+        rows = B * Tq * G * Hkv * p["num_splits"]
+        assert p["lse_part_offset"] == p["o_part_offset"] + rows * 128 * 4
+
+
+def test_groups_past_128_heads_are_refused(lib):
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(1, 129, 1, 128, 4096, "bf16", num_cus=256)
+    fd.fd_plan(1, 128, 1, 128, 4096, "bf16", num_cus=256)
+    with pytest.raises(fd.FdError):   # the vector ALU takes up to 16
+        fd.fd_plan(1, 32, 1, 128, 4096, "f32", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)

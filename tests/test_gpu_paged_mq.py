@@ -88,6 +88,7 @@ PAGED_SHAPES = [
     (4, 8, 1, 128, 600, 48, [600, 47, 48, 49]),
     (1, 4, 4, 64, 96, 16, [200]),                    # beyond capacity
     (1, 8, 1, 128, 9000, 16, [8999]),     # one chunk: > 32 tiles per wave
+    (2, 64, 2, 128, 900, 32, [900, 450]),            # 32 per KV head
 ]
 
 
@@ -186,6 +187,7 @@ PAGED_MQ_SHAPES = [
     (2, 4, 16, 4, 128, 700, 16, [700, 3]),
     (2, 3, 8, 8, 64, 640, 64, [641, 64]),
     (1, 16, 4, 4, 128, 9000, 48, [8999]),
+    (2, 2, 64, 4, 128, 700, 32, [700, 33]),          # 16 x 2 rows
 ]
 
 
@@ -248,6 +250,8 @@ MQ_SHAPES = [
     (2, 16, 4, 4, 128, 300, [300, 9]),                # 16 tokens, MHA
     (1, 1, 64, 4, 128, 400, [399]),                   # Tq = 1
     (2, 2, 8, 1, 128, 640, [641, 64]),                # clamped; G = 8
+    (2, 4, 32, 4, 128, 600, [600, 5]),                # 8 x 4 = 32 rows
+    (1, 3, 48, 1, 64, 500, [500]),                    # 48 x 3 = 144 rows
 ]
 
 

@@ -44,6 +44,15 @@ SMALL = {
         B=3, Hq=10, Hkv=2, Lmax=700),
     "f32_varlen_gqa8_d128": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
         B=5, Hq=16, Hkv=2, Lmax=2100, varlen=(1, 2100), dtype="f32"),
+    # more than 16 query heads per KV head: virtual KV heads
+    "gqa32_d128": W["b1_gqa8_h64_d128_l65536"].with_(B=2, Hq=64, Hkv=2,
+                                                     Lmax=1500),
+    "mqa48_d64": W["b1_gqa8_h64_d128_l65536"].with_(B=1, Hq=48, Hkv=1, D=64,
+                                                    Lmax=2100),
+    "f32_mqa64_d128": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
+        B=1, Hq=64, Hkv=1, D=128, Lmax=1000),
+    "varlen_gqa24": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=4, Hq=48, Hkv=2, Lmax=3000, varlen=(1, 3000)),
 }
 
 
@@ -83,6 +92,8 @@ def assert_parity(w, out, lse, ref_out, ref_lse, what=""):
 
 
 def variants_for(w):
+    if w.G > 16:
+        return [fd.FD_VARIANT_MFMA]      # virtual KV heads, matrix cores
     if w.dtype == "f32":
         return [fd.FD_VARIANT_MFMA, fd.FD_VARIANT_VALU]
     if w.G <= 4:
