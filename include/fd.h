@@ -169,17 +169,25 @@ typedef struct fd_plan_info {
                                the D axis; chunk s of sequence b exists iff
                                s < max(1, ceil(seqlens[b] / chunk)) */
     int partial_layout;     /* FD_PARTIALS_ROW_MAJOR or _CHUNK_MAJOR */
+    int partial_group;      /* P: query heads per group of the chunk-major
+                               layout: G = Hq / Hkv, or G / r when a KV
+                               head's G * Tq query rows run as r groups
+                               (more than 16 rows on the matrix cores;
+                               groups past 8 heads on the vector ALU) */
 } fd_plan_t;
 
 /* Layouts of the chunk partials (fd_plan_t.partial_layout), with S =
-   num_splits, G = Hq / Hkv, Tq query tokens per sequence (1 for decode):
+   num_splits, P = fd_plan_t.partial_group, Tq query tokens per sequence
+   (1 for decode):
      FD_PARTIALS_ROW_MAJOR    o_part [B][Tq][Hq][S][D], lse_part
                               [B][Tq][Hq][S]: a query row's chunks together
                               (plans whose chunks all run in one round of
                               workgroups);
-     FD_PARTIALS_CHUNK_MAJOR  o_part [B][Hkv][S][Tq][G][D], lse_part
-                              [B][Hkv][S][Tq][G]: one chunk's rows together
-                              (plans that run in several rounds). */
+     FD_PARTIALS_CHUNK_MAJOR  o_part [B][Hq/P][S][Tq][P][D], lse_part
+                              [B][Hq/P][S][Tq][P]: one chunk's rows of a
+                              group of P query heads together (plans that
+                              run in several rounds); P = Hq / Hkv unless a
+                              KV head's rows are split (see partial_group). */
 enum {
     FD_PARTIALS_ROW_MAJOR = 0,
     FD_PARTIALS_CHUNK_MAJOR = 1

@@ -49,7 +49,8 @@ class FdPlanStruct(ctypes.Structure):
                 ("waves_per_block", _ci), ("grid", _ci), ("combine", _ci),
                 ("merge", _ci), ("num_cus", _ci), ("workspace_bytes", _sz),
                 ("ticket_bytes", _sz), ("o_part_offset", _sz),
-                ("lse_part_offset", _sz), ("partial_layout", _ci)]
+                ("lse_part_offset", _sz), ("partial_layout", _ci),
+                ("partial_group", _ci)]
 
 
 SIGNATURES = {

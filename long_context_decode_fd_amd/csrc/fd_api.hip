@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 20000;  // 2.0.0
+constexpr int kVersion = 20100;  // 2.1.0
 
 bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -430,6 +430,7 @@ int fd_plan_ex(int B, int Tq, int Hq, int Hkv, int D, int Lmax,
   plan->lse_part_offset = p.combine ? lay.lse_part_off : 0;
   plan->partial_layout =
       p.chunk_major ? FD_PARTIALS_CHUNK_MAJOR : FD_PARTIALS_ROW_MAJOR;
+  plan->partial_group = p.G;
   return FD_OK;
 }
 

@@ -66,7 +66,7 @@ def test_status_strings_and_version(lib):
         s = fd.fd_status_string(code)
         assert s and s != "unknown status"
     assert fd.fd_status_string(12345) == "unknown status"
-    assert fd.fd_version() == 20000
+    assert fd.fd_version() == 20100
 
 
 # Fake, never dereferenced device addresses: every call below must be
@@ -636,3 +636,16 @@ def test_groups_past_128_heads_are_refused(lib):
     with pytest.raises(fd.FdError):   # the vector ALU takes up to 16
         fd.fd_plan(1, 32, 1, 128, 4096, "f32", variant=fd.FD_VARIANT_VALU,
                    num_cus=256)
+
+
+@pytest.mark.parametrize("Hq,Hkv,dtype,variant,P", [
+    (64, 8, "bf16", fd.FD_VARIANT_AUTO, 8),
+    (64, 2, "bf16", fd.FD_VARIANT_AUTO, 16),      # 32 rows: two groups
+    (48, 1, "f32", fd.FD_VARIANT_AUTO, 16),
+    (16, 1, "f32", fd.FD_VARIANT_VALU, 8),        # vector-ALU halves
+    (16, 1, "f32", fd.FD_VARIANT_MFMA, 16)])
+def test_partial_group_names_the_chunk_major_rows(lib, Hq, Hkv, dtype,
+                                                  variant, P):
+    p = fd.fd_plan(4, Hq, Hkv, 128, 65536, dtype, varlen=True,
+                   variant=variant, num_cus=256)
+    assert p["partial_group"] == P

@@ -370,10 +370,11 @@ def test_phase_calls_and_chunk_partials(cuda, oracle_mod, name, num_splits):
     o_flat = wsh[o_off:o_off + n * w.D * 4].view(np.float32)
     l_flat = wsh[l_off:l_off + n * 4].view(np.float32)
     if plan["partial_layout"] == fd.FD_PARTIALS_CHUNK_MAJOR:
-        # [B][Hkv][S][G] rows -> [B][Hq][S]
-        o_part = o_flat.reshape(w.B, w.Hkv, S, w.G, w.D).transpose(
+        # [B][Hq/P][S][P] rows -> [B][Hq][S]
+        P = plan["partial_group"]
+        o_part = o_flat.reshape(w.B, w.Hq // P, S, P, w.D).transpose(
             0, 1, 3, 2, 4).reshape(w.B, w.Hq, S, w.D)
-        l_part = l_flat.reshape(w.B, w.Hkv, S, w.G).transpose(
+        l_part = l_flat.reshape(w.B, w.Hq // P, S, P).transpose(
             0, 1, 3, 2).reshape(w.B, w.Hq, S)
     else:
         assert plan["partial_layout"] == fd.FD_PARTIALS_ROW_MAJOR
