@@ -39,7 +39,8 @@
  * Rows j >= seqlens[b] of a slab are never read (they may hold anything,
  * NaN included).  Pointers must be 16-byte aligned device pointers.
  *
- * Supported: D in {64, 128}; dtype FD_BF16 or FD_F32; 1 <= Hq/Hkv <= 128;
+ * Supported: D in {64, 128, 256} (256: the matrix-core kernels only);
+ * dtype FD_BF16 or FD_F32; 1 <= Hq/Hkv <= 128;
  * Lmax <= 2^30 keys.  A KV head serves up to 16 query rows per workgroup
  * (the matrix cores' q-tile); a larger group runs as the fewest equal
  * groups that fit, each reading the KV head's rows again (so K/V bytes are

@@ -593,6 +593,16 @@ template <>
 struct VecOf<4> {
   typedef uint2 type;
 };
+// D = 256: a lane's 16 columns are two 16-byte pieces 256 bytes apart (row
+// pieces of 128 columns, so that each load instruction reads whole
+// 256-byte stretches of the rows).
+struct U32x8 {
+  uint4 lo, hi;
+};
+template <>
+struct VecOf<16> {
+  typedef U32x8 type;
+};
 
 template <int VW>
 __device__ __forceinline__ uint32_t dword_of(const typename VecOf<VW>::type &v,
@@ -605,6 +615,23 @@ template <>
 __device__ __forceinline__ uint32_t dword_of<4>(const uint2 &v, int i) {
   return i == 0 ? v.x : v.y;
 }
+template <>
+__device__ __forceinline__ uint32_t dword_of<16>(const U32x8 &v, int i) {
+  return i < 4 ? dword_of<8>(v.lo, i) : dword_of<8>(v.hi, i - 4);
+}
+
+// The accumulator layout: element j of block e of lane (n16, q4) holds
+// query column n16 and head-dimension column acc_col(e, 4 q4 + j).
+// ROWS = 0: d = i * VW + e (a lane's V columns contiguous); ROWS = R > 0:
+// the lane's V columns come in pieces of R from row pieces of 16 R
+// columns, d = (e / R) * 16 R + R i + e % R.
+template <int VW, int ROWS>
+__device__ __forceinline__ constexpr int acc_col(int e, int i) {
+  return ROWS == 0 ? i * VW + e : (e / ROWS) * 16 * ROWS + ROWS * i + e % ROWS;
+}
+// bf16 V pieces: natural up to D = 128, 128-column row pieces at D = 256.
+template <int D>
+constexpr int kBf16Rows = D > 128 ? 8 : 0;
 
 // Where the key rows of a tile live.  Contiguous cache: row r of the tile
 // starting at key k0 is k[(k0 + r) * D].  Paged cache: the tile's two
@@ -675,8 +702,14 @@ __device__ __forceinline__ void tile_load_v(
   for (int i = 0; i < 8; ++i) {
     int r = (i >> 2) * 16 + q4 * 4 + (i & 3);
     if (TAIL) r = min(r, valid - 1);
-    vr[i] = load_stream(
-        reinterpret_cast<const VT *>(rows.vrow(r) + n16 * VW));
+    if constexpr (VW == 16) {
+      const uint16_t *p = rows.vrow(r) + n16 * 8;
+      vr[i].lo = load_stream(reinterpret_cast<const uint4 *>(p));
+      vr[i].hi = load_stream(reinterpret_cast<const uint4 *>(p + 128));
+    } else {
+      vr[i] = load_stream(
+          reinterpret_cast<const VT *>(rows.vrow(r) + n16 * VW));
+    }
   }
 }
 
@@ -928,9 +961,11 @@ __device__ __forceinline__ TileRows<D, PAGED> tile_rows(
 
 // The per-chunk kernel is held to two workgroups per CU (one of eight
 // wavefronts): left free, the compiler spends the registers of the K tile
-// loaded ahead until only one wavefront fits per SIMD.
-template <int NW>
-constexpr int kBlocksPerCU = NW >= 8 ? 1 : 2;
+// loaded ahead until only one wavefront fits per SIMD.  At D = 256 a
+// wavefront's tiles and accumulators need more than 256 registers: one
+// workgroup per CU, with the accumulation registers in use.
+template <int NW, int D = 128>
+constexpr int kBlocksPerCU = NW >= 8 || D > 128 ? 1 : 2;
 
 // The tiles of a chunk, wavefront `wave` taking tiles wave, wave + NW, ...
 // K of the next tile is loaded while this tile computes: per tile, V of
@@ -1050,14 +1085,13 @@ constexpr float kUniRange = 64.f;
 // 1.. park their accumulators in LDS as 16-byte vectors; after one barrier
 // wavefront 0 alone forms M = max m, W = sum 2^(m - M) l and the weights
 // 2^(m - M) / W, adds the weighted accumulators in wavefront order and
-// stores its lane's contiguous run of output columns, (q4 * 4 + j) * VW + e,
-// with vector stores.  A column that saw no key gets out 0 and lse -inf.
-// OutT: uint16_t (bf16 bits, rounded to nearest even) or float.  ROWS64:
-// accumulator block e holds, for lane row i = 4 q4 + j, column
-// d = 64 (e / 4) + 4 i + e % 4 (the fp32 kernel's V layout) instead of
-// d = i VW + e; either way a lane's four blocks 4 e4 .. 4 e4 + 3 of one j
-// are four consecutive columns.
-template <int D, int NW, typename OutT = uint16_t, bool ROWS64 = false>
+// stores its lane's runs of four consecutive output columns,
+// acc_col(4 e4, 4 q4 + j), with vector stores.  A column that saw no key
+// gets out 0 and lse -inf.  OutT: uint16_t (bf16 bits, rounded to nearest
+// even) or float.  ROWS: the accumulator layout (acc_col); with any of
+// them a lane's blocks 4 e4 .. 4 e4 + 3 of one j are four consecutive
+// columns.
+template <int D, int NW, typename OutT = uint16_t, int ROWS = 0>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
     int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
@@ -1116,8 +1150,7 @@ __device__ __forceinline__ void wave_merge_store(
         o.z += p.z * wt[sl];
         o.w += p.w * wt[sl];
       }
-      const int d0 = ROWS64 ? 64 * e4 + 4 * (q4 * 4 + j)
-                            : (q4 * 4 + j) * VW + 4 * e4;
+      const int d0 = acc_col<VW, ROWS>(4 * e4, q4 * 4 + j);
       if (mode == kModeDirect) {
         if constexpr (sizeof(OutT) == 2) {
           uint2 bits;
@@ -1237,8 +1270,9 @@ __device__ __forceinline__ void chunk_pass(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
-    wave_merge_store<D, NW>(sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l,
-                            acc, w, pl, mode, out, lse, o_part, lse_part);
+    wave_merge_store<D, NW, uint16_t, kBf16Rows<D>>(
+        sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l, acc, w, pl, mode,
+        out, lse, o_part, lse_part);
     return;
   }
   if (n16 < ncol) {
@@ -1250,7 +1284,8 @@ __device__ __forceinline__ void chunk_pass(
 #pragma unroll
     for (int e = 0; e < VW; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[(q4 * 4 + j) * VW + e] = acc[e][j];
+      for (int j = 0; j < 4; ++j)
+        o[acc_col<VW, kBf16Rows<D>>(e, q4 * 4 + j)] = acc[e][j];
   }
   __syncthreads();
   merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out,
@@ -1261,7 +1296,7 @@ __device__ __forceinline__ void chunk_pass(
 }
 
 template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
-__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
+__global__ __launch_bounds__(NW * 64, (kBlocksPerCU<NW, D>))
 void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
@@ -1315,7 +1350,7 @@ void split_mfma_kernel(
 // faster than 32 contiguous bytes per lane.  Element j of accumulator block
 // e is then column n16, d = 64 (e / 4) + 4 (4 q4 + j) + e % 4, and the
 // bf16 kernel's end-of-chunk merge is shared with that column order
-// (wave_merge_store's ROWS64).  P stays fp32 (no hi/lo split).  A wavefront works through its
+// (acc_col with ROWS = 4).  P stays fp32 (no hi/lo split).  A wavefront works through its
 // tiles in 16-key halves (one MFMA k-slice of scores each) and keeps the
 // next half's K and V in flight while the current half computes: 16 KB of
 // K/V per half at D = 128, two halves of registers, where a whole second
@@ -1545,9 +1580,9 @@ __device__ __forceinline__ void f32_chunk_pass(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
-    wave_merge_store<D, NW, float, true>(sm_m, sm_l, sm_o, wave, lane, n16,
-                                         q4, ncol, m, l, acc, w, pl, mode,
-                                         out, lse, o_part, lse_part);
+    wave_merge_store<D, NW, float, 4>(sm_m, sm_l, sm_o, wave, lane, n16, q4,
+                                      ncol, m, l, acc, w, pl, mode, out, lse,
+                                      o_part, lse_part);
     return;
   }
   if (n16 < ncol) {
@@ -1560,7 +1595,7 @@ __device__ __forceinline__ void f32_chunk_pass(
     for (int e = 0; e < VW; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        o[64 * (e >> 2) + 4 * (q4 * 4 + j) + (e & 3)] = acc[e][j];
+        o[acc_col<VW, 4>(e, q4 * 4 + j)] = acc[e][j];
   }
   __syncthreads();
   merge_and_store<D, float>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out, lse,
@@ -1572,7 +1607,7 @@ __device__ __forceinline__ void f32_chunk_pass(
 // Launched exactly like split_mfma_kernel (the same plan, grid and work
 // list; a workgroup may take a second chunk).
 template <int D, int NW, bool PAGED, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, kBlocksPerCU<NW>)
+__global__ __launch_bounds__(NW * 64, (kBlocksPerCU<NW, D>))
 void split_mfma_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc,
     const float *__restrict__ vc, const int32_t *__restrict__ seqlens,
@@ -2032,6 +2067,16 @@ hipError_t launch_mfma_f32_any(const Plan &p, const LaunchArgs &a, float sl2,
                            : launch_mfma_f32<D, false, false>(p, a, sl2, st));
 }
 
+template <int D>
+hipError_t launch_mfma_any(const Plan &p, const LaunchArgs &a, float sl2,
+                           hipStream_t st) {
+  const bool causal = p.Tq > 1;
+  return p.paged ? (causal ? launch_mfma<D, true, true>(p, a, sl2, st)
+                           : launch_mfma<D, true, false>(p, a, sl2, st))
+                 : (causal ? launch_mfma<D, false, true>(p, a, sl2, st)
+                           : launch_mfma<D, false, false>(p, a, sl2, st));
+}
+
 template <int D, typename OutT>
 void launch_combine(const Plan &p, const LaunchArgs &a, hipStream_t st) {
   const int rows = p.B * p.Tq * p.Hq;
@@ -2071,27 +2116,21 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
     // merge only
   } else if (p.variant == FD_VARIANT_MFMA && p.dtype == FD_F32) {
     // the planner keeps the unified maximum to bf16
-    e = p.unified ? hipErrorInvalidValue
+    e = p.unified        ? hipErrorInvalidValue
+        : p.D == 256 ? launch_mfma_f32_any<256>(p, a, sl2, st)
         : p.D == 128 ? launch_mfma_f32_any<128>(p, a, sl2, st)
                      : launch_mfma_f32_any<64>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA && p.unified) {
     // the planner allows the unified maximum for contiguous single-token
     // decode only
-    e = p.D == 128 ? launch_mfma<128, false, false, true>(p, a, sl2, st)
-                   : launch_mfma<64, false, false, true>(p, a, sl2, st);
+    e = p.D == 256   ? launch_mfma<256, false, false, true>(p, a, sl2, st)
+        : p.D == 128 ? launch_mfma<128, false, false, true>(p, a, sl2, st)
+                     : launch_mfma<64, false, false, true>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA) {
-    const bool causal = p.Tq > 1;
-    if (p.D == 128)
-      e = p.paged ? (causal ? launch_mfma<128, true, true>(p, a, sl2, st)
-                            : launch_mfma<128, true, false>(p, a, sl2, st))
-                  : (causal ? launch_mfma<128, false, true>(p, a, sl2, st)
-                            : launch_mfma<128, false, false>(p, a, sl2, st));
-    else
-      e = p.paged ? (causal ? launch_mfma<64, true, true>(p, a, sl2, st)
-                            : launch_mfma<64, true, false>(p, a, sl2, st))
-                  : (causal ? launch_mfma<64, false, true>(p, a, sl2, st)
-                            : launch_mfma<64, false, false>(p, a, sl2, st));
-  } else if (p.paged || p.Tq != 1) {
+    e = p.D == 256   ? launch_mfma_any<256>(p, a, sl2, st)
+        : p.D == 128 ? launch_mfma_any<128>(p, a, sl2, st)
+                     : launch_mfma_any<64>(p, a, sl2, st);
+  } else if (p.paged || p.Tq != 1 || p.D > 128) {
     e = hipErrorInvalidValue;  // the planner sends these to the MFMA kernel
   } else if (p.dtype == FD_BF16) {
     e = p.D == 128 ? launch_valu<uint16_t, 128, 4>(p, a, sl2, st)
@@ -2105,12 +2144,16 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
   if (e != hipSuccess) return (int)e;
   if ((a.phases & kPhaseMerge) && p.combine && !p.fused) {
     if (p.dtype == FD_BF16) {
-      if (p.D == 128)
+      if (p.D == 256)
+        launch_combine<256, uint16_t>(p, a, st);
+      else if (p.D == 128)
         launch_combine<128, uint16_t>(p, a, st);
       else
         launch_combine<64, uint16_t>(p, a, st);
     } else {
-      if (p.D == 128)
+      if (p.D == 256)
+        launch_combine<256, float>(p, a, st);
+      else if (p.D == 128)
         launch_combine<128, float>(p, a, st);
       else
         launch_combine<64, float>(p, a, st);

@@ -107,7 +107,7 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
     return FD_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FD_ERR_INVALID_ARG;
   if (dtype != FD_BF16 && dtype != FD_F32) return FD_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return FD_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return FD_ERR_UNSUPPORTED;
   if (Hq / Hkv > kMaxHeadsPerKv) return FD_ERR_UNSUPPORTED;
   // Keys per sequence: chunk sizes, key offsets and lo + C stay in int.
   // (2^30 keys of one KV head at D = 128 are 256 GB, beyond any GPU's HBM.)
@@ -183,13 +183,15 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   // 83.5 / 85.8, G = 4 91.7 / 85.8; D = 64, G = 1: 1024 keys 6.6 / 7.2,
   // 4096 keys 8.8 / 8.7, 16k keys 15.9 / 15.6; G = 3 at 1024 keys 8.1 / 7.4.
   // Paged caches and several tokens run on the matrix cores only.
+  // Head dimension 256: the matrix cores only.
   if (requested_variant != FD_VARIANT_AUTO)
     q.variant = requested_variant;
   else
-    q.variant = dtype == FD_BF16 || general || q.G >= 3 ||
+    q.variant = dtype == FD_BF16 || general || q.G >= 3 || D > 128 ||
                         (D == 64 && Lmax >= 4096)
                     ? FD_VARIANT_MFMA
                     : FD_VARIANT_VALU;
+  if (q.variant == FD_VARIANT_VALU && D > 128) return FD_ERR_UNSUPPORTED;
   // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
   // registers; beyond 4 rows the matrix-core kernel is the one to use.  The
   // fp32 one serves up to 16.

@@ -101,7 +101,7 @@ def call_ex(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(Lmax=0), fd.FD_ERR_INVALID_ARG),
     (dict(Hq=12, Hkv=8), fd.FD_ERR_INVALID_ARG),
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
-    (dict(D=256), fd.FD_ERR_UNSUPPORTED),
+    (dict(D=512), fd.FD_ERR_UNSUPPORTED),
     (dict(dtype=7), fd.FD_ERR_UNSUPPORTED),
     (dict(Hq=258, Hkv=2), fd.FD_ERR_UNSUPPORTED),    # 129 heads per KV head
     (dict(Lmax=(1 << 30) + 1), fd.FD_ERR_UNSUPPORTED),   # above 2^30 keys
@@ -649,3 +649,19 @@ def test_partial_group_names_the_chunk_major_rows(lib, Hq, Hkv, dtype,
     p = fd.fd_plan(4, Hq, Hkv, 128, 65536, dtype, varlen=True,
                    variant=variant, num_cus=256)
     assert p["partial_group"] == P
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 2, 8, 32])
+def test_head_dim_256_runs_on_the_matrix_cores(lib, dtype, G):
+    # D = 256: the matrix-core kernels only, planned like D = 128 with
+    # rows twice as long (512 or 1024 bytes)
+    p = fd.fd_plan(2, 4 * G, 4, 256, 8192, dtype, num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
+    assert p["waves_per_block"] == 4
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(2, 4 * G, 4, 256, 8192, dtype, variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
+    pp = fd.fd_plan_ex(2, 2, 4 * G, 4, 256, 8192, dtype, paged=True,
+                       num_cus=256)
+    assert pp["variant"] == fd.FD_VARIANT_MFMA

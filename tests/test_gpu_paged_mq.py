@@ -89,6 +89,7 @@ PAGED_SHAPES = [
     (1, 4, 4, 64, 96, 16, [200]),                    # beyond capacity
     (1, 8, 1, 128, 9000, 16, [8999]),     # one chunk: > 32 tiles per wave
     (2, 64, 2, 128, 900, 32, [900, 450]),            # 32 per KV head
+    (2, 16, 2, 256, 700, 16, [700, 301]),            # head dim 256
 ]
 
 
@@ -188,6 +189,7 @@ PAGED_MQ_SHAPES = [
     (2, 3, 8, 8, 64, 640, 64, [641, 64]),
     (1, 16, 4, 4, 128, 9000, 48, [8999]),
     (2, 2, 64, 4, 128, 700, 32, [700, 33]),          # 16 x 2 rows
+    (2, 3, 8, 2, 256, 500, 32, [500, 97]),           # head dim 256
 ]
 
 
@@ -252,6 +254,7 @@ MQ_SHAPES = [
     (2, 2, 8, 1, 128, 640, [641, 64]),                # clamped; G = 8
     (2, 4, 32, 4, 128, 600, [600, 5]),                # 8 x 4 = 32 rows
     (1, 3, 48, 1, 64, 500, [500]),                    # 48 x 3 = 144 rows
+    (2, 2, 8, 2, 256, 400, [400, 37]),                # head dim 256
 ]
 
 

@@ -53,6 +53,15 @@ SMALL = {
         B=1, Hq=64, Hkv=1, D=128, Lmax=1000),
     "varlen_gqa24": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
         B=4, Hq=48, Hkv=2, Lmax=3000, varlen=(1, 3000)),
+    # head dimension 256 (matrix cores only)
+    "gqa8_d256": W["b1_gqa8_h64_d128_l65536"].with_(B=2, Hq=16, Hkv=2, D=256,
+                                                    Lmax=1700),
+    "mha_d256_varlen": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=3, Hq=4, Hkv=4, D=256, Lmax=2500, varlen=(1, 2500)),
+    "f32_gqa2_d256": W["tiny_mha_f32_b1_h8_d64_l1024"].with_(
+        B=2, Hq=4, Hkv=2, D=256, Lmax=900),
+    "gqa32_d256": W["b1_gqa8_h64_d128_l65536"].with_(B=1, Hq=32, Hkv=1, D=256,
+                                                     Lmax=700),
 }
 
 
@@ -92,8 +101,8 @@ def assert_parity(w, out, lse, ref_out, ref_lse, what=""):
 
 
 def variants_for(w):
-    if w.G > 16:
-        return [fd.FD_VARIANT_MFMA]      # virtual KV heads, matrix cores
+    if w.G > 16 or w.D > 128:
+        return [fd.FD_VARIANT_MFMA]      # matrix cores only
     if w.dtype == "f32":
         return [fd.FD_VARIANT_MFMA, fd.FD_VARIANT_VALU]
     if w.G <= 4:

@@ -58,6 +58,8 @@ def draw_case(i):
         dtype = "f32"        # without a draw: the other fields stay as they were
     if i % 17 == 5:
         G *= 4               # past 16 query rows per KV head, also without a draw
+    if i % 13 == 7:
+        D = 256              # head dimension 256, also without a draw
     return dict(kind=kind, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=Lmax,
                 dtype=dtype, seqlens=seqlens, Tq=Tq, splits=splits,
                 flags=flags, page=page, head_major=head_major, phi=phi,
@@ -156,7 +158,8 @@ def _run_case(torch, oracle_mod, i, c):
         # vector ALU in turn
         variant = ((fd.FD_VARIANT_AUTO, fd.FD_VARIANT_MFMA,
                     fd.FD_VARIANT_VALU)[(i // 6) % 3]
-                   if w.dtype == "f32" and w.G <= 16 else fd.FD_VARIANT_AUTO)
+                   if w.dtype == "f32" and w.G <= 16 and w.D <= 128
+                   else fd.FD_VARIANT_AUTO)
         print(f"[random {i}] variant {variant}", flush=True)
         out, lse = fd.fd_decode_ex(qd, to_dev(k), to_dev(v), sld, w.scale,
                                    num_splits=c["splits"], variant=variant,
