@@ -859,9 +859,10 @@ __device__ __forceinline__ TileOrder tile_order(const Work &w, int Hkv,
 // tiles it0 .. it0 + 31 (lane 2 j + h: half h of tile it0 + j), the index
 // of its D-element row of KV head g (of the pool's Hkv) in the pool:
 // (page * page_size + t) * Hkv + g token-major, (page * Hkv + g) *
-// page_size + t head-major, with t the key's place in its page.  Halves at or beyond the chunk end read
-// nothing and give 0; page indices are clamped into the pool, so no entry
-// of the table can make a load leave the K/V buffers.
+// page_size + t head-major, with t the key's place in its page.  Halves
+// at or beyond the chunk end read nothing and give 0; page indices are
+// clamped into the pool, so no entry of the table can make a load leave
+// the K/V buffers.
 __device__ __forceinline__ int page_rows(const PagedKV &pk, const Work &w,
                                          const TileOrder &ord, int Hkv, int g,
                                          int wave, int nw, int it0, int lane) {
@@ -1350,11 +1351,11 @@ void split_mfma_kernel(
 // faster than 32 contiguous bytes per lane.  Element j of accumulator block
 // e is then column n16, d = 64 (e / 4) + 4 (4 q4 + j) + e % 4, and the
 // bf16 kernel's end-of-chunk merge is shared with that column order
-// (acc_col with ROWS = 4).  P stays fp32 (no hi/lo split).  A wavefront works through its
-// tiles in 16-key halves (one MFMA k-slice of scores each) and keeps the
-// next half's K and V in flight while the current half computes: 16 KB of
-// K/V per half at D = 128, two halves of registers, where a whole second
-// 32-key tile would not fit.
+// (acc_col with ROWS = 4).  P stays fp32 (no hi/lo split).  A wavefront works
+// through its tiles in 16-key halves (one MFMA k-slice of scores each) and
+// keeps the next half's K and V in flight while the current half computes:
+// 16 KB of K/V per half at D = 128, two halves of registers, where a whole
+// second 32-key tile would not fit (D = 256 keeps one half of registers).
 __device__ __forceinline__ floatx4 load_stream_f4(const float *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
 }
@@ -1526,53 +1527,62 @@ __device__ __forceinline__ void f32_chunk_pass(
     auto compute_full = [&](F32Half<D> &h) {
       f32_half_compute<D, false>(h, 16, 16, q4, qf, scale_log2, acc, m, l);
     };
-    // two register sets taken in turn (a copy between them would wait for
-    // the loads in flight)
     F32Half<D> h0, h1;
-    load(0, h0);
-    int i = 0;
-    if constexpr (!CAUSAL) {
-      for (; i + 2 < nh; i += 2) {
-        load(i + 1, h1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h0);
-        load(i + 2, h0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h1);
-      }
-      if (i + 2 == nh) {
-        load(i + 1, h1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h0);
-        compute(i + 1, h1);
-      } else {
+    if constexpr (D > 128) {
+      // D = 256: one register set (a half is 32 KB of K/V); two spilled,
+      // and measured 21-27% slower than this loop
+      for (int i = 0; i < nh; ++i) {
+        load(i, h0);
         compute(i, h0);
       }
     } else {
-      // halves before the last three are never cut
-      for (; i + 3 < nh; i += 2) {
-        load(i + 1, h1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h0);
-        load(i + 2, h0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h1);
-      }
-      if (i + 3 == nh) {
-        load(i + 1, h1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_full(h0);
-        load(i + 2, h0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i + 1, h1);
-        compute(i + 2, h0);
-      } else if (i + 2 == nh) {
-        load(i + 1, h1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i, h0);
-        compute(i + 1, h1);
+      // two register sets taken in turn (a copy between them would wait for
+      // the loads in flight)
+      load(0, h0);
+      int i = 0;
+      if constexpr (!CAUSAL) {
+        for (; i + 2 < nh; i += 2) {
+          load(i + 1, h1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h0);
+          load(i + 2, h0);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h1);
+        }
+        if (i + 2 == nh) {
+          load(i + 1, h1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h0);
+          compute(i + 1, h1);
+        } else {
+          compute(i, h0);
+        }
       } else {
-        compute(i, h0);
+        // halves before the last three are never cut
+        for (; i + 3 < nh; i += 2) {
+          load(i + 1, h1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h0);
+          load(i + 2, h0);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h1);
+        }
+        if (i + 3 == nh) {
+          load(i + 1, h1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_full(h0);
+          load(i + 2, h0);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(i + 1, h1);
+          compute(i + 2, h0);
+        } else if (i + 2 == nh) {
+          load(i + 1, h1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(i, h0);
+          compute(i + 1, h1);
+        } else {
+          compute(i, h0);
+        }
       }
     }
   }
