@@ -4,7 +4,8 @@
  * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
  * smoke check and the benchmark's CPU-baseline leg may load this library.
  * It shares no source, header, table or helper with the GPU library; it
- * decodes bf16 itself and needs nothing but libc, libm and OpenMP.
+ * decodes bf16 and fp16 itself and needs nothing but libc, libm and
+ * OpenMP.
  *
  * What it computes.  "Flash-Decoding for long-context inference" (Dao,
  * Haziza, Massa, Sizov; Stanford CRFM blog), section "Multi-head attention
@@ -58,10 +59,39 @@
 
 #define FDO_BF16 0
 #define FDO_F32 1
+#define FDO_F16 2
 
 #define FDO_OK 0
 #define FDO_EINVAL -1
 #define FDO_ENOMEM -2
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 holds zero and the subnormals (fraction * 2^-24), exponent 31
+ * infinity (fraction 0) and NaN; otherwise the value is
+ * (1024 + fraction) * 2^(exponent - 25).  Every binary16 value is exact in
+ * a double. */
+static double half_to_double(uint16_t h)
+{
+    const int e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+static int dtype_ok(int dtype)
+{
+    return dtype == FDO_BF16 || dtype == FDO_F32 || dtype == FDO_F16;
+}
+
+static size_t elem_bytes(int dtype)
+{
+    return dtype == FDO_F32 ? 4 : 2;
+}
 
 /* bf16 is the top half of an IEEE binary32; widening is exact. */
 static double load_elem(const void *base, size_t idx, int dtype)
@@ -72,6 +102,8 @@ static double load_elem(const void *base, size_t idx, int dtype)
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dtype == FDO_F16)
+        return half_to_double(((const uint16_t *)base)[idx]);
     return (double)((const float *)base)[idx];
 }
 
@@ -142,7 +174,7 @@ static int check_dims(int B, int Hq, int Hkv, int D, int Lmax, int dtype)
         return FDO_EINVAL;
     if (Hq % Hkv != 0)
         return FDO_EINVAL;
-    if (dtype != FDO_BF16 && dtype != FDO_F32)
+    if (!dtype_ok(dtype))
         return FDO_EINVAL;
     return FDO_OK;
 }
@@ -197,7 +229,7 @@ int fdo_attend_row(const void *q_row, const void *k_slab, const void *v_slab,
                    int L, int D, double scale, int dtype, double *out,
                    double *lse)
 {
-    if (D <= 0 || L < 0 || (dtype != FDO_BF16 && dtype != FDO_F32))
+    if (D <= 0 || L < 0 || !dtype_ok(dtype))
         return FDO_EINVAL;
     double *scratch = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
     if (!scratch)
@@ -221,7 +253,7 @@ int fdo_attend_row_split(const void *q_row, const void *k_slab,
                          double *lse, double *part_out, double *part_lse)
 {
     if (D <= 0 || L < 0 || chunk <= 0 || nchunks <= 0 ||
-        (dtype != FDO_BF16 && dtype != FDO_F32))
+        !dtype_ok(dtype))
         return FDO_EINVAL;
     if ((long)chunk * nchunks < L)
         return FDO_EINVAL;
@@ -301,7 +333,7 @@ int fdo_decode_split(const void *q, const void *k, const void *v,
     const int G = Hq / Hkv;
     const int nchunks = (Lmax + chunk - 1) / chunk;
     const long rows = (long)B * Hq;
-    const size_t elem = dtype == FDO_BF16 ? 2 : 4;
+    const size_t elem = elem_bytes(dtype);
     int err = 0;
     if (nthreads <= 0)
         nthreads = omp_get_max_threads();

@@ -15,8 +15,8 @@ log-sum-exp per row and chunk, merge the chunks by their log-sum-exp).
 (the Flash-Decoding search-result page notes both cache layouts that differ
 between frameworks and decoding several query tokens at once).
 
-Arrays: bf16 tensors are passed as ``numpy.uint16`` bit patterns, fp32 as
-``numpy.float32``.  Shapes: q [B, Hq, D], k/v [B, Hkv, Lmax, D], seqlens
+Arrays: bf16 tensors are passed as ``numpy.uint16`` bit patterns, fp16 as
+``numpy.float16``, fp32 as ``numpy.float32``.  Shapes: q [B, Hq, D], k/v [B, Hkv, Lmax, D], seqlens
 int32 [B] or None.  Results are float64: out [B, Hq, D], lse [B, Hq].
 """
 from __future__ import annotations
@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libfdoracle.so")
 
 _BF16 = 0
 _F32 = 1
+_F16 = 2
 
 
 def _bind(path: str):
@@ -75,8 +76,10 @@ def _dtype_code(a: np.ndarray) -> int:
         return _BF16
     if a.dtype == np.float32:
         return _F32
+    if a.dtype == np.float16:
+        return _F16
     raise TypeError(
-        f"oracle takes uint16 (bf16 bits) or float32, not {a.dtype}")
+        f"oracle takes uint16 (bf16 bits), float16 or float32, not {a.dtype}")
 
 
 def _ptr(a):

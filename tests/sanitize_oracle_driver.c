@@ -99,6 +99,10 @@ int main(void) {
     expect("split out", max_diff(o1, o2, nq) < 1e-12);
     expect("split lse", max_diff(l1, l2, (size_t)B * Hq) < 1e-12);
   }
+  /* the same bits read as fp16 (finite values; the NaN padding too) */
+  expect("decode f16", fdo_decode(q, k, v, seqlens, B, Hq, Hkv, D, Lmax,
+                                  scale, 2, 2, o2, l2) == 0);
+  for (size_t i = 0; i < nq; ++i) expect("finite f16 out", isfinite(o2[i]));
   /* lengths beyond Lmax are clamped */
   const int32_t too_long[B] = {Lmax + 50, 37, 0};
   expect("clamped", fdo_decode(q, k, v, too_long, B, Hq, Hkv, D, Lmax, scale,

@@ -19,6 +19,12 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(
 
 # (name, text in fd_oracle.c, replacement); every occurrence is replaced.
 MUTANTS = [
+    ("f16_exponent_bias", "v = ldexp((double)(m | 0x400), e - 25);",
+     "v = ldexp((double)(m | 0x400), e - 24);"),
+    ("f16_subnormal_scale", "v = ldexp((double)m, -24);",
+     "v = ldexp((double)m, -25);"),
+    ("f16_implicit_bit_dropped", "v = ldexp((double)(m | 0x400), e - 25);",
+     "v = ldexp((double)m, e - 25);"),
     ("lse_in_base2", "*lse = m + log(l);", "*lse = m + log2(l);"),
     ("lse_without_max", "*lse = m + log(l);", "*lse = log(l);"),
     ("scale_dropped", "double s = scale * dot;", "double s = dot;"),
@@ -94,6 +100,7 @@ PINS = [
     (pins.test_paged_multiquery_equals_contiguous_after_scatter,
      (False, "f32")),
     (pins.test_multiquery_single_token_is_decode, ("bf16",)),
+    (pins.test_f16_decoding_matches_numpy_for_every_bit_pattern, ()),
     (pins.test_multiquery_single_token_is_decode, ("f32",)),
     (pins.test_multiquery_identical_keys_closed_form, ()),
     (pins.test_multiquery_query_never_sees_later_tokens, ()),

@@ -528,3 +528,53 @@ def test_oracle_snapshot_unchanged(oracle_mod):
                                rtol=0, atol=1e-14)
     np.testing.assert_allclose(lse.ravel(), [float(x) for x in doc["lse"]],
                                rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# fp16 caches
+
+
+def test_f16_decoding_matches_numpy_for_every_bit_pattern(oracle_mod):
+    # One key: the output is that key's V row exactly (weight 1), so a V row
+    # holding all 65536 binary16 patterns shows the oracle's decoder; numpy's
+    # float16 -> float64 conversion is the reference (NaN where it is NaN).
+    v = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(
+        np.float16)[None, :]
+    q = np.zeros((65536,), np.float16)
+    k = np.zeros((1, 65536), np.float16)
+    out, lse = oracle_mod.attend_row(q, k, v, 1, 1.0)
+    ref = v[0].astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan)
+    assert np.array_equal(out[~nan], ref[~nan])
+    assert lse == 0.0
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_f16_cache_equals_f32_cache_of_the_same_values(oracle_mod, paged):
+    # Every binary16 value is exact in binary32: the same values as an fp32
+    # cache must give the same result bit for bit (decode, paged rows,
+    # several tokens).
+    rng = np.random.default_rng(61)
+    B, Hq, Hkv, D, L = 3, 8, 2, 16, 140
+    q16 = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    k16 = (rng.standard_normal((B, Hkv, L, D)) * 2).astype(np.float16)
+    v16 = rng.standard_normal((B, Hkv, L, D)).astype(np.float16)
+    seq = np.array([140, 3, 77], np.int32)
+    q32, k32, v32 = (a.astype(np.float32) for a in (q16, k16, v16))
+    if paged:
+        kp16, vp16, bt = scatter_to_pages(k16, v16, seq, 32, rng)
+        kp32, vp32 = kp16.astype(np.float32), vp16.astype(np.float32)
+        o1, l1 = oracle_mod.decode_paged(q16, kp16, vp16, bt, seq, 0.3)
+        o2, l2 = oracle_mod.decode_paged(q32, kp32, vp32, bt, seq, 0.3)
+    else:
+        o1, l1 = oracle_mod.decode(q16, k16, v16, seq, 0.3)
+        o2, l2 = oracle_mod.decode(q32, k32, v32, seq, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    m1, n1 = oracle_mod.decode_multiquery(q16[:, None].repeat(2, 1), k16, v16,
+                                          seq, 0.3)
+    m2, n2 = oracle_mod.decode_multiquery(q32[:, None].repeat(2, 1), k32, v32,
+                                          seq, 0.3)
+    np.testing.assert_array_equal(m1, m2)
+    np.testing.assert_array_equal(n1, n2)
