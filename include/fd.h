@@ -40,12 +40,12 @@
  * NaN included).  Pointers must be 16-byte aligned device pointers.
  *
  * Supported: D in {64, 128, 256} (256: the matrix-core kernels only);
- * dtype FD_BF16 or FD_F32; 1 <= Hq/Hkv <= 128;
+ * dtype FD_BF16, FD_F16 or FD_F32; 1 <= Hq/Hkv <= 128;
  * Lmax <= 2^30 keys.  A KV head serves up to 16 query rows per workgroup
  * (the matrix cores' q-tile); a larger group runs as the fewest equal
  * groups that fit, each reading the KV head's rows again (so K/V bytes are
- * read that many times).  bf16 scores and outputs are accumulated in fp32;
- * the bf16 output is rounded to nearest even.
+ * read that many times).  bf16 and fp16 scores and outputs are accumulated
+ * in fp32; a 16-bit output is rounded to nearest even.
  *
  * Ownership.  The caller owns every buffer.  `stream` is a hipStream_t
  * passed as void* (NULL = the default stream).  The library keeps no
@@ -94,7 +94,8 @@ extern "C" {
 
 typedef enum fd_dtype {
     FD_BF16 = 0, /* bfloat16 q/k/v/out */
-    FD_F32 = 1   /* float32 q/k/v/out */
+    FD_F32 = 1,  /* float32 q/k/v/out */
+    FD_F16 = 2   /* IEEE binary16 q/k/v/out */
 } fd_dtype_t;
 
 enum {
@@ -139,9 +140,9 @@ enum {
 /* Kernel variant chosen for the per-chunk pass. */
 enum {
     FD_VARIANT_AUTO = 0,
-    FD_VARIANT_MFMA = 1, /* matrix-core pass, q group padded to 16 (bf16
-                            or fp32; paged and several tokens: always) */
-    FD_VARIANT_VALU = 2  /* vector-ALU pass (fp32, or bf16 small groups) */
+    FD_VARIANT_MFMA = 1, /* matrix-core pass, q group padded to 16 (any
+                            dtype; paged and several tokens: always) */
+    FD_VARIANT_VALU = 2  /* vector-ALU pass (fp32, or 16-bit small groups) */
 };
 
 /* What the planner decided for one problem shape (filled by fd_plan). */
@@ -215,10 +216,10 @@ FD_API int fd_decode(const void *q, const void *k_cache,
  *   num_splits  0 = planner's choice, else chunks per Lmax-long sequence
  *               (clamped to [1, ceil(Lmax / 32)]); 1 disables the merge.
  *   variant     FD_VARIANT_AUTO / _MFMA / _VALU.  AUTO: the matrix cores
- *               for bf16, and for fp32 from groups of 3 query heads (at
- *               D = 64 also smaller groups from Lmax = 4096); the vector
- *               ALU for the other fp32 shapes.  VALU takes bf16 groups of
- *               at most 4 heads only.
+ *               for bf16 and fp16, and for fp32 from groups of 3 query
+ *               heads (at D = 64 also smaller groups from Lmax = 4096);
+ *               the vector ALU for the other fp32 shapes.  VALU takes
+ *               16-bit groups of at most 4 heads only.
  *   flags       0 or FD_FLAG_FUSED_MERGE.
  *   workspace   device buffer of at least fd_workspace_bytes(...) bytes
  *               for the same arguments, 256-byte aligned, or NULL with
@@ -341,8 +342,9 @@ enum {
  * page_size * Hkv at most INT_MAX.  A table entry outside [0, num_pages)
  * is a caller error that the kernel clamps into that range (never a read
  * outside the pools).
- * FD_BF16 or FD_F32 (both on the matrix cores), 1 <= Tq <= 16; groups of
- * more than 16 query rows (Tq * Hq/Hkv) are split as for fd_decode.
+ * FD_BF16, FD_F16 or FD_F32 (all on the matrix cores), 1 <= Tq <= 16;
+ * groups of more than 16 query rows (Tq * Hq/Hkv) are split as for
+ * fd_decode.
  * num_splits, flags: as for fd_decode_ex (chunks per max_pages * page_size
  * tokens; FD_FLAG_FUSED_MERGE allowed).  workspace, workspace_bytes: as
  * for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D,
@@ -371,8 +373,8 @@ FD_API int fd_decode_paged(const void *q, const void *k_pages,
  * sees no key gets out = 0, lse = -inf.  Tq = 1 is fd_decode.
  * The keys a token must not see (j in [L - Tq + 1, L)) are still loaded
  * for the tile and weighted by exactly 0: their V rows must be finite.
- * FD_BF16 or FD_F32, 1 <= Tq <= 16.  The Tq * Hq/Hkv query rows of a KV
- * head share one 16-column matrix-core tile, or, when there are more, the
+ * FD_BF16, FD_F16 or FD_F32, 1 <= Tq <= 16.  The Tq * Hq/Hkv query rows of
+ * a KV head share one 16-column matrix-core tile, or, when there are more, the
  * fewest equal groups of them that fit (each reading the KV head's rows);
  * with Tq = 1 fp32 may run on the vector ALU, as in fd_decode.  num_splits, flags and the workspace
  * as for fd_decode_ex, sized by fd_plan_ex(B, Tq, Hq, Hkv, D, Lmax, dtype,
@@ -397,12 +399,14 @@ FD_API int fd_decode_multiquery(const void *q, const void *k_cache,
  * of a running maximum, so tiles need no cross-lane maximum and no
  * rescaling of their sums.  phi is in the units of lse (natural log of
  * the scaled score), chosen by the caller from the model's score range
- * (0 suits unit-variance scores).  Fallback: when some row of a chunk
- * has scores beyond phi +- 64 ln 2 (where 2^x would lose range), that
+ * (0 suits unit-variance scores).  Fallback: when the largest score of
+ * some row of a chunk lies beyond phi +- 64 ln 2 (bf16; fp16: phi +-
+ * 14 ln 2, where 2^x would overflow or lose precision), that
  * chunk is recomputed with the running maximum, giving exactly the
  * fd_decode_ex result for it; either way the result is the same
  * attention within the usual rounding.  Contiguous cache, one token per
- * sequence, bf16 only (FD_ERR_UNSUPPORTED otherwise).  phi must be finite.
+ * sequence, bf16 or fp16 only (FD_ERR_UNSUPPORTED otherwise).  phi must be
+ * finite.
  * num_splits, flags (FD_FLAG_FUSED_MERGE), workspace: as for
  * fd_decode_ex; plan with FD_FLAG_UNIFIED_MAX for the workspace size.
  */

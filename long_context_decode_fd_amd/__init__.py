@@ -9,7 +9,7 @@ seeded synthetic workloads used by the tests and the benchmark.
 """
 from ._binding import (FD_BF16, FD_ERR_CAPTURE, FD_ERR_HIP,  # noqa: F401
                        FD_ERR_INVALID_ARG, FD_ERR_TOO_LARGE,
-                       FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F32,
+                       FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_F16, FD_F32,
                        FD_FLAG_FUSED_MERGE, FD_FLAG_PARTIALS,
                        FD_FLAG_UNIFIED_MAX, FD_MERGE_FUSED,
                        FD_MERGE_NONE,

@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("FD_LIBRARY") or os.path.join(_PKG, "libfd.so")
 
 FD_BF16 = 0
 FD_F32 = 1
+FD_F16 = 2
 FD_OK = 0
 FD_ERR_INVALID_ARG = -1
 FD_ERR_UNSUPPORTED = -2
@@ -136,11 +137,15 @@ def _dtype_code(dtype) -> int:
         return FD_BF16
     if dtype in (FD_F32, "f32", "fp32", "float32"):
         return FD_F32
+    if dtype in (FD_F16, "f16", "fp16", "float16"):
+        return FD_F16
     import torch
     if dtype == torch.bfloat16:
         return FD_BF16
     if dtype == torch.float32:
         return FD_F32
+    if dtype == torch.float16:
+        return FD_F16
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
@@ -180,8 +185,8 @@ def fd_workspace_bytes(B, Hq, Hkv, D, Lmax, dtype, varlen=False,
 
 def _check(q, k_cache, v_cache, seqlens, out, lse, need_out=True):
     import torch
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q/k/v must be bfloat16 or float32 tensors")
+    if q.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16, float16 or float32 tensors")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
@@ -299,7 +304,7 @@ def fd_decode_ex(q, k_cache, v_cache, seqlens, scale, out=None, lse=None,
                  workspace=None, stream=None):
     """out, lse = attention(q, k_cache, v_cache) -- see fd.h.
 
-    q [B,Hq,D], k_cache/v_cache [B,Hkv,Lmax,D] (bf16 or fp32, on the GPU),
+    q [B,Hq,D], k_cache/v_cache [B,Hkv,Lmax,D] (bf16, fp16 or fp32, on the GPU),
     seqlens int32 [B] on the GPU or None, scale a float.  Returns (out, lse);
     out/lse are allocated if not given.  workspace: a zero-filled uint8
     device tensor of at least fd_workspace_bytes(...) bytes (see fd.h for
@@ -404,7 +409,8 @@ def fd_merge_partials(seqlens, B, Hq, Hkv, D, Lmax, dtype, workspace, out,
                       stream=None):
     """Merge phase only: out/lse from the partials in `workspace`."""
     import torch
-    tdt = torch.bfloat16 if _dtype_code(dtype) == FD_BF16 else torch.float32
+    tdt = {FD_BF16: torch.bfloat16, FD_F16: torch.float16,
+           FD_F32: torch.float32}[_dtype_code(dtype)]
     if (out.shape != (B, Hq, D) or out.dtype != tdt or not out.is_cuda
             or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [B,Hq,D] device tensor")

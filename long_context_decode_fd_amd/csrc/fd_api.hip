@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 20100;  // 2.1.0
+constexpr int kVersion = 20200;  // 2.2.0
 
 bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;

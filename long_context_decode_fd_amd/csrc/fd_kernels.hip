@@ -53,6 +53,7 @@ namespace fd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -294,6 +295,45 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float x) {
 template <>
 __device__ __forceinline__ void store_out<float>(float *p, float x) {
   *p = x;
+}
+template <>
+__device__ __forceinline__ void store_out<_Float16>(_Float16 *p, float x) {
+  *p = (_Float16)x;  // round to nearest even
+}
+
+// Bit pattern of a 16-bit output element: bf16 bits (uint16_t) or fp16.
+template <typename T>
+__device__ __forceinline__ uint32_t bits16(float x);
+template <>
+__device__ __forceinline__ uint32_t bits16<uint16_t>(float x) {
+  return to_bf16_bits(x);
+}
+template <>
+__device__ __forceinline__ uint32_t bits16<_Float16>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// The 16-bit element types of the matrix-core pass, E = __bf16 or
+// _Float16 (IEEE binary16): the 8-element operand vector of one
+// v_mfma_f32_16x16x32 lane and the output element (bf16 outputs are kept
+// as their bit patterns).
+template <typename E>
+struct E16;
+template <>
+struct E16<__bf16> {
+  typedef bf16x8 vec;
+  typedef uint16_t out;
+};
+template <>
+struct E16<_Float16> {
+  typedef f16x8 vec;
+  typedef _Float16 out;
+};
+__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma32(f16x8 a, f16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -713,23 +753,24 @@ __device__ __forceinline__ void tile_load_v(
   }
 }
 
-template <int D, bool TAIL, bool UNI, bool PAGED_ROWS>
+template <int D, bool TAIL, bool UNI, bool PAGED_ROWS, typename E>
 __device__ __forceinline__ void tile_compute(
     const uint4 (&kr)[2][D / 32], typename VecOf<D / 16>::type (&vr)[8],
-    int valid, int lim, int n16, int q4, const bf16x8 (&qop)[D / 32],
+    int valid, int lim, int n16, int q4,
+    const typename E16<E>::vec (&qop)[D / 32],
     float scale_log2, float phi2, floatx4 (&acc)[D / 16], float &m,
     float &l) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   typedef typename VecOf<VW>::type VT;
+  typedef typename E16<E>::vec EV;
   floatx4 sc[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     sc[sub] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, kr[sub][kk]), qop[kk], sc[sub], 0, 0, 0);
+      sc[sub] = mfma32(__builtin_bit_cast(EV, kr[sub][kk]), qop[kk], sc[sub]);
   }
 
   float s[8];
@@ -755,16 +796,17 @@ __device__ __forceinline__ void tile_compute(
     alpha = exp2_f(m - mref);
   }
 
-  // P enters the matrix cores as an exact-to-2^-17 pair of bf16 operands
-  // (hi = bf16(p), lo = bf16(p - hi)); the running sum uses fp32 p.
-  bf16x8 p_hi, p_lo;
+  // P enters the matrix cores as a pair of operands of the cache's 16-bit
+  // type (hi = E(p), lo = E(p - hi); exact to 2^-17 in bf16); the running
+  // sum uses fp32 p.
+  EV p_hi, p_lo;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float p = exp2_f(s[i] - mref);
-    const __bf16 hi = (__bf16)p;
+    const E hi = (E)p;
     p_hi[i] = hi;
-    p_lo[i] = (__bf16)(p - (float)hi);
+    p_lo[i] = (E)(p - (float)hi);
     psum += p;
   }
   m = mn;
@@ -786,7 +828,7 @@ __device__ __forceinline__ void tile_compute(
   // here lets the exponentials overlap the V loads, as the contiguous loop
   // does by itself.
   if constexpr (PAGED_ROWS || UNI) __builtin_amdgcn_sched_barrier(0);
-  bf16x8 vt[VW];
+  EV vt[VW];
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -799,16 +841,12 @@ __device__ __forceinline__ void tile_compute(
                                 dword_of<VW>(vr[4], e >> 1), sel);
     t.w = __builtin_amdgcn_perm(dword_of<VW>(vr[7], e >> 1),
                                 dword_of<VW>(vr[6], e >> 1), sel);
-    vt[e] = __builtin_bit_cast(bf16x8, t);
+    vt[e] = __builtin_bit_cast(EV, t);
   }
 #pragma unroll
-  for (int e = 0; e < VW; ++e)
-    acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], p_hi, acc[e], 0,
-                                                     0, 0);
+  for (int e = 0; e < VW; ++e) acc[e] = mfma32(vt[e], p_hi, acc[e]);
 #pragma unroll
-  for (int e = 0; e < VW; ++e)
-    acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], p_lo, acc[e], 0,
-                                                     0, 0);
+  for (int e = 0; e < VW; ++e) acc[e] = mfma32(vt[e], p_lo, acc[e]);
 }
 
 // Order of a chunk's tiles.  When every KV slab starts at the same offset
@@ -976,12 +1014,13 @@ constexpr int kBlocksPerCU = NW >= 8 || D > 128 ? 1 : 2;
 // apart) cut into the chunk's last two tiles only, which with two or more
 // wavefronts are both some wavefront's last.  Loads clamp rows to the valid
 // count without branching.
-template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E>
 __device__ __forceinline__ void chunk_tiles(
     const Work &w, const PagedKV &pk, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, size_t slab, size_t prs, int Hkv,
     int hkv_kv, int g_kv, int hi_all, int hi_col, int wave, int lane,
-    int n16, int q4, const bf16x8 (&qop)[D / 32], float scale_log2,
+    int n16, int q4, const typename E16<E>::vec (&qop)[D / 32],
+    float scale_log2,
     float phi2, floatx4 (&acc)[D / 16], float &m, float &l, uint16_t *kbuf,
     bool rotate) {
   static_assert(NW >= 2, "the loop relies on two or more wavefronts");
@@ -1012,7 +1051,7 @@ __device__ __forceinline__ void chunk_tiles(
       load_k_rows(nxt, min(kKeyTile, w.hi - kn0), lane, kn);
       __builtin_amdgcn_sched_barrier(0);
       load_k_operand(kbuf, n16, q4, kr);
-      tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+      tile_compute<D, false, UNI, PAGED, E>(kr, vr, kKeyTile, kKeyTile, n16, q4,
                                          qop, scale_log2, phi2, acc, m, l);
       cur = nxt;
     }
@@ -1024,10 +1063,10 @@ __device__ __forceinline__ void chunk_tiles(
     tile_load_v<D, true>(cur, valid, n16, q4, vr);
     load_k_operand(kbuf, n16, q4, kr);
     if (full)
-      tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+      tile_compute<D, false, UNI, PAGED, E>(kr, vr, kKeyTile, kKeyTile, n16, q4,
                                          qop, scale_log2, phi2, acc, m, l);
     else
-      tile_compute<D, true, UNI, PAGED>(kr, vr, valid,
+      tile_compute<D, true, UNI, PAGED, E>(kr, vr, valid,
                                         CAUSAL ? hi_col - k0 : valid, n16, q4,
                                         qop, scale_log2, phi2, acc, m, l);
     return;
@@ -1051,7 +1090,7 @@ __device__ __forceinline__ void chunk_tiles(
     uint4 kn[2][D / 32];
     tile_load_k<D, true>(nxt, min(kKeyTile, w.hi - kn0), n16, q4, kn);
     __builtin_amdgcn_sched_barrier(0);
-    tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+    tile_compute<D, false, UNI, PAGED, E>(kr, vr, kKeyTile, kKeyTile, n16, q4,
                                        qop, scale_log2, phi2, acc, m, l);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -1065,20 +1104,24 @@ __device__ __forceinline__ void chunk_tiles(
   typename VecOf<D / 16>::type vr[8];
   tile_load_v<D, true>(cur, valid, n16, q4, vr);
   if (full)
-    tile_compute<D, false, UNI, PAGED>(kr, vr, kKeyTile, kKeyTile, n16, q4,
+    tile_compute<D, false, UNI, PAGED, E>(kr, vr, kKeyTile, kKeyTile, n16, q4,
                                        qop, scale_log2, phi2, acc, m, l);
   else
-    tile_compute<D, true, UNI, PAGED>(kr, vr, valid,
+    tile_compute<D, true, UNI, PAGED, E>(kr, vr, valid,
                                       CAUSAL ? hi_col - k0 : valid, n16, q4,
                                       qop, scale_log2, phi2, acc, m, l);
 }
 
 // Unified maximum: a chunk column whose largest score - phi lies outside
-// +-kUniRange (log2 units) is recomputed exactly.  Inside it, 2^x neither
-// overflows (sums of up to 2^31 terms of at most 2^64) nor loses the
-// terms that matter (the largest is at least 2^-64, far above fp32's
-// smallest normal).
+// +-kUniRange<E> (log2 units) is recomputed exactly.  Inside it, 2^x
+// neither overflows nor loses the terms that matter.  bf16 (fp32's
+// exponent range): sums of up to 2^31 terms of at most 2^64, and the
+// largest term at least 2^-64.  fp16, whose P operands stop at 65504 and
+// whose normals start at 2^-14: the largest term lies in [2^-14, 2^14].
+template <typename E>
 constexpr float kUniRange = 64.f;
+template <>
+constexpr float kUniRange<_Float16> = 14.f;
 
 // End of a chunk in the matrix-core kernel (direct and partial modes): the
 // wavefronts' states are merged with one weight per (wavefront, column).
@@ -1088,8 +1131,8 @@ constexpr float kUniRange = 64.f;
 // 2^(m - M) / W, adds the weighted accumulators in wavefront order and
 // stores its lane's runs of four consecutive output columns,
 // acc_col(4 e4, 4 q4 + j), with vector stores.  A column that saw no key
-// gets out 0 and lse -inf.  OutT: uint16_t (bf16 bits, rounded to nearest
-// even) or float.  ROWS: the accumulator layout (acc_col); with any of
+// gets out 0 and lse -inf.  OutT: uint16_t (bf16 bits), _Float16 (both
+// rounded to nearest even) or float.  ROWS: the accumulator layout (acc_col); with any of
 // them a lane's blocks 4 e4 .. 4 e4 + 3 of one j are four consecutive
 // columns.
 template <int D, int NW, typename OutT = uint16_t, int ROWS = 0>
@@ -1155,10 +1198,8 @@ __device__ __forceinline__ void wave_merge_store(
       if (mode == kModeDirect) {
         if constexpr (sizeof(OutT) == 2) {
           uint2 bits;
-          bits.x = (uint32_t)to_bf16_bits(o.x) |
-                   ((uint32_t)to_bf16_bits(o.y) << 16);
-          bits.y = (uint32_t)to_bf16_bits(o.z) |
-                   ((uint32_t)to_bf16_bits(o.w) << 16);
+          bits.x = bits16<OutT>(o.x) | (bits16<OutT>(o.y) << 16);
+          bits.y = bits16<OutT>(o.z) | (bits16<OutT>(o.w) << 16);
           *reinterpret_cast<uint2 *>(out + row * D + d0) = bits;
         } else {
           *reinterpret_cast<float4 *>(out + row * D + d0) = o;
@@ -1184,13 +1225,13 @@ __device__ __forceinline__ void wave_merge_store(
 // before).
 // UNI: unified-maximum softmax against phi2 (log2 units of the scaled
 // score) with an exact fallback.
-template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E>
 __device__ __forceinline__ void chunk_pass(
     const Work &w, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
     PagedKV pk, int B, int Hq, int Hkv, int kv_rep, int G, int Tq, int Lmax,
     int C, int S, float scale_log2, float phi2, int mode, bool chunk_major,
-    uint16_t *__restrict__ out, float *__restrict__ lse,
+    typename E16<E>::out *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part,
     int *__restrict__ tickets) {
   constexpr int KK = D / 32;
@@ -1209,7 +1250,8 @@ __device__ __forceinline__ void chunk_pass(
   const int n16 = lane & 15, q4 = lane >> 4;
   const int ncol = G * Tq;
 
-  bf16x8 qop[KK];
+  typedef typename E16<E>::out OutT;
+  typename E16<E>::vec qop[KK];
   {
     const bool live = n16 < ncol;
     const uint16_t *qr = q + row_of(w, G, Hq, Tq, live ? n16 : 0) * D + q4 * 8;
@@ -1217,7 +1259,7 @@ __device__ __forceinline__ void chunk_pass(
     for (int kk = 0; kk < KK; ++kk) {
       uint4 t = live ? *reinterpret_cast<const uint4 *>(qr + kk * 32)
                      : make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(bf16x8, t);
+      qop[kk] = __builtin_bit_cast(typename E16<E>::vec, t);
     }
   }
   // Causal limit among the Tq new tokens (the newest Tq keys of the
@@ -1245,25 +1287,26 @@ __device__ __forceinline__ void chunk_pass(
     // column's largest x = score - phi2 leaves [-kUniRange, kUniRange] the
     // fixed reference risks overflow or lost precision, and the whole
     // workgroup recomputes the chunk with the running maximum.
-    chunk_tiles<D, NW, PAGED, CAUSAL, true>(
+    chunk_tiles<D, NW, PAGED, CAUSAL, true, E>(
         w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
         lane, n16, q4, qop, scale_log2, phi2, acc, m, l, kbuf, rotate);
     float xm = fmaxf(m, __shfl_xor(m, 16, 64));
     xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
-    const bool bad = xm != FD_NEG_INF && !(xm >= -kUniRange && xm <= kUniRange);
+    const bool bad = xm != FD_NEG_INF &&
+                     !(xm >= -kUniRange<E> && xm <= kUniRange<E>);
     if (__syncthreads_or(bad)) {
 #pragma unroll
       for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
       m = FD_NEG_INF;
       l = 0.f;
-      chunk_tiles<D, NW, PAGED, CAUSAL, false>(
+      chunk_tiles<D, NW, PAGED, CAUSAL, false, E>(
           w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
           lane, n16, q4, qop, scale_log2, 0.f, acc, m, l, kbuf, rotate);
     } else {
       m = xm == FD_NEG_INF ? FD_NEG_INF : phi2;
     }
   } else {
-    chunk_tiles<D, NW, PAGED, CAUSAL, false>(
+    chunk_tiles<D, NW, PAGED, CAUSAL, false, E>(
         w, pk, kc, vc, slab, prs, Hkv, hkv_kv, g_kv, hi_all, hi_col, wave,
         lane, n16, q4, qop, scale_log2, 0.f, acc, m, l, kbuf, rotate);
   }
@@ -1271,7 +1314,7 @@ __device__ __forceinline__ void chunk_pass(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (mode != kModeFused) {
-    wave_merge_store<D, NW, uint16_t, kBf16Rows<D>>(
+    wave_merge_store<D, NW, OutT, kBf16Rows<D>>(
         sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l, acc, w, pl, mode,
         out, lse, o_part, lse_part);
     return;
@@ -1289,14 +1332,14 @@ __device__ __forceinline__ void chunk_pass(
         o[acc_col<VW, kBf16Rows<D>>(e, q4 * 4 + j)] = acc[e][j];
   }
   __syncthreads();
-  merge_and_store<D, uint16_t>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out,
+  merge_and_store<D, OutT>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out,
                                lse, o_part, lse_part);
   if (mode == kModeFused)
-    merge_group_if_last<D, uint16_t>(w, pl, o_part, lse_part, tickets, out,
+    merge_group_if_last<D, OutT>(w, pl, o_part, lse_part, tickets, out,
                                      lse, sm_o, &sm_flag);
 }
 
-template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E>
 __global__ __launch_bounds__(NW * 64, (kBlocksPerCU<NW, D>))
 void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
@@ -1304,7 +1347,7 @@ void split_mfma_kernel(
     PagedKV pk, int B, int Hq, int Hkv, int kv_rep, int G, int Tq, int Lmax,
     int C, int S, float scale_log2, float phi2, int mode, bool direct,
     bool chunk_major,
-    uint16_t *__restrict__ out,
+    typename E16<E>::out *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ o_part,
     float *__restrict__ lse_part, int *__restrict__ tickets) {
   // With per-sequence lengths the grid can be as small as half the work
@@ -1314,7 +1357,7 @@ void split_mfma_kernel(
   // spills.)
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
-  chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w0, q, kc, vc, seqlens, pk, B, Hq,
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E>(w0, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, kv_rep, G, Tq, Lmax, C, S,
                                         scale_log2, phi2, mode, chunk_major,
                                         out, lse, o_part, lse_part, tickets);
@@ -1327,7 +1370,7 @@ void split_mfma_kernel(
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
-  chunk_pass<D, NW, PAGED, CAUSAL, UNI>(w1, q, kc, vc, seqlens, pk, B, Hq,
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E>(w1, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, kv_rep, G, Tq, Lmax, C, S,
                                         scale_log2, phi2, mode, chunk_major,
                                         out, lse, o_part, lse_part, tickets);
@@ -1679,6 +1722,16 @@ struct Elem<uint16_t> {
     }
   }
 };
+template <>
+struct Elem<_Float16> {
+  static constexpr int kPerLane = 8;
+  __device__ static void load(const _Float16 *p, float (&x)[8]) {
+    const f16x8 t = __builtin_bit_cast(
+        f16x8, load_stream(reinterpret_cast<const uint4 *>(p)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)t[i];
+  }
+};
 
 template <typename T, int D, int NW, int GT>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(
@@ -2020,19 +2073,21 @@ hipError_t launch_valu(const Plan &p, const LaunchArgs &a, float sl2,
   return hipSuccess;
 }
 
-template <int D, bool PAGED, bool CAUSAL, bool UNI = false>
+template <int D, bool PAGED, bool CAUSAL, bool UNI, typename E>
 hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
                        hipStream_t st) {
+  typedef typename E16<E>::out OutT;
   const float phi2 = a.unified_max * kLog2e;
   const dim3 grid(p.grid);
   const int part = mode_of(p);
   const uint16_t *q = static_cast<const uint16_t *>(a.q);
   const uint16_t *k = static_cast<const uint16_t *>(a.k);
   const uint16_t *v = static_cast<const uint16_t *>(a.v);
-  uint16_t *out = static_cast<uint16_t *>(a.out);
+  OutT *out = static_cast<OutT *>(a.out);
 #define FD_MFMA_CASE(NWV)                                                    \
   case NWV:                                                                  \
-    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI>), grid,\
+    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI, E>),   \
+                       grid,                                                 \
                        dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
                        p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax,        \
                        p.chunk, p.splits, sl2, phi2, part, p.direct,         \
@@ -2077,14 +2132,28 @@ hipError_t launch_mfma_f32_any(const Plan &p, const LaunchArgs &a, float sl2,
                            : launch_mfma_f32<D, false, false>(p, a, sl2, st));
 }
 
-template <int D>
+template <int D, typename E>
 hipError_t launch_mfma_any(const Plan &p, const LaunchArgs &a, float sl2,
                            hipStream_t st) {
   const bool causal = p.Tq > 1;
-  return p.paged ? (causal ? launch_mfma<D, true, true>(p, a, sl2, st)
-                           : launch_mfma<D, true, false>(p, a, sl2, st))
-                 : (causal ? launch_mfma<D, false, true>(p, a, sl2, st)
-                           : launch_mfma<D, false, false>(p, a, sl2, st));
+  if (p.unified)  // the planner allows it for contiguous single-token calls
+    return p.paged || causal
+               ? hipErrorInvalidValue
+               : launch_mfma<D, false, false, true, E>(p, a, sl2, st);
+  return p.paged
+             ? (causal ? launch_mfma<D, true, true, false, E>(p, a, sl2, st)
+                       : launch_mfma<D, true, false, false, E>(p, a, sl2, st))
+             : (causal
+                    ? launch_mfma<D, false, true, false, E>(p, a, sl2, st)
+                    : launch_mfma<D, false, false, false, E>(p, a, sl2, st));
+}
+
+template <typename E>
+hipError_t launch_mfma_16(const Plan &p, const LaunchArgs &a, float sl2,
+                          hipStream_t st) {
+  return p.D == 256   ? launch_mfma_any<256, E>(p, a, sl2, st)
+         : p.D == 128 ? launch_mfma_any<128, E>(p, a, sl2, st)
+                      : launch_mfma_any<64, E>(p, a, sl2, st);
 }
 
 template <int D, typename OutT>
@@ -2130,21 +2199,17 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
         : p.D == 256 ? launch_mfma_f32_any<256>(p, a, sl2, st)
         : p.D == 128 ? launch_mfma_f32_any<128>(p, a, sl2, st)
                      : launch_mfma_f32_any<64>(p, a, sl2, st);
-  } else if (p.variant == FD_VARIANT_MFMA && p.unified) {
-    // the planner allows the unified maximum for contiguous single-token
-    // decode only
-    e = p.D == 256   ? launch_mfma<256, false, false, true>(p, a, sl2, st)
-        : p.D == 128 ? launch_mfma<128, false, false, true>(p, a, sl2, st)
-                     : launch_mfma<64, false, false, true>(p, a, sl2, st);
   } else if (p.variant == FD_VARIANT_MFMA) {
-    e = p.D == 256   ? launch_mfma_any<256>(p, a, sl2, st)
-        : p.D == 128 ? launch_mfma_any<128>(p, a, sl2, st)
-                     : launch_mfma_any<64>(p, a, sl2, st);
+    e = p.dtype == FD_F16 ? launch_mfma_16<_Float16>(p, a, sl2, st)
+                          : launch_mfma_16<__bf16>(p, a, sl2, st);
   } else if (p.paged || p.Tq != 1 || p.D > 128) {
     e = hipErrorInvalidValue;  // the planner sends these to the MFMA kernel
   } else if (p.dtype == FD_BF16) {
     e = p.D == 128 ? launch_valu<uint16_t, 128, 4>(p, a, sl2, st)
                    : launch_valu<uint16_t, 64, 4>(p, a, sl2, st);
+  } else if (p.dtype == FD_F16) {
+    e = p.D == 128 ? launch_valu<_Float16, 128, 4>(p, a, sl2, st)
+                   : launch_valu<_Float16, 64, 4>(p, a, sl2, st);
   } else {
     e = p.D == 128 ? launch_valu<float, 128, 4>(p, a, sl2, st)
                    : launch_valu<float, 64, 4>(p, a, sl2, st);
@@ -2160,6 +2225,13 @@ int launch_decode(const Plan &p, const LaunchArgs &a) {
         launch_combine<128, uint16_t>(p, a, st);
       else
         launch_combine<64, uint16_t>(p, a, st);
+    } else if (p.dtype == FD_F16) {
+      if (p.D == 256)
+        launch_combine<256, _Float16>(p, a, st);
+      else if (p.D == 128)
+        launch_combine<128, _Float16>(p, a, st);
+      else
+        launch_combine<64, _Float16>(p, a, st);
     } else {
       if (p.D == 256)
         launch_combine<256, float>(p, a, st);

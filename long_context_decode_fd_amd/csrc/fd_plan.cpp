@@ -106,7 +106,8 @@ int validate_shape(int B, int Hq, int Hkv, int D, int Lmax,
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Lmax <= 0)
     return FD_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FD_ERR_INVALID_ARG;
-  if (dtype != FD_BF16 && dtype != FD_F32) return FD_ERR_UNSUPPORTED;
+  if (dtype != FD_BF16 && dtype != FD_F16 && dtype != FD_F32)
+    return FD_ERR_UNSUPPORTED;
   if (D != 64 && D != 128 && D != 256) return FD_ERR_UNSUPPORTED;
   if (Hq / Hkv > kMaxHeadsPerKv) return FD_ERR_UNSUPPORTED;
   // Keys per sequence: chunk sizes, key offsets and lo + C stay in int.
@@ -151,10 +152,10 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
       requested_variant > FD_VARIANT_VALU)
     return FD_ERR_INVALID_ARG;
   if (flags & ~kKnownFlags) return FD_ERR_INVALID_ARG;
-  // The unified maximum (FlashDecoding++) is built for the bf16
-  // matrix-core pass over a contiguous cache, one token per sequence.
+  // The unified maximum (FlashDecoding++) is built for the 16-bit (bf16 or
+  // fp16) matrix-core pass over a contiguous cache, one token per sequence.
   const bool unified = flags & FD_FLAG_UNIFIED_MAX;
-  if (unified && (dtype != FD_BF16 || general ||
+  if (unified && (dtype == FD_F32 || general ||
                   requested_variant == FD_VARIANT_VALU))
     return FD_ERR_UNSUPPORTED;
 
@@ -172,7 +173,8 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   q.unified = unified;
   q.num_cus = num_cus;
 
-  // Kernel variant: bf16 on the matrix cores.  fp32 on the matrix cores too
+  // Kernel variant: bf16 and fp16 on the matrix cores.  fp32 on the matrix
+  // cores too
   // from groups of 3 query heads (and, at D = 64, for smaller groups from
   // 4096 keys on); below that on the vector ALU, whose cost per key grows
   // with G while the fp32 MFMA pass pays for 16 columns at any G.  Measured
@@ -187,15 +189,15 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
   if (requested_variant != FD_VARIANT_AUTO)
     q.variant = requested_variant;
   else
-    q.variant = dtype == FD_BF16 || general || q.G >= 3 || D > 128 ||
+    q.variant = dtype != FD_F32 || general || q.G >= 3 || D > 128 ||
                         (D == 64 && Lmax >= 4096)
                     ? FD_VARIANT_MFMA
                     : FD_VARIANT_VALU;
   if (q.variant == FD_VARIANT_VALU && D > 128) return FD_ERR_UNSUPPORTED;
-  // The bf16 vector-ALU kernel keeps G query rows of 8 values per lane in
+  // The 16-bit vector-ALU kernel keeps G query rows of 8 values per lane in
   // registers; beyond 4 rows the matrix-core kernel is the one to use.  The
   // fp32 one serves up to 16.
-  if (q.variant == FD_VARIANT_VALU && dtype == FD_BF16 && q.G > 4)
+  if (q.variant == FD_VARIANT_VALU && dtype != FD_F32 && q.G > 4)
     return FD_ERR_UNSUPPORTED;
   if (q.variant == FD_VARIANT_VALU && q.G > kMaxGroup)
     return FD_ERR_UNSUPPORTED;
@@ -273,7 +275,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int Lmax, fd_dtype_t dtype,
     // products (measured, fp32, 256 keys: 16 query heads on one KV head,
     // D = 64, 53 us unsplit against 17 in 8 chunks; 8 heads, D = 128,
     // 2 sequences, 11.2 against 7.1).
-    const int elem = dtype == FD_BF16 ? 2 : 4;
+    const int elem = dtype == FD_F32 ? 4 : 2;
     const int gain =
         kSplitGain * 256 / (D * elem) / (mfma ? 1 : q.G);
     if (Lmax - chunk <= gain) {

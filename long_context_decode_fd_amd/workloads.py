@@ -24,12 +24,15 @@ Recipe (every stream is an independent PCG64 seeded from
 * V[b, g]     spawn_key (2, b, g)   standard normal float32 rows [0, L_b)
 * peaks[b, g] spawn_key (3, b, g)   ceil(frac * L_b) distinct rows of K
                                      multiplied by ``peak_mult`` (exact)
-* rows >= L_b of a padded slab hold NaN (bf16 0xFFFF, fp32 0xFFFFFFFF) so
+* rows >= L_b of a padded slab hold NaN (bf16 and fp16 0xFFFF, fp32
+  0xFFFFFFFF) so
   that a kernel reading past the valid prefix is caught; so do the unused
   rows of a sequence's last page and every spare page of a paged pool.
 
 bf16 values are produced by rounding float32 to nearest-even on the bit
-pattern and are handled as ``numpy.uint16`` arrays throughout.
+pattern and are handled as ``numpy.uint16`` arrays throughout; fp16 values
+are numpy's own float32 -> float16 conversion (nearest-even) and are
+handled as ``numpy.float16`` arrays.
 """
 from __future__ import annotations
 
@@ -53,7 +56,7 @@ class Workload:
     Hkv: int
     D: int
     Lmax: int
-    dtype: str            # "bf16" or "f32"
+    dtype: str            # "bf16", "f16" or "f32"
     seed: int
     peak_frac: float = 0.0
     peak_mult: float = 8.0
@@ -73,11 +76,12 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return 4 if self.dtype == "f32" else 2
 
     @property
     def np_dtype(self):
-        return np.uint16 if self.dtype == "bf16" else np.float32
+        return {"bf16": np.uint16, "f16": np.float16,
+                "f32": np.float32}[self.dtype]
 
     @property
     def max_pages(self) -> int:
@@ -147,6 +151,12 @@ EXTRA_WORKLOADS = {
         WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
             name="f32_b1_gqa8_h64_d128_l65536", dtype="f32",
             note="the batch-1 64k shape with an fp32 cache"),
+        WORKLOADS["b1_gqa8_h64_d128_l65536"].with_(
+            name="f16_b1_gqa8_h64_d128_l65536", dtype="f16",
+            note="the batch-1 64k shape with an fp16 cache"),
+        WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+            name="f16_varlen_b16_gqa8_h64_d128_lmax131072", dtype="f16",
+            note="the variable-length batch with an fp16 cache"),
     ]
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
@@ -173,7 +183,9 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _encode(x32: np.ndarray, dtype: str) -> np.ndarray:
-    return bf16_bits(x32) if dtype == "bf16" else x32.astype(np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x32)
+    return x32.astype(np.float16 if dtype == "f16" else np.float32)
 
 
 def gen_seqlens(w: Workload) -> np.ndarray | None:
@@ -264,9 +276,9 @@ def fill_slab(w: Workload, b: int, g: int, L: int, k_out: np.ndarray,
     assert k_out.shape == (w.Lmax, w.D) and v_out.shape == (w.Lmax, w.D)
     k_out[:L], v_out[:L] = gen_slab_rows(w, b, g, L)
     if L < w.Lmax:
-        if w.dtype == "bf16":
-            k_out[L:] = BF16_NAN
-            v_out[L:] = BF16_NAN
+        if w.dtype != "f32":
+            k_out[L:].view(np.uint16)[:] = BF16_NAN   # NaN in fp16 too
+            v_out[L:].view(np.uint16)[:] = BF16_NAN
         else:
             k_out[L:].view(np.uint32)[:] = F32_NAN_BITS
             v_out[L:].view(np.uint32)[:] = F32_NAN_BITS
@@ -340,7 +352,8 @@ def gen_all(w: Workload, seqlens=None, threads: int | None = None):
 
 
 def to_device(a: np.ndarray, device: str = "cuda"):
-    """Host array (uint16 bf16 bits or float32) -> torch device tensor."""
+    """Host array (uint16 bf16 bits, float16 or float32) -> torch device
+    tensor."""
     import torch
     if a.dtype == np.uint16:
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
@@ -359,14 +372,15 @@ def device_inputs(w: Workload, seqlens=None, keep_host: bool = False,
     import torch
     if seqlens is None:
         seqlens = gen_seqlens(w)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16,
+           "f32": torch.float32}[w.dtype]
     q_h = gen_q(w)
     q = to_device(q_h, device)
     shape = (w.B, w.Hkv, w.Lmax, w.D)
     k = torch.empty(shape, dtype=tdt, device=device)
     v = torch.empty(shape, dtype=tdt, device=device)
     if seqlens is not None:
-        iv = torch.int16 if w.dtype == "bf16" else torch.int32
+        iv = torch.int32 if w.dtype == "f32" else torch.int16
         k.view(iv).fill_(-1)       # all-ones bit patterns are NaN
         v.view(iv).fill_(-1)
     host = None
@@ -410,7 +424,7 @@ def pages_from_contiguous(w: Workload, k, v, device: str = "cuda"):
     import torch
     bt = gen_block_table(w)
     P, mp = w.page_size, w.max_pages
-    iv = torch.int16 if w.dtype == "bf16" else torch.int32
+    iv = torch.int32 if w.dtype == "f32" else torch.int16
     pools = []
     for src in (k, v):
         shape = ((w.num_pages, w.Hkv, P, w.D) if w.head_major

@@ -12,7 +12,7 @@ dev_inputs = wl.device_inputs
 
 
 def out_to_host(t) -> np.ndarray:
-    """Device out tensor -> uint16 bf16 bits or float32."""
+    """Device out tensor -> uint16 bf16 bits, float16 or float32."""
     import torch
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -33,14 +33,15 @@ def upload_full(w: wl.Workload, oracle_mod=None, seqlens=None,
     import torch
     if seqlens is None:
         seqlens = wl.gen_seqlens(w)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16,
+           "f32": torch.float32}[w.dtype]
     q_h = wl.gen_q(w)
     q = to_dev(q_h, device)
     shape = (w.B, w.Hkv, w.Lmax, w.D)
     k = torch.empty(shape, dtype=tdt, device=device)
     v = torch.empty(shape, dtype=tdt, device=device)
     if seqlens is not None:
-        iv = torch.int16 if w.dtype == "bf16" else torch.int32
+        iv = torch.int32 if w.dtype == "f32" else torch.int16
         k.view(iv).fill_(-1)            # NaN past every length
         v.view(iv).fill_(-1)
     ref = None

@@ -1,10 +1,11 @@
 """Comparison rule between a GPU result and the fp64 oracle (test helper).
 
-Output (bf16 or fp32 ``out``): an element passes when
-|gpu - ref| <= max(1e-2, (1 + 2^-10) * ulp_bf16(ref) / 2) for bf16, and
-|gpu - ref| <= 1e-2 for fp32.  The second bf16 bound is correct rounding
-to the nearest bf16 value, the best any bf16 output can do; it exceeds
-1e-2 only once |ref| >= 4 (ulp 2^-5 there), so below 4 the bound is the
+Output (bf16, fp16 or fp32 ``out``): an element passes when
+|gpu - ref| <= max(1e-2, (1 + 2^-10) * ulp(ref) / 2) for the 16-bit types
+(ulp of bf16 or of fp16), and |gpu - ref| <= 1e-2 for fp32.  The second
+bound is correct rounding to the nearest value of the output type, the
+best any such output can do; it exceeds 1e-2 only once |ref| >= 4 in bf16
+(ulp 2^-5 there) or |ref| >= 32 in fp16, so below that the bound is the
 plain 1e-2.  The factor 1 + 2^-10 leaves room for the fp32 accumulation's
 own error when ref lies next to a rounding midpoint.
 LSE (fp32): |gpu - ref| <= 1e-3.  NaN must meet NaN, -inf must meet -inf.
@@ -34,6 +35,14 @@ def bf16_ulp(ref: np.ndarray) -> np.ndarray:
     return np.power(2.0, e - 7)
 
 
+def f16_ulp(ref: np.ndarray) -> np.ndarray:
+    """Spacing of IEEE binary16 values at |ref| (2^-24 below 2^-14)."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    a = np.maximum(a, 2.0 ** -14)
+    e = np.floor(np.log2(a))
+    return np.power(2.0, e - 10)
+
+
 def _special_match(gpu, ref):
     both_nan = np.isnan(gpu) & np.isnan(ref)
     same_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
@@ -41,8 +50,11 @@ def _special_match(gpu, ref):
 
 
 def check_out(gpu, ref, dtype: str):
-    """gpu: uint16 bf16 bits or float32 array; ref: float64 of same shape."""
+    """gpu: uint16 bf16 bits, float16 or float32 array; ref: float64 of the
+    same shape; dtype "bf16", "f16" or "f32"."""
     ref = np.asarray(ref, dtype=np.float64)
+    if dtype == "f16":
+        assert np.asarray(gpu).dtype == np.float16
     g = bf16_to_f64(gpu) if dtype == "bf16" else np.asarray(
         gpu, dtype=np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
@@ -51,6 +63,8 @@ def check_out(gpu, ref, dtype: str):
         ok = err <= OUT_ATOL
         if dtype == "bf16":
             ok |= err <= 0.5 * bf16_ulp(ref) * HALF_ULP_SLACK
+        elif dtype == "f16":
+            ok |= err <= 0.5 * f16_ulp(ref) * HALF_ULP_SLACK
         ok |= _special_match(g, ref)
         finite = np.isfinite(ref) & np.isfinite(g)
         ferr = np.where(finite, err, 0.0)

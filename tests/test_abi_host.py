@@ -66,7 +66,7 @@ def test_status_strings_and_version(lib):
         s = fd.fd_status_string(code)
         assert s and s != "unknown status"
     assert fd.fd_status_string(12345) == "unknown status"
-    assert fd.fd_version() == 20100
+    assert fd.fd_version() == 20200
 
 
 # Fake, never dereferenced device addresses: every call below must be
@@ -330,13 +330,47 @@ def test_plan_rejections(lib):
     with pytest.raises(fd.FdError):
         fd.fd_plan(1, 8, 8, 128, 64, "f32", variant=fd.FD_VARIANT_MFMA,
                    flags=fd.FD_FLAG_UNIFIED_MAX, num_cus=256)
-    with pytest.raises(fd.FdError):        # bf16 vector path: G <= 4
+    with pytest.raises(fd.FdError):        # 16-bit vector path: G <= 4
         fd.fd_plan(1, 64, 8, 128, 64, "bf16", variant=fd.FD_VARIANT_VALU,
                    num_cus=256)
     with pytest.raises(fd.FdError):
         fd.fd_plan(1, 8, 8, 128, 64, "bf16", flags=8, num_cus=256)
     assert plan(wl.WORKLOADS["b1_gqa8_h64_d128_l65536"],
                 num_splits=1)["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,L", [
+    (1, 64, 8, 128, 65536), (4, 32, 32, 128, 32768), (64, 32, 8, 128, 4096),
+    (1, 8, 8, 64, 1024), (2, 16, 2, 256, 1700), (1, 64, 2, 128, 1500),
+    (3, 8, 8, 128, 300)])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_fp16_plans_like_bf16(lib, B, Hq, Hkv, D, L, varlen):
+    # fp16 rows have the bf16 rows' size and run on the same matrix-core
+    # pass, so every planner decision is the same.
+    pb = fd.fd_plan(B, Hq, Hkv, D, L, "bf16", varlen=varlen, num_cus=256)
+    ph = fd.fd_plan(B, Hq, Hkv, D, L, "f16", varlen=varlen, num_cus=256)
+    assert ph == pb
+    assert fd.fd_workspace_bytes(B, Hq, Hkv, D, L, "f16", varlen=varlen) == \
+        fd.fd_workspace_bytes(B, Hq, Hkv, D, L, "bf16", varlen=varlen)
+
+
+def test_fp16_entry_point_rules(lib):
+    # unified maximum: bf16 and fp16, never fp32
+    fd.fd_plan(1, 8, 8, 128, 4096, "f16", flags=fd.FD_FLAG_UNIFIED_MAX,
+               num_cus=256)
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(1, 8, 8, 128, 4096, "f32", flags=fd.FD_FLAG_UNIFIED_MAX,
+                   num_cus=256)
+    # the 16-bit vector-ALU pass takes groups of at most 4 query heads
+    p = fd.fd_plan(1, 32, 8, 128, 4096, "f16", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_VALU
+    with pytest.raises(fd.FdError):
+        fd.fd_plan(1, 64, 8, 128, 64, "f16", variant=fd.FD_VARIANT_VALU,
+                   num_cus=256)
+    # paged and several-token plans accept fp16
+    p = fd.fd_plan_ex(1, 2, 8, 8, 128, 4096, "f16", paged=True, num_cus=256)
+    assert p["variant"] == fd.FD_VARIANT_MFMA
 
 
 def test_plan_scales_with_cu_count(lib):
@@ -413,7 +447,7 @@ def call_paged(lib, q=A, k=A, v=A, bt=A, max_pages=4, page_size=32,
     (dict(Tq=0), fd.FD_ERR_INVALID_ARG),
     (dict(Tq=3, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # 129 per KV head
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),
-    (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),        # bf16 or fp32 only
+    (dict(dtype=3), fd.FD_ERR_UNSUPPORTED),        # bf16, fp32 or fp16
     (dict(dtype=1, Tq=3, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),
     (dict(Hq=258, Hkv=2), fd.FD_ERR_UNSUPPORTED),    # 129 heads per KV head
@@ -444,7 +478,7 @@ def call_mq(lib, q=A, k=A, v=A, seqlens=None, B=1, Tq=2, Hq=8, Hkv=8,
     (dict(Tq=17, Hq=8, Hkv=8), fd.FD_ERR_UNSUPPORTED),   # 17 columns
     (dict(Tq=17, Hq=16, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # no split fits
     (dict(Tq=2, Hq=1032, Hkv=8), fd.FD_ERR_UNSUPPORTED),  # 129 per KV head
-    (dict(dtype=2), fd.FD_ERR_UNSUPPORTED),
+    (dict(dtype=3), fd.FD_ERR_UNSUPPORTED),
     (dict(Tq=1, dtype=-1), fd.FD_ERR_UNSUPPORTED),
     (dict(Tq=17, Hq=32, Hkv=8, dtype=1), fd.FD_ERR_UNSUPPORTED),
     (dict(B=1 << 20, Tq=16, Hq=128, Hkv=128), fd.FD_ERR_UNSUPPORTED),
@@ -507,7 +541,7 @@ def call_uni(lib, q=A, k=A, v=A, seqlens=None, B=1, Hq=8, Hkv=8, D=128,
     (dict(phi=float("nan")), fd.FD_ERR_INVALID_ARG),
     (dict(phi=float("inf")), fd.FD_ERR_INVALID_ARG),
     (dict(phi=-float("inf")), fd.FD_ERR_INVALID_ARG),
-    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),          # bf16 only
+    (dict(dtype=1), fd.FD_ERR_UNSUPPORTED),          # 16-bit only
     (dict(q=None), fd.FD_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fd.FD_ERR_INVALID_ARG),
     (dict(D=96), fd.FD_ERR_UNSUPPORTED),

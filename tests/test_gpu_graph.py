@@ -31,7 +31,7 @@ def torch():
 
 def _same(torch, a, b):
     """Bitwise equality of two bf16 or fp32 tensors."""
-    it = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    it = torch.int32 if a.dtype == torch.float32 else torch.int16
     return torch.equal(a.view(it), b.view(it))
 
 
@@ -90,7 +90,7 @@ def _replays_match_eager(torch, g, q, outs_g, eager, reps, tag):
 
 
 @pytest.mark.parametrize("flags", [0, fd.FD_FLAG_FUSED_MERGE])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_captured_paged_decode_with_caller_workspace(torch, flags, dtype):
     w = wl.EXTRA_WORKLOADS["paged_hm_p64_b1_gqa8_h64_d128_l65536"].with_(
         Lmax=4096, dtype=dtype)
@@ -117,7 +117,7 @@ def test_captured_paged_decode_with_caller_workspace(torch, flags, dtype):
         assert int(ws[:plan["ticket_bytes"]].count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_captured_multiquery_decode_with_caller_workspace(torch, dtype):
     w = wl.EXTRA_WORKLOADS["mq2_b1_gqa8_h64_d128_l65536"].with_(Lmax=4096,
                                                                  dtype=dtype)

@@ -35,8 +35,9 @@ def _note(msg):
 
 
 def _bits(torch, t):
-    """The raw bits of a bf16 or fp32 tensor, for bitwise comparisons."""
-    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+    """The raw bits of a bf16, fp16 or fp32 tensor, for bitwise
+    comparisons."""
+    return t.view(torch.int32 if t.dtype == torch.float32 else torch.int16)
 
 
 def _assert_parity(out, lse, ref_o, ref_l, tag, dtype="bf16"):
@@ -100,7 +101,7 @@ PAGED_SHAPES = [
                               f"_P{s[5]}" for s in PAGED_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (5, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm,
                               dtype):
     B, Hq, Hkv, D, L, P, sls = shape
@@ -121,7 +122,7 @@ def test_paged_matches_oracle(torch, oracle_mod, shape, splits, flags, hm,
 
 
 @pytest.mark.parametrize("hm", [False, True])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_paged_table_entries_past_the_length_are_not_read(torch, hm, dtype):
     w = wl.Workload("paged_tail", B=3, Hq=16, Hkv=2, D=128, Lmax=1024,
                     dtype=dtype, seed=47, page_size=64, head_major=hm)
@@ -139,7 +140,7 @@ def test_paged_table_entries_past_the_length_are_not_read(torch, hm, dtype):
 
 
 @pytest.mark.parametrize("hm", [False, True])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_paged_equals_contiguous_bitwise(torch, hm, dtype):
     # Same lengths, so the same plan; the pool holds the same rows (G = 8:
     # fp32 runs on the matrix cores either way).
@@ -200,7 +201,7 @@ PAGED_MQ_SHAPES = [
                               f"_L{s[5]}_P{s[6]}" for s in PAGED_MQ_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (7, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_paged_multiquery_matches_oracle(torch, oracle_mod, shape, splits,
                                          flags, hm, dtype):
     B, Tq, Hq, Hkv, D, L, P, sls = shape
@@ -263,7 +264,7 @@ MQ_SHAPES = [
                               f"_L{s[5]}" for s in MQ_SHAPES])
 @pytest.mark.parametrize("splits,flags", [(0, 0), (1, 0), (9, 0),
                                           (0, fd.FD_FLAG_FUSED_MERGE)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_multiquery_matches_oracle(torch, oracle_mod, shape, splits, flags,
                                    dtype):
     B, Tq, Hq, Hkv, D, L, sls = shape
@@ -285,7 +286,7 @@ def test_multiquery_matches_oracle(torch, oracle_mod, shape, splits, flags,
     _assert_parity(out, lse, ref_o, ref_l, f"mq {shape}", dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod,
                                                        dtype):
     # 32-key chunks: the last Tq - 1 keys straddle a chunk edge for some
@@ -293,8 +294,8 @@ def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod,
     # 16-key halves, a half edge).
     w = wl.Workload("mq_edges", B=8, Hq=8, Hkv=2, D=128, Lmax=256,
                     dtype=dtype, seed=70, Tq=4)
-    seqlens = np.array([256, 255, 226, 225, 224, 33, 32, 4] if dtype ==
-                       "bf16" else [256, 242, 241, 209, 18, 17, 16, 2],
+    seqlens = np.array([256, 255, 226, 225, 224, 33, 32, 4] if dtype !=
+                       "f32" else [256, 242, 241, 209, 18, 17, 16, 2],
                        np.int32)
     q, k, v, _ = _gen_with(w, seqlens)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
@@ -308,7 +309,7 @@ def test_multiquery_causal_boundary_inside_every_chunk(torch, oracle_mod,
                        dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_multiquery_one_token_is_decode_bitwise(torch, dtype):
     w = wl.Workload("mq1", B=3, Hq=32, Hkv=4, D=128, Lmax=2000,
                     dtype=dtype, seed=71)

@@ -5,7 +5,8 @@ still span several 32-key tiles, several chunks and a ragged tail, for all
 five workload shapes, every kernel variant and forced split counts; plus
 edge lengths, NaN padding, determinism, streams/workspaces and negative
 controls that show the comparison can fail.  The rule (tests/parity.py):
-|out - ref| <= 1e-2 or faithful bf16 rounding, |lse - ref| <= 1e-3.
+|out - ref| <= 1e-2 or correct rounding to the output type,
+|lse - ref| <= 1e-3.
 """
 import math
 
@@ -62,6 +63,19 @@ SMALL = {
         B=2, Hq=4, Hkv=2, D=256, Lmax=900),
     "gqa32_d256": W["b1_gqa8_h64_d128_l65536"].with_(B=1, Hq=32, Hkv=1, D=256,
                                                      Lmax=700),
+    # fp16 caches (the same value recipe rounded to IEEE binary16)
+    "f16_b1_gqa8": W["b1_gqa8_h64_d128_l65536"].with_(Lmax=4133,
+                                                      dtype="f16"),
+    "f16_mha_peaked": W["b4_mha_h32_d128_l32768_peaked"].with_(
+        B=2, Hq=8, Hkv=8, Lmax=3001, dtype="f16"),
+    "f16_varlen_gqa8": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=6, Lmax=4096, varlen=(1, 4096), dtype="f16"),
+    "f16_gqa4_d64": W["b64_gqa4_h32_d128_l4096"].with_(B=3, D=64, Lmax=517,
+                                                       dtype="f16"),
+    "f16_gqa8_d256": W["b1_gqa8_h64_d128_l65536"].with_(
+        B=2, Hq=16, Hkv=2, D=256, Lmax=1700, dtype="f16"),
+    "f16_gqa32_d128": W["b1_gqa8_h64_d128_l65536"].with_(
+        B=2, Hq=64, Hkv=2, Lmax=1500, dtype="f16"),
 }
 
 
@@ -132,7 +146,8 @@ def test_small_workloads_match_oracle(cuda, oracle_mod, name, num_splits):
 
 @pytest.mark.parametrize("G,D,dtype", [(8, 128, "bf16"), (1, 128, "bf16"),
                                        (4, 64, "bf16"), (1, 64, "f32"),
-                                       (2, 128, "f32")])
+                                       (2, 128, "f32"), (8, 128, "f16"),
+                                       (2, 64, "f16")])
 @pytest.mark.parametrize("num_splits", [0, 1, 4])
 def test_edge_lengths_with_nan_padding(cuda, oracle_mod, G, D, dtype,
                                        num_splits):

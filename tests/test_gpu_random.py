@@ -7,7 +7,8 @@ oracle (at most a few hundred thousand key rows per case) while spanning
 several tiles, chunks and ragged tails; some cases draw 60-80 short
 sequences, whose work lists go past one round of workgroups, and the long
 cases caches of up to 24k keys.  The rule is the suite's (tests/parity.py):
-|out - ref| <= max(1e-2, half a bf16 ulp of ref), |lse - ref| <= 1e-3.
+|out - ref| <= max(1e-2, half an ulp of ref in the output type),
+|lse - ref| <= 1e-3.
 """
 import numpy as np
 import pytest
@@ -60,6 +61,8 @@ def draw_case(i):
         G *= 4               # past 16 query rows per KV head, also without a draw
     if i % 13 == 7:
         D = 256              # head dimension 256, also without a draw
+    if dtype == "bf16" and i % 5 == 3:
+        dtype = "f16"        # fp16 caches, also without a draw
     return dict(kind=kind, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=Lmax,
                 dtype=dtype, seqlens=seqlens, Tq=Tq, splits=splits,
                 flags=flags, page=page, head_major=head_major, phi=phi,

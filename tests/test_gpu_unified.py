@@ -30,6 +30,10 @@ SMALL = {
                                                    Lmax=1999),
     "gqa16_d128": W["b1_gqa8_h64_d128_l65536"].with_(B=1, Hq=32, Hkv=2,
                                                      Lmax=777),
+    "f16_b1_gqa8": W["b1_gqa8_h64_d128_l65536"].with_(Lmax=4133,
+                                                      dtype="f16"),
+    "f16_varlen_gqa8": W["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=6, Lmax=4096, varlen=(1, 4096), dtype="f16"),
 }
 
 
@@ -88,6 +92,28 @@ def test_fallback_reproduces_the_exact_pass_bitwise(torch, phi, splits):
     torch.cuda.synchronize()
     assert torch.equal(uo.view(torch.int16), eo.view(torch.int16))
     assert torch.equal(ul, el)
+
+
+@pytest.mark.parametrize("phi,fallback", [(-20.0, True), (20.0, True),
+                                          (-3.0, False), (4.0, False)])
+def test_fp16_window_is_narrower(torch, oracle_mod, phi, fallback):
+    # fp16 P operands stop at 65504: a chunk row whose largest score lies
+    # more than 14 ln 2 (~9.7) from phi is recomputed with the running
+    # maximum (bitwise fd_decode_ex); within it the unified pass stands
+    # and still meets the oracle.
+    w = SMALL["f16_varlen_gqa8"]
+    q, k, v, sl, seqlens, host = inputs("f16_varlen_gqa8", w)
+    uo, ul = fd.fd_decode_unified_max(q, k, v, sl, w.scale, phi)
+    eo, el = fd.fd_decode_ex(q, k, v, sl, w.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mod.decode(*host, seqlens, w.scale)
+    _parity(w, uo, ul, ref_o, ref_l, f"fp16 window phi={phi}")
+    same = (torch.equal(uo.view(torch.int16), eo.view(torch.int16))
+            and torch.equal(ul, el))
+    if fallback:
+        assert same
+    else:
+        assert not same
 
 
 def test_fallback_in_some_chunks_only(torch, oracle_mod):

@@ -61,3 +61,35 @@ def test_fp32_and_special_values():
     assert check_lse(np.array([2.0009, -np.inf]), np.array([2.0, -np.inf]))[0]
     assert not check_lse(np.array([2.0011]), np.array([2.0]))[0]
     assert not check_lse(np.array([-np.inf]), np.array([-50.0]))[0]
+
+
+def test_fp16_nearest_value_passes_and_far_ones_fail():
+    rng = np.random.default_rng(3)
+    # numpy's float64 -> float16 conversion rounds to nearest even
+    ref = np.concatenate([rng.uniform(-60, 60, 20000), [0.0, 32.0, -63.9]])
+    ok, rep = check_out(ref.astype(np.float16), ref, "f16")
+    assert ok, rep
+    # below 32 the bound is the plain 1e-2: 0.012 away fails
+    small = rng.uniform(-31.9, 31.9, 2000)
+    off = (small + 0.012 * np.sign(small)).astype(np.float16)
+    bad = np.abs(off.astype(np.float64) - small) > 1e-2
+    assert bad.any()
+    for r, g in zip(small[bad][:200], off[bad][:200]):
+        assert not check_out(np.array([g]), np.array([r]), "f16")[0], (r, g)
+    # from 32 on (ulp 2^-5) correct rounding is the bound: the nearest
+    # fp16 value passes, the next one beyond it fails
+    big = rng.uniform(32.0, 64.0, 2000)
+    near = big.astype(np.float16)
+    far = np.where(near.astype(np.float64) < big,
+                   np.nextafter(near, np.float16(np.inf)),
+                   np.nextafter(near, np.float16(-np.inf)))
+    assert check_out(near, big, "f16")[0]
+    assert np.all(np.abs(far.astype(np.float64) - big) > 1e-2)
+    for r, f in zip(big[:200], far[:200]):
+        assert not check_out(np.array([f]), np.array([r]), "f16")[0], (r, f)
+
+
+def test_fp16_rule_needs_fp16_results():
+    import pytest
+    with pytest.raises(AssertionError):
+        check_out(np.array([1.0], np.float32), np.array([1.0]), "f16")

@@ -154,3 +154,37 @@ def test_threaded_generation_matches_one_slab_at_a_time():
         np.testing.assert_array_equal(vr, v1[:L])
     k_serial = wl.gen_all(w, seqlens=seqlens, threads=1)[1]
     np.testing.assert_array_equal(k, k_serial)
+
+
+def test_fp16_inputs_are_the_same_draws_rounded_to_fp16():
+    torch = pytest.importorskip("torch")
+    w = wl.WORKLOADS["varlen_b16_gqa8_h64_d128_lmax131072"].with_(
+        B=3, Hq=4, Hkv=2, Lmax=300, varlen=(1, 300))
+    wh = w.with_(dtype="f16")
+    q, k, v, sl = wl.gen_all(w)
+    qh, kh, vh, slh = wl.gen_all(wh)
+    np.testing.assert_array_equal(sl, slh)
+    assert qh.dtype == np.float16 and kh.dtype == np.float16
+    assert wh.elem_bytes == 2
+    # the same float32 draws, rounded to nearest even as torch rounds them
+    x = _f32_of_generator(w)
+    np.testing.assert_array_equal(
+        qh.view(np.uint16),
+        torch.from_numpy(x).to(torch.float16).numpy().view(np.uint16))
+    for b in range(w.B):
+        L = int(sl[b])
+        for arr_h, arr_b in ((kh, k), (vh, v)):
+            # valid rows: fp16 of the value whose bf16 rounding the bf16
+            # workload holds; padding: NaN
+            assert np.all(np.isnan(arr_h[b, :, L:]))
+            assert not np.isnan(arr_h[b, :, :L]).any()
+            near = np.abs(arr_h[b, :, :L].astype(np.float32)
+                          - wl.bf16_to_f32(arr_b[b, :, :L]))
+            assert near.max() <= 2.0 ** -7 * max(
+                1.0, float(np.abs(arr_h[b, :, :L].astype(np.float32)).max()))
+
+
+def _f32_of_generator(w):
+    """q's float32 draws, from the generator's own stream."""
+    shape = (w.B, w.Hq, w.D)
+    return wl._rng(w.seed, 0).standard_normal(shape, dtype=np.float32)

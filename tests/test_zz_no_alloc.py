@@ -35,7 +35,8 @@ def _note(msg):
 
 
 def _bits(torch, t):
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16,
+                                              torch.float16) else t
 
 
 def _check_case(torch, oracle_mod, w, seqlens, num_splits, tag):
@@ -76,6 +77,9 @@ def test_two_calls_in_a_row_second_smaller(torch, oracle_mod):
     f32 = wl.ALL_WORKLOADS["f32_b1_gqa8_h64_d128_l65536"].with_(Lmax=2000)
     p4 = _check_case(torch, oracle_mod, f32, None, 0, "fourth, fp32 MFMA")
     assert p4["variant"] == fd.FD_VARIANT_MFMA
+    # an fp16 cache
+    f16 = wl.ALL_WORKLOADS["f16_b1_gqa8_h64_d128_l65536"].with_(Lmax=2500)
+    _check_case(torch, oracle_mod, f16, None, 0, "fifth, fp16")
 
 
 def test_single_pass_plan_uses_no_scratch(torch, oracle_mod):
