@@ -338,7 +338,7 @@ __device__ __forceinline__ floatx4 mfma32(f16x8 a, f16x8 b, floatx4 c) {
 
 // ---------------------------------------------------------------------------
 // Merge of the workgroup's softmax states and the chunk's store (the
-// vector-ALU kernel, and the matrix-core kernel under the fused merge).
+// vector-ALU kernel).
 //
 // Slot sl holds, for query row h of the group: running max m (log2 units of
 // the scaled score), running sum l, and the unnormalised accumulator
@@ -405,28 +405,36 @@ __device__ void merge_and_store(const float *sm_m, const float *sm_l,
 //
 // Ordering across MI355X's eight XCDs, whose L2 caches are not coherent
 // with each other:
-//   writers  every partial is an agent-scope atomic store, which gfx950
-//            writes through its XCD's L2 to the device coherence point;
-//            each thread then waits for all of its memory operations to
+//   writers  every partial is stored with the cache policy of an
+//            agent-scope atomic store (sc1), which gfx950 writes through
+//            its XCD's L2 to the device coherence point: 16-byte stores
+//            (store_through) from the matrix-core kernels, agent-scope
+//            atomic stores of 4 bytes from the vector-ALU kernel.  Each
+//            thread then waits for all of its memory operations to
 //            complete (s_waitcnt 0) before the workgroup barrier, and only
 //            then does one thread take the ticket (an agent-scope atomic).
 //            This is the part of an agent-scope release that concerns
-//            atomic stores; the other part, an L2 write-back for plain
-//            stores, is left out on purpose: there are none to publish,
-//            and it would write back the XCD's whole L2 once per
+//            written-through stores; the other part, an L2 write-back of
+//            ordinary stores, is left out on purpose: there are none to
+//            publish, and it would write back the XCD's whole L2 once per
 //            workgroup (measured: far slower than a second launch).
 //   reader   the last workgroup issues an agent-scope acquire fence after
 //            its ticket came back (one L1/L2 invalidate per group, not per
-//            workgroup) and reads the partials with agent-scope atomic
-//            loads.
+//            workgroup); its ordinary 16-byte loads of the partials then
+//            miss the invalidated caches and read the coherence point.
 //
 // The merge spreads the group's G x D outputs over the workgroup as
 // (row, 4 columns) items; when there are fewer items than threads, each
 // item's chunks are split over `slices` threads whose states meet in LDS.
 constexpr int kTailBatch = 16;
 
-__device__ __forceinline__ float load_coherent(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// 16 bytes written through the XCD's L2 to the device coherence point
+// (sc1: the cache policy of an agent-scope atomic store), for a partial
+// that another workgroup of the same launch reads.
+__device__ __forceinline__ void store_through(float *p, float4 v) {
+  const floatx4 t = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(t)
+               : "memory");
 }
 
 struct TailState {
@@ -437,10 +445,7 @@ struct TailState {
 // Folds chunks s = s_first, s_first + s_step, ... of item `it` (q-tile
 // column it / (D/4), output columns 4 (it % (D/4)) ..) into a TailState,
 // kTailBatch chunks per step with all of a step's loads issued first.
-// COHERENT: the partials were written by other workgroups of the same
-// launch (the fused merge) and are read with agent-scope loads; otherwise
-// (a later kernel) with plain 16-byte loads.
-template <int D, bool COHERENT>
+template <int D>
 __device__ TailState merge_item(const Work &w, const PartLayout &pl, int it,
                                 int s_first, int s_step,
                                 const float *__restrict__ o_part,
@@ -462,14 +467,8 @@ __device__ TailState merge_item(const Work &w, const PartLayout &pl, int it,
       const int sc = s < w.nb ? s : s0;
       const float *l1 = lp + (size_t)sc * ls_step;
       const float *o4 = op + (size_t)sc * o_step;
-      if constexpr (COHERENT) {
-        ls[j] = s < w.nb ? load_coherent(l1) : FD_NEG_INF;
-        ov[j] = make_float4(load_coherent(o4), load_coherent(o4 + 1),
-                            load_coherent(o4 + 2), load_coherent(o4 + 3));
-      } else {
-        ls[j] = s < w.nb ? *l1 : FD_NEG_INF;
-        ov[j] = *reinterpret_cast<const float4 *>(o4);
-      }
+      ls[j] = s < w.nb ? *l1 : FD_NEG_INF;
+      ov[j] = *reinterpret_cast<const float4 *>(o4);
     }
     float mb = ls[0];
 #pragma unroll
@@ -522,7 +521,7 @@ __device__ void store_item(const Work &w, int G, int Tq, int Hq, int it,
 // [it0, it1) of the group's G * Tq * D / 4 (row, 4 columns) items, with
 // the whole workgroup (the fused path's last workgroup takes all items;
 // the merge pass splits a group's items over several workgroups).
-template <int D, typename OutT, bool COHERENT>
+template <int D, typename OutT>
 __device__ void group_merge(const Work &w, const PartLayout &pl, int it0,
                             int it1, const float *__restrict__ o_part,
                             const float *__restrict__ lse_part,
@@ -536,7 +535,7 @@ __device__ void group_merge(const Work &w, const PartLayout &pl, int it0,
   const int slices = max(1, T / items);
   if (slices == 1) {
     for (int it = it0 + tid; it < it1; it += T) {
-      const TailState st = merge_item<D, COHERENT>(w, pl, it, 0, 1, o_part,
+      const TailState st = merge_item<D>(w, pl, it, 0, 1, o_part,
                                                    lse_part);
       store_item<D, OutT>(w, G, Tq, Hq, it, st.M, st.W, st.acc, out, lse);
     }
@@ -546,7 +545,7 @@ __device__ void group_merge(const Work &w, const PartLayout &pl, int it0,
   float4 *sA = reinterpret_cast<float4 *>(scratch + 2 * T);
   TailState st{FD_NEG_INF, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   if (tid < items * slices)
-    st = merge_item<D, COHERENT>(w, pl, it0 + tid % items, tid / items,
+    st = merge_item<D>(w, pl, it0 + tid % items, tid / items,
                                  slices, o_part, lse_part);
   sM[tid] = st.M;
   sW[tid] = st.W;
@@ -599,8 +598,8 @@ __device__ void merge_group_if_last(const Work &w, const PartLayout &pl,
   // Reader side: acquire at agent scope after the ticket, then read the
   // partials with agent-scope atomic loads.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  group_merge<D, OutT, true>(w, pl, 0, pl.G * pl.Tq * (D / 4), o_part,
-                             lse_part, out, lse, scratch);
+  group_merge<D, OutT>(w, pl, 0, pl.G * pl.Tq * (D / 4), o_part, lse_part,
+                       out, lse, scratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1123,8 +1122,8 @@ constexpr float kUniRange = 64.f;
 template <>
 constexpr float kUniRange<_Float16> = 14.f;
 
-// End of a chunk in the matrix-core kernel (direct and partial modes): the
-// wavefronts' states are merged with one weight per (wavefront, column).
+// End of a chunk in the matrix-core kernels: the wavefronts' states are
+// merged with one weight per (wavefront, column).
 // Every wavefront publishes its column maxima m and sums l, and wavefronts
 // 1.. park their accumulators in LDS as 16-byte vectors; after one barrier
 // wavefront 0 alone forms M = max m, W = sum 2^(m - M) l and the weights
@@ -1132,10 +1131,14 @@ constexpr float kUniRange<_Float16> = 14.f;
 // stores its lane's runs of four consecutive output columns,
 // acc_col(4 e4, 4 q4 + j), with vector stores.  A column that saw no key
 // gets out 0 and lse -inf.  OutT: uint16_t (bf16 bits), _Float16 (both
-// rounded to nearest even) or float.  ROWS: the accumulator layout (acc_col); with any of
-// them a lane's blocks 4 e4 .. 4 e4 + 3 of one j are four consecutive
-// columns.
-template <int D, int NW, typename OutT = uint16_t, int ROWS = 0>
+// rounded to nearest even) or float.  ROWS: the accumulator layout
+// (acc_col); with any of them a lane's blocks 4 e4 .. 4 e4 + 3 of one j
+// are four consecutive columns.  FUSED: the partial is read by another
+// workgroup of the same launch (the fused merge), so it is written through
+// to the device coherence point; a separate instantiation keeps the
+// two-launch path's code as it is.
+template <int D, int NW, typename OutT = uint16_t, int ROWS = 0,
+          bool FUSED = false>
 __device__ __forceinline__ void wave_merge_store(
     float *sm_m, float *sm_l, float *sm_o, int wave, int lane, int n16,
     int q4, int ncol, float m, float l, const floatx4 (&acc)[D / 16],
@@ -1204,6 +1207,8 @@ __device__ __forceinline__ void wave_merge_store(
         } else {
           *reinterpret_cast<float4 *>(out + row * D + d0) = o;
         }
+      } else if constexpr (FUSED) {
+        store_through(o_part + row * D + d0, o);
       } else {
         *reinterpret_cast<float4 *>(o_part + row * D + d0) = o;
       }
@@ -1213,6 +1218,9 @@ __device__ __forceinline__ void wave_merge_store(
     const float ls = M == FD_NEG_INF ? FD_NEG_INF : (M + log2_f(W)) * kLn2;
     if (mode == kModeDirect)
       lse[row] = ls;
+    else if constexpr (FUSED)
+      __hip_atomic_store(lse_part + row, ls, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     else
       lse_part[row] = ls;
   }
@@ -1225,7 +1233,8 @@ __device__ __forceinline__ void wave_merge_store(
 // before).
 // UNI: unified-maximum softmax against phi2 (log2 units of the scaled
 // score) with an exact fallback.
-template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E,
+          bool FUSED>
 __device__ __forceinline__ void chunk_pass(
     const Work &w, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ seqlens,
@@ -1313,33 +1322,18 @@ __device__ __forceinline__ void chunk_pass(
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (mode != kModeFused) {
-    wave_merge_store<D, NW, OutT, kBf16Rows<D>>(
-        sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l, acc, w, pl, mode,
-        out, lse, o_part, lse_part);
-    return;
-  }
-  if (n16 < ncol) {
-    if (q4 == 0) {
-      sm_m[wave * 16 + n16] = m;
-      sm_l[wave * 16 + n16] = l;
-    }
-    float *o = sm_o + (wave * 16 + n16) * (D + 1);
-#pragma unroll
-    for (int e = 0; e < VW; ++e)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[acc_col<VW, kBf16Rows<D>>(e, q4 * 4 + j)] = acc[e][j];
-  }
-  __syncthreads();
-  merge_and_store<D, OutT>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out,
-                               lse, o_part, lse_part);
-  if (mode == kModeFused)
-    merge_group_if_last<D, OutT>(w, pl, o_part, lse_part, tickets, out,
-                                     lse, sm_o, &sm_flag);
+  // FUSED (mode kModeFused) is its own instantiation, so that the
+  // two-launch kernels carry no code of the single-launch merge.
+  wave_merge_store<D, NW, OutT, kBf16Rows<D>, FUSED>(
+      sm_m, sm_l, sm_o, wave, lane, n16, q4, ncol, m, l, acc, w, pl, mode,
+      out, lse, o_part, lse_part);
+  if constexpr (FUSED)
+    merge_group_if_last<D, OutT>(w, pl, o_part, lse_part, tickets, out, lse,
+                                 sm_o, &sm_flag);
 }
 
-template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool UNI, typename E,
+          bool FUSED>
 __global__ __launch_bounds__(NW * 64, (kBlocksPerCU<NW, D>))
 void split_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
@@ -1357,7 +1351,7 @@ void split_mfma_kernel(
   // spills.)
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
-  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E>(w0, q, kc, vc, seqlens, pk, B, Hq,
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E, FUSED>(w0, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, kv_rep, G, Tq, Lmax, C, S,
                                         scale_log2, phi2, mode, chunk_major,
                                         out, lse, o_part, lse_part, tickets);
@@ -1370,7 +1364,7 @@ void split_mfma_kernel(
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
-  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E>(w1, q, kc, vc, seqlens, pk, B, Hq,
+  chunk_pass<D, NW, PAGED, CAUSAL, UNI, E, FUSED>(w1, q, kc, vc, seqlens, pk, B, Hq,
                                         Hkv, kv_rep, G, Tq, Lmax, C, S,
                                         scale_log2, phi2, mode, chunk_major,
                                         out, lse, o_part, lse_part, tickets);
@@ -1488,7 +1482,7 @@ __device__ __forceinline__ void f32_half_compute(
 // into the chunk's last two tiles, each some wavefront's last, so only a
 // wavefront's last two halves can need masks.  PAGED: the halves' pool
 // rows are staged 64 at a time (page_rows, one table entry per lane).
-template <int D, int NW, bool PAGED, bool CAUSAL>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool FUSED>
 __device__ __forceinline__ void f32_chunk_pass(
     const Work &w, const float *__restrict__ q, const float *__restrict__ kc,
     const float *__restrict__ vc, const PagedKV &pk, int Hq, int Hkv,
@@ -1632,34 +1626,17 @@ __device__ __forceinline__ void f32_chunk_pass(
 
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (mode != kModeFused) {
-    wave_merge_store<D, NW, float, 4>(sm_m, sm_l, sm_o, wave, lane, n16, q4,
-                                      ncol, m, l, acc, w, pl, mode, out, lse,
-                                      o_part, lse_part);
-    return;
-  }
-  if (n16 < ncol) {
-    if (q4 == 0) {
-      sm_m[wave * 16 + n16] = m;
-      sm_l[wave * 16 + n16] = l;
-    }
-    float *o = sm_o + (wave * 16 + n16) * (D + 1);
-#pragma unroll
-    for (int e = 0; e < VW; ++e)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[acc_col<VW, 4>(e, q4 * 4 + j)] = acc[e][j];
-  }
-  __syncthreads();
-  merge_and_store<D, float>(sm_m, sm_l, sm_o, NW, 16, pl, w, mode, out, lse,
-                            o_part, lse_part);
-  merge_group_if_last<D, float>(w, pl, o_part, lse_part, tickets, out, lse,
-                                sm_o, &sm_flag);
+  wave_merge_store<D, NW, float, 4, FUSED>(sm_m, sm_l, sm_o, wave, lane, n16,
+                                           q4, ncol, m, l, acc, w, pl, mode,
+                                           out, lse, o_part, lse_part);
+  if constexpr (FUSED)
+    merge_group_if_last<D, float>(w, pl, o_part, lse_part, tickets, out, lse,
+                                  sm_o, &sm_flag);
 }
 
 // Launched exactly like split_mfma_kernel (the same plan, grid and work
 // list; a workgroup may take a second chunk).
-template <int D, int NW, bool PAGED, bool CAUSAL>
+template <int D, int NW, bool PAGED, bool CAUSAL, bool FUSED>
 __global__ __launch_bounds__(NW * 64, (kBlocksPerCU<NW, D>))
 void split_mfma_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc,
@@ -1671,7 +1648,7 @@ void split_mfma_f32_kernel(
     int *__restrict__ tickets) {
   const Work w0 = find_work(blockIdx.x, seqlens, B, Hkv, Lmax, C, direct);
   if (!w0.valid) return;
-  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w0, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
+  f32_chunk_pass<D, NW, PAGED, CAUSAL, FUSED>(w0, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
                                        Tq, Lmax, S, scale_log2, mode,
                                        chunk_major, out, lse, o_part,
                                        lse_part, tickets);
@@ -1681,7 +1658,7 @@ void split_mfma_f32_kernel(
   const Work w1 = find_work((int)id1, seqlens, B, Hkv, Lmax, C, false);
   if (!w1.valid) return;
   __syncthreads();  // the second chunk reuses the LDS
-  f32_chunk_pass<D, NW, PAGED, CAUSAL>(w1, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
+  f32_chunk_pass<D, NW, PAGED, CAUSAL, FUSED>(w1, q, kc, vc, pk, Hq, Hkv, kv_rep, G,
                                        Tq, Lmax, S, scale_log2, mode,
                                        chunk_major, out, lse, o_part,
                                        lse_part, tickets);
@@ -2007,8 +1984,7 @@ __global__ __launch_bounds__(kGroupMergeThreads) void group_combine_kernel(
   const int it0 = blockIdx.y * share;
   const int it1 = min(items, it0 + share);
   if (it0 >= it1) return;
-  group_merge<D, OutT, false>(w, pl, it0, it1, o_part, lse_part, out, lse,
-                              sm);
+  group_merge<D, OutT>(w, pl, it0, it1, o_part, lse_part, out, lse, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -2086,13 +2062,20 @@ hipError_t launch_mfma(const Plan &p, const LaunchArgs &a, float sl2,
   OutT *out = static_cast<OutT *>(a.out);
 #define FD_MFMA_CASE(NWV)                                                    \
   case NWV:                                                                  \
-    hipLaunchKernelGGL((split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI, E>),   \
-                       grid,                                                 \
-                       dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged,   \
-                       p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax,        \
-                       p.chunk, p.splits, sl2, phi2, part, p.direct,         \
-                       p.chunk_major,                                        \
-                       out, a.lse, a.o_part, a.lse_part, a.tickets);         \
+    if (p.fused)                                                             \
+      hipLaunchKernelGGL(                                                    \
+          (split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI, E, true>), grid,    \
+          dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged, p.B, p.Hq,     \
+          p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax, p.chunk, p.splits, sl2, phi2,  \
+          part, p.direct, p.chunk_major, out, a.lse, a.o_part, a.lse_part,   \
+          a.tickets);                                                        \
+    else                                                                     \
+      hipLaunchKernelGGL(                                                    \
+          (split_mfma_kernel<D, NWV, PAGED, CAUSAL, UNI, E, false>), grid,   \
+          dim3(NWV * 64), 0, st, q, k, v, a.seqlens, a.paged, p.B, p.Hq,     \
+          p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax, p.chunk, p.splits, sl2, phi2,  \
+          part, p.direct, p.chunk_major, out, a.lse, a.o_part, a.lse_part,   \
+          a.tickets);                                                        \
     break;
   switch (p.waves) {
     FD_MFMA_CASE(2)
@@ -2109,16 +2092,24 @@ template <int D, bool PAGED, bool CAUSAL>
 hipError_t launch_mfma_f32(const Plan &p, const LaunchArgs &a, float sl2,
                            hipStream_t st) {
   if (p.waves != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4, PAGED, CAUSAL>),
-                     dim3(p.grid), dim3(4 * 64), 0, st,
-                     static_cast<const float *>(a.q),
-                     static_cast<const float *>(a.k),
-                     static_cast<const float *>(a.v), a.seqlens, a.paged,
-                     p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax, p.chunk,
-                     p.splits,
-                     sl2, mode_of(p), p.direct, p.chunk_major,
-                     static_cast<float *>(a.out), a.lse, a.o_part,
-                     a.lse_part, a.tickets);
+  const float *q = static_cast<const float *>(a.q);
+  const float *k = static_cast<const float *>(a.k);
+  const float *v = static_cast<const float *>(a.v);
+  float *out = static_cast<float *>(a.out);
+  if (p.fused)
+    hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4, PAGED, CAUSAL, true>),
+                       dim3(p.grid), dim3(4 * 64), 0, st, q, k, v, a.seqlens,
+                       a.paged, p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax,
+                       p.chunk, p.splits, sl2, mode_of(p), p.direct,
+                       p.chunk_major, out, a.lse, a.o_part, a.lse_part,
+                       a.tickets);
+  else
+    hipLaunchKernelGGL((split_mfma_f32_kernel<D, 4, PAGED, CAUSAL, false>),
+                       dim3(p.grid), dim3(4 * 64), 0, st, q, k, v, a.seqlens,
+                       a.paged, p.B, p.Hq, p.Hkv, p.kv_rep, p.G, p.Tq, p.Lmax,
+                       p.chunk, p.splits, sl2, mode_of(p), p.direct,
+                       p.chunk_major, out, a.lse, a.o_part, a.lse_part,
+                       a.tickets);
   return hipSuccess;
 }
 
