@@ -400,8 +400,9 @@ FD_API int fd_decode_multiquery(const void *q, const void *k_cache,
  * rescaling of their sums.  phi is in the units of lse (natural log of
  * the scaled score), chosen by the caller from the model's score range
  * (0 suits unit-variance scores).  Fallback: when the largest score of
- * some row of a chunk lies beyond phi +- 64 ln 2 (bf16; fp16: phi +-
- * 14 ln 2, where 2^x would overflow or lose precision), that
+ * some row of a chunk lies outside phi +- 64 ln 2 (bf16) or outside
+ * [phi, phi + 14 ln 2] (fp16), where 2^x would overflow or lose
+ * precision, that
  * chunk is recomputed with the running maximum, giving exactly the
  * fd_decode_ex result for it; either way the result is the same
  * attention within the usual rounding.  Contiguous cache, one token per

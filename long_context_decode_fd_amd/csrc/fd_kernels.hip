@@ -1111,16 +1111,22 @@ __device__ __forceinline__ void chunk_tiles(
                                       qop, scale_log2, phi2, acc, m, l);
 }
 
-// Unified maximum: a chunk column whose largest score - phi lies outside
-// +-kUniRange<E> (log2 units) is recomputed exactly.  Inside it, 2^x
-// neither overflows nor loses the terms that matter.  bf16 (fp32's
-// exponent range): sums of up to 2^31 terms of at most 2^64, and the
-// largest term at least 2^-64.  fp16, whose P operands stop at 65504 and
-// whose normals start at 2^-14: the largest term lies in [2^-14, 2^14].
+// Unified maximum: a chunk column whose largest x = score - phi (log2
+// units) lies outside [kUniLo<E>, kUniHi<E>] is recomputed exactly.
+// Inside it, 2^x neither overflows nor loses the terms that matter.  bf16
+// (fp32's exponent range): sums of up to 2^31 terms of at most 2^64, and
+// the largest term at least 2^-64.  fp16, whose P operands stop at 65504
+// and flush below 2^-24: the largest term lies in [1, 2^14], so the
+// weights lost to the flush are as small against the row's sum as in the
+// running-maximum pass, whose largest term is 1.
 template <typename E>
-constexpr float kUniRange = 64.f;
+constexpr float kUniLo = -64.f;
+template <typename E>
+constexpr float kUniHi = 64.f;
 template <>
-constexpr float kUniRange<_Float16> = 14.f;
+constexpr float kUniLo<_Float16> = 0.f;
+template <>
+constexpr float kUniHi<_Float16> = 14.f;
 
 // End of a chunk in the matrix-core kernels: the wavefronts' states are
 // merged with one weight per (wavefront, column).
@@ -1293,7 +1299,7 @@ __device__ __forceinline__ void chunk_pass(
 
   if constexpr (UNI) {
     // Unified maximum (FlashDecoding++): one pass against phi2.  If a
-    // column's largest x = score - phi2 leaves [-kUniRange, kUniRange] the
+    // column's largest x = score - phi2 leaves [kUniLo, kUniHi] the
     // fixed reference risks overflow or lost precision, and the whole
     // workgroup recomputes the chunk with the running maximum.
     chunk_tiles<D, NW, PAGED, CAUSAL, true, E>(
@@ -1302,7 +1308,7 @@ __device__ __forceinline__ void chunk_pass(
     float xm = fmaxf(m, __shfl_xor(m, 16, 64));
     xm = fmaxf(xm, __shfl_xor(xm, 32, 64));
     const bool bad = xm != FD_NEG_INF &&
-                     !(xm >= -kUniRange<E> && xm <= kUniRange<E>);
+                     !(xm >= kUniLo<E> && xm <= kUniHi<E>);
     if (__syncthreads_or(bad)) {
 #pragma unroll
       for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
