@@ -43,7 +43,8 @@ def _compare_all_rows(name, label, out, lse, ref, dtype):
 
 @pytest.mark.parametrize("name", wl.WORKLOAD_ORDER +
                          ["f32_b1_gqa8_h64_d128_l65536",
-                          "f16_b1_gqa8_h64_d128_l65536"])
+                          "f16_b1_gqa8_h64_d128_l65536",
+                          "f16_varlen_b16_gqa8_h64_d128_lmax131072"])
 def test_full_size_workload(cuda, oracle_mod, name):
     torch = cuda
     w = wl.ALL_WORKLOADS[name]
