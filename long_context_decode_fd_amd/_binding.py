@@ -455,7 +455,7 @@ def fd_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale,
                     head_major=False, workspace=None, stream=None):
     """Decode attention over a paged KV cache -- see fd.h.
 
-    q [B,Hq,D] bf16 or fp32, or [B,Tq,Hq,D] for Tq causal new tokens;
+    q [B,Hq,D] bf16, fp16 or fp32, or [B,Tq,Hq,D] for Tq causal new tokens;
     k_pages/v_pages [num_pages,page_size,Hkv,D] of q's dtype (token-major) or
     [num_pages,Hkv,page_size,D] (head_major); block_table int32
     [B,max_pages]; seqlens int32 [B] (required); all on the GPU.  Returns
@@ -509,7 +509,7 @@ def fd_decode_multiquery(q, k_cache, v_cache, seqlens, scale, out=None,
                          stream=None):
     """Tq causal query tokens per sequence -- see fd.h.
 
-    q [B,Tq,Hq,D] bf16 or fp32; k_cache/v_cache [B,Hkv,Lmax,D] of q's
+    q [B,Tq,Hq,D] bf16, fp16 or fp32; k_cache/v_cache [B,Hkv,Lmax,D] of q's
     dtype; seqlens int32 [B]
     on the GPU or None.  Returns (out [B,Tq,Hq,D], lse [B,Tq,Hq]).
     workspace: a uint8 device tensor of fd_plan_ex(B, Tq, ...)'s
